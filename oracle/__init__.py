@@ -1,0 +1,13 @@
+"""CPU oracle for exact attention (test infrastructure only).
+
+Only the test suite, the smoke check and the bench's CPU-baseline leg may import
+this package; the GPU library never does.
+"""
+from .attn_ref import (  # noqa: F401
+    attn_ref_bwd,
+    attn_ref_bwd_loop,
+    attn_ref_fwd,
+    head_backward,
+    head_forward,
+    to_f64,
+)

@@ -1,0 +1,239 @@
+"""Plain fp64 CPU oracle for exact scaled-dot-product attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the bench's
+CPU-baseline leg may import this module.  The GPU library never calls it and shares
+no code with it.
+
+Pages cited (by title and section):
+  [SA8]  "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析"
+         section 2.1 (matrix-product and softmax derivatives, the attention backward
+         chain), section 2.2 (CPU reference loop nest), Appendix A.1-A.3 (formula sheet).
+  [FAT]  "FlashAttention Triton实现中的内存访问模式优化与寄存器分配策略"
+         section 2.2 (one program per query block; running max and running sum).
+
+What is computed (the plain definition, S and P materialised, float64 throughout):
+  forward   S = scale * Q K^T                      [SA8 2.1, A.1]
+            causal: S[i, j] = -inf for key j > query i (the loop bound t2 <= t of
+            the CPU reference in [SA8 2.2]; top-left aligned, T_q == T_k)
+            P = softmax(S) row by row                [SA8 2.1, A.1]
+            O = P V                                  [SA8 2.1, A.1]
+            LSE_i = m_i + ln(sum_j exp(S_ij - m_i)),  m_i = max_j S_ij
+            (the pages' "softmax stats" [SA8 1.2, 1.3] are never defined; this
+            natural-log logsumexp is the reading taken)
+  backward  dV = P^T dO                              [SA8 2.1 step 1, A.2]
+            dP = dO V^T                              [SA8 2.1 step 2, A.2]
+            dS = P * (dP - (dP * P) 1)               [SA8 2.1 step 3, A.2]
+            dQ = scale * dS K                        [SA8 2.1 step 4, A.2]
+            dK = scale * dS^T Q                      [SA8 2.1 step 5, A.2]
+
+Layout: every tensor argument is (B, T, NH, d) (token-major, heads inside), the layout
+of the pages' output O; LSE is (B, NH, T).  Inputs may be numpy arrays or torch
+tensors of any float dtype; they are converted exactly to float64.
+
+Memory: for long sequences the per-head work is split into blocks of query rows.
+Each block still forms complete rows of S and P, and the sums over query rows that
+make up dV and dK are added block after block, so the arithmetic is the definition
+above with its sum over queries split into consecutive parts.  Under the causal mask
+the columns past a block's last query are left out: their P entries are exactly zero.
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "to_f64",
+    "head_forward",
+    "head_backward",
+    "attn_ref_fwd",
+    "attn_ref_bwd",
+    "attn_ref_bwd_loop",
+]
+
+
+def to_f64(x) -> np.ndarray:
+    """Exact upcast of a numpy array or a (CPU or GPU) torch tensor to float64."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch  # only reached when a torch tensor is passed
+
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, row0: int) -> np.ndarray:
+    """S = scale * Q K^T for query rows row0 .. row0+len(q)-1 against all given keys,
+    with the causal mask (key index > query index -> -inf)."""
+    S = scale * (q @ k.T)
+    if causal:
+        qi = np.arange(row0, row0 + q.shape[0])[:, None]
+        kj = np.arange(k.shape[0])[None, :]
+        S = np.where(kj > qi, -np.inf, S)
+    return S
+
+
+def _softmax_rows(S: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Row-wise softmax and natural-log logsumexp, shifted by the row maximum."""
+    m = S.max(axis=1, keepdims=True)
+    e = np.exp(S - m)
+    l = e.sum(axis=1, keepdims=True)
+    return e / l, (m + np.log(l))[:, 0]
+
+
+def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
+                 block_rows: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """One head: q, k (T, d_qk), v (T, d_v) float64 -> O (T, d_v), LSE (T,)."""
+    T = q.shape[0]
+    br = T if block_rows is None else block_rows
+    O = np.empty((T, v.shape[1]))
+    lse = np.empty(T)
+    for r0 in range(0, T, br):
+        r1 = min(T, r0 + br)
+        nk = r1 if causal else T          # keys past the last query are all masked
+        S = _scores(q[r0:r1], k[:nk], scale, causal, r0)
+        P, lse[r0:r1] = _softmax_rows(S)
+        O[r0:r1] = P @ v[:nk]
+    return O, lse
+
+
+def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
+                  causal: bool, block_rows: Optional[int] = None):
+    """One head: returns dQ, dK, dV and also O, LSE and D = (dP * P) 1 (all float64)."""
+    T = q.shape[0]
+    br = T if block_rows is None else block_rows
+    O = np.empty((T, v.shape[1]))
+    lse = np.empty(T)
+    D = np.empty(T)
+    dQ = np.empty_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    for r0 in range(0, T, br):
+        r1 = min(T, r0 + br)
+        nk = r1 if causal else T
+        S = _scores(q[r0:r1], k[:nk], scale, causal, r0)
+        P, lse[r0:r1] = _softmax_rows(S)
+        O[r0:r1] = P @ v[:nk]
+        dV[:nk] += P.T @ do[r0:r1]                      # dV = P^T dO
+        dP = do[r0:r1] @ v[:nk].T                       # dP = dO V^T
+        Dr = (dP * P).sum(axis=1)                       # (dP * P) 1
+        dS = P * (dP - Dr[:, None])                     # dS = P * (dP - (dP * P) 1)
+        dQ[r0:r1] = scale * (dS @ k[:nk])               # dQ = dS K / sqrt(d_k)
+        dK[:nk] += scale * (dS.T @ q[r0:r1])            # dK = dS^T Q / sqrt(d_k)
+        D[r0:r1] = Dr
+    return dQ, dK, dV, O, lse, D
+
+
+def _heads(B: int, NH: int, heads: Optional[Iterable[Tuple[int, int]]]):
+    if heads is None:
+        return [(b, h) for b in range(B) for h in range(NH)]
+    return [(int(b), int(h)) for b, h in heads]
+
+
+def _block_rows(T: int, width: int) -> int:
+    # keep each block's S/P/dP/dS at a few hundred MB
+    return max(1, min(T, (1 << 25) // max(T, 1) // max(1, width // 64)))
+
+
+def attn_ref_fwd(q, k, v, causal: bool, scale: Optional[float] = None,
+                 heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """Forward over (B, T, NH, d) tensors.
+
+    Returns O (B, T, NH, d_v) and LSE (B, NH, T) in float64.  With ``heads`` given,
+    only those (b, h) pairs are computed and every other entry is NaN.
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, T, NH, dqk = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    O = np.full((B, T, NH, v.shape[3]), np.nan)
+    lse = np.full((B, NH, T), np.nan)
+    br = _block_rows(T, dqk)
+    for b, h in _heads(B, NH, heads):
+        O[b, :, h], lse[b, h] = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, br)
+    return O, lse
+
+
+def attn_ref_bwd(q, k, v, do, causal: bool, scale: Optional[float] = None,
+                 heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """Backward over (B, T, NH, d) tensors.
+
+    Returns a dict with dq, dk, dv (B, T, NH, d), o (B, T, NH, d_v), lse and D (B, NH, T),
+    all float64; entries of heads not listed in ``heads`` are NaN.
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    B, T, NH, dqk = q.shape
+    dv_ = v.shape[3]
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    out = {
+        "dq": np.full((B, T, NH, dqk), np.nan),
+        "dk": np.full((B, T, NH, dqk), np.nan),
+        "dv": np.full((B, T, NH, dv_), np.nan),
+        "o": np.full((B, T, NH, dv_), np.nan),
+        "lse": np.full((B, NH, T), np.nan),
+        "D": np.full((B, NH, T), np.nan),
+    }
+    br = _block_rows(T, dqk)
+    for b, h in _heads(B, NH, heads):
+        dQ, dK, dV, O, lse, D = head_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h],
+                                              scale, causal, br)
+        out["dq"][b, :, h], out["dk"][b, :, h], out["dv"][b, :, h] = dQ, dK, dV
+        out["o"][b, :, h], out["lse"][b, h], out["D"][b, h] = O, lse, D
+    return out
+
+
+def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None):
+    """Independent loop formulation for small T (T <= 64), written from the softmax
+    Jacobian dy_i/dx_j = y_i (delta_ij - y_j) [SA8 2.1, A.3] and the per-(b, t, h)
+    loop nest of the CPU reference in [SA8 2.2]:
+
+      for each (b, t, h):
+        att[t2]      = softmax over t2 (t2 <= t when causal) of scale * <q_t, k_t2>
+        datt[t2]     = <v_t2, do_t>                       (gradient w.r.t. att)
+        dv_t2       += att[t2] * do_t
+        dpreatt[t3]  = scale * sum_t2 att[t2] (delta(t2, t3) - att[t3]) datt[t2]
+        dq_t        += sum_t2 dpreatt[t2] k_t2
+        dk_t2       += dpreatt[t2] q_t
+
+    The scale sits inside dpreatt, so dq and dk take no second factor.  It does not
+    share a line with head_forward/head_backward and serves to pin them.
+    Returns dq, dk, dv, o (B, T, NH, d) and lse (B, NH, T) in float64.
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    B, T, NH, dqk = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    o = np.zeros((B, T, NH, v.shape[3]))
+    lse = np.zeros((B, NH, T))
+    for b in range(B):
+        for t in range(T):
+            for h in range(NH):
+                last = t + 1 if causal else T
+                # forward row by loops: preatt, max, exp, sum, normalise
+                pre = [scale * float(np.dot(q[b, t, h], k[b, t2, h])) for t2 in range(last)]
+                mx = max(pre)
+                ex = [np.exp(p - mx) for p in pre]
+                tot = sum(ex)
+                att = [e / tot for e in ex]
+                lse[b, h, t] = mx + np.log(tot)
+                for t2 in range(last):
+                    o[b, t, h] += att[t2] * v[b, t2, h]
+                # backward through O = att . V
+                datt = [float(np.dot(v[b, t2, h], do[b, t, h])) for t2 in range(last)]
+                for t2 in range(last):
+                    dv[b, t2, h] += att[t2] * do[b, t, h]
+                # backward through the softmax by its Jacobian
+                dpre = [0.0] * last
+                for t2 in range(last):
+                    for t3 in range(last):
+                        ind = 1.0 if t2 == t3 else 0.0
+                        dpre[t3] += scale * att[t2] * (ind - att[t3]) * datt[t2]
+                # backward through preatt = scale * q . k
+                for t2 in range(last):
+                    dq[b, t, h] += dpre[t2] * k[b, t2, h]
+                    dk[b, t2, h] += dpre[t2] * q[b, t, h]
+    return dq, dk, dv, o, lse

@@ -1,0 +1,236 @@
+"""Pins for the CPU oracle: checks against facts that the pages and the mathematics
+fix, not against the oracle's own formulas.
+
+Every pin takes ``ref``, an object with the oracle's public functions
+(attn_ref_fwd, attn_ref_bwd, attn_ref_bwd_loop), so that the same pins can be run
+against copies of the oracle with a planted mistake (test_oracle.py checks that
+each planted mistake trips at least one pin).
+
+Pages cited:
+  [SA8] "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析", sections 2.1, 2.2, A.1-A.3.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import workloads
+
+TINY = workloads.WORKLOADS["tiny"]
+
+
+def _inputs(B, T, NH, dqk, dv, seed, sigma=1.0):
+    w = workloads.Workload("pin", B, NH, T, dqk, dv, True, seed, sigma=sigma)
+    x = workloads.make_inputs(w)
+    return [x[n].to(torch.float64).numpy() for n in ("q", "k", "v", "do")]
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    bound = rtol * max(np.max(np.abs(b)) if b.size else 0.0, 1e-300) + atol
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    assert err <= bound, f"{what}: max err {err:.3e} > {bound:.3e}"
+
+
+# ---------------------------------------------------------------------------------
+# 1. Central finite differences of f(Q, K, V) = sum(O * dO)       [SA8 2.1 chain rule]
+# ---------------------------------------------------------------------------------
+def pin_finite_differences(ref, causal: bool, T: int = 16, h: float = 1e-5):
+    """dQ, dK, dV of the oracle equal central differences of sum(O * dO).
+
+    Tiny shape (B=1, NH=2, d=64) at T=16, float64; every input element is perturbed.
+    """
+    q, k, v, do = _inputs(1, T, 2, TINY.d_qk, TINY.d_v, TINY.seed)
+    scale = 1.0 / math.sqrt(q.shape[-1])
+    g = ref.attn_ref_bwd(q, k, v, do, causal, scale)
+
+    def f(qq, kk, vv):
+        o, _ = ref.attn_ref_fwd(qq, kk, vv, causal, scale)
+        return float(np.sum(o * do))
+
+    for name, x, grad in (("dq", q, g["dq"]), ("dk", k, g["dk"]), ("dv", v, g["dv"])):
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args_p = [q, k, v]; args_m = [q, k, v]
+            pos = {"dq": 0, "dk": 1, "dv": 2}[name]
+            args_p[pos] = xp; args_m[pos] = xm
+            fd[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        _close(grad, fd, rtol=1e-6, atol=1e-9, what=f"finite differences {name} causal={causal}")
+
+
+# ---------------------------------------------------------------------------------
+# 2. Matrix form against the Jacobian loop form                    [SA8 2.2, A.3]
+# ---------------------------------------------------------------------------------
+def pin_loop_form(ref, causal: bool, T: int = 23, dqk: int = 16, dv: int = 24):
+    q, k, v, do = _inputs(1, T, 2, dqk, dv, 777)
+    scale = 0.37
+    g = ref.attn_ref_bwd(q, k, v, do, causal, scale)
+    dq, dk, dv_, o, lse = ref.attn_ref_bwd_loop(q, k, v, do, causal, scale)
+    for name, a, b in (("o", g["o"], o), ("lse", g["lse"], lse), ("dq", g["dq"], dq),
+                       ("dk", g["dk"], dk), ("dv", g["dv"], dv_)):
+        _close(a, b, rtol=1e-12, what=f"loop form {name} causal={causal}")
+
+
+# ---------------------------------------------------------------------------------
+# 3. Softmax invariants                                             [SA8 2.1]
+# ---------------------------------------------------------------------------------
+def pin_softmax_invariants(ref, causal: bool, T: int = 40):
+    """With V = I (d_v = T), O is P itself: rows sum to 1, entries are >= 0, and
+    under the causal mask P_ij = 0 for j > i.  With dO = I as well, dV = P^T dO = P^T
+    (the closed form dV = P^T dO).  D = (dP * P) 1 equals rowsum(dO * O)."""
+    q, k, _, _ = _inputs(1, T, 2, 32, 32, 4242, sigma=1.5)
+    eye = np.broadcast_to(np.eye(T)[None, :, None, :], (1, T, 2, T)).copy()
+    scale = 1.0 / math.sqrt(32)
+    g = ref.attn_ref_bwd(q, k, eye, eye, causal, scale)
+    P = g["o"]                                   # (1, T, 2, T): row t, key j
+    _close(P.sum(axis=-1), np.ones((1, T, 2)), rtol=1e-13, what="rows of P sum to 1")
+    assert np.all(P >= 0.0), "P has negative entries"
+    if causal:
+        mask = np.triu(np.ones((T, T), dtype=bool), 1)
+        assert np.all(P[0, :, 0][mask] == 0.0) and np.all(P[0, :, 1][mask] == 0.0), \
+            "causal P has weight above the diagonal"
+    # dV = P^T dO with dO = I:  dV[j, :] = P[:, j]
+    for h in range(2):
+        _close(g["dv"][0, :, h], P[0, :, h].T, rtol=1e-13, what="dV = P^T dO")
+    # D identity on a random dO
+    q, k, v, do = _inputs(2, T, 3, 16, 8, 99)
+    g = ref.attn_ref_bwd(q, k, v, do, causal, 0.5)
+    D2 = np.einsum("btnd,btnd->bnt", do, g["o"])
+    _close(g["D"], D2, rtol=1e-12, what="D = rowsum(dP*P) = rowsum(dO*O)")
+
+
+def pin_shift_invariance(ref, causal: bool, T: int = 29):
+    """K -> K + 1 c^T adds the same constant to every allowed key of a row of S, so
+    P, O, LSE - scale <q_i, c> and dV are unchanged, and dQ is unchanged because
+    each row of dS sums to zero (rowsum(dS) = 0)."""
+    q, k, v, do = _inputs(1, T, 2, 16, 16, 31337)
+    c = np.linspace(-1.0, 2.0, 16)
+    scale = 0.25
+    g0 = ref.attn_ref_bwd(q, k, v, do, causal, scale)
+    g1 = ref.attn_ref_bwd(q, k + c, v, do, causal, scale)
+    _close(g1["o"], g0["o"], rtol=1e-12, what="shift: O")
+    _close(g1["dv"], g0["dv"], rtol=1e-12, what="shift: dV")
+    _close(g1["dq"], g0["dq"], rtol=1e-10, atol=1e-13, what="shift: dQ (rowsum dS = 0)")
+    shift = scale * np.einsum("btnd,d->bnt", q, c)
+    _close(g1["lse"] - shift, g0["lse"], rtol=1e-12, what="shift: LSE")
+
+
+# ---------------------------------------------------------------------------------
+# 4. Closed forms and special cases
+# ---------------------------------------------------------------------------------
+def pin_zero_queries(ref, causal: bool, T: int = 37):
+    """Q = 0 makes every score 0: P is uniform over the allowed keys, so O_i is the
+    mean of V over those keys and LSE_i = ln(count)."""
+    _, k, v, do = _inputs(1, T, 2, 16, 12, 5)
+    q = np.zeros_like(k)
+    o, lse = ref.attn_ref_fwd(q, k, v, causal, 0.3)
+    cnt = np.arange(1, T + 1) if causal else np.full(T, T)
+    if causal:
+        mean = np.cumsum(v, axis=1) / cnt[None, :, None, None]
+    else:
+        mean = np.broadcast_to(v.mean(axis=1, keepdims=True), v.shape)
+    _close(o, mean, rtol=1e-13, what="Q=0: O = mean of allowed V")
+    _close(lse, np.broadcast_to(np.log(cnt)[None, None, :], lse.shape), rtol=1e-13,
+           what="Q=0: LSE = ln(count)")
+
+
+def pin_single_token(ref, causal: bool):
+    """T = 1: P = [1], so O = V, LSE = scale <q, k>, dV = dO, dQ = dK = 0."""
+    q, k, v, do = _inputs(2, 1, 3, 16, 8, 11)
+    g = ref.attn_ref_bwd(q, k, v, do, causal, 0.7)
+    _close(g["o"], v, rtol=1e-15, what="T=1: O = V")
+    _close(g["lse"], 0.7 * np.einsum("btnd,btnd->bnt", q, k), rtol=1e-14, what="T=1: LSE")
+    _close(g["dv"], do, rtol=1e-15, what="T=1: dV = dO")
+    assert np.max(np.abs(g["dq"])) <= 1e-14 and np.max(np.abs(g["dk"])) <= 1e-14, "T=1: dQ, dK != 0"
+
+
+def pin_causal_first_row(ref, T: int = 19):
+    """Causal row 0 sees only key 0: O_0 = V_0, LSE_0 = scale <q_0, k_0>, dQ_0 = 0."""
+    q, k, v, do = _inputs(1, T, 2, 16, 16, 12)
+    g = ref.attn_ref_bwd(q, k, v, do, True, 0.4)
+    _close(g["o"][:, 0], v[:, 0], rtol=1e-15, what="causal row 0: O")
+    _close(g["lse"][:, :, 0], 0.4 * np.einsum("bnd,bnd->bn", q[:, 0], k[:, 0]), rtol=1e-14,
+           what="causal row 0: LSE")
+    assert np.max(np.abs(g["dq"][:, 0])) <= 1e-14, "causal row 0: dQ != 0"
+
+
+def pin_two_keys_closed_form(ref):
+    """T = 2, d = 1, no mask: softmax over two scores is the logistic function,
+    P_i0 = sigma(s_i0 - s_i1) with sigma(x) = 1 / (1 + e^-x), so
+      O_i   = v_1 + (v_0 - v_1) sigma(a q_i),        a = scale (k_0 - k_1)
+      LSE_i = s_i1 + ln(1 + e^(s_i0 - s_i1))
+      dQ_i  = dO_i (v_0 - v_1) sigma'(a q_i) a,       sigma' = sigma (1 - sigma)
+      dV_j  = sum_i P_ij dO_i.
+    Values chosen by hand; everything below is that closed form, evaluated directly."""
+    q = np.array([0.5, -1.25]).reshape(1, 2, 1, 1)
+    k = np.array([2.0, -0.75]).reshape(1, 2, 1, 1)
+    v = np.array([3.0, -1.0]).reshape(1, 2, 1, 1)
+    do = np.array([0.25, 2.0]).reshape(1, 2, 1, 1)
+    scale = 0.8
+    g = ref.attn_ref_bwd(q, k, v, do, False, scale)
+    qs, ks, vs, ds = q.ravel(), k.ravel(), v.ravel(), do.ravel()
+    a = scale * (ks[0] - ks[1])
+    sig = 1.0 / (1.0 + np.exp(-a * qs))
+    o = vs[1] + (vs[0] - vs[1]) * sig
+    s0, s1 = scale * qs * ks[0], scale * qs * ks[1]
+    lse = s1 + np.log1p(np.exp(s0 - s1))
+    dq = ds * (vs[0] - vs[1]) * sig * (1 - sig) * a
+    P = np.stack([sig, 1 - sig], axis=1)         # P[i, j]
+    dv = P.T @ ds
+    # dK_j = sum_i dS_ij scale q_i with dS_i0 = -dS_i1 = sig (1 - sig) (v_0 - v_1) dO_i
+    dS0 = sig * (1 - sig) * (vs[0] - vs[1]) * ds
+    dk = np.array([np.sum(dS0 * scale * qs), -np.sum(dS0 * scale * qs)])
+    _close(g["o"].ravel(), o, rtol=1e-15, what="two keys: O")
+    _close(g["lse"].ravel(), lse, rtol=1e-15, what="two keys: LSE")
+    _close(g["dq"].ravel(), dq, rtol=1e-14, what="two keys: dQ")
+    _close(g["dk"].ravel(), dk, rtol=1e-14, what="two keys: dK")
+    _close(g["dv"].ravel(), dv, rtol=1e-15, what="two keys: dV")
+
+
+# ---------------------------------------------------------------------------------
+# 5. Library cross-check: torch float64 autograd through softmax(scale Q K^T) V
+# ---------------------------------------------------------------------------------
+def pin_torch_autograd(ref, causal: bool, B=2, T=37, NH=3, dqk=16, dv=24):
+    q, k, v, do = _inputs(B, T, NH, dqk, dv, 2024)
+    scale = 1.0 / math.sqrt(dqk)
+    g = ref.attn_ref_bwd(q, k, v, do, causal, scale)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = torch.einsum("bind,bjnd->bnij", tq, tk) * scale
+    if causal:
+        s = s.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    o = torch.einsum("bnij,bjnd->bind", p, tv)
+    lse = torch.logsumexp(s, dim=-1)
+    o.backward(torch.tensor(do))
+    for name, a, b in (("o", g["o"], o.detach()), ("lse", g["lse"], lse.detach()),
+                       ("dq", g["dq"], tq.grad), ("dk", g["dk"], tk.grad), ("dv", g["dv"], tv.grad)):
+        _close(a, b.numpy(), rtol=1e-12, what=f"torch autograd {name} causal={causal}")
+
+
+ALL_PINS = [
+    ("finite_differences_causal", lambda r: pin_finite_differences(r, True)),
+    ("finite_differences_full", lambda r: pin_finite_differences(r, False)),
+    ("loop_form_causal", lambda r: pin_loop_form(r, True)),
+    ("loop_form_full", lambda r: pin_loop_form(r, False)),
+    ("softmax_invariants_causal", lambda r: pin_softmax_invariants(r, True)),
+    ("softmax_invariants_full", lambda r: pin_softmax_invariants(r, False)),
+    ("shift_invariance_causal", lambda r: pin_shift_invariance(r, True)),
+    ("shift_invariance_full", lambda r: pin_shift_invariance(r, False)),
+    ("zero_queries_causal", lambda r: pin_zero_queries(r, True)),
+    ("zero_queries_full", lambda r: pin_zero_queries(r, False)),
+    ("single_token_causal", lambda r: pin_single_token(r, True)),
+    ("single_token_full", lambda r: pin_single_token(r, False)),
+    ("causal_first_row", pin_causal_first_row),
+    ("two_keys_closed_form", pin_two_keys_closed_form),
+    ("torch_autograd_causal", lambda r: pin_torch_autograd(r, True)),
+    ("torch_autograd_full", lambda r: pin_torch_autograd(r, False)),
+]

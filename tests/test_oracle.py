@@ -1,0 +1,84 @@
+"""The CPU oracle against its pins, plus planted-mistake checks on copies of it.
+
+Runs on the CPU only (no GPU marker).
+"""
+import os
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attn_ref
+from tests import oracle_pins
+
+PINS = dict(oracle_pins.ALL_PINS)
+
+
+@pytest.mark.parametrize("name", list(PINS))
+def test_pin(name):
+    PINS[name](oracle)
+
+
+def test_block_rows_match_whole_rows():
+    """Splitting the query rows into blocks only splits the sums over queries."""
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal((2, 45, 16))
+    v, do = rng.standard_normal((2, 45, 8))
+    for causal in (True, False):
+        a = attn_ref.head_backward(q, k, v, do, 0.3, causal, None)
+        b = attn_ref.head_backward(q, k, v, do, 0.3, causal, 7)
+        for x, y in zip(a, b):
+            np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+
+
+def test_heads_subset_leaves_others_nan():
+    rng = np.random.default_rng(4)
+    q, k, v, do = rng.standard_normal((4, 1, 9, 3, 8))
+    full = attn_ref.attn_ref_bwd(q, k, v, do, True)
+    part = attn_ref.attn_ref_bwd(q, k, v, do, True, heads=[(0, 1)])
+    np.testing.assert_array_equal(part["dq"][0, :, 1], full["dq"][0, :, 1])
+    assert np.isnan(part["dq"][0, :, 0]).all()
+
+
+# ---------------------------------------------------------------------------------
+# Planted mistakes: each is a one-place edit of the oracle's source text, built into
+# a fresh module.  Every one of them must make at least one pin fail.
+# ---------------------------------------------------------------------------------
+MUTANTS = {
+    "drop_D_term": ("dS = P * (dP - Dr[:, None])", "dS = P * dP"),
+    "dS_sign": ("dS = P * (dP - Dr[:, None])", "dS = P * (Dr[:, None] - dP)"),
+    "dV_untransposed": ("dV[:nk] += P.T @ do[r0:r1]", "dV[:nk] += P @ do[r0:r1]"),
+    "dQ_no_scale": ("dQ[r0:r1] = scale * (dS @ k[:nk])", "dQ[r0:r1] = (dS @ k[:nk])"),
+    "dK_no_scale": ("dK[:nk] += scale * (dS.T @ q[r0:r1])", "dK[:nk] += (dS.T @ q[r0:r1])"),
+    "dK_uses_k": ("dK[:nk] += scale * (dS.T @ q[r0:r1])", "dK[:nk] += scale * (dS.T @ k[r0:r1])"),
+    "dP_uses_q": ("dP = do[r0:r1] @ v[:nk].T", "dP = do[r0:r1] @ v[:nk].T + 1e-3 * q[r0:r1] @ k[:nk].T"),
+    "mask_off_by_one": ("S = np.where(kj > qi, -np.inf, S)", "S = np.where(kj > qi + 1, -np.inf, S)"),
+    "lse_log2": ("return e / l, (m + np.log(l))[:, 0]", "return e / l, (m + np.log2(l))[:, 0]"),
+    "lse_no_max": ("return e / l, (m + np.log(l))[:, 0]", "return e / l, (np.log(l))[:, 0]"),
+    "D_from_dP_only": ("Dr = (dP * P).sum(axis=1)", "Dr = dP.sum(axis=1)"),
+    "scores_no_scale": ("S = scale * (q @ k.T)", "S = (q @ k.T)"),
+}
+
+
+def _mutant(old: str, new: str):
+    src = open(attn_ref.__file__).read()
+    assert src.count(old) == 1, f"planted-mistake anchor not found once: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = os.path.join(os.path.dirname(attn_ref.__file__), "mutant.py")
+    exec(compile(src.replace(old, new), mod.__file__, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("mutant", list(MUTANTS))
+def test_planted_mistake_is_caught(mutant):
+    mod = _mutant(*MUTANTS[mutant])
+    failed = []
+    for name, pin in oracle_pins.ALL_PINS:
+        if name.startswith("finite_differences"):
+            continue  # the slowest pins; the others must already catch every mutant
+        try:
+            pin(mod)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            failed.append(name)
+    assert failed, f"no pin caught the planted mistake {mutant}"

@@ -1,0 +1,89 @@
+"""Seeded synthetic attention workloads, shared by the tests, the bench and the smoke check.
+
+This module only draws random inputs and describes shapes.  It holds none of the
+attention arithmetic: both the GPU library and the CPU oracle receive the very same
+bf16 tensors that it produces.
+
+The pages measure on no dataset.  The FlashAttention-4 backward page ("2-CTA MMA mode
+and memory-access optimisation", section 4.1) sweeps head dims 64/128/(192,128),
+sequence lengths 1K-32K and keeps the total token count at 32K; the self-attention
+CUDA page (section 1.3) uses a GPT-2 style packed (B, T, 3, NH, HS) QKV input.  The
+configurations below stand in for those sweeps.
+
+Recipe (every workload):
+  * values are float32 standard normals from ``torch.Generator().manual_seed(seed + k)``,
+    multiplied by sigma, then rounded to bfloat16 (round-to-nearest-even);
+  * k = 0, 1, 2, 3 draw Q, K, V, dO in that order (separate layout), or
+    k = 0 draws the packed QKV block and k = 1 draws dO (packed layout);
+  * sigma is a standard deviation (the GPT-2 case uses 0.5 for QKV, 1 for dO).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    NH: int
+    T: int
+    d_qk: int
+    d_v: int
+    causal: bool
+    seed: int
+    sigma: float = 1.0       # std of Q, K, V
+    sigma_do: float = 1.0    # std of dO
+    packed: bool = False     # Q, K, V are views of one (B, T, 3, NH, HS) tensor
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_qk)
+
+    def pairs(self) -> int:
+        """Unmasked (query, key) pairs over all heads."""
+        per_head = self.T * (self.T + 1) // 2 if self.causal else self.T * self.T
+        return self.B * self.NH * per_head
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", 1, 2, 128, 64, 64, True, 53001),
+    "gpt2": Workload("gpt2", 4, 12, 1024, 64, 64, True, 53002, sigma=0.5, packed=True),
+    "mid_causal": Workload("mid_causal", 16, 16, 2048, 128, 128, True, 53003),
+    "mid_full": Workload("mid_full", 16, 16, 2048, 128, 128, False, 53003),
+    "long": Workload("long", 1, 16, 32768, 128, 128, True, 53004),
+    "asym": Workload("asym", 4, 16, 8192, 192, 128, True, 53005),
+    "headline": Workload("headline", 4, 16, 8192, 128, 128, True, 53006),
+}
+
+
+def _randn(shape, seed: int, sigma: float) -> torch.Tensor:
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * sigma).to(torch.bfloat16)
+
+
+def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
+    """CPU bf16 tensors for one workload.
+
+    Returns q, k, v of shape (B, T, NH, d) (possibly strided views of a packed block,
+    which is then also returned as ``qkv``) and do of shape (B, T, NH, d_v).
+    """
+    B, T, NH = w.B, w.T, w.NH
+    if w.packed:
+        if w.d_qk != w.d_v:
+            raise ValueError("packed QKV needs d_qk == d_v")
+        qkv = _randn((B, T, 3, NH, w.d_qk), w.seed + 0, w.sigma)
+        do = _randn((B, T, NH, w.d_v), w.seed + 1, w.sigma_do)
+        return {"qkv": qkv, "q": qkv[:, :, 0], "k": qkv[:, :, 1], "v": qkv[:, :, 2], "do": do}
+    q = _randn((B, T, NH, w.d_qk), w.seed + 0, w.sigma)
+    k = _randn((B, T, NH, w.d_qk), w.seed + 1, w.sigma)
+    v = _randn((B, T, NH, w.d_v), w.seed + 2, w.sigma)
+    do = _randn((B, T, NH, w.d_v), w.seed + 3, w.sigma_do)
+    return {"q": q, "k": k, "v": v, "do": do}
