@@ -1,0 +1,195 @@
+"""Fused exact attention (forward + backward) for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/attn53.h`` (library
+``libattn53.so``, built in-tree by ``exact_attention_53_amd._build``).  The binding
+only marshals arguments: it takes device pointers and strides from torch tensors,
+allocates outputs and the workspace with torch, and passes torch's current HIP
+stream.  Every step of the computation runs in the library's HIP kernels; there is
+no fallback path, and a missing library raises.
+
+Tensor layout: 4-D bf16 tensors in (B, T, NH, d) order by default (``layout="bthd"``,
+the layout of the pages' output O), or (B, NH, T, d) (``layout="bhtd"``); any strides
+whose last one is 1 and whose others are multiples of 8 elements.  Packed QKV blocks
+(B, T, 3, NH, HS) are accepted through ``qkv[:, :, 0]`` etc. or ``fwd_packed``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "AttnError", "lib_path", "load", "fwd", "fwd_packed", "bwd", "bwd_packed",
+    "workspace_bytes", "PREPROCESS", "MAIN", "FINALIZE", "ALL_STAGES", "version",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libattn53.so")
+
+PREPROCESS, MAIN, FINALIZE, ALL_STAGES = 1, 2, 4, 7
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"attn53 status {status}: {message}")
+        self.status = status
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("t", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads libattn53.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} is missing: build it with `python -m exact_attention_53_amd._build`")
+    lib = ctypes.CDLL(lib_path)
+    vp, S, i, f, sz = ctypes.c_void_p, Strides, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_version.restype = i
+    lib.attn_version.argtypes = []
+    lib.attn_fwd.restype = i
+    lib.attn_fwd.argtypes = [vp, S, vp, S, vp, S, vp, S, vp, i, i, i, i, i, f, i, vp]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    bwd_args = [vp, S, vp, S, vp, S, vp, S, vp, vp, S, vp, S, vp, S, vp, S,
+                i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd.argtypes = bwd_args
+    lib.attn_bwd_staged.restype = i
+    lib.attn_bwd_staged.argtypes = bwd_args + [ctypes.c_uint]
+    _lib = lib
+    return lib
+
+
+def version() -> int:
+    return load().attn_version()
+
+
+def _check(status: int):
+    if status != 0:
+        raise AttnError(status, load().attn_status_string(status).decode())
+
+
+def _strides(x: torch.Tensor, layout: str) -> Strides:
+    if x.dim() != 4:
+        raise ValueError(f"expected a 4-D tensor, got shape {tuple(x.shape)}")
+    if x.stride(3) != 1:
+        raise ValueError("the head-dim stride must be 1")
+    if layout == "bthd":
+        return Strides(x.stride(0), x.stride(2), x.stride(1))
+    if layout == "bhtd":
+        return Strides(x.stride(0), x.stride(1), x.stride(2))
+    raise ValueError(f"layout must be 'bthd' or 'bhtd', not {layout!r}")
+
+
+def _dims(x: torch.Tensor, layout: str) -> Tuple[int, int, int, int]:
+    B, a, c, d = x.shape
+    return (B, c, a, d) if layout == "bthd" else (B, a, c, d)  # -> B, NH, T, d
+
+
+def _need(x: torch.Tensor, name: str, dev: torch.device):
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {x.dtype}")
+    if x.device != dev:
+        raise ValueError(f"{name} is on {x.device}, expected {dev}")
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+        scale: Optional[float] = None, return_lse: bool = True, layout: str = "bthd",
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Exact attention forward.  Returns (o, lse); lse is None when return_lse is False
+    (inference mode: the kernel skips the stats)."""
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("fwd runs on the GPU only; got a CPU tensor")
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, n, dev)
+    B, NH, T, dqk = _dims(q, layout)
+    dv = v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        shape = (B, T, NH, dv) if layout == "bthd" else (B, NH, T, dv)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    with torch.cuda.device(dev):
+        _check(lib.attn_fwd(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                            v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
+                            lse.data_ptr() if return_lse else None, B, NH, T, dqk, dv, float(scale),
+                            int(bool(causal)), _stream(dev)))
+    return out, (lse if return_lse else None)
+
+
+def fwd_packed(qkv: torch.Tensor, causal: bool = True, scale: Optional[float] = None, return_lse: bool = True):
+    """Forward on a packed (B, T, 3, NH, HS) QKV block; o is (B, T, NH, HS)."""
+    if qkv.dim() != 5 or qkv.shape[2] != 3:
+        raise ValueError("qkv must have shape (B, T, 3, NH, HS)")
+    return fwd(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], causal, scale, return_lse)
+
+
+def workspace_bytes(B: int, NH: int, T: int, d_qk: int, d_v: int, deterministic: bool) -> int:
+    return int(load().attn_bwd_workspace_bytes(B, NH, T, d_qk, d_v, int(bool(deterministic))))
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
+        deterministic: bool = False, layout: str = "bthd", dq=None, dk=None, dv=None,
+        workspace: Optional[torch.Tensor] = None, stages: int = ALL_STAGES):
+    """Exact attention backward.  Returns (dq, dk, dv)."""
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("bwd runs on the GPU only; got a CPU tensor")
+    for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _need(x, n, dev)
+    B, NH, T, dqk = _dims(q, layout)
+    dvd = v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    need = workspace_bytes(B, NH, T, dqk, dvd, deterministic)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_bwd_staged(
+            q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+            v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
+            lse.data_ptr(), do.data_ptr(), _strides(do, layout),
+            dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
+            dv.data_ptr(), _strides(dv, layout), B, NH, T, dqk, dvd, float(scale),
+            int(bool(causal)), int(bool(deterministic)), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(dev), int(stages)))
+    return dq, dk, dv
+
+
+def bwd_packed(qkv, o, lse, do, causal: bool = True, scale: Optional[float] = None,
+               deterministic: bool = False, dqkv: Optional[torch.Tensor] = None, workspace=None):
+    """Backward on a packed (B, T, 3, NH, HS) QKV block; returns dqkv of the same layout."""
+    if dqkv is None:
+        dqkv = torch.empty_like(qkv, memory_format=torch.contiguous_format)
+    bwd(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], o, lse, do, causal, scale, deterministic,
+        dq=dqkv[:, :, 0], dk=dqkv[:, :, 1], dv=dqkv[:, :, 2], workspace=workspace)
+    return dqkv

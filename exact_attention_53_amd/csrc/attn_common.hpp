@@ -1,0 +1,189 @@
+// Device-side building blocks shared by the attention kernels (gfx950 / CDNA4 only).
+//
+// Pages cited (by title and section):
+//   [SA8]  "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析"
+//   [2CTA] "深度学习反向传播优化：2-CTA MMA模式与内存访问优化"
+//   [FAT]  "FlashAttention Triton实现中的内存访问模式优化与寄存器分配策略"
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, one 64-lane wavefront; lane l,
+// half g = l / 32):
+//   A operand (32 x 16): lane l holds A[l % 32][8g .. 8g+7]
+//   B operand (16 x 32): lane l holds B[8g .. 8g+7][l % 32]
+//   accumulator (32 x 32, 16 fp32 per lane): element r of lane l is
+//       D[8 (r / 4) + 4 g + (r % 4)][l % 32]
+// A product whose accumulator is transposed so that its rows are the contraction
+// index of the next product (P feeding P V, dS feeding dS K, ...) can feed that next
+// product straight from registers: the 8 accumulator values r = 8m .. 8m+7 of one
+// lane form a valid A/B operand fragment if the *other* operand lists its
+// contraction index in the same order, {16m + 4g + 0..3, 16m + 4g + 8..11}.  The
+// transposed LDS reads below produce exactly that order.
+//
+// LDS tiles.  A tile of R rows x C columns of bf16 (C a multiple of 64) is stored as
+// C/64 panels, each R rows of 128 bytes.  Within a row the eight 16-byte chunks are
+// permuted by XOR with swz(row).  With 64 LDS banks of 4 bytes this makes both access
+// patterns conflict-free:
+//   * row reads  (ds_read_b128): 16 lanes read the same chunk of 16 consecutive rows;
+//   * column reads (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows x 64 bytes.
+// This is the permuted shared-memory layout that [FAT 3.3] recommends over copying a
+// transposed K in HBM, re-derived for the gfx950 bank geometry.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn53 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------------
+// matrix core
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// 8 consecutive accumulator values (r = 8m .. 8m+7) rounded to bf16 (RNE).
+__device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int m) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)acc[8 * m + e];
+  return r;
+}
+
+// ---------------------------------------------------------------------------------
+// special functions and cross-lane reductions
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane l ^ 32 combined with the own value (one v_permlane32_swap).
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------------
+// swizzled LDS tiles (byte offsets relative to the tile base)
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t swz(uint32_t row) {
+  return (((row >> 1) & 1u) << 2) | ((row >> 2) & 3u);
+}
+
+template <int ROWS>
+__device__ __forceinline__ uint32_t tile_off(uint32_t row, uint32_t col) {
+  const uint32_t panel = col >> 6, chunk = (col >> 3) & 7u, e = col & 7u;
+  return panel * (ROWS * 128u) + row * 128u + ((chunk ^ swz(row)) << 4) + (e << 1);
+}
+
+// Row read: 8 consecutive columns col .. col+7 of one row (col % 8 == 0).
+template <int ROWS>
+__device__ __forceinline__ bf16x8 lds_row8(const ATTN_LDS char* tile, uint32_t row, uint32_t col) {
+  return *reinterpret_cast<const ATTN_LDS bf16x8*>(tile + tile_off<ROWS>(row, col));
+}
+
+// Column read for an MFMA operand whose contraction index runs along the tile's rows.
+// Returns, for lane l, the 8 values X[k][j] with j = j0 + (l % 32) and
+// k = k0 + 4 g + {0..3, 8..11} (g = l / 32): two ds_read_b64_tr_b16.  Within each
+// 16-lane group, lane p supplies the address of row (k0 + 4g + 8h + p / 4),
+// columns j0 + 16 * ((l / 16) % 2) + 4 (p % 4) .. +3.
+template <int ROWS>
+__device__ __forceinline__ bf16x8 lds_col8(const ATTN_LDS char* tile, uint32_t k0, uint32_t j0, uint32_t lane) {
+  const uint32_t p = lane & 15u, g = lane >> 5;
+  const uint32_t col = j0 + 16u * ((lane >> 4) & 1u) + 4u * (p & 3u);
+  const uint32_t row0 = k0 + 4u * g + (p >> 2);
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (ATTN_LDS i16x4*)(tile + tile_off<ROWS>(row0, col)));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (ATTN_LDS i16x4*)(tile + tile_off<ROWS>(row0 + 8u, col)));
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------------
+// global <-> LDS tile staging through registers
+// ---------------------------------------------------------------------------------
+// A tile of ROWS x COLS bf16 starting at global row `row0` of a (T, COLS) matrix with
+// row stride `ld` elements.  Rows >= T are filled with zeros.  NT threads cooperate;
+// each holds CHUNKS 16-byte chunks.  Chunk x -> panel x / (ROWS * 8), row (x / 8) %
+// ROWS, chunk-in-row x % 8: eight consecutive lanes read one 128-byte row segment.
+template <int ROWS, int COLS, int NT>
+struct TileStage {
+  static constexpr int CHUNKS = ROWS * COLS / 8 / NT;
+  static_assert(ROWS * COLS / 8 % NT == 0, "tile not divisible among threads");
+  u32x4 v[CHUNKS];
+
+  __device__ __forceinline__ void load(const bf16* __restrict__ g, int64_t ld, int row0, int T, int tid) {
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int x = tid + NT * i;
+      const int panel = x / (ROWS * 8), rem = x % (ROWS * 8);
+      const int row = rem >> 3, col = panel * 64 + (rem & 7) * 8;
+      const int gr = row0 + row;
+      if (gr < T) {
+        v[i] = *reinterpret_cast<const u32x4*>(g + (int64_t)gr * ld + col);
+      } else {
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(ATTN_LDS char* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int x = tid + NT * i;
+      const int panel = x / (ROWS * 8), rem = x % (ROWS * 8);
+      const int row = rem >> 3, col = panel * 64 + (rem & 7) * 8;
+      *reinterpret_cast<ATTN_LDS u32x4*>(tile + tile_off<ROWS>(row, col)) = v[i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------
+// work schedule: longest items first, heads grouped per XCD
+// ---------------------------------------------------------------------------------
+// Workgroup ids are handed to the 8 XCDs round robin (id % 8).  When the number of
+// (batch, head) pairs is a multiple of 8, each XCD gets a contiguous group of heads,
+// so the workgroups that share a head's K/V (forward) or Q/dO (backward) share one L2
+// — the head/batch swizzle of [2CTA 3.2].  Within an XCD, ids run over `rank`
+// (0 = longest item first) and then over the XCD's heads.
+struct Item {
+  int rank;  // 0 .. nrank-1, in dispatch order
+  int bh;    // b * NH + h
+};
+__device__ __forceinline__ Item schedule(int bid, int nbh) {
+  Item it;
+  if ((nbh & 7) == 0) {
+    const int xcd = bid & 7, local = bid >> 3, per = nbh >> 3;
+    it.bh = xcd * per + local % per;
+    it.rank = local / per;
+  } else {
+    it.bh = bid % nbh;
+    it.rank = bid / nbh;
+  }
+  return it;
+}
+
+}  // namespace attn53

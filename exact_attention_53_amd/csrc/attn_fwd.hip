@@ -1,0 +1,186 @@
+// Exact attention forward for gfx950.
+//
+// Pages cited (by title and section):
+//   [SA8]  "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析" 2.1, A.1 (S, P, O), 1.2-1.3 (stats,
+//          inference mode, packed QKV strides)
+//   [FAT]  "FlashAttention Triton实现中的内存访问模式优化与寄存器分配策略" 2.2 (one program per query
+//          block, Q loaded once, running max/sum in on-chip state), 4.2 (deferred normalisation)
+//   [2CTA] "深度学习反向传播优化：2-CTA MMA模式与内存访问优化" 3.2, 6.2 (head/batch swizzle,
+//          longest-first order, diagonal-first causal traversal)
+//
+// Structure.  A workgroup of 4 wavefronts owns FWD_BM = 128 query rows of one (b, h);
+// wavefront w owns rows 32w .. 32w+31 and keeps them in registers as the B operand of
+// S^T = K Q^T (so each lane owns one query row and its running max / sum).  Key/value
+// tiles of FWD_BN = 64 rows are staged into double-buffered, swizzled LDS.  For each
+// tile:  S^T (2 x d_qk/16 MFMAs), scale into base 2, causal / tail mask, running max
+// across the tile (one lane swap), p = 2^(x - m), l = alpha l + sum p,
+// O^T = alpha O^T + V^T P^T (d_v/32 x 4 MFMAs with P^T straight from the S^T
+// accumulators).  After the last tile O = O^T / l and LSE = ln 2 (m + log2 l).
+// Causal: tiles wholly above the diagonal are never loaded; the one or two diagonal
+// tiles come first and are the only ones masked; a wavefront skips tiles that lie
+// wholly above its own rows.
+#include "attn_common.hpp"
+#include "attn_kernels.hpp"
+
+namespace attn53 {
+
+constexpr int FWD_BM = 128;
+constexpr int FWD_BN = 64;
+constexpr int FWD_NT = 256;
+
+template <int DQK, int DV, bool CAUSAL>
+__global__ __launch_bounds__(FWD_NT) void fwd_kernel(FwdParams p) {
+  constexpr int KS = DQK / 16;
+  constexpr int NDT = DV / 32;
+  constexpr int KT_BYTES = FWD_BN * DQK * 2;
+  constexpr int VT_BYTES = FWD_BN * DV * 2;
+  __shared__ __attribute__((aligned(16))) char smem[2 * (KT_BYTES + VT_BYTES)];
+  ATTN_LDS char* lds = (ATTN_LDS char*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
+  const int T = p.T;
+  const int nqb = (T + FWD_BM - 1) / FWD_BM;
+  const Item item = schedule(blockIdx.x, p.B * p.NH);
+  const int qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
+  const int b = item.bh / p.NH, h = item.bh % p.NH;
+
+  const bf16* qg = (const bf16*)p.q + b * p.sq.b + h * p.sq.h;
+  const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
+  const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
+  bf16* og = (bf16*)p.o + b * p.so.b + h * p.so.h;
+
+  const int q0 = qb * FWD_BM;
+  const int qw = q0 + 32 * w;
+  const int my_q = qw + lq;
+
+  // Q rows of this wavefront, as B-operand fragments of S^T = K Q^T.
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (my_q < T) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)my_q * p.sq.t + 16 * ks + 8 * g);
+    qf[ks] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  const int kv_end = CAUSAL ? min(T, q0 + FWD_BM) : T;
+  const int n_kv = (kv_end + FWD_BN - 1) / FWD_BN;
+
+  TileStage<FWD_BN, DQK, FWD_NT> kst;
+  TileStage<FWD_BN, DV, FWD_NT> vst;
+  kst.load(kg, p.sk.t, (n_kv - 1) * FWD_BN, T, tid);
+  vst.load(vg, p.sv.t, (n_kv - 1) * FWD_BN, T, tid);
+  kst.store(lds, tid);
+  vst.store(lds + 2 * KT_BYTES, tid);
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = zero16();
+
+  for (int it = 0; it < n_kv; ++it) {
+    const int j = n_kv - 1 - it;  // diagonal / tail tile first
+    const int buf = it & 1;
+    const bool more = it + 1 < n_kv;
+    if (more) {
+      kst.load(kg, p.sk.t, (j - 1) * FWD_BN, T, tid);
+      vst.load(vg, p.sv.t, (j - 1) * FWD_BN, T, tid);
+    }
+    const int key0 = j * FWD_BN;
+    const bool active = !CAUSAL || key0 <= qw + 31;
+    if (active) {
+      const ATTN_LDS char* kt = lds + buf * KT_BYTES;
+      const ATTN_LDS char* vt = lds + 2 * KT_BYTES + buf * VT_BYTES;
+      // S^T = K Q^T for keys key0 .. key0+63 (two 32-key accumulators)
+      f32x16 s0 = zero16(), s1 = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a0 = lds_row8<FWD_BN>(kt, lq, 16 * ks + 8 * g);
+        const bf16x8 a1 = lds_row8<FWD_BN>(kt, 32 + lq, 16 * ks + 8 * g);
+        s0 = mfma32(a0, qf[ks], s0);
+        s1 = mfma32(a1, qf[ks], s1);
+      }
+      // scale into base 2, mask, tile max
+      const bool need_mask = (CAUSAL && key0 + FWD_BN - 1 > qw) || (key0 + FWD_BN > T);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x0 = s0[r] * p.scale_log2, x1 = s1[r] * p.scale_log2;
+        if (need_mask) {
+          const int kk0 = key0 + 8 * (r >> 2) + 4 * g + (r & 3), kk1 = kk0 + 32;
+          if (kk0 >= T || (CAUSAL && kk0 > my_q)) x0 = -INFINITY;
+          if (kk1 >= T || (CAUSAL && kk1 > my_q)) x1 = -INFINITY;
+        }
+        s0[r] = x0;
+        s1[r] = x1;
+        mx = fmaxf(mx, fmaxf(x0, x1));
+      }
+      mx = max_halves(mx);
+      // Every processed tile holds key key0 <= every row of this wave, so m_new is finite.
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - m_new);
+      m_run = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p0 = exp2_fast(s0[r] - m_new), p1 = exp2_fast(s1[r] - m_new);
+        rs += p0 + p1;
+        s0[r] = p0;
+        s1[r] = p1;
+      }
+      l_run = l_run * alpha + rs;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      const bf16x8 pb0 = pack8(s0, 0), pb1 = pack8(s0, 1), pb2 = pack8(s1, 0), pb3 = pack8(s1, 1);
+      // O^T += V^T P^T
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[dt] = mfma32(lds_col8<FWD_BN>(vt, 0, 32 * dt, lane), pb0, o[dt]);
+        o[dt] = mfma32(lds_col8<FWD_BN>(vt, 16, 32 * dt, lane), pb1, o[dt]);
+        o[dt] = mfma32(lds_col8<FWD_BN>(vt, 32, 32 * dt, lane), pb2, o[dt]);
+        o[dt] = mfma32(lds_col8<FWD_BN>(vt, 48, 32 * dt, lane), pb3, o[dt]);
+      }
+    }
+    if (more) {
+      kst.store(lds + (buf ^ 1) * KT_BYTES, tid);
+      vst.store(lds + 2 * KT_BYTES + (buf ^ 1) * VT_BYTES, tid);
+    }
+    __syncthreads();
+  }
+
+  // deferred normalisation and stats
+  const float l_tot = sum_halves(l_run);
+  if (my_q < T) {
+    const float inv = 1.f / l_tot;
+    bf16* orow = og + (int64_t)my_q * p.so.t;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[dt][4 * a + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * g) = v;
+      }
+    if (p.lse != nullptr && g == 0)
+      p.lse[(int64_t)item.bh * T + my_q] = (m_run + log2_fast(l_tot)) * kLn2;
+  }
+}
+
+template <int DQK, int DV, bool CAUSAL>
+static hipError_t fwd_launch(const FwdParams& p, hipStream_t s) {
+  const int nqb = (p.T + FWD_BM - 1) / FWD_BM;
+  hipLaunchKernelGGL((fwd_kernel<DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(FWD_NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
+  if (d_qk == 64 && d_v == 64) return causal ? fwd_launch<64, 64, true>(p, s) : fwd_launch<64, 64, false>(p, s);
+  if (d_qk == 128 && d_v == 128) return causal ? fwd_launch<128, 128, true>(p, s) : fwd_launch<128, 128, false>(p, s);
+  if (d_qk == 192 && d_v == 128) return causal ? fwd_launch<192, 128, true>(p, s) : fwd_launch<192, 128, false>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn53

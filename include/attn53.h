@@ -1,0 +1,167 @@
+/*
+ * attn53.h — C ABI of a fused, tiled, exact scaled-dot-product attention library for
+ * AMD Instinct MI355X (gfx950).  Forward and backward, bf16 in/out, fp32 accumulation.
+ *
+ * Pages cited (by title and section):
+ *   [SA8]  "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析"
+ *   [2CTA] "深度学习反向传播优化：2-CTA MMA模式与内存访问优化"
+ *   [FAT]  "FlashAttention Triton实现中的内存访问模式优化与寄存器分配策略"
+ *
+ * Tensor conventions shared by every entry point
+ * ---------------------------------------------
+ *  - Q, K, V, O, dO, dQ, dK, dV are bf16 tensors with logical shape (B, NH, T, d).
+ *    Each is described by a device pointer plus an attn_strides value holding its
+ *    element strides along b, h and t; the stride along d is always 1.  This covers
+ *    the (B, T, NH, d) layout of the pages' output O, a (B, NH, T, d) layout, and the
+ *    packed (B, T, 3, NH, HS) QKV block of [SA8 1.3]: with C = NH*HS, Q, K and V are
+ *    base, base + C and base + 2C, each with strides {T*3*C, HS, 3*C}.  dQ, dK, dV may
+ *    point into one packed buffer the same way.
+ *  - Supported head widths (d_qk, d_v): (64, 64), (128, 128), (192, 128) — the head
+ *    dims of the FA4 backward sweep [2CTA 4.1].  Anything else: ATTN_ERR_HEADDIM.
+ *  - T_q == T_k == T >= 1, any value; partial tiles are masked inside the kernels.
+ *  - Every tensor pointer must be 16-byte aligned and every stride a non-negative
+ *    multiple of 8 elements, so that all global accesses are 128-bit; otherwise the
+ *    call returns ATTN_ERR_ALIGN / ATTN_ERR_STRIDE.  There is no slow fallback.
+ *  - LSE ("softmax stats" of [SA8 1.2, 1.3]) is fp32, contiguous (B, NH, T), and holds
+ *    the natural-log logsumexp of each row of S = scale * Q K^T (mask applied).
+ *  - causal = 1 masks key j > query i (top-left aligned, [SA8 2.2] loop bound).
+ *  - scale multiplies Q K^T; the pages use 1/sqrt(d_k) [SA8 2.1].  Must be finite.
+ *
+ * Ownership, errors, execution
+ * ----------------------------
+ *  - The caller owns every buffer, including the backward workspace.  The library
+ *    allocates no device memory and keeps no state between calls; calls are
+ *    re-entrant and may run concurrently on different streams with distinct outputs.
+ *  - Inputs are never written.  Outputs are overwritten (never accumulated into) and
+ *    must not overlap any input's address range (ATTN_ERR_ALIAS).
+ *  - Arguments are validated on the host before anything is launched; on error
+ *    nothing is launched and nothing is written.  Launch failures report
+ *    ATTN_ERR_HIP.  No C++ exception crosses this interface.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the legacy
+ *    default stream).  Results are valid once the stream has been synchronised.
+ */
+#ifndef ATTN53_H
+#define ATTN53_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,       /* a required pointer is NULL                         */
+  ATTN_ERR_SHAPE = 2,      /* B, NH or T < 1, or the sizes overflow              */
+  ATTN_ERR_HEADDIM = 3,    /* (d_qk, d_v) not one of the supported pairs          */
+  ATTN_ERR_STRIDE = 4,     /* a stride is negative or not a multiple of 8         */
+  ATTN_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned                    */
+  ATTN_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required             */
+  ATTN_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed          */
+  ATTN_ERR_ARG = 8,        /* scale not finite, a flag not 0/1, bad stage mask     */
+  ATTN_ERR_ALIAS = 9       /* an output overlaps an input                         */
+} attn_status;
+
+/* Element strides of a (B, NH, T, d) view along b, h and t (the d stride is 1). */
+typedef struct {
+  int64_t b, h, t;
+} attn_strides;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* attn_status_string(attn_status s);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+/*
+ * attn_fwd — exact attention forward [SA8 2.1 and A.1; FAT 2.2 and 4.2]:
+ *   S = scale * Q K^T, causal mask, P = softmax(S) row-wise, O = P V,
+ *   LSE_i = max_j S_ij + ln sum_j exp(S_ij - max_j S_ij).
+ * One workgroup per query block keeps its Q tile on chip and streams K/V tiles with a
+ * running max and running sum; O is normalised once at the end.
+ *   q, k  : (B, NH, T, d_qk) bf16, strides sq, sk        (read)
+ *   v     : (B, NH, T, d_v)  bf16, strides sv            (read)
+ *   o     : (B, NH, T, d_v)  bf16, strides so            (written)
+ *   lse   : (B, NH, T) fp32 contiguous, 4-byte aligned  (written), or NULL for
+ *           inference, which skips the stats as the pages' inference mode does
+ *           [SA8 1.2, 1.3].
+ */
+attn_status attn_fwd(const void* q, attn_strides sq,
+                     const void* k, attn_strides sk,
+                     const void* v, attn_strides sv,
+                     void* o, attn_strides so,
+                     float* lse,
+                     int B, int NH, int T, int d_qk, int d_v,
+                     float scale, int causal, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes — device workspace that attn_bwd needs for these sizes.
+ * Holds D_i = sum_k dO_ik O_ik (fp32, one per row) and, in atomic mode, the fp32 dQ
+ * accumulator.  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic);
+
+/*
+ * attn_bwd — exact attention backward [SA8 2.1 and A.2; 2CTA 2.2, 3.1, 3.2]:
+ *   D   = rowsum(dO * O)            (equals (dP * P) 1 of [SA8 2.1 step 3])
+ *   P   = exp(scale * Q K^T - LSE)  (recomputed from the forward's LSE)
+ *   dV  = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+ *   dQ  = scale * dS K,  dK = scale * dS^T Q.
+ * Workgroups own a key/value block, keep K, V and their dK, dV accumulators on chip
+ * and loop over query blocks.  dQ needs a sum over key blocks [2CTA 2.2]:
+ *   deterministic = 0: fp32 atomic adds into an fp32 accumulator in the workspace,
+ *                      then one conversion pass to bf16 (run-to-run bits may differ);
+ *   deterministic = 1: every dQ row block is summed over key blocks in one fixed
+ *                      order inside a single workgroup, so all outputs are
+ *                      bit-identical from run to run [2CTA 3.2].
+ *   q, k, v, o, do_ : bf16 inputs as in attn_fwd (o is the forward's output)
+ *   lse             : the forward's (B, NH, T) fp32 stats (read; must not be NULL)
+ *   dq, dk, dv      : bf16 outputs (written), shapes of q, k, v
+ *   workspace       : device memory of at least attn_bwd_workspace_bytes(...) bytes,
+ *                     16-byte aligned, owned by the caller, clobbered by the call.
+ */
+attn_status attn_bwd(const void* q, attn_strides sq,
+                     const void* k, attn_strides sk,
+                     const void* v, attn_strides sv,
+                     const void* o, attn_strides so,
+                     const float* lse,
+                     const void* do_, attn_strides sdo,
+                     void* dq, attn_strides sdq,
+                     void* dk, attn_strides sdk,
+                     void* dv, attn_strides sdv,
+                     int B, int NH, int T, int d_qk, int d_v,
+                     float scale, int causal, int deterministic,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage bits for attn_bwd_staged. */
+#define ATTN_BWD_PREPROCESS 1u /* D = rowsum(dO * O); clear the fp32 dQ accumulator  */
+#define ATTN_BWD_MAIN 2u       /* P recompute, dV, dP, dS, dK, dQ partial sums        */
+#define ATTN_BWD_FINALIZE 4u   /* dQ = scale * accumulator -> bf16 (atomic mode only) */
+#define ATTN_BWD_ALL 7u
+
+/*
+ * attn_bwd_staged — attn_bwd restricted to the stages in `stages` (a non-empty subset
+ * of ATTN_BWD_ALL).  Running the three stages one after another on one stream with the
+ * same arguments and workspace is exactly attn_bwd.  Exists so that each stage's
+ * kernels can be timed on their own; returns ATTN_ERR_ARG for an empty or unknown mask.
+ */
+attn_status attn_bwd_staged(const void* q, attn_strides sq,
+                            const void* k, attn_strides sk,
+                            const void* v, attn_strides sv,
+                            const void* o, attn_strides so,
+                            const float* lse,
+                            const void* do_, attn_strides sdo,
+                            void* dq, attn_strides sdq,
+                            void* dk, attn_strides sdk,
+                            void* dv, attn_strides sdv,
+                            int B, int NH, int T, int d_qk, int d_v,
+                            float scale, int causal, int deterministic,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            unsigned stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN53_H */

@@ -1,0 +1,39 @@
+"""Deterministic dQ mode: every output bit-identical over 10 runs; atomic and
+deterministic modes agree within the bf16 tolerance."""
+import pytest
+import torch
+
+import exact_attention_53_amd as attn
+import workloads
+from tests.gpu_cases import check_bf16, gpu_inputs, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["mid_causal", "mid_full", "gpt2"])
+def test_bit_identical_over_10_runs(name):
+    w = workloads.WORKLOADS[name]
+    if not w.packed:
+        w = w.with_(B=4)  # same shape per head, fewer heads, to keep the test short
+    say(f"case determinism {w.name} B={w.B}")
+    _, gpu = gpu_inputs(w)
+    q, k, v, do = gpu["q"], gpu["k"], gpu["v"], gpu["do"]
+    o, lse = attn.fwd(q, k, v, w.causal, w.scale)
+    ref = None
+    for run in range(10):
+        o2, lse2 = attn.fwd(q, k, v, w.causal, w.scale)
+        dq, dk, dv = attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, deterministic=True)
+        torch.cuda.synchronize()
+        cur = [x.clone() for x in (o2, lse2, dq, dk, dv)]
+        if ref is None:
+            ref = cur
+        else:
+            for n, a, b in zip(("o", "lse", "dq", "dk", "dv"), ref, cur):
+                assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                                   b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), \
+                    f"{n} differs on run {run}"
+    # atomic mode agrees with deterministic mode within tolerance
+    dqa, dka, dva = attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, deterministic=False)
+    torch.cuda.synchronize()
+    for n, a, b in zip(("dq", "dk", "dv"), ref[2:], (dqa, dka, dva)):
+        check_bf16(f"atomic vs deterministic {n}", to_np(b), to_np(a))
