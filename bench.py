@@ -1,0 +1,192 @@
+"""Throughput of the fused exact-attention path (forward + backward) on one MI355X.
+
+A step is one forward and one backward pass (every stage of the hot path) over one
+batch of synthetic input already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--deterministic] [--no-cpu-baseline]
+
+FLOP convention: per unmasked (query, key) pair and head, the forward counts
+2 (d_qk + d_v) (S = QK^T, O = PV) and the backward 2 (3 d_qk + 2 d_v) (S recomputed,
+dQ, dK over d_qk; dP, dV over d_v).  Exp, max and elementwise work are not counted.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal attention fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(w):
+    pairs = w.pairs()
+    return 2.0 * (w.d_qk + w.d_v) * pairs, 2.0 * (3 * w.d_qk + 2 * w.d_v) * pairs
+
+
+def cpu_baseline(w, seconds_budget: float = 20.0):
+    """Times the CPU oracle (numpy float64) on a bounded sample of the same workload:
+    complete forward + backward of whole (b, h) heads."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads
+    from oracle import attn_ref
+
+    cpu = workloads.make_inputs(w)
+    per_head_flops = sum(flops(w.with_(B=1, NH=1)))
+    done, t_total, heads = 0, 0.0, []
+    all_heads = [(b, h) for b in range(w.B) for h in range(w.NH)]
+    while done < len(all_heads) and t_total < seconds_budget * 0.5:
+        hd = all_heads[done]
+        t0 = time.perf_counter()
+        attn_ref.attn_ref_heads(cpu["q"], cpu["k"], cpu["v"], cpu["do"], w.causal, w.scale, heads=[hd])
+        t_total += time.perf_counter() - t0
+        heads.append(hd)
+        done += 1
+    threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    return {
+        "value": per_head_flops * done / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(all_heads)} (b,h) heads of the {w.name} workload, full forward+backward "
+                  f"per head in numpy float64 ({t_total:.1f} s)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(attention shards over (batch, head) with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_53_amd as attn
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    cpu = workloads.make_inputs(w)
+    if w.packed:
+        qkv = cpu["qkv"].to(dev)
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    else:
+        q, k, v = (cpu[n].to(dev) for n in ("q", "k", "v"))
+    do = cpu["do"].to(dev)
+    del cpu
+    B, T, NH = w.B, w.T, w.NH
+    o = torch.empty((B, T, NH, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, NH, w.d_qk), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty((B, T, NH, w.d_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, args.deterministic), dtype=torch.uint8, device=dev)
+    det = args.deterministic
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws,
+                 stages=attn.PREPROCESS)
+        if ev is not None:
+            ev[2].record()
+        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws, stages=attn.MAIN)
+        if ev is not None:
+            ev[3].record()
+        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws,
+                 stages=attn.FINALIZE)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+
+    def avg(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
+
+    t_fwd, t_pre, t_main, t_fin = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    f_fwd, f_bwd = flops(w)
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    kernels = {
+        "attn_fwd": {"ms": t_fwd, "tflops": f_fwd / (t_fwd * 1e-3) / 1e12},
+        "bwd_preprocess": {"ms": t_pre},
+        "bwd_main": {"ms": t_main, "tflops": f_bwd / (t_main * 1e-3) / 1e12},
+        "bwd_finalize": {"ms": t_fin},
+    }
+    dom = "bwd_main" if t_main >= t_fwd else "attn_fwd"
+    achieved = kernels[dom]["tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B={B} NH={NH} T={T} d_qk={w.d_qk} d_v={w.d_v} "
+                        f"{'causal' if w.causal else 'non-causal'}, {'packed QKV' if w.packed else 'BTHD'}, "
+                        f"dQ mode {'deterministic' if det else 'atomic'}",
+            "B": B, "NH": NH, "T": T, "d_qk": w.d_qk, "d_v": w.d_v, "causal": w.causal,
+            "dq_mode": "deterministic" if det else "atomic",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / ((t_pre + t_main + t_fin) * 1e-3) / 1e12, 2),
+        "kernels_ms": {n: round(v["ms"], 4) for n, v in kernels.items()},
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

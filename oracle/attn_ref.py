@@ -38,7 +38,7 @@ the columns past a block's last query are left out: their P entries are exactly 
 """
 from __future__ import annotations
 
-from typing import Iterable, Optional, Sequence, Tuple
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -48,6 +48,7 @@ __all__ = [
     "head_backward",
     "attn_ref_fwd",
     "attn_ref_bwd",
+    "attn_ref_heads",
     "attn_ref_bwd_loop",
 ]
 
@@ -124,63 +125,69 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
     return dQ, dK, dV, O, lse, D
 
 
-def _heads(B: int, NH: int, heads: Optional[Iterable[Tuple[int, int]]]):
-    if heads is None:
-        return [(b, h) for b in range(B) for h in range(NH)]
-    return [(int(b), int(h)) for b, h in heads]
-
-
 def _block_rows(T: int, width: int) -> int:
     # keep each block's S/P/dP/dS at a few hundred MB
     return max(1, min(T, (1 << 25) // max(T, 1) // max(1, width // 64)))
 
 
-def attn_ref_fwd(q, k, v, causal: bool, scale: Optional[float] = None,
-                 heads: Optional[Sequence[Tuple[int, int]]] = None):
-    """Forward over (B, T, NH, d) tensors.
-
-    Returns O (B, T, NH, d_v) and LSE (B, NH, T) in float64.  With ``heads`` given,
-    only those (b, h) pairs are computed and every other entry is NaN.
-    """
+def attn_ref_fwd(q, k, v, causal: bool, scale: Optional[float] = None):
+    """Forward over (B, T, NH, d) tensors.  Returns O (B, T, NH, d_v) and LSE (B, NH, T)
+    in float64."""
     q, k, v = to_f64(q), to_f64(k), to_f64(v)
     B, T, NH, dqk = q.shape
     if scale is None:
         scale = 1.0 / np.sqrt(dqk)
-    O = np.full((B, T, NH, v.shape[3]), np.nan)
-    lse = np.full((B, NH, T), np.nan)
+    O = np.empty((B, T, NH, v.shape[3]))
+    lse = np.empty((B, NH, T))
     br = _block_rows(T, dqk)
-    for b, h in _heads(B, NH, heads):
-        O[b, :, h], lse[b, h] = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, br)
+    for b in range(B):
+        for h in range(NH):
+            O[b, :, h], lse[b, h] = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, br)
     return O, lse
 
 
-def attn_ref_bwd(q, k, v, do, causal: bool, scale: Optional[float] = None,
-                 heads: Optional[Sequence[Tuple[int, int]]] = None):
-    """Backward over (B, T, NH, d) tensors.
-
-    Returns a dict with dq, dk, dv (B, T, NH, d), o (B, T, NH, d_v), lse and D (B, NH, T),
-    all float64; entries of heads not listed in ``heads`` are NaN.
-    """
+def attn_ref_bwd(q, k, v, do, causal: bool, scale: Optional[float] = None):
+    """Backward over (B, T, NH, d) tensors.  Returns a dict with dq, dk, dv
+    (B, T, NH, d), o (B, T, NH, d_v), lse and D (B, NH, T), all float64."""
     q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
     B, T, NH, dqk = q.shape
-    dv_ = v.shape[3]
     if scale is None:
         scale = 1.0 / np.sqrt(dqk)
     out = {
-        "dq": np.full((B, T, NH, dqk), np.nan),
-        "dk": np.full((B, T, NH, dqk), np.nan),
-        "dv": np.full((B, T, NH, dv_), np.nan),
-        "o": np.full((B, T, NH, dv_), np.nan),
-        "lse": np.full((B, NH, T), np.nan),
-        "D": np.full((B, NH, T), np.nan),
+        "dq": np.empty((B, T, NH, dqk)),
+        "dk": np.empty((B, T, NH, dqk)),
+        "dv": np.empty((B, T, NH, v.shape[3])),
+        "o": np.empty((B, T, NH, v.shape[3])),
+        "lse": np.empty((B, NH, T)),
+        "D": np.empty((B, NH, T)),
     }
     br = _block_rows(T, dqk)
-    for b, h in _heads(B, NH, heads):
-        dQ, dK, dV, O, lse, D = head_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h],
-                                              scale, causal, br)
-        out["dq"][b, :, h], out["dk"][b, :, h], out["dv"][b, :, h] = dQ, dK, dV
-        out["o"][b, :, h], out["lse"][b, h], out["D"][b, h] = O, lse, D
+    for b in range(B):
+        for h in range(NH):
+            r = head_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal, br)
+            for name, x in zip(("dq", "dk", "dv", "o"), r[:4]):
+                out[name][b, :, h] = x
+            out["lse"][b, h], out["D"][b, h] = r[4], r[5]
     return out
+
+
+def attn_ref_heads(q, k, v, do, causal: bool, scale: Optional[float] = None,
+                   heads: Sequence[Tuple[int, int]] = ()):
+    """Forward and backward of selected (b, h) heads of (B, T, NH, d) tensors; only
+    those heads are converted to float64.  Returns {(b, h): {"dq", "dk", "dv", "o":
+    (T, d) arrays, "lse", "D": (T,) arrays}}."""
+    dqk = q.shape[3]
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    T = q.shape[1]
+    br = _block_rows(T, dqk)
+    res = {}
+    for b, h in heads:
+        b, h = int(b), int(h)
+        qh, kh, vh, dh = (np.ascontiguousarray(to_f64(x[b, :, h])) for x in (q, k, v, do))
+        r = head_backward(qh, kh, vh, dh, scale, causal, br)
+        res[(b, h)] = dict(zip(("dq", "dk", "dv", "o", "lse", "D"), r))
+    return res
 
 
 def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None):

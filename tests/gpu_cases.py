@@ -66,7 +66,7 @@ def gpu_inputs(w: workloads.Workload, layout: str = "bthd") -> Tuple[Dict[str, t
 
 
 def run_gpu(w: workloads.Workload, gpu: Dict[str, torch.Tensor], deterministic: bool, layout: str = "bthd"):
-    """Forward then backward on the GPU; returns numpy (B, T, NH, d) / (B, NH, T) arrays."""
+    """Forward then backward on the GPU; returns host tensors (B, T, NH, d) / (B, NH, T)."""
     if w.packed:
         o, lse = attn.fwd_packed(gpu["qkv"], w.causal, w.scale)
         dqkv = attn.bwd_packed(gpu["qkv"], o, lse, gpu["do"], w.causal, w.scale, deterministic)
@@ -79,28 +79,35 @@ def run_gpu(w: workloads.Workload, gpu: Dict[str, torch.Tensor], deterministic: 
     out = {"o": o, "dq": dq, "dk": dk, "dv": dv}
     if layout == "bhtd" and not w.packed:
         out = {n: x.permute(0, 2, 1, 3) for n, x in out.items()}
-    res = {n: to_np(x) for n, x in out.items()}
-    res["lse"] = to_np(lse)
+    res = {n: x.to("cpu") for n, x in out.items()}  # bf16 on the host; heads converted on demand
+    res["lse"] = lse.to("cpu")
     return res
 
 
-def compare(w: workloads.Workload, got: Dict[str, np.ndarray], ref: Dict[str, np.ndarray],
-            heads: Optional[Sequence[Tuple[int, int]]] = None, tag: str = "") -> Dict[str, float]:
-    """Element-by-element comparison over all heads, or over the listed (b, h) heads."""
-    hs = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.NH)]
+def compare(w: workloads.Workload, got: Dict[str, np.ndarray], ref, heads=None, tag: str = "") -> Dict[str, float]:
+    """Element-by-element comparison.  ``ref`` is either the oracle's full result
+    (heads=None: every head is compared) or its per-head result {(b, h): {...}}."""
+    if heads is None:
+        hs = [(b, h) for b in range(w.B) for h in range(w.NH)]
+        per = {(b, h): {n: ref[n][b, :, h] for n in ("o", "dq", "dk", "dv")} | {"lse": ref["lse"][b, h]}
+               for b, h in hs}
+    else:
+        hs, per = list(heads), ref
     ratios = {}
     for name in ("o", "dq", "dk", "dv"):
-        g = np.stack([got[name][b, :, h] for b, h in hs])
-        r = np.stack([ref[name][b, :, h] for b, h in hs])
+        g = np.stack([to_np(got[name][b, :, h]) for b, h in hs])
+        r = np.stack([per[(b, h)][name] for b, h in hs])
         ratios[name] = check_bf16(f"{tag}{w.name} {name}", g, r)
-    g = np.stack([got["lse"][b, h] for b, h in hs])
-    r = np.stack([ref["lse"][b, h] for b, h in hs])
+    g = np.stack([to_np(got["lse"][b, h]) for b, h in hs])
+    r = np.stack([per[(b, h)]["lse"] for b, h in hs])
     ratios["lse"] = check_lse(f"{tag}{w.name} lse", g, r)
     return ratios
 
 
 def oracle(w: workloads.Workload, cpu: Dict[str, torch.Tensor], heads=None):
-    return attn_ref.attn_ref_bwd(cpu["q"], cpu["k"], cpu["v"], cpu["do"], w.causal, w.scale, heads=heads)
+    if heads is None:
+        return attn_ref.attn_ref_bwd(cpu["q"], cpu["k"], cpu["v"], cpu["do"], w.causal, w.scale)
+    return attn_ref.attn_ref_heads(cpu["q"], cpu["k"], cpu["v"], cpu["do"], w.causal, w.scale, heads=heads)
 
 
 def sample_heads(w: workloads.Workload, n: int, seed: int = 0):

@@ -32,13 +32,16 @@ def test_block_rows_match_whole_rows():
             np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
 
 
-def test_heads_subset_leaves_others_nan():
+def test_selected_heads_match_full_run():
     rng = np.random.default_rng(4)
-    q, k, v, do = rng.standard_normal((4, 1, 9, 3, 8))
+    q, k, v, do = rng.standard_normal((4, 2, 9, 3, 8))
     full = attn_ref.attn_ref_bwd(q, k, v, do, True)
-    part = attn_ref.attn_ref_bwd(q, k, v, do, True, heads=[(0, 1)])
-    np.testing.assert_array_equal(part["dq"][0, :, 1], full["dq"][0, :, 1])
-    assert np.isnan(part["dq"][0, :, 0]).all()
+    part = attn_ref.attn_ref_heads(q, k, v, do, True, heads=[(0, 1), (1, 2)])
+    assert sorted(part) == [(0, 1), (1, 2)]
+    for (b, h), r in part.items():
+        for name in ("dq", "dk", "dv", "o"):
+            np.testing.assert_array_equal(r[name], full[name][b, :, h])
+        np.testing.assert_array_equal(r["lse"], full["lse"][b, h])
 
 
 # ---------------------------------------------------------------------------------
