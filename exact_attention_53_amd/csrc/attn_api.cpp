@@ -72,7 +72,7 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
-    case ATTN_ERR_ARG: return "invalid argument: scale must be finite, flags 0 or 1, stage mask non-empty";
+    case ATTN_ERR_ARG: return "invalid argument: scale must be finite and > 0, flags 0 or 1, stage mask non-empty";
     case ATTN_ERR_ALIAS: return "an output tensor overlaps an input tensor";
   }
   return "unknown attn_status";
@@ -85,7 +85,7 @@ attn_status attn_fwd(const void* q, attn_strides sq, const void* k, attn_strides
                      int d_v, float scale, int causal, void* stream) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
-  if (!std::isfinite(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
   Extent eq, ek, ev, eo;
   if ((st = check_tensor(q, sq, B, NH, T, d_qk, &eq)) != ATTN_OK) return st;
   if ((st = check_tensor(k, sk, B, NH, T, d_qk, &ek)) != ATTN_OK) return st;
@@ -123,7 +123,8 @@ attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_
                             unsigned stages) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
-  if (!std::isfinite(scale) || (causal != 0 && causal != 1) || (deterministic != 0 && deterministic != 1))
+  if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1) ||
+      (deterministic != 0 && deterministic != 1))
     return ATTN_ERR_ARG;
   if (stages == 0 || (stages & ~ATTN_BWD_ALL) != 0) return ATTN_ERR_ARG;
   Extent eq, ek, ev, eo, edo, edq, edk, edv;

@@ -4,21 +4,32 @@
 //   [SA8]  "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析" 2.1, A.1 (S, P, O), 1.2-1.3 (stats,
 //          inference mode, packed QKV strides)
 //   [FAT]  "FlashAttention Triton实现中的内存访问模式优化与寄存器分配策略" 2.2 (one program per query
-//          block, Q loaded once, running max/sum in on-chip state), 4.2 (deferred normalisation)
+//          block, Q loaded once, running max/sum in on-chip state), 3 (bank conflicts of
+//          column reads of K), 4.2 (deferred normalisation), 5 (special-function cost)
 //   [2CTA] "深度学习反向传播优化：2-CTA MMA模式与内存访问优化" 3.2, 6.2 (head/batch swizzle,
 //          longest-first order, diagonal-first causal traversal)
 //
 // Structure.  A workgroup of 4 wavefronts owns FWD_BM = 128 query rows of one (b, h);
 // wavefront w owns rows 32w .. 32w+31 and keeps them in registers as the B operand of
-// S^T = K Q^T (so each lane owns one query row and its running max / sum).  Key/value
-// tiles of FWD_BN = 64 rows are staged into double-buffered, swizzled LDS.  For each
-// tile:  S^T (2 x d_qk/16 MFMAs), scale into base 2, causal / tail mask, running max
-// across the tile (one lane swap), p = 2^(x - m), l = alpha l + sum p,
-// O^T = alpha O^T + V^T P^T (d_v/32 x 4 MFMAs with P^T straight from the S^T
-// accumulators).  After the last tile O = O^T / l and LSE = ln 2 (m + log2 l).
-// Causal: tiles wholly above the diagonal are never loaded; the one or two diagonal
-// tiles come first and are the only ones masked; a wavefront skips tiles that lie
-// wholly above its own rows.
+// S^T = K Q^T, so each lane owns one query row and its running max / sum.  Two
+// workgroups share a CU (<= 256 registers per lane), so one wavefront's softmax
+// overlaps another's matrix work.  Key/value tiles of FWD_BN = 64 rows are
+// double-buffered in LDS:
+//   * K [64 keys][d_qk] row-major in swizzled 128-byte rows, filled by direct
+//     global->LDS loads (global_load_lds_dwordx4; the swizzle is applied by choosing
+//     which global chunk each lane fetches);
+//   * V [64 keys][d_v] the same way; the A operand of O^T += V^T P^T is read
+//     column-wise with ds_read_b64_tr_b16, which the swizzle keeps conflict-free (two
+//     8-byte transposed reads cost the same LDS cycles as one 16-byte row read).  The
+//     key order of those reads matches the accumulator layout of S^T, so P^T feeds
+//     the MFMA straight from registers.
+// Per tile: S^T (2 x d_qk/16 MFMAs), causal / tail mask on diagonal tiles only, row
+// max across the tile (one lane swap), p = 2^(S c - m), l += sum p,
+// O^T += V^T P^T (d_v/32 x 4 MFMAs).  The running max m is only raised, and O and l
+// only rescaled, when a row's maximum grows by more than 2^8; between raises p <= 2^8.
+// The result O = O^T / l and LSE = ln 2 (m + log2 l) do not depend on when m was raised.
+// Causal: tiles wholly above the diagonal are never loaded; the diagonal tile(s) come
+// first; a wavefront skips tiles that lie wholly above its rows.
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 
@@ -27,15 +38,22 @@ namespace attn53 {
 constexpr int FWD_BM = 128;
 constexpr int FWD_BN = 64;
 constexpr int FWD_NT = 256;
+constexpr float kRescaleThreshold = 8.f;  // log2 units
 
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(FWD_NT) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr int KS = DQK / 16;
   constexpr int NDT = DV / 32;
   constexpr int KT_BYTES = FWD_BN * DQK * 2;
   constexpr int VT_BYTES = FWD_BN * DV * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * (KT_BYTES + VT_BYTES)];
+  constexpr int K_LOADS = KT_BYTES / 1024 / (FWD_NT / 64);  // 1 KB global->LDS blocks per wave
+  constexpr int V_LOADS = VT_BYTES / 1024 / (FWD_NT / 64);
+  static_assert(KT_BYTES % (1024 * (FWD_NT / 64)) == 0 && VT_BYTES % (1024 * (FWD_NT / 64)) == 0,
+                "tiles not divisible into wave blocks");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * (KT_BYTES + VT_BYTES)];
   ATTN_LDS char* lds = (ATTN_LDS char*)smem;
+  ATTN_LDS char* ktile = lds;                   // [2][KT_BYTES]
+  ATTN_LDS char* vtile = lds + 2 * KT_BYTES;    // [2][VT_BYTES]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
   const int T = p.T;
@@ -48,6 +66,7 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(FwdParams p) {
   const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
   const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
   bf16* og = (bf16*)p.o + b * p.so.b + h * p.so.h;
+  const int64_t skt = p.sk.t, svt = p.sv.t;
 
   const int q0 = qb * FWD_BM;
   const int qw = q0 + 32 * w;
@@ -62,92 +81,97 @@ __global__ __launch_bounds__(FWD_NT) void fwd_kernel(FwdParams p) {
     qf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
 
+  // Direct global->LDS tile loads: wave w fills 1 KB blocks w, w+4, ...; a block is 8
+  // rows x 128 bytes of one 64-column panel and lane l lands at byte 16 l of it, so the
+  // lane fetches the global chunk that the swizzle puts there.  Rows past T are
+  // clamped to T-1 (always masked afterwards).
+  const int blk_row = lane >> 3;
+  auto load_tile = [&](const bf16* src, int64_t ld, int row0, ATTN_LDS char* dst, int nloads) {
+    for (int i = 0; i < nloads; ++i) {
+      const int blk = w + (FWD_NT / 64) * i;
+      const int r = 8 * (blk % (FWD_BN / 8)) + blk_row;
+      const int col = 64 * (blk / (FWD_BN / 8)) + 8 * ((lane & 7) ^ (int)swz(r));
+      const int row = min(row0 + r, T - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(src + row * ld + col), (ATTN_LDS void*)(dst + blk * 1024),
+                                       16, 0, 0);
+    }
+  };
+  auto load_kv = [&](int key0, int buf) {
+    load_tile(kg, skt, key0, ktile + buf * KT_BYTES, K_LOADS);
+    load_tile(vg, svt, key0, vtile + buf * VT_BYTES, V_LOADS);
+  };
+
   const int kv_end = CAUSAL ? min(T, q0 + FWD_BM) : T;
   const int n_kv = (kv_end + FWD_BN - 1) / FWD_BN;
-
-  TileStage<FWD_BN, DQK, FWD_NT> kst;
-  TileStage<FWD_BN, DV, FWD_NT> vst;
-  kst.load(kg, p.sk.t, (n_kv - 1) * FWD_BN, T, tid);
-  vst.load(vg, p.sv.t, (n_kv - 1) * FWD_BN, T, tid);
-  kst.store(lds, tid);
-  vst.store(lds + 2 * KT_BYTES, tid);
-  __syncthreads();
+  const float c = p.scale_log2;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = zero16();
 
+  load_kv((n_kv - 1) * FWD_BN, 0);
+
   for (int it = 0; it < n_kv; ++it) {
     const int j = n_kv - 1 - it;  // diagonal / tail tile first
     const int buf = it & 1;
-    const bool more = it + 1 < n_kv;
-    if (more) {
-      kst.load(kg, p.sk.t, (j - 1) * FWD_BN, T, tid);
-      vst.load(vg, p.sv.t, (j - 1) * FWD_BN, T, tid);
-    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile j has landed in LDS
+    __syncthreads();                // ... and every other wave's; buffer buf^1 is free
+    if (it + 1 < n_kv) load_kv((j - 1) * FWD_BN, buf ^ 1);
     const int key0 = j * FWD_BN;
     const bool active = !CAUSAL || key0 <= qw + 31;
-    if (active) {
-      const ATTN_LDS char* kt = lds + buf * KT_BYTES;
-      const ATTN_LDS char* vt = lds + 2 * KT_BYTES + buf * VT_BYTES;
-      // S^T = K Q^T for keys key0 .. key0+63 (two 32-key accumulators)
-      f32x16 s0 = zero16(), s1 = zero16();
+    if (!active) continue;
+    const ATTN_LDS char* kt = ktile + buf * KT_BYTES;
+    const ATTN_LDS char* vt = vtile + buf * VT_BYTES;
+    // S^T = K Q^T for keys key0 .. key0+63 (two 32-key accumulators)
+    f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a0 = lds_row8<FWD_BN>(kt, lq, 16 * ks + 8 * g);
-        const bf16x8 a1 = lds_row8<FWD_BN>(kt, 32 + lq, 16 * ks + 8 * g);
-        s0 = mfma32(a0, qf[ks], s0);
-        s1 = mfma32(a1, qf[ks], s1);
-      }
-      // scale into base 2, mask, tile max
-      const bool need_mask = (CAUSAL && key0 + FWD_BN - 1 > qw) || (key0 + FWD_BN > T);
-      float mx = -INFINITY;
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = mfma32(lds_row8<FWD_BN>(kt, lq, 16 * ks + 8 * g), qf[ks], s0);
+      s1 = mfma32(lds_row8<FWD_BN>(kt, 32 + lq, 16 * ks + 8 * g), qf[ks], s1);
+    }
+    if ((CAUSAL && key0 + FWD_BN - 1 > qw) || key0 + FWD_BN > T) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x0 = s0[r] * p.scale_log2, x1 = s1[r] * p.scale_log2;
-        if (need_mask) {
-          const int kk0 = key0 + 8 * (r >> 2) + 4 * g + (r & 3), kk1 = kk0 + 32;
-          if (kk0 >= T || (CAUSAL && kk0 > my_q)) x0 = -INFINITY;
-          if (kk1 >= T || (CAUSAL && kk1 > my_q)) x1 = -INFINITY;
-        }
-        s0[r] = x0;
-        s1[r] = x1;
-        mx = fmaxf(mx, fmaxf(x0, x1));
+        const int kk0 = key0 + 8 * (r >> 2) + 4 * g + (r & 3), kk1 = kk0 + 32;
+        if (kk0 >= T || (CAUSAL && kk0 > my_q)) s0[r] = -INFINITY;
+        if (kk1 >= T || (CAUSAL && kk1 > my_q)) s1[r] = -INFINITY;
       }
-      mx = max_halves(mx);
-      // Every processed tile holds key key0 <= every row of this wave, so m_new is finite.
-      const float m_new = fmaxf(m_run, mx);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    // Every processed tile holds key key0 <= every row of this wave, so mx is finite.
+    const float m_tile = max_halves(mx) * c;
+    if (__any(m_tile > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, m_tile);
       const float alpha = exp2_fast(m_run - m_new);
       m_run = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p0 = exp2_fast(s0[r] - m_new), p1 = exp2_fast(s1[r] - m_new);
-        rs += p0 + p1;
-        s0[r] = p0;
-        s1[r] = p1;
-      }
-      l_run = l_run * alpha + rs;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      const bf16x8 pb0 = pack8(s0, 0), pb1 = pack8(s0, 1), pb2 = pack8(s1, 0), pb3 = pack8(s1, 1);
-      // O^T += V^T P^T
+    }
+    float rs = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        o[dt] = mfma32(lds_col8<FWD_BN>(vt, 0, 32 * dt, lane), pb0, o[dt]);
-        o[dt] = mfma32(lds_col8<FWD_BN>(vt, 16, 32 * dt, lane), pb1, o[dt]);
-        o[dt] = mfma32(lds_col8<FWD_BN>(vt, 32, 32 * dt, lane), pb2, o[dt]);
-        o[dt] = mfma32(lds_col8<FWD_BN>(vt, 48, 32 * dt, lane), pb3, o[dt]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = exp2_fast(__builtin_fmaf(s0[r], c, -m_run));
+      const float p1 = exp2_fast(__builtin_fmaf(s1[r], c, -m_run));
+      rs += p0 + p1;
+      s0[r] = p0;
+      s1[r] = p1;
     }
-    if (more) {
-      kst.store(lds + (buf ^ 1) * KT_BYTES, tid);
-      vst.store(lds + 2 * KT_BYTES + (buf ^ 1) * VT_BYTES, tid);
+    l_run += rs;
+    const bf16x8 pb0 = pack8(s0, 0), pb1 = pack8(s0, 1), pb2 = pack8(s1, 0), pb3 = pack8(s1, 1);
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      o[dt] = mfma32(lds_col8<FWD_BN>(vt, 0, 32 * dt, lane), pb0, o[dt]);
+      o[dt] = mfma32(lds_col8<FWD_BN>(vt, 16, 32 * dt, lane), pb1, o[dt]);
+      o[dt] = mfma32(lds_col8<FWD_BN>(vt, 32, 32 * dt, lane), pb2, o[dt]);
+      o[dt] = mfma32(lds_col8<FWD_BN>(vt, 48, 32 * dt, lane), pb3, o[dt]);
     }
-    __syncthreads();
   }
 
   // deferred normalisation and stats

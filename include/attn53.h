@@ -25,7 +25,8 @@
  *  - LSE ("softmax stats" of [SA8 1.2, 1.3]) is fp32, contiguous (B, NH, T), and holds
  *    the natural-log logsumexp of each row of S = scale * Q K^T (mask applied).
  *  - causal = 1 masks key j > query i (top-left aligned, [SA8 2.2] loop bound).
- *  - scale multiplies Q K^T; the pages use 1/sqrt(d_k) [SA8 2.1].  Must be finite.
+ *  - scale multiplies Q K^T; the pages use 1/sqrt(d_k) [SA8 2.1].  Must be finite and
+ *    > 0 (the kernels take each row maximum before scaling).
  *
  * Ownership, errors, execution
  * ----------------------------
@@ -59,7 +60,7 @@ typedef enum {
   ATTN_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned                    */
   ATTN_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required             */
   ATTN_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed          */
-  ATTN_ERR_ARG = 8,        /* scale not finite, a flag not 0/1, bad stage mask     */
+  ATTN_ERR_ARG = 8,        /* scale not finite or <= 0, a flag not 0/1, bad stage mask */
   ATTN_ERR_ALIAS = 9       /* an output overlaps an input                         */
 } attn_status;
 

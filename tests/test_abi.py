@@ -76,6 +76,8 @@ def test_fwd_validation(lib):
     assert fwd(lib, sq=S(-8, 64, 128)) == STRIDE
     assert fwd(lib, scale=float("nan")) == ARG
     assert fwd(lib, scale=float("inf")) == ARG
+    assert fwd(lib, scale=0.0) == ARG
+    assert fwd(lib, scale=-0.125) == ARG
     assert fwd(lib, causal=2) == ARG
     assert fwd(lib, o=GOOD) == ALIAS               # output overlaps q
     assert fwd(lib, lse=GOOD + 0x300002) == ALIGN   # lse must be 4-byte aligned
@@ -104,6 +106,7 @@ def test_bwd_validation(lib):
     assert bwd(lib, dq=GOOD) == ALIAS          # dq overlaps q
     assert bwd(lib, ws=GOOD + 0x100000) == ALIAS  # workspace overlaps k
     assert bwd(lib, scale=float("nan")) == ARG
+    assert bwd(lib, scale=-1.0) == ARG
 
 
 def test_workspace_bytes(lib):
