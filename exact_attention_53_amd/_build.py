@@ -61,8 +61,19 @@ def build(verbose: bool = False) -> str:
                 print(out)
     tmp = OUT + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    _check_kernel_stubs(tmp)
     os.replace(tmp, OUT)
     return OUT
+
+
+def _check_kernel_stubs(path: str) -> None:
+    """Every kernel launched from host code must have its host-side stub defined; a
+    silently dropped instantiation would otherwise only fail when the library loads."""
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    r = subprocess.run([nm, "-C", path], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    missing = [l.strip() for l in r.stdout.splitlines() if "__device_stub__" in l and l.strip().startswith("U ")]
+    if missing:
+        raise RuntimeError("build produced undefined kernel stubs:\n" + "\n".join(missing))
 
 
 if __name__ == "__main__":

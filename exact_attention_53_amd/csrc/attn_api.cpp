@@ -38,6 +38,7 @@ attn_status check_tensor(const void* ptr, attn_strides s, int B, int NH, int T, 
   if (ptr == nullptr) return ATTN_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return ATTN_ERR_ALIGN;
   if (s.b < 0 || s.h < 0 || s.t < 0 || s.b % 8 || s.h % 8 || s.t % 8) return ATTN_ERR_STRIDE;
+  if (s.t > (int64_t)1 << 24) return ATTN_ERR_STRIDE;  // keeps per-tile byte offsets within 32 bits
   const int64_t last = s.b * (B - 1) + s.h * (NH - 1) + s.t * (int64_t)(T - 1) + d;
   ext->lo = reinterpret_cast<uintptr_t>(ptr);
   ext->hi = ext->lo + (uintptr_t)last * 2u;
@@ -68,7 +69,7 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "B, NH and T must be >= 1 and B*NH*T must fit in int32";
     case ATTN_ERR_HEADDIM: return "unsupported head dims: (d_qk, d_v) must be (64,64), (128,128) or (192,128)";
-    case ATTN_ERR_STRIDE: return "strides must be non-negative multiples of 8 elements";
+    case ATTN_ERR_STRIDE: return "strides must be non-negative multiples of 8 elements, the t stride at most 2^24";
     case ATTN_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";

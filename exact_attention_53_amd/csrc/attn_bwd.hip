@@ -27,6 +27,8 @@
 //                      registers (S and dP recomputed), so dQ is bit-identical from run
 //                      to run; the kv kernel then issues no atomics.
 //   bwd_finalize_kernel dQ = scale * accumulator -> bf16 (atomic mode).
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 
@@ -74,27 +76,38 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int d_qk, int
 // ---------------------------------------------------------------------------------
 // main backward: key/value-stationary
 // ---------------------------------------------------------------------------------
+// LDS (d = 128): K block 32 KB (B operand of the partial dQ = dS K), Q and dO tiles
+// 2 x 16 KB each (double-buffered direct global->LDS loads), dS^T 2 x 16 KB, LSE and
+// D 2 x 256 B each.  Every buffer is its own LDS object so that reads of one buffer
+// do not wait for the loads in flight into the other.  Per query block i (one step):
+//   top:    wait for this step's tiles, barrier, start the loads of step i+1;
+//   dQ:     partial dQ of step i-1 (64 x d_qk) = dS K from the dS^T tile that step
+//           left in LDS, then fp32 atomic adds into the accumulator [2CTA 3.1]; the
+//           adds drain behind this step's matrix work;
+//   S, dP   (2 x d/16 MFMAs each; A operands are row reads of Q / dO);
+//   P, dS   on the VALU; dV += P^T dO and dK += dS^T Q with the B operands read
+//           column-wise (ds_read_b64_tr_b16);
+//   dS^T -> LDS for the next step's dQ.
+// With d_qk = 192 LDS holds one dS^T buffer only; a barrier then separates the last
+// reads of the previous tile from the writes of the new one.
 template <int DQK, int DV, bool CAUSAL, bool ATOMIC_DQ>
 __global__ __launch_bounds__(BWD_NT) void bwd_kv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
-  constexpr int NDQ = DQK / 32 / 2;                     // dQ tiles per wavefront
-  constexpr int QT_BYTES = BWD_BM * DQK * 2;            // Q tile
-  constexpr int OT_BYTES = BWD_BM * DV * 2;             // dO tile
-  constexpr int KD_BYTES = ATOMIC_DQ ? BWD_BN * DQK * 2 : 0;   // K block for dQ = dS K
-  constexpr int ST_BYTES = ATOMIC_DQ ? BWD_BN * BWD_BM * 2 : 0;  // dS^T tile
-  constexpr int OFF_Q = 0;
-  constexpr int OFF_O = OFF_Q + 2 * QT_BYTES;
-  constexpr int OFF_K = OFF_O + 2 * OT_BYTES;
-  constexpr int OFF_S = OFF_K + KD_BYTES;
-  constexpr int OFF_L = OFF_S + ST_BYTES;                // lse*log2e and D, 2 buffers
-  constexpr int LDS_BYTES = OFF_L + 2 * 2 * BWD_BM * 4;
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-  ATTN_LDS char* lds = (ATTN_LDS char*)smem;
+  constexpr int NDQ = DQK / 32 / 2;  // dQ tiles per wavefront
+  constexpr int QT_BYTES = BWD_BM * DQK * 2;
+  constexpr int OT_BYTES = BWD_BM * DV * 2;
+  constexpr int KD_BYTES = ATOMIC_DQ ? BWD_BN * DQK * 2 : 16;
+  constexpr int ST_BYTES = ATOMIC_DQ ? BWD_BN * BWD_BM * 2 : 16;
+  constexpr bool ST_DOUBLE = DQK <= 128;
+  __shared__ __attribute__((aligned(1024))) char qbuf0[QT_BYTES], qbuf1[QT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char obuf0[OT_BYTES], obuf1[OT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kd_lds[KD_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st0[ST_BYTES], st1[ST_DOUBLE ? ST_BYTES : 16];
+  __shared__ __attribute__((aligned(256))) float lse0[BWD_BM], lse1[BWD_BM], dd0[BWD_BM], dd1[BWD_BM];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
   const int T = p.T;
-  const int nkb = (T + BWD_BN - 1) / BWD_BN;
   const int nqb = (T + BWD_BM - 1) / BWD_BM;
   const Item item = schedule(blockIdx.x, p.B * p.NH);
   const int kb = item.rank;  // causal: block 0 has the most query blocks -> first
@@ -106,12 +119,13 @@ __global__ __launch_bounds__(BWD_NT) void bwd_kv_kernel(BwdParams p) {
   const bf16* dog = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h;
   const float* lseg = p.lse + (int64_t)item.bh * T;
   const float* Dg = p.D + (int64_t)item.bh * p.Tpad;
-  float* dqacc = p.dq_acc + (int64_t)item.bh * p.Tpad * DQK;
-  (void)nkb;
+  const int64_t sqt = p.sq.t, sdot = p.sdo.t;
 
+  const LdsLane L = lds_lane(lane);
   const int key0 = kb * BWD_BN;
   const int kw = 32 * w;
   const int my_key = key0 + kw + lq;
+  const float c = p.scale_log2;
 
   // K and V rows of this wavefront as B-operand fragments of S = Q K^T and dP = dO V^T.
   bf16x8 kf[KSQ], vf[KSV];
@@ -128,134 +142,177 @@ __global__ __launch_bounds__(BWD_NT) void bwd_kv_kernel(BwdParams p) {
     vf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  const int i0 = CAUSAL ? key0 / BWD_BM : 0;
-  const int n_q = nqb - i0;
-
-  TileStage<BWD_BM, DQK, BWD_NT> qst;
-  TileStage<BWD_BM, DV, BWD_NT> ost;
-  float lsev = 0.f, dval = 0.f;  // threads 0..63: LSE*log2e, threads 64..127: D
-  auto load_rows = [&](int qb) {
-    qst.load(qg, p.sq.t, qb * BWD_BM, T, tid);
-    ost.load(dog, p.sdo.t, qb * BWD_BM, T, tid);
-    const int r = qb * BWD_BM + (tid & 63);
-    if (tid < 64) lsev = r < T ? lseg[r] * kLog2e : INFINITY;  // rows >= T: P = 0
-    else if (tid < 128) dval = r < T ? Dg[r] : 0.f;
-  };
-  auto store_rows = [&](int buf) {
-    qst.store(lds + OFF_Q + buf * QT_BYTES, tid);
-    ost.store(lds + OFF_O + buf * OT_BYTES, tid);
-    float* lb = (float*)(smem + OFF_L + buf * 2 * BWD_BM * 4);
-    if (tid < 64) lb[tid] = lsev;
-    else if (tid < 128) lb[BWD_BM + tid - 64] = dval;
+  DirectTile<BWD_BM, DQK, BWD_NT / 64> qload;
+  DirectTile<BWD_BM, DV, BWD_NT / 64> oload;
+  qload.init(sqt, w, lane);
+  oload.init(sdot, w, lane);
+  auto load_step = [&](int qb, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int r0 = qb * BWD_BM;
+    qload.issue(qg + r0 * sqt, sqt, T - r0, (ATTN_LDS char*)(BUF ? qbuf1 : qbuf0), w);
+    oload.issue(dog + r0 * sdot, sdot, T - r0, (ATTN_LDS char*)(BUF ? obuf1 : obuf0), w);
+    if (w == 0) {  // 64 rows of LSE (clamped; rows past T are masked) and of D (padded)
+      const int r = min(r0 + lane, T - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(lseg + r), (ATTN_LDS void*)(BUF ? lse1 : lse0), 4, 0, 0);
+    } else if (w == 1) {
+      __builtin_amdgcn_global_load_lds((const void*)(Dg + r0 + lane), (ATTN_LDS void*)(BUF ? dd1 : dd0), 4, 0, 0);
+    }
   };
 
-  if (ATOMIC_DQ) {
+  if constexpr (ATOMIC_DQ) {
     TileStage<BWD_BN, DQK, BWD_NT> kst;
     kst.load(kg, p.sk.t, key0, T, tid);
-    kst.store(lds + OFF_K, tid);
+    kst.store((ATTN_LDS char*)kd_lds, tid);
   }
-  load_rows(i0);
-  store_rows(0);
-  __syncthreads();
+
+  const int i0 = CAUSAL ? key0 / BWD_BM : 0;
+  const int n_q = nqb - i0;
 
   f32x16 dk[NDK], dv[NDV];
 #pragma unroll
   for (int t = 0; t < NDK; ++t) dk[t] = zero16();
 #pragma unroll
   for (int t = 0; t < NDV; ++t) dv[t] = zero16();
+  const int tq = w & 1;               // dQ: query tile of this wavefront
+  const int dq_t0 = (w >> 1) * NDQ;   //     first d tile
+  float* dqacc = ATOMIC_DQ ? p.dq_acc + (int64_t)item.bh * p.Tpad * DQK : nullptr;
 
-  for (int it = 0; it < n_q; ++it) {
-    const int qb = i0 + it;
-    const int buf = it & 1;
-    const bool more = it + 1 < n_q;
-    if (more) load_rows(qb + 1);
-    const int q0 = qb * BWD_BM;
-    const ATTN_LDS char* qt = lds + OFF_Q + buf * QT_BYTES;
-    const ATTN_LDS char* ot = lds + OFF_O + buf * OT_BYTES;
-    const float* lb = (const float*)(smem + OFF_L + buf * 2 * BWD_BM * 4);
+  // partial dQ of the query block at q0 from the dS^T tile in `st`, added atomically
+  auto dq_partial = [&](const ATTN_LDS char* st, int q0) {
+    f32x16 dq[NDQ];
+#pragma unroll
+    for (int n = 0; n < NDQ; ++n) dq[n] = zero16();
+    const ATTN_LDS char* kd = (const ATTN_LDS char*)kd_lds;
+#pragma unroll
+    for (int m = 0; m < BWD_BN / 16; ++m) {
+      const bf16x8 a = lds_col8<BWD_BN>(st, L, 16 * m, 32 * tq);
+#pragma unroll
+      for (int n = 0; n < NDQ; ++n) dq[n] = mfma32(a, lds_col8<BWD_BN>(kd, L, 16 * m, 32 * (dq_t0 + n)), dq[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < NDQ; ++n) {
+      const int d = 32 * (dq_t0 + n) + lq;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 32 * tq + 8 * (r >> 2) + 4 * g + (r & 3);  // < Tpad
+        unsafeAtomicAdd(dqacc + (int64_t)q * DQK + d, dq[n][r]);
+      }
+    }
+  };
 
+  load_step(i0, std::integral_constant<int, 0>{});
+
+  // One query block.  MASKED: the block touches the diagonal or a ragged edge.  The
+  // body is one basic block in source order S, dP, P, dV, dS, dK so that the matrix
+  // work of dP and dV can run beside the VALU work of P and dS.
+  auto step_body = [&](int q0, auto bufc, auto maskc) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr bool MASKED = decltype(maskc)::value;
+    ATTN_LDS char* st_cur = (ATTN_LDS char*)((ST_DOUBLE && BUF) ? st1 : st0);
+    const ATTN_LDS char* qt = (const ATTN_LDS char*)(BUF ? qbuf1 : qbuf0);
+    const ATTN_LDS char* ot = (const ATTN_LDS char*)(BUF ? obuf1 : obuf0);
+    const float* lb = BUF ? lse1 : lse0;
+    const float* db = BUF ? dd1 : dd0;
+    if (MASKED && CAUSAL && key0 + kw > q0 + BWD_BM - 1) {
+      // every key of this wavefront lies above every query of the block: P = dS = 0
+      if constexpr (ATOMIC_DQ) {
+        if constexpr (!ST_DOUBLE) __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          *reinterpret_cast<ATTN_LDS u32x2*>(st_cur + tile_off<BWD_BN>(kw + lq, 16 * m + 4 * g)) = u32x2{0u, 0u};
+          *reinterpret_cast<ATTN_LDS u32x2*>(st_cur + tile_off<BWD_BN>(kw + lq, 16 * m + 8 + 4 * g)) = u32x2{0u, 0u};
+        }
+      }
+      return;
+    }
     // S = Q K^T and dP = dO V^T for 64 queries x this wavefront's 32 keys
     f32x16 s[2], dp[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = zero16();
-      dp[t] = zero16();
+    for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) s[t] = mfma32(lds_row8<BWD_BM>(qt, 32 * t + lq, 16 * ks + 8 * g), kf[ks], s[t]);
+      for (int t = 0; t < 2; ++t)
+        s[t] = mfma32(lds_row8<BWD_BM>(qt, L, 32 * t, ks), kf[ks], ks == 0 ? zero16() : s[t]);
 #pragma unroll
-      for (int ks = 0; ks < KSV; ++ks) dp[t] = mfma32(lds_row8<BWD_BM>(ot, 32 * t + lq, 16 * ks + 8 * g), vf[ks], dp[t]);
-    }
-    // P = 2^(S scale log2e - LSE log2e), dS = P (dP - D); element r of tile t is
-    // query q0 + 32 t + 8 (r / 4) + 4 g + r % 4, key my_key.
-    const bool need_mask = (CAUSAL && key0 + BWD_BN - 1 > q0) || (key0 + BWD_BN > T) || (q0 + BWD_BM > T);
+    for (int ks = 0; ks < KSV; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        dp[t] = mfma32(lds_row8<BWD_BM>(ot, L, 32 * t, ks), vf[ks], ks == 0 ? zero16() : dp[t]);
+    // P = 2^(S c - LSE log2 e); element r of tile t: query q0 + 32 t + 8 (r / 4) + 4 g + r % 4
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int qi = 32 * t + 8 * a + 4 * g;
-        const f32x4 L = *reinterpret_cast<const f32x4*>(lb + qi);
-        const f32x4 Dd = *reinterpret_cast<const f32x4*>(lb + BWD_BM + qi);
+        const f32x4 Lv = *reinterpret_cast<const f32x4*>(lb + qi);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * a + e;
-          float pv = exp2_fast(s[t][r] * p.scale_log2 - L[e]);
-          if (need_mask) {
+          float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -Lv[e] * kLog2e));
+          if constexpr (MASKED) {
             const int q = q0 + qi + e;
-            if (my_key >= T || q >= T || (CAUSAL && my_key > q)) pv = 0.f;
+            pv = (my_key >= T || q >= T || (CAUSAL && my_key > q)) ? 0.f : pv;
           }
           s[t][r] = pv;
-          dp[t][r] = pv * (dp[t][r] - Dd[e]);
         }
       }
     const bf16x8 pb[4] = {pack8(s[0], 0), pack8(s[0], 1), pack8(s[1], 0), pack8(s[1], 1)};
+    // dV += P^T dO  (contraction over the 64 queries)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int t = 0; t < NDV; ++t) dv[t] = mfma32(pb[m], lds_col8<BWD_BM>(ot, L, 16 * m, 32 * t), dv[t]);
+    // dS = P (dP - D)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 Dd = *reinterpret_cast<const f32x4*>(db + 32 * t + 8 * a + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[t][4 * a + e] = s[t][4 * a + e] * (dp[t][4 * a + e] - Dd[e]);
+      }
     const bf16x8 sb[4] = {pack8(dp[0], 0), pack8(dp[0], 1), pack8(dp[1], 0), pack8(dp[1], 1)};
-    // dV += P^T dO,  dK += dS^T Q   (contraction over the 64 queries)
+    // dK += dS^T Q
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int t = 0; t < NDV; ++t) dv[t] = mfma32(pb[m], lds_col8<BWD_BM>(ot, 16 * m, 32 * t, lane), dv[t]);
-#pragma unroll
-      for (int t = 0; t < NDK; ++t) dk[t] = mfma32(sb[m], lds_col8<BWD_BM>(qt, 16 * m, 32 * t, lane), dk[t]);
-    }
+      for (int t = 0; t < NDK; ++t) dk[t] = mfma32(sb[m], lds_col8<BWD_BM>(qt, L, 16 * m, 32 * t), dk[t]);
     if constexpr (ATOMIC_DQ) {
-      // dS^T tile in LDS: row = key (128), column = query (64)
-      ATTN_LDS char* st = lds + OFF_S;
+      if constexpr (!ST_DOUBLE) __syncthreads();  // every wave has read the previous dS^T
+      // dS^T tile in LDS: row = key (128), column = query (64); sb[m] holds queries
+      // 16 m + 4 g + {0..3} (elements 0..3) and 16 m + 8 + 4 g + {0..3} (elements 4..7)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (bf16)dp[t][4 * a + e];
-          *reinterpret_cast<ATTN_LDS bf16x4*>(st + tile_off<BWD_BN>(kw + lq, 32 * t + 8 * a + 4 * g)) = v;
-        }
-      __syncthreads();
-      // partial dQ (64 x DQK) = dS K over this block's 128 keys; wavefront w owns query
-      // tile w % 2 and d tiles (w / 2) * NDQ .. +NDQ-1
-      const int tq = w & 1;
-      f32x16 dq[NDQ];
-#pragma unroll
-      for (int n = 0; n < NDQ; ++n) dq[n] = zero16();
-      const ATTN_LDS char* kd = lds + OFF_K;
-#pragma unroll
-      for (int m = 0; m < BWD_BN / 16; ++m) {
-        const bf16x8 a = lds_col8<BWD_BN>(st, 16 * m, 32 * tq, lane);
-#pragma unroll
-        for (int n = 0; n < NDQ; ++n)
-          dq[n] = mfma32(a, lds_col8<BWD_BN>(kd, 16 * m, 32 * ((w >> 1) * NDQ + n), lane), dq[n]);
-      }
-#pragma unroll
-      for (int n = 0; n < NDQ; ++n) {
-        const int d = 32 * ((w >> 1) * NDQ + n) + lq;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = q0 + 32 * tq + 8 * (r >> 2) + 4 * g + (r & 3);  // < Tpad
-          unsafeAtomicAdd(dqacc + (int64_t)q * DQK + d, dq[n][r]);
-        }
+      for (int m = 0; m < 4; ++m) {
+        const u32x4 v = __builtin_bit_cast(u32x4, sb[m]);
+        *reinterpret_cast<ATTN_LDS u32x2*>(st_cur + tile_off<BWD_BN>(kw + lq, 16 * m + 4 * g)) = u32x2{v[0], v[1]};
+        *reinterpret_cast<ATTN_LDS u32x2*>(st_cur + tile_off<BWD_BN>(kw + lq, 16 * m + 8 + 4 * g)) = u32x2{v[2], v[3]};
       }
     }
-    if (more) store_rows(buf ^ 1);
-    __syncthreads();
+  };
+
+  auto step = [&](int it, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int qb = i0 + it;
+    const int q0 = qb * BWD_BM;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads (and its atomics of the step before) are done
+    __syncthreads();                // every wave's tiles are in; the other buffers are free
+    if (it + 1 < n_q) load_step(qb + 1, std::integral_constant<int, 1 - BUF>{});
+    if constexpr (ATOMIC_DQ) {
+      if (it > 0) dq_partial((const ATTN_LDS char*)((ST_DOUBLE && !BUF) ? st1 : st0), q0 - BWD_BM);
+    }
+    const bool masked = (CAUSAL && key0 + BWD_BN - 1 > q0) || key0 + BWD_BN > T || q0 + BWD_BM > T;
+    if (masked)
+      step_body(q0, bufc, std::true_type{});
+    else
+      step_body(q0, bufc, std::false_type{});
+  };
+  for (int it = 0; it < n_q; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_q) step(it + 1, std::integral_constant<int, 1>{});
+  }
+  if constexpr (ATOMIC_DQ) {
+    __syncthreads();  // the last dS^T tile is complete
+    const bool last_odd = ((n_q - 1) & 1) != 0;
+    dq_partial((const ATTN_LDS char*)((ST_DOUBLE && last_odd) ? st1 : st0), (i0 + n_q - 1) * BWD_BM);
   }
 
   // dK = scale dS^T Q, dV; element r of tile t: key key0 + kw + 8 (r / 4) + 4 g + r % 4,
@@ -275,15 +332,22 @@ __global__ __launch_bounds__(BWD_NT) void bwd_kv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------
-// deterministic dQ: query-stationary, fixed key-block order
+// dQ without atomics: query-stationary, fixed key-block order
 // ---------------------------------------------------------------------------------
+// One workgroup of 4 wavefronts per 128 query rows (32 per wavefront, held in
+// registers as B operands together with their dO rows, LSE and D), two workgroups per
+// CU.  Key/value tiles of 64 rows stream through double-buffered LDS by direct loads,
+// in descending order.  Per tile: S^T = K Q^T and dP^T = V dO^T (2 x d/16 MFMAs each),
+// P^T = 2^(S^T c - LSE log2 e), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T with the
+// K^T operand read column-wise.  Every dQ row is summed over the key blocks in one
+// fixed order inside one wavefront, so the result is bit-identical from run to run.
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(BWD_NT) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(BWD_NT, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16, NDQ = DQK / 32;
   constexpr int KT_BYTES = DQ_BN * DQK * 2;
   constexpr int VT_BYTES = DQ_BN * DV * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * (KT_BYTES + VT_BYTES)];
-  ATTN_LDS char* lds = (ATTN_LDS char*)smem;
+  __shared__ __attribute__((aligned(1024))) char kbuf0[KT_BYTES], kbuf1[KT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[VT_BYTES], vbuf1[VT_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
   const int T = p.T;
@@ -297,8 +361,11 @@ __global__ __launch_bounds__(BWD_NT) void bwd_dq_kernel(BwdParams p) {
   const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
   const bf16* dog = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h;
   bf16* dqg = (bf16*)p.dq + b * p.sdq.b + h * p.sdq.h;
+  const int64_t skt = p.sk.t, svt = p.sv.t;
 
+  const LdsLane L = lds_lane(lane);
   const int q0 = qb * DQ_BM, qw = q0 + 32 * w, my_q = qw + lq;
+  const float c = p.scale_log2;
 
   // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T
   bf16x8 qf[KSQ], df[KSV];
@@ -317,68 +384,80 @@ __global__ __launch_bounds__(BWD_NT) void bwd_dq_kernel(BwdParams p) {
   const float lse2 = my_q < T ? p.lse[(int64_t)item.bh * T + my_q] * kLog2e : INFINITY;
   const float Dq = my_q < T ? p.D[(int64_t)item.bh * p.Tpad + my_q] : 0.f;
 
+  DirectTile<DQ_BN, DQK, BWD_NT / 64> kload;
+  DirectTile<DQ_BN, DV, BWD_NT / 64> vload;
+  kload.init(skt, w, lane);
+  vload.init(svt, w, lane);
+  auto load_kv = [&](int key0, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    kload.issue(kg + key0 * skt, skt, T - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), w);
+    vload.issue(vg + key0 * svt, svt, T - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), w);
+  };
+
   const int kv_end = CAUSAL ? min(T, q0 + DQ_BM) : T;
   const int n_kv = (kv_end + DQ_BN - 1) / DQ_BN;
-
-  TileStage<DQ_BN, DQK, BWD_NT> kst;
-  TileStage<DQ_BN, DV, BWD_NT> vst;
-  kst.load(kg, p.sk.t, (n_kv - 1) * DQ_BN, T, tid);
-  vst.load(vg, p.sv.t, (n_kv - 1) * DQ_BN, T, tid);
-  kst.store(lds, tid);
-  vst.store(lds + 2 * KT_BYTES, tid);
-  __syncthreads();
 
   f32x16 dq[NDQ];
 #pragma unroll
   for (int t = 0; t < NDQ; ++t) dq[t] = zero16();
 
-  for (int it = 0; it < n_kv; ++it) {
-    const int j = n_kv - 1 - it;  // fixed order: descending key block
-    const int buf = it & 1;
-    const bool more = it + 1 < n_kv;
-    if (more) {
-      kst.load(kg, p.sk.t, (j - 1) * DQ_BN, T, tid);
-      vst.load(vg, p.sv.t, (j - 1) * DQ_BN, T, tid);
-    }
-    const int key0 = j * DQ_BN;
-    const bool active = !CAUSAL || key0 <= qw + 31;
-    if (active) {
-      const ATTN_LDS char* kt = lds + buf * KT_BYTES;
-      const ATTN_LDS char* vt = lds + 2 * KT_BYTES + buf * VT_BYTES;
-      f32x16 s[2], dp[2];
+  auto tile_body = [&](int key0, auto bufc, auto maskc) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr bool MASKED = decltype(maskc)::value;
+    const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
+    const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
+    f32x16 s[2], dp[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        s[t] = zero16();
-        dp[t] = zero16();
+    for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KSQ; ++ks) s[t] = mfma32(lds_row8<DQ_BN>(kt, 32 * t + lq, 16 * ks + 8 * g), qf[ks], s[t]);
+      for (int t = 0; t < 2; ++t) s[t] = mfma32(lds_row8<DQ_BN>(kt, L, 32 * t, ks), qf[ks], ks == 0 ? zero16() : s[t]);
 #pragma unroll
-        for (int ks = 0; ks < KSV; ++ks) dp[t] = mfma32(lds_row8<DQ_BN>(vt, 32 * t + lq, 16 * ks + 8 * g), df[ks], dp[t]);
-      }
-      const bool need_mask = (CAUSAL && key0 + DQ_BN - 1 > qw) || (key0 + DQ_BN > T);
+    for (int ks = 0; ks < KSV; ++ks)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) dp[t] = mfma32(lds_row8<DQ_BN>(vt, L, 32 * t, ks), df[ks], ks == 0 ? zero16() : dp[t]);
+    // Phases stay in program order: the second wavefront on the SIMD supplies the
+    // overlap, and unbounded hoisting of LDS reads would exhaust the registers.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = exp2_fast(s[t][r] * p.scale_log2 - lse2);
-          if (need_mask) {
-            const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= T || (CAUSAL && key > my_q)) pv = 0.f;
-          }
-          dp[t][r] = pv * (dp[t][r] - Dq);
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -lse2));
+        if constexpr (MASKED) {
+          const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+          pv = (key >= T || (CAUSAL && key > my_q)) ? 0.f : pv;
         }
-      const bf16x8 sb[4] = {pack8(dp[0], 0), pack8(dp[0], 1), pack8(dp[1], 0), pack8(dp[1], 1)};
-      // dQ^T += K^T dS^T
+        dp[t][r] = pv * (dp[t][r] - Dq);
+      }
+      const bf16x8 sb0 = pack8(dp[t], 0), sb1 = pack8(dp[t], 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // dQ^T += K^T dS^T for the 32 keys of this tile half
 #pragma unroll
-      for (int t = 0; t < NDQ; ++t)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) dq[t] = mfma32(lds_col8<DQ_BN>(kt, 16 * m, 32 * t, lane), sb[m], dq[t]);
+      for (int n = 0; n < NDQ; ++n) {
+        dq[n] = mfma32(lds_col8<DQ_BN>(kt, L, 32 * t, 32 * n), sb0, dq[n]);
+        dq[n] = mfma32(lds_col8<DQ_BN>(kt, L, 32 * t + 16, 32 * n), sb1, dq[n]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      kst.store(lds + (buf ^ 1) * KT_BYTES, tid);
-      vst.store(lds + 2 * KT_BYTES + (buf ^ 1) * VT_BYTES, tid);
-    }
+  };
+
+  load_kv((n_kv - 1) * DQ_BN, std::integral_constant<int, 0>{});
+  auto step = [&](int it, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int j = n_kv - 1 - it;  // fixed order: descending key block
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (it + 1 < n_kv) load_kv((j - 1) * DQ_BN, std::integral_constant<int, 1 - BUF>{});
+    const int key0 = j * DQ_BN;
+    if (CAUSAL && key0 > qw + 31) return;  // tile wholly above this wavefront's rows
+    if ((CAUSAL && key0 + DQ_BN - 1 > qw) || key0 + DQ_BN > T)
+      tile_body(key0, bufc, std::true_type{});
+    else
+      tile_body(key0, bufc, std::false_type{});
+  };
+  for (int it = 0; it < n_kv; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_kv) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   if (my_q < T) {

@@ -99,29 +99,91 @@ __device__ __forceinline__ uint32_t tile_off(uint32_t row, uint32_t col) {
   return panel * (ROWS * 128u) + row * 128u + ((chunk ^ swz(row)) << 4) + (e << 1);
 }
 
-// Row read: 8 consecutive columns col .. col+7 of one row (col % 8 == 0).
+// Per-lane address bases.  For the access patterns below the swizzled offset splits
+// into a per-lane base, an XOR with a small compile-time constant and an immediate
+// offset, because the row index only enters swz() through bits that the loop steps
+// (multiples of 16 rows) never touch, and the stepped column bits are disjoint from
+// the rest of the base.  Keeping the bases in a few registers (instead of one
+// address per tile and step) is what keeps the kernels free of spills.
+struct LdsLane {
+  uint32_t row;   // row reads:    lq * 128 + ((g ^ swz(lq)) << 4)
+  uint32_t col0;  // column reads: rows 4g + p/4     (p = lane % 16)
+  uint32_t col1;  //               rows 4g + p/4 + 8
+};
+__device__ __forceinline__ LdsLane lds_lane(uint32_t lane) {
+  const uint32_t lq = lane & 31u, g = lane >> 5, p = lane & 15u;
+  const uint32_t cl = (((lane >> 4) & 1u) << 1) | ((p & 3u) >> 1);  // chunk bits 0-1 of the column
+  const uint32_t r0 = 4u * g + (p >> 2), r1 = r0 + 8u;
+  LdsLane L;
+  L.row = lq * 128u + ((g ^ swz(lq)) << 4);
+  L.col0 = r0 * 128u + ((cl ^ swz(r0)) << 4) + 8u * (p & 1u);
+  L.col1 = r1 * 128u + ((cl ^ swz(r1)) << 4) + 8u * (p & 1u);
+  return L;
+}
+
+// Row read: lane l gets columns 16 ks + 8 g .. +7 of row R0 + l % 32 (R0 % 16 == 0).
 template <int ROWS>
-__device__ __forceinline__ bf16x8 lds_row8(const ATTN_LDS char* tile, uint32_t row, uint32_t col) {
-  return *reinterpret_cast<const ATTN_LDS bf16x8*>(tile + tile_off<ROWS>(row, col));
+__device__ __forceinline__ bf16x8 lds_row8(const ATTN_LDS char* tile, const LdsLane& L, int R0, int ks) {
+  const uint32_t off = (uint32_t)(ks >> 2) * (ROWS * 128u) + (uint32_t)R0 * 128u + (L.row ^ ((uint32_t)(ks & 3) << 5));
+  return *reinterpret_cast<const ATTN_LDS bf16x8*>(tile + off);
 }
 
 // Column read for an MFMA operand whose contraction index runs along the tile's rows.
 // Returns, for lane l, the 8 values X[k][j] with j = j0 + (l % 32) and
-// k = k0 + 4 g + {0..3, 8..11} (g = l / 32): two ds_read_b64_tr_b16.  Within each
-// 16-lane group, lane p supplies the address of row (k0 + 4g + 8h + p / 4),
-// columns j0 + 16 * ((l / 16) % 2) + 4 (p % 4) .. +3.
+// k = k0 + 4 g + {0..3, 8..11} (g = l / 32), k0 % 16 == 0, j0 % 32 == 0: two
+// ds_read_b64_tr_b16.  Within each 16-lane group, lane p supplies the address of row
+// (k0 + 4g + 8h + p / 4), columns j0 + 16 * ((l / 16) % 2) + 4 (p % 4) .. +3.
 template <int ROWS>
-__device__ __forceinline__ bf16x8 lds_col8(const ATTN_LDS char* tile, uint32_t k0, uint32_t j0, uint32_t lane) {
-  const uint32_t p = lane & 15u, g = lane >> 5;
-  const uint32_t col = j0 + 16u * ((lane >> 4) & 1u) + 4u * (p & 3u);
-  const uint32_t row0 = k0 + 4u * g + (p >> 2);
-  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (ATTN_LDS i16x4*)(tile + tile_off<ROWS>(row0, col)));
-  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (ATTN_LDS i16x4*)(tile + tile_off<ROWS>(row0 + 8u, col)));
+__device__ __forceinline__ bf16x8 lds_col8(const ATTN_LDS char* tile, const LdsLane& L, int k0, int j0) {
+  const uint32_t x = (uint32_t)((j0 >> 5) & 1) << 6;
+  const uint32_t base = (uint32_t)(j0 >> 6) * (ROWS * 128u) + (uint32_t)k0 * 128u;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(tile + base + (L.col0 ^ x)));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(tile + base + (L.col1 ^ x)));
   i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
+
+// ---------------------------------------------------------------------------------
+// direct global -> LDS tile loads (buffer_load_dwordx4 ... lds)
+// ---------------------------------------------------------------------------------
+// A tile of ROWS x COLS bf16 (rows of a matrix with row stride `ld` elements) is
+// written to LDS in the swizzled panel layout by NW wavefronts.  Wavefront w fills the
+// 1 KB blocks w, w + NW, ...; a block is 8 rows x 128 bytes of one panel, and lane l
+// of the wavefront lands at byte 16 l of it, so the lane fetches the global chunk that
+// the swizzle puts there.  Each lane keeps one 32-bit byte offset per block; the tile
+// enters through a buffer resource (uniform) whose size ends at the last valid row, so
+// rows at or past the end of the matrix read as zeros.  Row strides are limited to
+// 2^24 elements by the API, which keeps every offset within 32 bits.
+constexpr int kBufferResourceWord3 = 0x00020000;  // raw buffer, gfx9-family format
+
+template <int ROWS, int COLS, int NW>
+struct DirectTile {
+  static constexpr int LOADS = ROWS * COLS * 2 / 1024 / NW;
+  static_assert(ROWS * COLS * 2 % (1024 * NW) == 0, "tile not divisible into wave blocks");
+  uint32_t off[LOADS];
+
+  __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = w + NW * i;
+      const int r = 8 * (blk % (ROWS / 8)) + (lane >> 3);
+      const int col = 64 * (blk / (ROWS / 8)) + 8 * ((lane & 7) ^ (int)swz((uint32_t)r));
+      off[i] = (uint32_t)((r * ld + col) * 2);
+    }
+  }
+  // tile = matrix + row0 * ld (uniform); valid = number of matrix rows from row0 on (>= 1).
+  __device__ __forceinline__ void issue(const bf16* tile, int64_t ld, int valid, ATTN_LDS char* dst, int w) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer-resource builtins exist only for the GPU target
+    const int64_t rows = valid < ROWS ? valid : ROWS;
+    const int64_t bytes = ((rows - 1) * ld + COLS) * 2;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)tile, (short)0, (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), kBufferResourceWord3);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (ATTN_LDS void*)(dst + (w + NW * i) * 1024), 16, off[i], 0, 0, 0);
+#endif
+  }
+};
 
 // ---------------------------------------------------------------------------------
 // global <-> LDS tile staging through registers

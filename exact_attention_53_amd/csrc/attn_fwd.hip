@@ -30,6 +30,8 @@
 // The result O = O^T / l and LSE = ln 2 (m + log2 l) do not depend on when m was raised.
 // Causal: tiles wholly above the diagonal are never loaded; the diagonal tile(s) come
 // first; a wavefront skips tiles that lie wholly above its rows.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 
@@ -46,14 +48,10 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr int NDT = DV / 32;
   constexpr int KT_BYTES = FWD_BN * DQK * 2;
   constexpr int VT_BYTES = FWD_BN * DV * 2;
-  constexpr int K_LOADS = KT_BYTES / 1024 / (FWD_NT / 64);  // 1 KB global->LDS blocks per wave
-  constexpr int V_LOADS = VT_BYTES / 1024 / (FWD_NT / 64);
-  static_assert(KT_BYTES % (1024 * (FWD_NT / 64)) == 0 && VT_BYTES % (1024 * (FWD_NT / 64)) == 0,
-                "tiles not divisible into wave blocks");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * (KT_BYTES + VT_BYTES)];
-  ATTN_LDS char* lds = (ATTN_LDS char*)smem;
-  ATTN_LDS char* ktile = lds;                   // [2][KT_BYTES]
-  ATTN_LDS char* vtile = lds + 2 * KT_BYTES;    // [2][VT_BYTES]
+  // One LDS object per buffer: the compiler can then tell the reads of one buffer
+  // from the direct loads in flight into the other and does not wait on them.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[KT_BYTES], kbuf1[KT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[VT_BYTES], vbuf1[VT_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
   const int T = p.T;
@@ -68,6 +66,7 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   bf16* og = (bf16*)p.o + b * p.so.b + h * p.so.h;
   const int64_t skt = p.sk.t, svt = p.sv.t;
 
+  const LdsLane L = lds_lane(lane);
   const int q0 = qb * FWD_BM;
   const int qw = q0 + 32 * w;
   const int my_q = qw + lq;
@@ -81,24 +80,14 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     qf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  // Direct global->LDS tile loads: wave w fills 1 KB blocks w, w+4, ...; a block is 8
-  // rows x 128 bytes of one 64-column panel and lane l lands at byte 16 l of it, so the
-  // lane fetches the global chunk that the swizzle puts there.  Rows past T are
-  // clamped to T-1 (always masked afterwards).
-  const int blk_row = lane >> 3;
-  auto load_tile = [&](const bf16* src, int64_t ld, int row0, ATTN_LDS char* dst, int nloads) {
-    for (int i = 0; i < nloads; ++i) {
-      const int blk = w + (FWD_NT / 64) * i;
-      const int r = 8 * (blk % (FWD_BN / 8)) + blk_row;
-      const int col = 64 * (blk / (FWD_BN / 8)) + 8 * ((lane & 7) ^ (int)swz(r));
-      const int row = min(row0 + r, T - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(src + row * ld + col), (ATTN_LDS void*)(dst + blk * 1024),
-                                       16, 0, 0);
-    }
-  };
-  auto load_kv = [&](int key0, int buf) {
-    load_tile(kg, skt, key0, ktile + buf * KT_BYTES, K_LOADS);
-    load_tile(vg, svt, key0, vtile + buf * VT_BYTES, V_LOADS);
+  DirectTile<FWD_BN, DQK, FWD_NT / 64> kload;
+  DirectTile<FWD_BN, DV, FWD_NT / 64> vload;
+  kload.init(skt, w, lane);
+  vload.init(svt, w, lane);
+  auto load_kv = [&](int key0, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    kload.issue(kg + key0 * skt, skt, T - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), w);
+    vload.issue(vg + key0 * svt, svt, T - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), w);
   };
 
   const int kv_end = CAUSAL ? min(T, q0 + FWD_BM) : T;
@@ -110,25 +99,26 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = zero16();
 
-  load_kv((n_kv - 1) * FWD_BN, 0);
+  load_kv((n_kv - 1) * FWD_BN, std::integral_constant<int, 0>{});
 
-  for (int it = 0; it < n_kv; ++it) {
+  // One key/value tile; BUF is this tile's buffer, the next tile goes to the other one.
+  auto step = [&](int it, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int j = n_kv - 1 - it;  // diagonal / tail tile first
-    const int buf = it & 1;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile j has landed in LDS
-    __syncthreads();                // ... and every other wave's; buffer buf^1 is free
-    if (it + 1 < n_kv) load_kv((j - 1) * FWD_BN, buf ^ 1);
+    __syncthreads();                // ... and every other wave's; the other buffer is free
+    if (it + 1 < n_kv) load_kv((j - 1) * FWD_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * FWD_BN;
     const bool active = !CAUSAL || key0 <= qw + 31;
-    if (!active) continue;
-    const ATTN_LDS char* kt = ktile + buf * KT_BYTES;
-    const ATTN_LDS char* vt = vtile + buf * VT_BYTES;
+    if (!active) return;
+    const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
+    const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
     // S^T = K Q^T for keys key0 .. key0+63 (two 32-key accumulators)
     f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s0 = mfma32(lds_row8<FWD_BN>(kt, lq, 16 * ks + 8 * g), qf[ks], s0);
-      s1 = mfma32(lds_row8<FWD_BN>(kt, 32 + lq, 16 * ks + 8 * g), qf[ks], s1);
+      s0 = mfma32(lds_row8<FWD_BN>(kt, L, 0, ks), qf[ks], s0);
+      s1 = mfma32(lds_row8<FWD_BN>(kt, L, 32, ks), qf[ks], s1);
     }
     if ((CAUSAL && key0 + FWD_BN - 1 > qw) || key0 + FWD_BN > T) {
 #pragma unroll
@@ -167,11 +157,15 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] = mfma32(lds_col8<FWD_BN>(vt, 0, 32 * dt, lane), pb0, o[dt]);
-      o[dt] = mfma32(lds_col8<FWD_BN>(vt, 16, 32 * dt, lane), pb1, o[dt]);
-      o[dt] = mfma32(lds_col8<FWD_BN>(vt, 32, 32 * dt, lane), pb2, o[dt]);
-      o[dt] = mfma32(lds_col8<FWD_BN>(vt, 48, 32 * dt, lane), pb3, o[dt]);
+      o[dt] = mfma32(lds_col8<FWD_BN>(vt, L, 0, 32 * dt), pb0, o[dt]);
+      o[dt] = mfma32(lds_col8<FWD_BN>(vt, L, 16, 32 * dt), pb1, o[dt]);
+      o[dt] = mfma32(lds_col8<FWD_BN>(vt, L, 32, 32 * dt), pb2, o[dt]);
+      o[dt] = mfma32(lds_col8<FWD_BN>(vt, L, 48, 32 * dt), pb3, o[dt]);
     }
+  };
+  for (int it = 0; it < n_kv; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_kv) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   // deferred normalisation and stats

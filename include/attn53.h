@@ -20,8 +20,9 @@
  *    dims of the FA4 backward sweep [2CTA 4.1].  Anything else: ATTN_ERR_HEADDIM.
  *  - T_q == T_k == T >= 1, any value; partial tiles are masked inside the kernels.
  *  - Every tensor pointer must be 16-byte aligned and every stride a non-negative
- *    multiple of 8 elements, so that all global accesses are 128-bit; otherwise the
- *    call returns ATTN_ERR_ALIGN / ATTN_ERR_STRIDE.  There is no slow fallback.
+ *    multiple of 8 elements, so that all global accesses are 128-bit; the t stride is
+ *    at most 2^24 elements.  Otherwise the call returns ATTN_ERR_ALIGN /
+ *    ATTN_ERR_STRIDE.  There is no slow fallback.
  *  - LSE ("softmax stats" of [SA8 1.2, 1.3]) is fp32, contiguous (B, NH, T), and holds
  *    the natural-log logsumexp of each row of S = scale * Q K^T (mask applied).
  *  - causal = 1 masks key j > query i (top-left aligned, [SA8 2.2] loop bound).
@@ -56,7 +57,7 @@ typedef enum {
   ATTN_ERR_NULL = 1,       /* a required pointer is NULL                         */
   ATTN_ERR_SHAPE = 2,      /* B, NH or T < 1, or the sizes overflow              */
   ATTN_ERR_HEADDIM = 3,    /* (d_qk, d_v) not one of the supported pairs          */
-  ATTN_ERR_STRIDE = 4,     /* a stride is negative or not a multiple of 8         */
+  ATTN_ERR_STRIDE = 4,     /* a stride negative, not a multiple of 8, t > 2^24    */
   ATTN_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned                    */
   ATTN_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required             */
   ATTN_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed          */

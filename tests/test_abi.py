@@ -74,6 +74,7 @@ def test_fwd_validation(lib):
     assert fwd(lib, q=GOOD + 8) == ALIGN
     assert fwd(lib, sq=S(64 * 2 * 64, 64, 2 * 64 + 4)) == STRIDE
     assert fwd(lib, sq=S(-8, 64, 128)) == STRIDE
+    assert fwd(lib, sq=S(8, 8, (1 << 24) + 8)) == STRIDE
     assert fwd(lib, scale=float("nan")) == ARG
     assert fwd(lib, scale=float("inf")) == ARG
     assert fwd(lib, scale=0.0) == ARG
