@@ -4,7 +4,7 @@ A step is one forward and one backward pass (every stage of the hot path) over o
 batch of synthetic input already resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--deterministic] [--no-cpu-baseline]
+                  [--dq-mode deterministic|atomic] [--no-cpu-baseline]
 
 FLOP convention: per unmasked (query, key) pair and head, the forward counts
 2 (d_qk + d_v) (S = QK^T, O = PV) and the backward 2 (3 d_qk + 2 d_v) (S recomputed,
@@ -68,7 +68,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline")
-    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--dq-mode", choices=["deterministic", "atomic"], default="deterministic",
+                    help="dQ summed in a fixed order without atomics (default) or by fp32 atomics")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -97,8 +98,8 @@ def main():
     dq = torch.empty((B, T, NH, w.d_qk), dtype=torch.bfloat16, device=dev)
     dk = torch.empty_like(dq)
     dv = torch.empty((B, T, NH, w.d_v), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, args.deterministic), dtype=torch.uint8, device=dev)
-    det = args.deterministic
+    det = args.dq_mode == "deterministic"
+    ws = torch.empty(attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, det), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         if ev is not None:
@@ -114,7 +115,7 @@ def main():
         if ev is not None:
             ev[3].record()
         attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws,
-                 stages=attn.FINALIZE)
+                 stages=attn.DQ)
         if ev is not None:
             ev[4].record()
 
@@ -137,16 +138,24 @@ def main():
     def avg(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
 
-    t_fwd, t_pre, t_main, t_fin = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    t_fwd, t_pre, t_main, t_dq = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
     f_fwd, f_bwd = flops(w)
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    # Algorithmic flops carried by each kernel (recomputation is not counted): the
+    # key/value kernel forms S, dP, dV, dK (and, in atomic mode, the dQ products); the
+    # deterministic dQ kernel contributes the dQ product only.
+    pairs = w.pairs()
+    f_dq = 2.0 * w.d_qk * pairs
+    f_main = f_bwd if not det else f_bwd - f_dq
     kernels = {
-        "attn_fwd": {"ms": t_fwd, "tflops": f_fwd / (t_fwd * 1e-3) / 1e12},
-        "bwd_preprocess": {"ms": t_pre},
-        "bwd_main": {"ms": t_main, "tflops": f_bwd / (t_main * 1e-3) / 1e12},
-        "bwd_finalize": {"ms": t_fin},
+        "attn_fwd": {"ms": t_fwd, "flops": f_fwd},
+        "bwd_preprocess": {"ms": t_pre, "flops": 0.0},
+        "bwd_kv": {"ms": t_main, "flops": f_main},
+        "bwd_dq" if det else "bwd_dq_convert": {"ms": t_dq, "flops": f_dq if det else 0.0},
     }
-    dom = "bwd_main" if t_main >= t_fwd else "attn_fwd"
+    for k_ in kernels.values():
+        k_["tflops"] = k_["flops"] / (k_["ms"] * 1e-3) / 1e12 if k_["ms"] > 0 else 0.0
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
     achieved = kernels[dom]["tflops"]
     line = {
         "metric": METRIC,
@@ -164,14 +173,15 @@ def main():
         "config": {
             "workload": f"{w.name}: B={B} NH={NH} T={T} d_qk={w.d_qk} d_v={w.d_v} "
                         f"{'causal' if w.causal else 'non-causal'}, {'packed QKV' if w.packed else 'BTHD'}, "
-                        f"dQ mode {'deterministic' if det else 'atomic'}",
+                        f"dQ mode {args.dq_mode}",
             "B": B, "NH": NH, "T": T, "d_qk": w.d_qk, "d_v": w.d_v, "causal": w.causal,
-            "dq_mode": "deterministic" if det else "atomic",
+            "dq_mode": args.dq_mode,
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(f_bwd / ((t_pre + t_main + t_fin) * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / ((t_pre + t_main + t_dq) * 1e-3) / 1e12, 2),
         "kernels_ms": {n: round(v["ms"], 4) for n, v in kernels.items()},
+        "kernels_tflops": {n: round(v["tflops"], 1) for n, v in kernels.items() if v["flops"] > 0},
         "wall_s_timed": round(t_wall, 3),
         "roofline": {
             "kernel": dom,

@@ -23,13 +23,13 @@ import torch
 
 __all__ = [
     "AttnError", "lib_path", "load", "fwd", "fwd_packed", "bwd", "bwd_packed",
-    "workspace_bytes", "PREPROCESS", "MAIN", "FINALIZE", "ALL_STAGES", "version",
+    "workspace_bytes", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libattn53.so")
 
-PREPROCESS, MAIN, FINALIZE, ALL_STAGES = 1, 2, 4, 7
+PREPROCESS, MAIN, DQ, ALL_STAGES = 1, 2, 4, 7
 
 
 class AttnError(RuntimeError):

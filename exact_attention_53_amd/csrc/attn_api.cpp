@@ -111,7 +111,7 @@ attn_status attn_fwd(const void* q, attn_strides sq, const void* k, attn_strides
 
 size_t attn_bwd_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic) {
   if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK) return 0;
-  size_t n = ws_D_bytes(B, NH, T);
+  size_t n = 2 * ws_D_bytes(B, NH, T);  // D and LSE log2(e)
   if (!deterministic) n += ws_acc_bytes(B, NH, T, d_qk);
   return n;
 }
@@ -165,8 +165,9 @@ attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
   p.D = static_cast<float*>(workspace);
+  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_D_bytes(B, NH, T));
   p.dq_acc = deterministic ? nullptr
-                           : reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_D_bytes(B, NH, T));
+                           : reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * ws_D_bytes(B, NH, T));
   const hipStream_t s = (hipStream_t)stream;
   if (stages & ATTN_BWD_PREPROCESS) {
     st = hip_status(attn53::launch_bwd_preprocess(p, d_qk, d_v, !deterministic, s));
@@ -176,8 +177,9 @@ attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_
     st = hip_status(attn53::launch_bwd_main(p, d_qk, d_v, causal != 0, deterministic != 0, s));
     if (st != ATTN_OK) return st;
   }
-  if ((stages & ATTN_BWD_FINALIZE) && !deterministic) {
-    st = hip_status(attn53::launch_bwd_finalize(p, d_qk, s));
+  if (stages & ATTN_BWD_DQ) {
+    st = hip_status(deterministic ? attn53::launch_bwd_dq(p, d_qk, d_v, causal != 0, s)
+                                  : attn53::launch_bwd_finalize(p, d_qk, s));
     if (st != ATTN_OK) return st;
   }
   return ATTN_OK;

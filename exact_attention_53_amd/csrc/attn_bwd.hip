@@ -10,7 +10,8 @@
 //
 // Kernels, in stream order:
 //   bwd_pre_kernel     D_i = sum_k dO_ik O_ik  (= (dP * P) 1 of [SA8 2.1]: summing
-//                      P_ij dP_ij = P_ij sum_k dO_ik V_jk over j gives sum_k dO_ik O_ik);
+//                      P_ij dP_ij = P_ij sum_k dO_ik V_jk over j gives sum_k dO_ik O_ik)
+//                      and LSE_i log2(e) (padding rows +inf), both into the workspace;
 //                      clears the fp32 dQ accumulator (atomic mode).
 //   bwd_kv_kernel      one workgroup per key/value block of BWD_BN = 128 keys; each of
 //                      its 4 wavefronts owns 32 keys, keeps K and V as B operands and dK,
@@ -70,7 +71,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int d_qk, int
   }
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, G);
-  if (row < nrows && c == 0) p.D[row] = sum;
+  if (row < nrows && c == 0) {
+    const int t = (int)(row % p.Tpad);
+    const int bh = (int)(row / p.Tpad);
+    p.D[row] = sum;
+    // LSE in base-2 units; padding rows get +inf, which makes their P exactly 0
+    p.lse2[row] = t < p.T ? p.lse[(int64_t)bh * p.T + t] * kLog2e : INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -91,7 +98,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int d_qk, int
 // With d_qk = 192 LDS holds one dS^T buffer only; a barrier then separates the last
 // reads of the previous tile from the writes of the new one.
 template <int DQK, int DV, bool CAUSAL, bool ATOMIC_DQ>
-__global__ __launch_bounds__(BWD_NT) void bwd_kv_kernel(BwdParams p) {
+__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
   constexpr int NDQ = DQK / 32 / 2;  // dQ tiles per wavefront
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(BWD_NT) void bwd_kv_kernel(BwdParams p) {
   const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
   const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
   const bf16* dog = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h;
-  const float* lseg = p.lse + (int64_t)item.bh * T;
+  const float* lseg = p.lse2 + (int64_t)item.bh * p.Tpad;
   const float* Dg = p.D + (int64_t)item.bh * p.Tpad;
   const int64_t sqt = p.sq.t, sdot = p.sdo.t;
 
@@ -151,9 +158,8 @@ __global__ __launch_bounds__(BWD_NT) void bwd_kv_kernel(BwdParams p) {
     const int r0 = qb * BWD_BM;
     qload.issue(qg + r0 * sqt, sqt, T - r0, (ATTN_LDS char*)(BUF ? qbuf1 : qbuf0), w);
     oload.issue(dog + r0 * sdot, sdot, T - r0, (ATTN_LDS char*)(BUF ? obuf1 : obuf0), w);
-    if (w == 0) {  // 64 rows of LSE (clamped; rows past T are masked) and of D (padded)
-      const int r = min(r0 + lane, T - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(lseg + r), (ATTN_LDS void*)(BUF ? lse1 : lse0), 4, 0, 0);
+    if (w == 0) {  // 64 rows of LSE log2(e) and of D (both padded to Tpad rows)
+      __builtin_amdgcn_global_load_lds((const void*)(lseg + r0 + lane), (ATTN_LDS void*)(BUF ? lse1 : lse0), 4, 0, 0);
     } else if (w == 1) {
       __builtin_amdgcn_global_load_lds((const void*)(Dg + r0 + lane), (ATTN_LDS void*)(BUF ? dd1 : dd0), 4, 0, 0);
     }
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(BWD_NT) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * a + e;
-          float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -Lv[e] * kLog2e));
+          float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -Lv[e]));
           if constexpr (MASKED) {
             const int q = q0 + qi + e;
             pv = (my_key >= T || q >= T || (CAUSAL && my_key > q)) ? 0.f : pv;
@@ -276,6 +282,34 @@ __global__ __launch_bounds__(BWD_NT) void bwd_kv_kernel(BwdParams p) {
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int t = 0; t < NDK; ++t) dk[t] = mfma32(sb[m], lds_col8<BWD_BM>(qt, L, 16 * m, 32 * t), dk[t]);
+    if constexpr (!MASKED) {
+      // Software pipeline for the matrix cores: LDS reads run a few MFMAs ahead, the
+      // P computation fills the gaps of the dP products and the dS computation those
+      // of the dV products.
+      ATTN_SCHED_GROUP(kSchedDsRead, 4);
+#pragma unroll
+      for (int i = 0; i < 2 * KSQ; ++i) {  // S
+        ATTN_SCHED_GROUP(kSchedMfma, 1);
+        ATTN_SCHED_GROUP(kSchedDsRead, 1);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * KSV; ++i) {  // dP || P
+        ATTN_SCHED_GROUP(kSchedMfma, 1);
+        ATTN_SCHED_GROUP(kSchedDsRead, 2);
+        ATTN_SCHED_GROUP(kSchedValu, 10);
+      }
+#pragma unroll
+      for (int i = 0; i < 4 * NDV; ++i) {  // dV || dS
+        ATTN_SCHED_GROUP(kSchedMfma, 1);
+        ATTN_SCHED_GROUP(kSchedDsRead, 2);
+        ATTN_SCHED_GROUP(kSchedValu, 6);
+      }
+#pragma unroll
+      for (int i = 0; i < 4 * NDK; ++i) {  // dK
+        ATTN_SCHED_GROUP(kSchedMfma, 1);
+        ATTN_SCHED_GROUP(kSchedDsRead, 2);
+      }
+    }
     if constexpr (ATOMIC_DQ) {
       if constexpr (!ST_DOUBLE) __syncthreads();  // every wave has read the previous dS^T
       // dS^T tile in LDS: row = key (128), column = query (64); sb[m] holds queries
@@ -381,7 +415,7 @@ __global__ __launch_bounds__(BWD_NT, 2) void bwd_dq_kernel(BwdParams p) {
     if (my_q < T) raw = *reinterpret_cast<const u32x4*>(dog + (int64_t)my_q * p.sdo.t + 16 * ks + 8 * g);
     df[ks] = __builtin_bit_cast(bf16x8, raw);
   }
-  const float lse2 = my_q < T ? p.lse[(int64_t)item.bh * T + my_q] * kLog2e : INFINITY;
+  const float lse2 = p.lse2[(int64_t)item.bh * p.Tpad + my_q];  // +inf on padding rows
   const float Dq = my_q < T ? p.D[(int64_t)item.bh * p.Tpad + my_q] : 0.f;
 
   DirectTile<DQ_BN, DQK, BWD_NT / 64> kload;
@@ -521,15 +555,17 @@ template <int DQK, int DV, bool CAUSAL>
 static hipError_t bwd_main_t(const BwdParams& p, bool deterministic, hipStream_t s) {
   const int nkb = (p.T + BWD_BN - 1) / BWD_BN;
   const dim3 grid_kv(nkb * p.B * p.NH);
-  if (deterministic) {
+  if (deterministic)
     hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, CAUSAL, false>), grid_kv, dim3(BWD_NT), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nqb = (p.T + DQ_BM - 1) / DQ_BM;
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
-  } else {
+  else
     hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, CAUSAL, true>), grid_kv, dim3(BWD_NT), 0, s, p);
-  }
+  return hipGetLastError();
+}
+
+template <int DQK, int DV, bool CAUSAL>
+static hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
+  const int nqb = (p.T + DQ_BM - 1) / DQ_BM;
+  hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -540,6 +576,13 @@ hipError_t launch_bwd_main(const BwdParams& p, int d_qk, int d_v, bool causal, b
     return causal ? bwd_main_t<128, 128, true>(p, deterministic, s) : bwd_main_t<128, 128, false>(p, deterministic, s);
   if (d_qk == 192 && d_v == 128)
     return causal ? bwd_main_t<192, 128, true>(p, deterministic, s) : bwd_main_t<192, 128, false>(p, deterministic, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
+  if (d_qk == 64 && d_v == 64) return causal ? bwd_dq_t<64, 64, true>(p, s) : bwd_dq_t<64, 64, false>(p, s);
+  if (d_qk == 128 && d_v == 128) return causal ? bwd_dq_t<128, 128, true>(p, s) : bwd_dq_t<128, 128, false>(p, s);
+  if (d_qk == 192 && d_v == 128) return causal ? bwd_dq_t<192, 128, true>(p, s) : bwd_dq_t<192, 128, false>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -87,6 +87,15 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // ---------------------------------------------------------------------------------
+// instruction-scheduling groups (__builtin_amdgcn_sched_group_barrier masks)
+// ---------------------------------------------------------------------------------
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedValu = 0x002 | 0x400;  // VALU including transcendental
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
+#define ATTN_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+// ---------------------------------------------------------------------------------
 // swizzled LDS tiles (byte offsets relative to the tile base)
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t swz(uint32_t row) {

@@ -33,7 +33,8 @@ struct BwdParams {
   int B, NH, T, Tpad;      // Tpad = T rounded up to kRowPad
   float scale;
   float scale_log2;
-  float* D;                // workspace: (B, NH, Tpad) fp32
+  float* D;                // workspace: (B, NH, Tpad) fp32, rowsum(dO * O)
+  float* lse2;             // workspace: (B, NH, Tpad) fp32, LSE * log2(e) (+inf on padding)
   float* dq_acc;           // workspace: (B, NH, Tpad, d_qk) fp32, atomic mode only
 };
 
@@ -43,6 +44,7 @@ constexpr int kRowPad = 128;
 hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdParams& p, int d_qk, int d_v, bool zero_acc, hipStream_t s);
 hipError_t launch_bwd_main(const BwdParams& p, int d_qk, int d_v, bool causal, bool deterministic, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s);
 hipError_t launch_bwd_finalize(const BwdParams& p, int d_qk, hipStream_t s);
 
 }  // namespace attn53

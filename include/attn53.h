@@ -99,8 +99,9 @@ attn_status attn_fwd(const void* q, attn_strides sq,
 
 /*
  * attn_bwd_workspace_bytes — device workspace that attn_bwd needs for these sizes.
- * Holds D_i = sum_k dO_ik O_ik (fp32, one per row) and, in atomic mode, the fp32 dQ
- * accumulator.  Returns 0 for invalid sizes.
+ * Holds D_i = sum_k dO_ik O_ik and LSE_i log2(e) (fp32, one per row, rows padded to
+ * a multiple of 128) and, in atomic mode, the fp32 dQ accumulator.  Returns 0 for
+ * invalid sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic);
 
@@ -136,10 +137,12 @@ attn_status attn_bwd(const void* q, attn_strides sq,
                      float scale, int causal, int deterministic,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage bits for attn_bwd_staged. */
-#define ATTN_BWD_PREPROCESS 1u /* D = rowsum(dO * O); clear the fp32 dQ accumulator  */
-#define ATTN_BWD_MAIN 2u       /* P recompute, dV, dP, dS, dK, dQ partial sums        */
-#define ATTN_BWD_FINALIZE 4u   /* dQ = scale * accumulator -> bf16 (atomic mode only) */
+/* Stage bits for attn_bwd_staged; each stage is one kernel launch. */
+#define ATTN_BWD_PREPROCESS 1u /* D = rowsum(dO * O); atomic mode: clear the accumulator */
+#define ATTN_BWD_MAIN 2u       /* key/value-stationary kernel: P recompute, dP, dS, dV,  */
+                               /* dK; atomic mode also adds partial dQ sums atomically  */
+#define ATTN_BWD_DQ 4u         /* atomic mode: dQ = scale * accumulator -> bf16;        */
+                               /* deterministic mode: query-stationary dQ kernel        */
 #define ATTN_BWD_ALL 7u
 
 /*

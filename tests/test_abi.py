@@ -112,10 +112,11 @@ def test_bwd_validation(lib):
 
 def test_workspace_bytes(lib):
     f = lib.attn_bwd_workspace_bytes
-    # D: B*NH*Tpad fp32; atomic mode adds B*NH*Tpad*d_qk fp32 (Tpad = T rounded up to 128)
-    assert f(1, 2, 64, 64, 64, 1) == 1024
-    assert f(1, 2, 64, 64, 64, 0) == 1024 + 2 * 128 * 64 * 4
-    assert f(4, 16, 8192, 128, 128, 0) == 4 * 16 * 8192 * 4 + 4 * 16 * 8192 * 128 * 4
+    # D and LSE log2(e): 2 x B*NH*Tpad fp32; atomic mode adds B*NH*Tpad*d_qk fp32
+    # (Tpad = T rounded up to 128)
+    assert f(1, 2, 64, 64, 64, 1) == 2 * 1024
+    assert f(1, 2, 64, 64, 64, 0) == 2 * 1024 + 2 * 128 * 64 * 4
+    assert f(4, 16, 8192, 128, 128, 0) == 2 * 4 * 16 * 8192 * 4 + 4 * 16 * 8192 * 128 * 4
     assert f(0, 1, 1, 64, 64, 0) == 0
     assert f(1, 1, 1, 64, 32, 0) == 0
 
