@@ -38,8 +38,7 @@ namespace attn53 {
 constexpr int BWD_BN = 128;  // keys per workgroup (32 per wavefront)
 constexpr int BWD_BM = 64;   // queries per step
 constexpr int BWD_NT = 256;
-constexpr int DQ_BM = 128;   // deterministic dQ kernel: queries per workgroup
-constexpr int DQ_BN = 64;    //                           keys per step
+constexpr int DQ_BN = 64;    // dQ kernel: keys per step
 
 // ---------------------------------------------------------------------------------
 // preprocess: D = rowsum(dO * O); optional clear of the dQ accumulator
@@ -368,16 +367,29 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 // ---------------------------------------------------------------------------------
 // dQ without atomics: query-stationary, fixed key-block order
 // ---------------------------------------------------------------------------------
-// One workgroup of 4 wavefronts per 128 query rows (32 per wavefront, held in
-// registers as B operands together with their dO rows, LSE and D), two workgroups per
-// CU.  Key/value tiles of 64 rows stream through double-buffered LDS by direct loads,
-// in descending order.  Per tile: S^T = K Q^T and dP^T = V dO^T (2 x d/16 MFMAs each),
-// P^T = 2^(S^T c - LSE log2 e), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T with the
-// K^T operand read column-wise.  Every dQ row is summed over the key blocks in one
-// fixed order inside one wavefront, so the result is bit-identical from run to run.
+// One workgroup of 4 wavefronts per DQ_QT * 128 query rows; each wavefront owns
+// DQ_QT tiles of 32 rows, held in registers as B operands together with their dO rows,
+// LSE and D.  With two tiles per wavefront (d_qk <= 128; one wavefront per SIMD) every
+// K or V fragment read from LDS feeds two products; with d_qk = 192 a wavefront owns
+// one tile and two workgroups share a CU.  Key/value tiles of 64 rows stream through
+// double-buffered LDS by direct loads, in descending order.  Per tile:
+// S^T = K Q^T and dP^T = V dO^T, P^T = 2^(S^T c - LSE log2 e), dS^T = P^T (dP^T - D),
+// dQ^T += K^T dS^T with the K^T operand read column-wise.  Every dQ row is summed over
+// the key blocks in one fixed order inside one wavefront, so the result is
+// bit-identical from run to run.
+template <int DQK>
+struct DqShape {
+  static constexpr int QT = DQK <= 128 ? 2 : 1;  // 32-row query tiles per wavefront
+  static constexpr int BM = 128 * QT;            // query rows per workgroup
+  static constexpr int WAVES_PER_EU = QT == 2 ? 1 : 2;
+};
+
 template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(BWD_NT, 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
+                                                                         DqShape<DQK>::WAVES_PER_EU)))
+void bwd_dq_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16, NDQ = DQK / 32;
+  constexpr int QT = DqShape<DQK>::QT, BM = DqShape<DQK>::BM;
   constexpr int KT_BYTES = DQ_BN * DQK * 2;
   constexpr int VT_BYTES = DQ_BN * DV * 2;
   __shared__ __attribute__((aligned(1024))) char kbuf0[KT_BYTES], kbuf1[KT_BYTES];
@@ -385,7 +397,7 @@ __global__ __launch_bounds__(BWD_NT, 2) void bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
   const int T = p.T;
-  const int nqb = (T + DQ_BM - 1) / DQ_BM;
+  const int nqb = (T + BM - 1) / BM;
   const Item item = schedule(blockIdx.x, p.B * p.NH);
   const int qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
   const int b = item.bh / p.NH, h = item.bh % p.NH;
@@ -398,25 +410,30 @@ __global__ __launch_bounds__(BWD_NT, 2) void bwd_dq_kernel(BwdParams p) {
   const int64_t skt = p.sk.t, svt = p.sv.t;
 
   const LdsLane L = lds_lane(lane);
-  const int q0 = qb * DQ_BM, qw = q0 + 32 * w, my_q = qw + lq;
+  const int q0 = qb * BM, qw = q0 + 32 * QT * w;  // first row of this wavefront
   const float c = p.scale_log2;
 
   // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T
-  bf16x8 qf[KSQ], df[KSV];
+  bf16x8 qf[QT][KSQ], df[QT][KSV];
+  float lse2[QT], Dq[QT];
 #pragma unroll
-  for (int ks = 0; ks < KSQ; ++ks) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (my_q < T) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)my_q * p.sq.t + 16 * ks + 8 * g);
-    qf[ks] = __builtin_bit_cast(bf16x8, raw);
-  }
+  for (int u = 0; u < QT; ++u) {
+    const int q = qw + 32 * u + lq;
 #pragma unroll
-  for (int ks = 0; ks < KSV; ++ks) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (my_q < T) raw = *reinterpret_cast<const u32x4*>(dog + (int64_t)my_q * p.sdo.t + 16 * ks + 8 * g);
-    df[ks] = __builtin_bit_cast(bf16x8, raw);
+    for (int ks = 0; ks < KSQ; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (q < T) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)q * p.sq.t + 16 * ks + 8 * g);
+      qf[u][ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (q < T) raw = *reinterpret_cast<const u32x4*>(dog + (int64_t)q * p.sdo.t + 16 * ks + 8 * g);
+      df[u][ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+    lse2[u] = p.lse2[(int64_t)item.bh * p.Tpad + min(q, p.Tpad - 1)];  // +inf on padding rows
+    Dq[u] = q < T ? p.D[(int64_t)item.bh * p.Tpad + q] : 0.f;
   }
-  const float lse2 = p.lse2[(int64_t)item.bh * p.Tpad + my_q];  // +inf on padding rows
-  const float Dq = my_q < T ? p.D[(int64_t)item.bh * p.Tpad + my_q] : 0.f;
 
   DirectTile<DQ_BN, DQK, BWD_NT / 64> kload;
   DirectTile<DQ_BN, DV, BWD_NT / 64> vload;
@@ -428,50 +445,97 @@ __global__ __launch_bounds__(BWD_NT, 2) void bwd_dq_kernel(BwdParams p) {
     vload.issue(vg + key0 * svt, svt, T - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), w);
   };
 
-  const int kv_end = CAUSAL ? min(T, q0 + DQ_BM) : T;
+  const int kv_end = CAUSAL ? min(T, q0 + BM) : T;
   const int n_kv = (kv_end + DQ_BN - 1) / DQ_BN;
 
-  f32x16 dq[NDQ];
+  f32x16 dq[QT][NDQ];
 #pragma unroll
-  for (int t = 0; t < NDQ; ++t) dq[t] = zero16();
+  for (int u = 0; u < QT; ++u)
+#pragma unroll
+    for (int t = 0; t < NDQ; ++t) dq[u][t] = zero16();
 
   auto tile_body = [&](int key0, auto bufc, auto maskc) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASKED = decltype(maskc)::value;
     const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
     const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
-    f32x16 s[2], dp[2];
+    f32x16 s[2][QT], dp[2][QT];  // [32-key half][query tile]
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) s[t] = mfma32(lds_row8<DQ_BN>(kt, L, 32 * t, ks), qf[ks], ks == 0 ? zero16() : s[t]);
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 a = lds_row8<DQ_BN>(kt, L, 32 * t, ks);
+#pragma unroll
+        for (int u = 0; u < QT; ++u) s[t][u] = mfma32(a, qf[u][ks], ks == 0 ? zero16() : s[t][u]);
+      }
 #pragma unroll
     for (int ks = 0; ks < KSV; ++ks)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) dp[t] = mfma32(lds_row8<DQ_BN>(vt, L, 32 * t, ks), df[ks], ks == 0 ? zero16() : dp[t]);
-    // Phases stay in program order: the second wavefront on the SIMD supplies the
-    // overlap, and unbounded hoisting of LDS reads would exhaust the registers.
-    __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 a = lds_row8<DQ_BN>(vt, L, 32 * t, ks);
+#pragma unroll
+        for (int u = 0; u < QT; ++u) dp[t][u] = mfma32(a, df[u][ks], ks == 0 ? zero16() : dp[t][u]);
+      }
+    // P^T = 2^(S^T c - LSE log2 e)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < QT; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
+          if constexpr (MASKED) {
+            const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+            pv = (key >= T || (CAUSAL && key > qw + 32 * u + lq)) ? 0.f : pv;
+          }
+          s[t][u][r] = pv;
+        }
+    // dS^T = P^T (dP^T - D); dQ^T += K^T dS^T, one 32-key half at a time
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      bf16x8 sb[QT][2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -lse2));
-        if constexpr (MASKED) {
-          const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-          pv = (key >= T || (CAUSAL && key > my_q)) ? 0.f : pv;
+      for (int u = 0; u < QT; ++u) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[t][u][r] = s[t][u][r] * (dp[t][u][r] - Dq[u]);
+        sb[u][0] = pack8(dp[t][u], 0);
+        sb[u][1] = pack8(dp[t][u], 1);
+      }
+#pragma unroll
+      for (int n = 0; n < NDQ; ++n)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x8 a = lds_col8<DQ_BN>(kt, L, 32 * t + 16 * hh, 32 * n);
+#pragma unroll
+          for (int u = 0; u < QT; ++u) dq[u][n] = mfma32(a, sb[u][hh], dq[u][n]);
         }
-        dp[t][r] = pv * (dp[t][r] - Dq);
-      }
-      const bf16x8 sb0 = pack8(dp[t], 0), sb1 = pack8(dp[t], 1);
-      __builtin_amdgcn_sched_barrier(0);
-      // dQ^T += K^T dS^T for the 32 keys of this tile half
+    }
+    if constexpr (!MASKED) {
+      // MFMA software pipeline: operand reads run ahead; the P computation fills the
+      // dP products, the second half's dS the first half's dQ products.
+      ATTN_SCHED_GROUP(kSchedDsRead, 2);
 #pragma unroll
-      for (int n = 0; n < NDQ; ++n) {
-        dq[n] = mfma32(lds_col8<DQ_BN>(kt, L, 32 * t, 32 * n), sb0, dq[n]);
-        dq[n] = mfma32(lds_col8<DQ_BN>(kt, L, 32 * t + 16, 32 * n), sb1, dq[n]);
+      for (int i = 0; i < 2 * KSQ; ++i) {  // S
+        ATTN_SCHED_GROUP(kSchedMfma, QT);
+        ATTN_SCHED_GROUP(kSchedDsRead, 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2 * KSV; ++i) {  // dP || P
+        ATTN_SCHED_GROUP(kSchedMfma, QT);
+        ATTN_SCHED_GROUP(kSchedDsRead, 1);
+        ATTN_SCHED_GROUP(kSchedValu, 6 * QT);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NDQ; ++i) {  // dQ (first half) || dS (second half)
+        ATTN_SCHED_GROUP(kSchedMfma, QT);
+        ATTN_SCHED_GROUP(kSchedDsRead, 2);
+        ATTN_SCHED_GROUP(kSchedValu, 6 * QT);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NDQ; ++i) {  // dQ (second half)
+        ATTN_SCHED_GROUP(kSchedMfma, QT);
+        ATTN_SCHED_GROUP(kSchedDsRead, 2);
+      }
     }
   };
 
@@ -483,7 +547,7 @@ __global__ __launch_bounds__(BWD_NT, 2) void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
     if (it + 1 < n_kv) load_kv((j - 1) * DQ_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * DQ_BN;
-    if (CAUSAL && key0 > qw + 31) return;  // tile wholly above this wavefront's rows
+    if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
     if ((CAUSAL && key0 + DQ_BN - 1 > qw) || key0 + DQ_BN > T)
       tile_body(key0, bufc, std::true_type{});
     else
@@ -494,17 +558,21 @@ __global__ __launch_bounds__(BWD_NT, 2) void bwd_dq_kernel(BwdParams p) {
     if (it + 1 < n_kv) step(it + 1, std::integral_constant<int, 1>{});
   }
 
-  if (my_q < T) {
-    bf16* row = dqg + (int64_t)my_q * p.sdq.t;
 #pragma unroll
-    for (int t = 0; t < NDQ; ++t)
+  for (int u = 0; u < QT; ++u) {
+    const int q = qw + 32 * u + lq;
+    if (q < T) {
+      bf16* row = dqg + (int64_t)q * p.sdq.t;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        bf16x4 v;
+      for (int t = 0; t < NDQ; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(dq[t][4 * a + e] * p.scale);
-        *reinterpret_cast<bf16x4*>(row + 32 * t + 8 * a + 4 * g) = v;
-      }
+        for (int a = 0; a < 4; ++a) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)(dq[u][t][4 * a + e] * p.scale);
+          *reinterpret_cast<bf16x4*>(row + 32 * t + 8 * a + 4 * g) = v;
+        }
+    }
   }
 }
 
@@ -564,7 +632,7 @@ static hipError_t bwd_main_t(const BwdParams& p, bool deterministic, hipStream_t
 
 template <int DQK, int DV, bool CAUSAL>
 static hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
-  const int nqb = (p.T + DQ_BM - 1) / DQ_BM;
+  const int nqb = (p.T + DqShape<DQK>::BM - 1) / DqShape<DQK>::BM;
   hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
