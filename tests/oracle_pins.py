@@ -11,7 +11,10 @@ Pages cited:
 """
 from __future__ import annotations
 
+import json
 import math
+import os
+from fractions import Fraction
 
 import numpy as np
 import torch
@@ -196,6 +199,38 @@ def pin_two_keys_closed_form(ref):
     _close(g["dv"].ravel(), dv, rtol=1e-15, what="two keys: dV")
 
 
+def pin_worked_example(ref, case: str):
+    """The hand-worked three-token example of tests/golden/worked_example.json: Q = I,
+    scale = 1 and K chosen so that exp(S) is a small integer matrix, which makes P, O,
+    dV, D and dS exact rationals (worked out by hand in the file) and LSE the log of
+    an integer."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_example.json")
+    with open(path) as fh:
+        ex = json.load(fh)
+    want = ex["cases"][case]
+    frac = lambda m: np.array([[float(Fraction(x)) for x in row] for row in m]) if isinstance(m[0], list) \
+        else np.array([float(Fraction(x)) for x in m])
+    a = np.array(ex["a"], dtype=np.float64)
+    q = np.eye(3).reshape(1, 3, 1, 3)
+    k = np.log(a).T.reshape(1, 3, 1, 3)             # K[j][c] = ln a[c][j]
+    v = np.array(ex["v"], dtype=np.float64).reshape(1, 3, 1, 2)
+    do = np.array(ex["do"], dtype=np.float64).reshape(1, 3, 1, 2)
+    g = ref.attn_ref_bwd(q, k, v, do, case == "causal", 1.0)
+    ds = frac(want["ds"])
+    _close(g["o"][0, :, 0], frac(want["o"]), rtol=1e-15, atol=1e-15, what=f"worked {case}: O")
+    _close(g["lse"][0, 0], np.log(np.array(want["lse_ln_of"], dtype=np.float64)), rtol=1e-15, atol=1e-15,
+           what=f"worked {case}: LSE")
+    _close(g["dv"][0, :, 0], frac(want["dv"]), rtol=1e-15, atol=1e-15, what=f"worked {case}: dV")
+    _close(g["dk"][0, :, 0], ds.T, rtol=1e-14, atol=1e-15, what=f"worked {case}: dK")
+    # dQ[i][c] = sum_j dS[i][j] ln a[c][j], from the hand-derived dS
+    _close(g["dq"][0, :, 0], ds @ np.log(a).T, rtol=1e-14, atol=1e-15, what=f"worked {case}: dQ")
+    # the forward alone gives the same O and LSE
+    o, lse = ref.attn_ref_fwd(q, k, v, case == "causal", 1.0)
+    _close(o[0, :, 0], frac(want["o"]), rtol=1e-15, atol=1e-15, what=f"worked {case}: forward O")
+    _close(lse[0, 0], np.log(np.array(want["lse_ln_of"], dtype=np.float64)), rtol=1e-15, atol=1e-15,
+           what=f"worked {case}: forward LSE")
+
+
 # ---------------------------------------------------------------------------------
 # 5. Library cross-check: torch float64 autograd through softmax(scale Q K^T) V
 # ---------------------------------------------------------------------------------
@@ -231,6 +266,8 @@ ALL_PINS = [
     ("single_token_full", lambda r: pin_single_token(r, False)),
     ("causal_first_row", pin_causal_first_row),
     ("two_keys_closed_form", pin_two_keys_closed_form),
+    ("worked_example_full", lambda r: pin_worked_example(r, "full")),
+    ("worked_example_causal", lambda r: pin_worked_example(r, "causal")),
     ("torch_autograd_causal", lambda r: pin_torch_autograd(r, True)),
     ("torch_autograd_full", lambda r: pin_torch_autograd(r, False)),
 ]
