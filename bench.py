@@ -26,6 +26,47 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0
 
 
+# HBM traffic per launch on the headline workload (B4 NH16 T8192 d128 causal,
+# deterministic dQ), from two rocprofv3 --pmc passes over `bench.py --steps 1 --warmup 0
+# --no-cpu-baseline`: FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch.  They are scaled by
+# what the same counters read for a streaming kernel of known size (`bench.py
+# --copy-calibration 1024`, 1 GiB read and 1 GiB written per launch): FETCH_SIZE read
+# 524294.5 KiB there, WRITE_SIZE 1048576 KiB.  The figures hold only for the kernel
+# sources they were taken on, identified by a hash; any change makes them null.
+TRAFFIC_SOURCES = "f7fa6f76c46fac27"
+TRAFFIC_KIB = {  # kernel: (FETCH_SIZE, WRITE_SIZE) per dispatch
+    "attn_fwd": (1181654.6875, 133136.03125),
+    "bwd_preprocess": (133165.375, 4096.4375),
+    "bwd_kv": (1261578.375, 262144.0),
+    "bwd_dq": (805818.6875, 131072.84375),
+}
+FETCH_SCALE = 1048576.0 / 524294.5
+WRITE_SCALE = 1048576.0 / 1048576.0
+
+
+def kernel_sources_hash() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_53_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def hbm_traffic(kernel: str, w, dq_mode: str):
+    """Measured HBM bytes per launch of `kernel`, or None where no measurement of the
+    current sources on this workload exists."""
+    if w.name != "headline" or dq_mode != "deterministic" or kernel not in TRAFFIC_KIB:
+        return None
+    if kernel_sources_hash() != TRAFFIC_SOURCES:
+        return None
+    fetch, write = TRAFFIC_KIB[kernel]
+    return round((fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024.0)
+
+
 def flops(w):
     pairs = w.pairs()
     return 2.0 * (w.d_qk + w.d_v) * pairs, 2.0 * (3 * w.d_qk + 2 * w.d_v) * pairs
@@ -62,6 +103,21 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
     }
 
 
+def copy_calibration(mib: int):
+    """A streaming kernel of known size: an elementwise negation that reads and writes
+    exactly mib MiB per launch (a kernel, unlike a DMA copy, is seen by the counters).
+    The FETCH_SIZE / WRITE_SIZE counters of these launches give the factor that turns
+    the counters of the attention kernels into bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -71,11 +127,18 @@ def main():
     ap.add_argument("--dq-mode", choices=["deterministic", "atomic"], default="deterministic",
                     help="dQ summed in a fixed order without atomics (default) or by fp32 atomics")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the known-size "
+                         "kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(attention shards over (batch, head) with no communication; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} given): attention shards over "
+              f"(batch, head) pairs with no communication, so each GPU runs its share as this "
+              f"one-GPU workload", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
 
@@ -190,7 +253,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": hbm_traffic(dom, w, args.dq_mode),
+            "traffic_unit": "bytes per launch",
         },
     }
     if not args.no_cpu_baseline:
