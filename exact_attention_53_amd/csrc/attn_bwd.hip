@@ -1,607 +1,9 @@
-// Exact attention backward for gfx950.
-//
-// Pages cited (by title and section):
-//   [SA8]  "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析" 2.1 and A.2 (dV = P^T dO,
-//          dP = dO V^T, dS = P * (dP - (dP * P) 1), dQ = dS K / sqrt(d_k), dK = dS^T Q / sqrt(d_k)),
-//          4.1 (recompute instead of storing P), 5.3 (simplified softmax-backward term)
-//   [2CTA] "深度学习反向传播优化：2-CTA MMA模式与内存访问优化" 2.2 (dQ is a sum over key/value
-//          blocks), 3.1 (global atomic accumulation of dQ), 3.2 (deterministic mode,
-//          head/batch swizzle, longest-first order), 6.2 (diagonal-first)
-//
-// Kernels, in stream order:
-//   bwd_pre_kernel     D_i = sum_k dO_ik O_ik  (= (dP * P) 1 of [SA8 2.1]: summing
-//                      P_ij dP_ij = P_ij sum_k dO_ik V_jk over j gives sum_k dO_ik O_ik)
-//                      and LSE_i log2(e) (padding rows +inf), both into the workspace;
-//                      clears the fp32 dQ accumulator (atomic mode).
-//   bwd_kv_kernel      one workgroup per key/value block of BWD_BN = 128 keys; each of
-//                      its 4 wavefronts owns 32 keys, keeps K and V as B operands and dK,
-//                      dV as accumulators, and loops over query blocks of BWD_BM = 64:
-//                        S = Q K^T, P = 2^(S scale log2e - LSE log2e)  (recomputed)
-//                        dP = dO V^T, dS = P * (dP - D)
-//                        dV += P^T dO, dK += dS^T Q  (P, dS straight from registers,
-//                                                     dO, Q read column-wise from LDS)
-//                      atomic mode: dS is staged in LDS, the 64 x d_qk partial dQ = dS K
-//                      over this block's keys is formed with MFMAs and added with fp32
-//                      atomics into the accumulator [2CTA 3.1].
-//   bwd_dq_kernel      deterministic mode only: one workgroup per query block of 128 rows,
-//                      looping over key blocks in one fixed order and summing dQ in
-//                      registers (S and dP recomputed), so dQ is bit-identical from run
-//                      to run; the kv kernel then issues no atomics.
-//   bwd_finalize_kernel dQ = scale * accumulator -> bf16 (atomic mode).
-#include <type_traits>
-
-#include "attn_common.hpp"
-#include "attn_kernels.hpp"
+// Exact attention backward for gfx950: launchers of the preprocess and finalize
+// kernels and dispatch of the per-configuration key/value and dQ launchers.  The
+// kernels themselves are in attn_bwd_kernels.hpp.
+#include "attn_bwd_kernels.hpp"
 
 namespace attn53 {
-
-constexpr int BWD_BN = 128;  // keys per workgroup (32 per wavefront)
-constexpr int BWD_BM = 64;   // queries per step
-constexpr int BWD_NT = 256;
-constexpr int DQ_BN = 64;    // dQ kernel: keys per step
-
-// ---------------------------------------------------------------------------------
-// preprocess: D = rowsum(dO * O); optional clear of the dQ accumulator
-// ---------------------------------------------------------------------------------
-template <int DV>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int d_qk, int zero_acc) {
-  constexpr int G = DV / 8;  // lanes per row
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / G;  // over B * NH * Tpad
-  const int c = (int)(gid % G);
-  const int64_t nrows = (int64_t)p.B * p.NH * p.Tpad;
-  float sum = 0.f;
-  if (row < nrows) {
-    const int t = (int)(row % p.Tpad);
-    const int bh = (int)(row / p.Tpad);
-    const int b = bh / p.NH, h = bh % p.NH;
-    if (t < p.T) {
-      const bf16* orow = (const bf16*)p.o + b * p.so.b + h * p.so.h + (int64_t)t * p.so.t;
-      const bf16* drow = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h + (int64_t)t * p.sdo.t;
-      const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(orow + 8 * c));
-      const bf16x8 dv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(drow + 8 * c));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sum += (float)ov[e] * (float)dv[e];
-    }
-    if (zero_acc) {
-      float* acc = p.dq_acc + row * d_qk;
-      for (int x = 4 * c; x < d_qk; x += 4 * G) *reinterpret_cast<f32x4*>(acc + x) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-#pragma unroll
-  for (int off = G / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, G);
-  if (row < nrows && c == 0) {
-    const int t = (int)(row % p.Tpad);
-    const int bh = (int)(row / p.Tpad);
-    p.D[row] = sum;
-    // LSE in base-2 units; padding rows get +inf, which makes their P exactly 0
-    p.lse2[row] = t < p.T ? p.lse[(int64_t)bh * p.T + t] * kLog2e : INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------------
-// main backward: key/value-stationary
-// ---------------------------------------------------------------------------------
-// LDS (d = 128): K block 32 KB (B operand of the partial dQ = dS K), Q and dO tiles
-// 2 x 16 KB each (double-buffered direct global->LDS loads), dS^T 2 x 16 KB, LSE and
-// D 2 x 256 B each.  Every buffer is its own LDS object so that reads of one buffer
-// do not wait for the loads in flight into the other.  Per query block i (one step):
-//   top:    wait for this step's tiles, barrier, start the loads of step i+1;
-//   dQ:     partial dQ of step i-1 (64 x d_qk) = dS K from the dS^T tile that step
-//           left in LDS, then fp32 atomic adds into the accumulator [2CTA 3.1]; the
-//           adds drain behind this step's matrix work;
-//   S, dP   (2 x d/16 MFMAs each; A operands are row reads of Q / dO);
-//   P, dS   on the VALU; dV += P^T dO and dK += dS^T Q with the B operands read
-//           column-wise (ds_read_b64_tr_b16);
-//   dS^T -> LDS for the next step's dQ.
-// With d_qk = 192 LDS holds one dS^T buffer only; a barrier then separates the last
-// reads of the previous tile from the writes of the new one.
-template <int DQK, int DV, bool CAUSAL, bool ATOMIC_DQ>
-__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_kernel(BwdParams p) {
-  constexpr int KSQ = DQK / 16, KSV = DV / 16;
-  constexpr int NDK = DQK / 32, NDV = DV / 32;
-  constexpr int NDQ = DQK / 32 / 2;  // dQ tiles per wavefront
-  constexpr int QT_BYTES = BWD_BM * DQK * 2;
-  constexpr int OT_BYTES = BWD_BM * DV * 2;
-  constexpr int KD_BYTES = ATOMIC_DQ ? BWD_BN * DQK * 2 : 16;
-  constexpr int ST_BYTES = ATOMIC_DQ ? BWD_BN * BWD_BM * 2 : 16;
-  constexpr bool ST_DOUBLE = DQK <= 128;
-  __shared__ __attribute__((aligned(1024))) char qbuf0[QT_BYTES], qbuf1[QT_BYTES];
-  __shared__ __attribute__((aligned(1024))) char obuf0[OT_BYTES], obuf1[OT_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kd_lds[KD_BYTES];
-  __shared__ __attribute__((aligned(1024))) char st0[ST_BYTES], st1[ST_DOUBLE ? ST_BYTES : 16];
-  __shared__ __attribute__((aligned(256))) float lse0[BWD_BM], lse1[BWD_BM], dd0[BWD_BM], dd1[BWD_BM];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
-  const int T = p.T;
-  const int nqb = (T + BWD_BM - 1) / BWD_BM;
-  const Item item = schedule(blockIdx.x, p.B * p.NH);
-  const int kb = item.rank;  // causal: block 0 has the most query blocks -> first
-  const int b = item.bh / p.NH, h = item.bh % p.NH;
-
-  const bf16* qg = (const bf16*)p.q + b * p.sq.b + h * p.sq.h;
-  const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
-  const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
-  const bf16* dog = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h;
-  const float* lseg = p.lse2 + (int64_t)item.bh * p.Tpad;
-  const float* Dg = p.D + (int64_t)item.bh * p.Tpad;
-  const int64_t sqt = p.sq.t, sdot = p.sdo.t;
-
-  const LdsLane L = lds_lane(lane);
-  const int key0 = kb * BWD_BN;
-  const int kw = 32 * w;
-  const int my_key = key0 + kw + lq;
-  const float c = p.scale_log2;
-
-  // K and V rows of this wavefront as B-operand fragments of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[KSQ], vf[KSV];
-#pragma unroll
-  for (int ks = 0; ks < KSQ; ++ks) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (my_key < T) raw = *reinterpret_cast<const u32x4*>(kg + (int64_t)my_key * p.sk.t + 16 * ks + 8 * g);
-    kf[ks] = __builtin_bit_cast(bf16x8, raw);
-  }
-#pragma unroll
-  for (int ks = 0; ks < KSV; ++ks) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (my_key < T) raw = *reinterpret_cast<const u32x4*>(vg + (int64_t)my_key * p.sv.t + 16 * ks + 8 * g);
-    vf[ks] = __builtin_bit_cast(bf16x8, raw);
-  }
-
-  DirectTile<BWD_BM, DQK, BWD_NT / 64> qload;
-  DirectTile<BWD_BM, DV, BWD_NT / 64> oload;
-  qload.init(sqt, w, lane);
-  oload.init(sdot, w, lane);
-  auto load_step = [&](int qb, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-    const int r0 = qb * BWD_BM;
-    qload.issue(qg + r0 * sqt, sqt, T - r0, (ATTN_LDS char*)(BUF ? qbuf1 : qbuf0), w);
-    oload.issue(dog + r0 * sdot, sdot, T - r0, (ATTN_LDS char*)(BUF ? obuf1 : obuf0), w);
-    if (w == 0) {  // 64 rows of LSE log2(e) and of D (both padded to Tpad rows)
-      __builtin_amdgcn_global_load_lds((const void*)(lseg + r0 + lane), (ATTN_LDS void*)(BUF ? lse1 : lse0), 4, 0, 0);
-    } else if (w == 1) {
-      __builtin_amdgcn_global_load_lds((const void*)(Dg + r0 + lane), (ATTN_LDS void*)(BUF ? dd1 : dd0), 4, 0, 0);
-    }
-  };
-
-  if constexpr (ATOMIC_DQ) {
-    TileStage<BWD_BN, DQK, BWD_NT> kst;
-    kst.load(kg, p.sk.t, key0, T, tid);
-    kst.store((ATTN_LDS char*)kd_lds, tid);
-  }
-
-  const int i0 = CAUSAL ? key0 / BWD_BM : 0;
-  const int n_q = nqb - i0;
-
-  f32x16 dk[NDK], dv[NDV];
-#pragma unroll
-  for (int t = 0; t < NDK; ++t) dk[t] = zero16();
-#pragma unroll
-  for (int t = 0; t < NDV; ++t) dv[t] = zero16();
-  const int tq = w & 1;               // dQ: query tile of this wavefront
-  const int dq_t0 = (w >> 1) * NDQ;   //     first d tile
-  float* dqacc = ATOMIC_DQ ? p.dq_acc + (int64_t)item.bh * p.Tpad * DQK : nullptr;
-
-  // partial dQ of the query block at q0 from the dS^T tile in `st`, added atomically
-  auto dq_partial = [&](const ATTN_LDS char* st, int q0) {
-    f32x16 dq[NDQ];
-#pragma unroll
-    for (int n = 0; n < NDQ; ++n) dq[n] = zero16();
-    const ATTN_LDS char* kd = (const ATTN_LDS char*)kd_lds;
-#pragma unroll
-    for (int m = 0; m < BWD_BN / 16; ++m) {
-      const bf16x8 a = lds_col8<BWD_BN>(st, L, 16 * m, 32 * tq);
-#pragma unroll
-      for (int n = 0; n < NDQ; ++n) dq[n] = mfma32(a, lds_col8<BWD_BN>(kd, L, 16 * m, 32 * (dq_t0 + n)), dq[n]);
-    }
-#pragma unroll
-    for (int n = 0; n < NDQ; ++n) {
-      const int d = 32 * (dq_t0 + n) + lq;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 32 * tq + 8 * (r >> 2) + 4 * g + (r & 3);  // < Tpad
-        unsafeAtomicAdd(dqacc + (int64_t)q * DQK + d, dq[n][r]);
-      }
-    }
-  };
-
-  load_step(i0, std::integral_constant<int, 0>{});
-
-  // One query block.  MASKED: the block touches the diagonal or a ragged edge.  The
-  // body is one basic block in source order S, dP, P, dV, dS, dK so that the matrix
-  // work of dP and dV can run beside the VALU work of P and dS.
-  auto step_body = [&](int q0, auto bufc, auto maskc) {
-    constexpr int BUF = decltype(bufc)::value;
-    constexpr bool MASKED = decltype(maskc)::value;
-    ATTN_LDS char* st_cur = (ATTN_LDS char*)((ST_DOUBLE && BUF) ? st1 : st0);
-    const ATTN_LDS char* qt = (const ATTN_LDS char*)(BUF ? qbuf1 : qbuf0);
-    const ATTN_LDS char* ot = (const ATTN_LDS char*)(BUF ? obuf1 : obuf0);
-    const float* lb = BUF ? lse1 : lse0;
-    const float* db = BUF ? dd1 : dd0;
-    if (MASKED && CAUSAL && key0 + kw > q0 + BWD_BM - 1) {
-      // every key of this wavefront lies above every query of the block: P = dS = 0
-      if constexpr (ATOMIC_DQ) {
-        if constexpr (!ST_DOUBLE) __syncthreads();
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          *reinterpret_cast<ATTN_LDS u32x2*>(st_cur + tile_off<BWD_BN>(kw + lq, 16 * m + 4 * g)) = u32x2{0u, 0u};
-          *reinterpret_cast<ATTN_LDS u32x2*>(st_cur + tile_off<BWD_BN>(kw + lq, 16 * m + 8 + 4 * g)) = u32x2{0u, 0u};
-        }
-      }
-      return;
-    }
-    // S = Q K^T and dP = dO V^T for 64 queries x this wavefront's 32 keys
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        s[t] = mfma32(lds_row8<BWD_BM>(qt, L, 32 * t, ks), kf[ks], ks == 0 ? zero16() : s[t]);
-#pragma unroll
-    for (int ks = 0; ks < KSV; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        dp[t] = mfma32(lds_row8<BWD_BM>(ot, L, 32 * t, ks), vf[ks], ks == 0 ? zero16() : dp[t]);
-    // P = 2^(S c - LSE log2 e); element r of tile t: query q0 + 32 t + 8 (r / 4) + 4 g + r % 4
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int qi = 32 * t + 8 * a + 4 * g;
-        const f32x4 Lv = *reinterpret_cast<const f32x4*>(lb + qi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * a + e;
-          float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -Lv[e]));
-          if constexpr (MASKED) {
-            const int q = q0 + qi + e;
-            pv = (my_key >= T || q >= T || (CAUSAL && my_key > q)) ? 0.f : pv;
-          }
-          s[t][r] = pv;
-        }
-      }
-    const bf16x8 pb[4] = {pack8(s[0], 0), pack8(s[0], 1), pack8(s[1], 0), pack8(s[1], 1)};
-    // dV += P^T dO  (contraction over the 64 queries)
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int t = 0; t < NDV; ++t) dv[t] = mfma32(pb[m], lds_col8<BWD_BM>(ot, L, 16 * m, 32 * t), dv[t]);
-    // dS = P (dP - D)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 Dd = *reinterpret_cast<const f32x4*>(db + 32 * t + 8 * a + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dp[t][4 * a + e] = s[t][4 * a + e] * (dp[t][4 * a + e] - Dd[e]);
-      }
-    const bf16x8 sb[4] = {pack8(dp[0], 0), pack8(dp[0], 1), pack8(dp[1], 0), pack8(dp[1], 1)};
-    // dK += dS^T Q
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int t = 0; t < NDK; ++t) dk[t] = mfma32(sb[m], lds_col8<BWD_BM>(qt, L, 16 * m, 32 * t), dk[t]);
-    if constexpr (!MASKED) {
-      // Software pipeline for the matrix cores: LDS reads run a few MFMAs ahead, the
-      // P computation fills the gaps of the dP products and the dS computation those
-      // of the dV products.
-      ATTN_SCHED_GROUP(kSchedDsRead, 4);
-#pragma unroll
-      for (int i = 0; i < 2 * KSQ; ++i) {  // S
-        ATTN_SCHED_GROUP(kSchedMfma, 1);
-        ATTN_SCHED_GROUP(kSchedDsRead, 1);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * KSV; ++i) {  // dP || P
-        ATTN_SCHED_GROUP(kSchedMfma, 1);
-        ATTN_SCHED_GROUP(kSchedDsRead, 2);
-        ATTN_SCHED_GROUP(kSchedValu, 10);
-      }
-#pragma unroll
-      for (int i = 0; i < 4 * NDV; ++i) {  // dV || dS
-        ATTN_SCHED_GROUP(kSchedMfma, 1);
-        ATTN_SCHED_GROUP(kSchedDsRead, 2);
-        ATTN_SCHED_GROUP(kSchedValu, 6);
-      }
-#pragma unroll
-      for (int i = 0; i < 4 * NDK; ++i) {  // dK
-        ATTN_SCHED_GROUP(kSchedMfma, 1);
-        ATTN_SCHED_GROUP(kSchedDsRead, 2);
-      }
-    }
-    if constexpr (ATOMIC_DQ) {
-      if constexpr (!ST_DOUBLE) __syncthreads();  // every wave has read the previous dS^T
-      // dS^T tile in LDS: row = key (128), column = query (64); sb[m] holds queries
-      // 16 m + 4 g + {0..3} (elements 0..3) and 16 m + 8 + 4 g + {0..3} (elements 4..7)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const u32x4 v = __builtin_bit_cast(u32x4, sb[m]);
-        *reinterpret_cast<ATTN_LDS u32x2*>(st_cur + tile_off<BWD_BN>(kw + lq, 16 * m + 4 * g)) = u32x2{v[0], v[1]};
-        *reinterpret_cast<ATTN_LDS u32x2*>(st_cur + tile_off<BWD_BN>(kw + lq, 16 * m + 8 + 4 * g)) = u32x2{v[2], v[3]};
-      }
-    }
-  };
-
-  auto step = [&](int it, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-    const int qb = i0 + it;
-    const int q0 = qb * BWD_BM;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads (and its atomics of the step before) are done
-    __syncthreads();                // every wave's tiles are in; the other buffers are free
-    if (it + 1 < n_q) load_step(qb + 1, std::integral_constant<int, 1 - BUF>{});
-    if constexpr (ATOMIC_DQ) {
-      if (it > 0) dq_partial((const ATTN_LDS char*)((ST_DOUBLE && !BUF) ? st1 : st0), q0 - BWD_BM);
-    }
-    const bool masked = (CAUSAL && key0 + BWD_BN - 1 > q0) || key0 + BWD_BN > T || q0 + BWD_BM > T;
-    if (masked)
-      step_body(q0, bufc, std::true_type{});
-    else
-      step_body(q0, bufc, std::false_type{});
-  };
-  for (int it = 0; it < n_q; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_q) step(it + 1, std::integral_constant<int, 1>{});
-  }
-  if constexpr (ATOMIC_DQ) {
-    __syncthreads();  // the last dS^T tile is complete
-    const bool last_odd = ((n_q - 1) & 1) != 0;
-    dq_partial((const ATTN_LDS char*)((ST_DOUBLE && last_odd) ? st1 : st0), (i0 + n_q - 1) * BWD_BM);
-  }
-
-  // dK = scale dS^T Q, dV; element r of tile t: key key0 + kw + 8 (r / 4) + 4 g + r % 4,
-  // column 32 t + lq.
-  bf16* dkg = (bf16*)p.dk + b * p.sdk.b + h * p.sdk.h;
-  bf16* dvg = (bf16*)p.dv + b * p.sdv.b + h * p.sdv.h;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = key0 + kw + 8 * (r >> 2) + 4 * g + (r & 3);
-    if (key < T) {
-#pragma unroll
-      for (int t = 0; t < NDK; ++t) dkg[(int64_t)key * p.sdk.t + 32 * t + lq] = (bf16)(dk[t][r] * p.scale);
-#pragma unroll
-      for (int t = 0; t < NDV; ++t) dvg[(int64_t)key * p.sdv.t + 32 * t + lq] = (bf16)dv[t][r];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------
-// dQ without atomics: query-stationary, fixed key-block order
-// ---------------------------------------------------------------------------------
-// One workgroup of 4 wavefronts per DQ_QT * 128 query rows; each wavefront owns
-// DQ_QT tiles of 32 rows, held in registers as B operands together with their dO rows,
-// LSE and D.  With two tiles per wavefront (d_qk <= 128; one wavefront per SIMD) every
-// K or V fragment read from LDS feeds two products; with d_qk = 192 a wavefront owns
-// one tile and two workgroups share a CU.  Key/value tiles of 64 rows stream through
-// double-buffered LDS by direct loads, in descending order.  Per tile:
-// S^T = K Q^T and dP^T = V dO^T, P^T = 2^(S^T c - LSE log2 e), dS^T = P^T (dP^T - D),
-// dQ^T += K^T dS^T with the K^T operand read column-wise.  Every dQ row is summed over
-// the key blocks in one fixed order inside one wavefront, so the result is
-// bit-identical from run to run.
-template <int DQK>
-struct DqShape {
-  static constexpr int QT = DQK <= 128 ? 2 : 1;  // 32-row query tiles per wavefront
-  static constexpr int BM = 128 * QT;            // query rows per workgroup
-  static constexpr int WAVES_PER_EU = QT == 2 ? 1 : 2;
-};
-
-template <int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
-                                                                         DqShape<DQK>::WAVES_PER_EU)))
-void bwd_dq_kernel(BwdParams p) {
-  constexpr int KSQ = DQK / 16, KSV = DV / 16, NDQ = DQK / 32;
-  constexpr int QT = DqShape<DQK>::QT, BM = DqShape<DQK>::BM;
-  constexpr int KT_BYTES = DQ_BN * DQK * 2;
-  constexpr int VT_BYTES = DQ_BN * DV * 2;
-  __shared__ __attribute__((aligned(1024))) char kbuf0[KT_BYTES], kbuf1[KT_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[VT_BYTES], vbuf1[VT_BYTES];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
-  const int T = p.T;
-  const int nqb = (T + BM - 1) / BM;
-  const Item item = schedule(blockIdx.x, p.B * p.NH);
-  const int qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
-  const int b = item.bh / p.NH, h = item.bh % p.NH;
-
-  const bf16* qg = (const bf16*)p.q + b * p.sq.b + h * p.sq.h;
-  const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
-  const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
-  const bf16* dog = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h;
-  bf16* dqg = (bf16*)p.dq + b * p.sdq.b + h * p.sdq.h;
-  const int64_t skt = p.sk.t, svt = p.sv.t;
-
-  const LdsLane L = lds_lane(lane);
-  const int q0 = qb * BM, qw = q0 + 32 * QT * w;  // first row of this wavefront
-  const float c = p.scale_log2;
-
-  // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T
-  bf16x8 qf[QT][KSQ], df[QT][KSV];
-  float lse2[QT], Dq[QT];
-#pragma unroll
-  for (int u = 0; u < QT; ++u) {
-    const int q = qw + 32 * u + lq;
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (q < T) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)q * p.sq.t + 16 * ks + 8 * g);
-      qf[u][ks] = __builtin_bit_cast(bf16x8, raw);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KSV; ++ks) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (q < T) raw = *reinterpret_cast<const u32x4*>(dog + (int64_t)q * p.sdo.t + 16 * ks + 8 * g);
-      df[u][ks] = __builtin_bit_cast(bf16x8, raw);
-    }
-    lse2[u] = p.lse2[(int64_t)item.bh * p.Tpad + min(q, p.Tpad - 1)];  // +inf on padding rows
-    Dq[u] = q < T ? p.D[(int64_t)item.bh * p.Tpad + q] : 0.f;
-  }
-
-  DirectTile<DQ_BN, DQK, BWD_NT / 64> kload;
-  DirectTile<DQ_BN, DV, BWD_NT / 64> vload;
-  kload.init(skt, w, lane);
-  vload.init(svt, w, lane);
-  auto load_kv = [&](int key0, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-    kload.issue(kg + key0 * skt, skt, T - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), w);
-    vload.issue(vg + key0 * svt, svt, T - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), w);
-  };
-
-  const int kv_end = CAUSAL ? min(T, q0 + BM) : T;
-  const int n_kv = (kv_end + DQ_BN - 1) / DQ_BN;
-
-  f32x16 dq[QT][NDQ];
-#pragma unroll
-  for (int u = 0; u < QT; ++u)
-#pragma unroll
-    for (int t = 0; t < NDQ; ++t) dq[u][t] = zero16();
-
-  auto tile_body = [&](int key0, auto bufc, auto maskc) {
-    constexpr int BUF = decltype(bufc)::value;
-    constexpr bool MASKED = decltype(maskc)::value;
-    const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
-    const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
-    f32x16 s[2][QT], dp[2][QT];  // [32-key half][query tile]
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 a = lds_row8<DQ_BN>(kt, L, 32 * t, ks);
-#pragma unroll
-        for (int u = 0; u < QT; ++u) s[t][u] = mfma32(a, qf[u][ks], ks == 0 ? zero16() : s[t][u]);
-      }
-#pragma unroll
-    for (int ks = 0; ks < KSV; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 a = lds_row8<DQ_BN>(vt, L, 32 * t, ks);
-#pragma unroll
-        for (int u = 0; u < QT; ++u) dp[t][u] = mfma32(a, df[u][ks], ks == 0 ? zero16() : dp[t][u]);
-      }
-    // P^T = 2^(S^T c - LSE log2 e)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < QT; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
-          if constexpr (MASKED) {
-            const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            pv = (key >= T || (CAUSAL && key > qw + 32 * u + lq)) ? 0.f : pv;
-          }
-          s[t][u][r] = pv;
-        }
-    // dS^T = P^T (dP^T - D); dQ^T += K^T dS^T, one 32-key half at a time
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      bf16x8 sb[QT][2];
-#pragma unroll
-      for (int u = 0; u < QT; ++u) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[t][u][r] = s[t][u][r] * (dp[t][u][r] - Dq[u]);
-        sb[u][0] = pack8(dp[t][u], 0);
-        sb[u][1] = pack8(dp[t][u], 1);
-      }
-#pragma unroll
-      for (int n = 0; n < NDQ; ++n)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8 a = lds_col8<DQ_BN>(kt, L, 32 * t + 16 * hh, 32 * n);
-#pragma unroll
-          for (int u = 0; u < QT; ++u) dq[u][n] = mfma32(a, sb[u][hh], dq[u][n]);
-        }
-    }
-    if constexpr (!MASKED) {
-      // MFMA software pipeline: operand reads run ahead; the P computation fills the
-      // dP products, the second half's dS the first half's dQ products.
-      ATTN_SCHED_GROUP(kSchedDsRead, 2);
-#pragma unroll
-      for (int i = 0; i < 2 * KSQ; ++i) {  // S
-        ATTN_SCHED_GROUP(kSchedMfma, QT);
-        ATTN_SCHED_GROUP(kSchedDsRead, 1);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * KSV; ++i) {  // dP || P
-        ATTN_SCHED_GROUP(kSchedMfma, QT);
-        ATTN_SCHED_GROUP(kSchedDsRead, 1);
-        ATTN_SCHED_GROUP(kSchedValu, 6 * QT);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * NDQ; ++i) {  // dQ (first half) || dS (second half)
-        ATTN_SCHED_GROUP(kSchedMfma, QT);
-        ATTN_SCHED_GROUP(kSchedDsRead, 2);
-        ATTN_SCHED_GROUP(kSchedValu, 6 * QT);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * NDQ; ++i) {  // dQ (second half)
-        ATTN_SCHED_GROUP(kSchedMfma, QT);
-        ATTN_SCHED_GROUP(kSchedDsRead, 2);
-      }
-    }
-  };
-
-  load_kv((n_kv - 1) * DQ_BN, std::integral_constant<int, 0>{});
-  auto step = [&](int it, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-    const int j = n_kv - 1 - it;  // fixed order: descending key block
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 < n_kv) load_kv((j - 1) * DQ_BN, std::integral_constant<int, 1 - BUF>{});
-    const int key0 = j * DQ_BN;
-    if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
-    if ((CAUSAL && key0 + DQ_BN - 1 > qw) || key0 + DQ_BN > T)
-      tile_body(key0, bufc, std::true_type{});
-    else
-      tile_body(key0, bufc, std::false_type{});
-  };
-  for (int it = 0; it < n_kv; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_kv) step(it + 1, std::integral_constant<int, 1>{});
-  }
-
-#pragma unroll
-  for (int u = 0; u < QT; ++u) {
-    const int q = qw + 32 * u + lq;
-    if (q < T) {
-      bf16* row = dqg + (int64_t)q * p.sdq.t;
-#pragma unroll
-      for (int t = 0; t < NDQ; ++t)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (bf16)(dq[u][t][4 * a + e] * p.scale);
-          *reinterpret_cast<bf16x4*>(row + 32 * t + 8 * a + 4 * g) = v;
-        }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------
-// finalize: dQ = scale * accumulator -> bf16
-// ---------------------------------------------------------------------------------
-template <int DQK>
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
-  constexpr int G = DQK / 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / G;
-  const int c = (int)(gid % G);
-  if (row >= (int64_t)p.B * p.NH * p.Tpad) return;
-  const int t = (int)(row % p.Tpad);
-  if (t >= p.T) return;
-  const int bh = (int)(row / p.Tpad);
-  const int b = bh / p.NH, h = bh % p.NH;
-  const float* src = p.dq_acc + row * DQK + 8 * c;
-  const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-  const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-  bf16x8 v;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    v[e] = (bf16)(x0[e] * p.scale);
-    v[4 + e] = (bf16)(x1[e] * p.scale);
-  }
-  bf16* dst = (bf16*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)t * p.sdq.t + 8 * c;
-  *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, v);
-}
 
 // ---------------------------------------------------------------------------------
 // launchers
@@ -616,24 +18,6 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, int d_qk, int d_v, bool zer
     hipLaunchKernelGGL((bwd_pre_kernel<128>), dim3(blocks_for(rows * 16)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
   else
     return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-template <int DQK, int DV, bool CAUSAL>
-static hipError_t bwd_main_t(const BwdParams& p, bool deterministic, hipStream_t s) {
-  const int nkb = (p.T + BWD_BN - 1) / BWD_BN;
-  const dim3 grid_kv(nkb * p.B * p.NH);
-  if (deterministic)
-    hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, CAUSAL, false>), grid_kv, dim3(BWD_NT), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, CAUSAL, true>), grid_kv, dim3(BWD_NT), 0, s, p);
-  return hipGetLastError();
-}
-
-template <int DQK, int DV, bool CAUSAL>
-static hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
-  const int nqb = (p.T + DqShape<DQK>::BM - 1) / DqShape<DQK>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 

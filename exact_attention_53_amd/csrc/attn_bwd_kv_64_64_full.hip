@@ -1,0 +1,7 @@
+// Key/value kernel instances for d_qk = 64, d_v = 64, no mask
+// (one file per configuration so that the configurations compile in parallel).
+#include "attn_bwd_kernels.hpp"
+
+namespace attn53 {
+template hipError_t bwd_main_t<64, 64, false>(const BwdParams&, bool, hipStream_t);
+}  // namespace attn53

@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn53 {
 
 typedef __bf16 bf16;
@@ -75,6 +77,18 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int m) {
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Calls f(std::integral_constant<int, I>{}) for I = B .. E-1, in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Ends a scheduling region: the compiler moves no instruction across it.
+#define ATTN_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Value held by lane l ^ 32 combined with the own value (one v_permlane32_swap).
 __device__ __forceinline__ float max_halves(float x) {
@@ -193,6 +207,18 @@ struct DirectTile {
 #endif
   }
 };
+
+// 64 consecutive fp32 values src[0 .. 63] -> LDS dst[0 .. 63], one dword per lane of one
+// wavefront, by a direct buffer->LDS load; values at or past `valid` read as zero.  (A
+// buffer load rather than a global one: the compiler then keeps counting the LDS reads
+// in flight instead of waiting for all of them.)
+__device__ __forceinline__ void load_f32x64_lds(const float* src, int valid, ATTN_LDS float* dst, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, valid * 4, kBufferResourceWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (ATTN_LDS void*)dst, 4, (uint32_t)lane * 4u, 0, 0, 0);
+#endif
+}
 
 // ---------------------------------------------------------------------------------
 // global <-> LDS tile staging through registers
