@@ -363,6 +363,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       constexpr int NS = Plan::NS, NP = Plan::NP, NV = Plan::NV, LA = Plan::LA, RING = Plan::RING;
       bf16x8 fr[RING];
       f32x4 lsev[2][4], ddv[2][4];
+      f32x16 pv[2], dsv[2];  // P and dS, apart from the S and dP accumulators
       auto read_frag = [&](auto jc) -> bf16x8 {
         constexpr int j = decltype(jc)::value;
         if constexpr (j < NS) {
@@ -381,14 +382,14 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         constexpr int h = k < 9 ? 0 : 1, r = k < 8 ? k : k - 1;
         if constexpr (grp < 2) {
           if constexpr (Plan::is_pack(o))
-            pb[2 * t + h] = pack8(s[t], h);
+            pb[2 * t + h] = pack8(pv[t], h);
           else
-            s[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, -lsev[t][r >> 2][r & 3]));
+            pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, -lsev[t][r >> 2][r & 3]));
         } else {
           if constexpr (Plan::is_pack(o))
-            sb[2 * t + h] = pack8(dp[t], h);
+            sb[2 * t + h] = pack8(dsv[t], h);
           else
-            dp[t][r] = s[t][r] * (dp[t][r] - ddv[t][r >> 2][r & 3]);
+            dsv[t][r] = pv[t][r] * (dp[t][r] - ddv[t][r >> 2][r & 3]);
         }
       };
       static_for<0, LA>([&](auto jc) { fr[decltype(jc)::value % RING] = read_frag(jc); });
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
   };
 
-  auto step = [&](int it, auto bufc) {
+  auto step = [&](int it, auto bufc, auto maskc) {
     constexpr int BUF = decltype(bufc)::value;
     const int qb = i0 + it;
     const int q0 = qb * BWD_BM;
@@ -446,15 +447,34 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     if constexpr (ATOMIC_DQ) {
       if (it > 0) dq_partial((const ATTN_LDS char*)((ST_DOUBLE && !BUF) ? st1 : st0), q0 - BWD_BM);
     }
-    const bool masked = (CAUSAL && key0 + BWD_BN - 1 > q0) || key0 + BWD_BN > T || q0 + BWD_BM > T;
-    if (masked)
-      step_body(q0, bufc, std::true_type{});
-    else
-      step_body(q0, bufc, std::false_type{});
+    step_body(q0, bufc, maskc);
   };
-  for (int it = 0; it < n_q; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_q) step(it + 1, std::integral_constant<int, 1>{});
+  // The steps that touch the diagonal (the first BWD_BN / BWD_BM under the causal mask),
+  // a ragged key block (all steps) or the ragged last query block carry the mask; they
+  // are peeled off the loop so that its body is one straight-line program.
+  constexpr auto MASK = std::true_type{};
+  constexpr auto NOMASK = std::false_type{};
+  constexpr auto B0 = std::integral_constant<int, 0>{};
+  constexpr auto B1 = std::integral_constant<int, 1>{};
+  const bool ragged_keys = key0 + BWD_BN > T;
+  const int n_head = ragged_keys ? n_q : (CAUSAL ? min(BWD_BN / BWD_BM, n_q) : 0);  // even, or n_q
+  const int n_tail = (n_head < n_q && T % BWD_BM != 0) ? 1 : 0;
+  const int mid_end = n_q - n_tail;
+  for (int it = 0; it < n_head; it += 2) {
+    step(it, B0, MASK);
+    if (it + 1 < n_head) step(it + 1, B1, MASK);
+  }
+  int it = n_head;
+  for (; it + 1 < mid_end; it += 2) {
+    step(it, B0, NOMASK);
+    step(it + 1, B1, NOMASK);
+  }
+  if (it < mid_end) step(it++, B0, NOMASK);
+  if (it < n_q) {
+    if (it & 1)
+      step(it, B1, MASK);
+    else
+      step(it, B0, MASK);
   }
   if constexpr (ATOMIC_DQ) {
     __syncthreads();  // the last dS^T tile is complete
