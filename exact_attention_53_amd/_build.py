@@ -17,8 +17,9 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libattn53.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"] + [
-    f"attn_bwd_kv_{dqk}_{dv}_{mask}.hip" for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in ("causal", "full")
+_CONFIGS = [(dqk, dv, mask) for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in ("causal", "full")]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip"] + [
+    f"attn_bwd_{kind}_{dqk}_{dv}_{mask}.hip" for kind in ("kv", "dq") for dqk, dv, mask in _CONFIGS
 ] + ["attn_api.cpp"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU instructions.

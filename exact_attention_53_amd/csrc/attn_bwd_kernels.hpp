@@ -511,6 +511,68 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 // dQ^T += K^T dS^T with the K^T operand read column-wise.  Every dQ row is summed over
 // the key blocks in one fixed order inside one wavefront, so the result is
 // bit-identical from run to run.
+// Placement of the work of one unmasked key tile in the dQ kernel (explicit pipeline).
+// Bundle b issues one LDS operand read (for bundle b + LA) and the QT MFMAs that share
+// the fragment of bundle b, in the order S (key half t = 0), dP (t = 0), S (t = 1),
+// dP (t = 1), dQ over t = 0, dQ over t = 1.  The VALU work: P of half 0 (QT x 16
+// elements), dS of half 0 with the bf16 pack of each group of eight, then the same for
+// half 1; placed greedily (P element 6, dS element 3, pack 4 cost units) no earlier
+// than two bundles after the MFMAs producing its inputs, with the smallest per-bundle
+// budget for which every pack lands before the dQ bundles that read it.
+template <int DQK, int DV, int QT>
+struct DqPlan {
+  static constexpr int KSQ = DQK / 16, KSV = DV / 16, NDQ = DQK / 32;
+  static constexpr int S0 = 0, P0 = KSQ, S1 = KSQ + KSV, P1 = 2 * KSQ + KSV, Q0 = 2 * KSQ + 2 * KSV;
+  static constexpr int Q1 = Q0 + 2 * NDQ, N = Q1 + 2 * NDQ;
+  static constexpr int LA = 4, RING = LA + 1;
+  static constexpr int PER = 16 * QT + 2 * QT;  // ops per half: P elements, then dS elements + packs
+  static constexpr int NOPS = 2 * (16 * QT + 18 * QT);
+  // op o: half t = o / (34 QT); within: k < 16 QT: P element (u = k / 16, r = k % 16);
+  // else k' = k - 16 QT: u = k' / 18, e = k' % 18: e = 8 pack half 0, e = 17 pack half 1,
+  // else dS element r = e < 8 ? e : e - 1.
+  static constexpr int half(int o) { return o / (34 * QT); }
+  static constexpr bool is_p(int o) { return o % (34 * QT) < 16 * QT; }
+  static constexpr bool is_pack(int o) {
+    return !is_p(o) && ((o % (34 * QT) - 16 * QT) % 18 == 8 || (o % (34 * QT) - 16 * QT) % 18 == 17);
+  }
+  static constexpr int cost(int o) { return is_p(o) ? 6 : (is_pack(o) ? 4 : 3); }
+  static constexpr int earliest(int o) {
+    const int t = half(o);
+    return is_p(o) ? (t ? P1 : P0) + 1 : (t ? Q0 : S1) + 1;
+  }
+  static constexpr int deadline(int o) { return (half(o) ? Q1 : Q0) - 1; }
+  struct Table {
+    int bundle[NOPS];
+    int ok;
+  };
+  static constexpr Table make(int cap) {
+    Table tb{};
+    tb.ok = 1;
+    int cur = 0, used = 0;
+    for (int o = 0; o < NOPS; ++o) {
+      if (earliest(o) > cur) {
+        cur = earliest(o);
+        used = 0;
+      }
+      if (used > 0 && used + cost(o) > cap) {
+        ++cur;
+        used = 0;
+      }
+      tb.bundle[o] = cur;
+      used += cost(o);
+      if ((is_pack(o) && cur > deadline(o)) || cur >= N) tb.ok = 0;
+    }
+    return tb;
+  }
+  static constexpr Table choose() {
+    for (int cap = 8; cap < 256; ++cap)
+      if (make(cap).ok) return make(cap);
+    return make(256);
+  }
+  static constexpr Table plan = choose();
+  static_assert(plan.ok, "no feasible placement of the tile's VALU work");
+};
+
 template <int DQK>
 struct DqShape {
   static constexpr int QT = DQK <= 128 ? 2 : 1;  // 32-row query tiles per wavefront
@@ -673,24 +735,111 @@ void bwd_dq_kernel(BwdParams p) {
     }
   };
 
+  // ---- unmasked tiles: an explicit pipeline (DqPlan) ----
+  using Plan = DqPlan<DQK, DV, QT>;
+  auto tile_pipe = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
+    const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
+    f32x16 s[2][QT], dp[2][QT];
+    f32x16 pv[QT];         // P, then dS, of the half being worked on
+    bf16x8 sb[2][QT][2];
+    bf16x8 fr[Plan::RING];
+    auto read_at = [&](auto bc) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int b = decltype(bc)::value;
+      if constexpr (b < Plan::P0)
+        return lds_row8<DQ_BN>(kt, L, 0, b);
+      else if constexpr (b < Plan::S1)
+        return lds_row8<DQ_BN>(vt, L, 0, b - Plan::P0);
+      else if constexpr (b < Plan::P1)
+        return lds_row8<DQ_BN>(kt, L, 32, b - Plan::S1);
+      else if constexpr (b < Plan::Q0)
+        return lds_row8<DQ_BN>(vt, L, 32, b - Plan::P1);
+      else {
+        constexpr int t = b < Plan::Q1 ? 0 : 1, jj = b - (t ? Plan::Q1 : Plan::Q0);
+        return lds_col8<DQ_BN>(kt, L, 32 * t + 16 * (jj % 2), 32 * (jj / 2));
+      }
+    };
+    auto valu_op = [&](auto oc) __attribute__((always_inline)) {
+      constexpr int o = decltype(oc)::value, t = Plan::half(o), k = o % (34 * QT);
+      if constexpr (Plan::is_p(o)) {
+        constexpr int u = k / 16, r = k % 16;
+        pv[u][r] = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
+      } else {
+        constexpr int kk = k - 16 * QT, u = kk / 18, e = kk % 18;
+        if constexpr (e == 8 || e == 17) {
+          sb[t][u][e == 8 ? 0 : 1] = pack8(pv[u], e == 8 ? 0 : 1);
+        } else {
+          constexpr int r = e < 8 ? e : e - 1;
+          pv[u][r] = pv[u][r] * (dp[t][u][r] - Dq[u]);
+        }
+      }
+    };
+    static_for<0, Plan::LA>([&](auto bc) __attribute__((always_inline)) { fr[decltype(bc)::value % Plan::RING] = read_at(bc); });
+    ATTN_SCHED_FENCE();
+    static_for<0, Plan::N>([&](auto bc) __attribute__((always_inline)) {
+      constexpr int b = decltype(bc)::value;
+      const bf16x8 f = fr[b % Plan::RING];
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        if constexpr (b < Plan::P0)
+          s[0][u] = mfma32(f, qf[u][b], b == 0 ? zero16() : s[0][u]);
+        else if constexpr (b < Plan::S1)
+          dp[0][u] = mfma32(f, df[u][b - Plan::P0], b == Plan::P0 ? zero16() : dp[0][u]);
+        else if constexpr (b < Plan::P1)
+          s[1][u] = mfma32(f, qf[u][b - Plan::S1], b == Plan::S1 ? zero16() : s[1][u]);
+        else if constexpr (b < Plan::Q0)
+          dp[1][u] = mfma32(f, df[u][b - Plan::P1], b == Plan::P1 ? zero16() : dp[1][u]);
+        else {
+          constexpr int t = b < Plan::Q1 ? 0 : 1, jj = b - (t ? Plan::Q1 : Plan::Q0);
+          dq[u][jj / 2] = mfma32(f, sb[t][u][jj % 2], dq[u][jj / 2]);
+        }
+      }
+      if constexpr (b + Plan::LA < Plan::N) fr[(b + Plan::LA) % Plan::RING] = read_at(std::integral_constant<int, b + Plan::LA>{});
+      static_for<0, Plan::NOPS>([&](auto oc) __attribute__((always_inline)) {
+        if constexpr (Plan::plan.bundle[decltype(oc)::value] == b) valu_op(oc);
+      });
+      ATTN_SCHED_FENCE();
+    });
+  };
+
   load_kv((n_kv - 1) * DQ_BN, std::integral_constant<int, 0>{});
-  auto step = [&](int it, auto bufc) {
+  auto step = [&](int it, auto bufc, auto maskc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     const int j = n_kv - 1 - it;  // fixed order: descending key block
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (it + 1 < n_kv) load_kv((j - 1) * DQ_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * DQ_BN;
-    if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
-    if ((CAUSAL && key0 + DQ_BN - 1 > qw) || key0 + DQ_BN > T)
-      tile_body(key0, bufc, std::true_type{});
-    else
-      tile_body(key0, bufc, std::false_type{});
+    if constexpr (decltype(maskc)::value) {
+      if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
+      if ((CAUSAL && key0 + DQ_BN - 1 > qw) || key0 + DQ_BN > T)
+        tile_body(key0, bufc, std::true_type{});
+      else
+        tile_body(key0, bufc, std::false_type{});
+    } else {
+      tile_pipe(bufc);
+    }
   };
-  for (int it = 0; it < n_kv; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_kv) step(it + 1, std::integral_constant<int, 1>{});
+  // The first tiles (the workgroup's diagonal ones under the causal mask, or the ragged
+  // last key block) may carry a mask for some wavefront; they run as plain code, the
+  // rest as the pipeline.
+  const int n_head = CAUSAL ? min(n_kv, n_kv - q0 / DQ_BN) : (T % DQ_BN != 0 ? 1 : 0);
+  constexpr auto B0 = std::integral_constant<int, 0>{};
+  constexpr auto B1 = std::integral_constant<int, 1>{};
+  int it = 0;
+  for (; it < n_head; ++it) {
+    if (it & 1)
+      step(it, B1, std::true_type{});
+    else
+      step(it, B0, std::true_type{});
   }
+  if ((it & 1) && it < n_kv) step(it++, B1, std::false_type{});
+  for (; it + 1 < n_kv; it += 2) {
+    step(it, B0, std::false_type{});
+    step(it + 1, B1, std::false_type{});
+  }
+  if (it < n_kv) step(it, B0, std::false_type{});
 
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
