@@ -185,7 +185,8 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   __shared__ __attribute__((aligned(1024))) char st0[ST_BYTES], st1[ST_DOUBLE ? ST_BYTES : 16];
   __shared__ __attribute__((aligned(256))) float lse0[BWD_BM], lse1[BWD_BM], dd0[BWD_BM], dd1[BWD_BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in a scalar register
   const int T = p.T;
   const int nqb = (T + BWD_BM - 1) / BWD_BM;
   const Item item = schedule(blockIdx.x, p.B * p.NH);
@@ -591,7 +592,9 @@ void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char kbuf0[KT_BYTES], kbuf1[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[VT_BYTES], vbuf1[VT_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the same, in a scalar register
   const int T = p.T;
   const int nqb = (T + BM - 1) / BM;
   const Item item = schedule(blockIdx.x, p.B * p.NH);
@@ -637,8 +640,8 @@ void bwd_dq_kernel(BwdParams p) {
   vload.init(svt, w, lane);
   auto load_kv = [&](int key0, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    kload.issue(kg + key0 * skt, skt, T - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), w);
-    vload.issue(vg + key0 * svt, svt, T - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), w);
+    kload.issue(kg + key0 * skt, skt, T - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), wu);
+    vload.issue(vg + key0 * svt, svt, T - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), wu);
   };
 
   const int kv_end = CAUSAL ? min(T, q0 + BM) : T;

@@ -65,6 +65,16 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 
 // 8 consecutive accumulator values (r = 8m .. 8m+7) rounded to bf16 (RNE).
+// acc + the sum of the eight values of x, by four v_dot2_f32_bf16 with (1, 1).
+__device__ __forceinline__ float sum_pairs(const bf16x8& x, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
+}
+
 __device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int m) {
   bf16x8 r;
 #pragma unroll

@@ -53,7 +53,8 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char kbuf0[KT_BYTES], kbuf1[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[VT_BYTES], vbuf1[VT_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, lq = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in a scalar register
   const int T = p.T;
   const int nqb = (T + FWD_BM - 1) / FWD_BM;
   const Item item = schedule(blockIdx.x, p.B * p.NH);
@@ -102,15 +103,16 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   load_kv((n_kv - 1) * FWD_BN, std::integral_constant<int, 0>{});
 
   // One key/value tile; BUF is this tile's buffer, the next tile goes to the other one.
-  auto step = [&](int it, auto bufc) {
+  // MASKED: the tile may hold keys past a row's diagonal or past T (the first tiles).
+  auto step = [&](int it, auto bufc, auto maskc) {
     constexpr int BUF = decltype(bufc)::value;
+    constexpr bool MASKED = decltype(maskc)::value;
     const int j = n_kv - 1 - it;  // diagonal / tail tile first
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile j has landed in LDS
     __syncthreads();                // ... and every other wave's; the other buffer is free
     if (it + 1 < n_kv) load_kv((j - 1) * FWD_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * FWD_BN;
-    const bool active = !CAUSAL || key0 <= qw + 31;
-    if (!active) return;
+    if (MASKED && CAUSAL && key0 > qw + 31) return;  // tile wholly above this wavefront's rows
     const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
     const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
     // S^T = K Q^T for keys key0 .. key0+63 (two 32-key accumulators)
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
       s0 = mfma32(lds_row8<FWD_BN>(kt, L, 0, ks), qf[ks], s0);
       s1 = mfma32(lds_row8<FWD_BN>(kt, L, 32, ks), qf[ks], s1);
     }
-    if ((CAUSAL && key0 + FWD_BN - 1 > qw) || key0 + FWD_BN > T) {
+    if constexpr (MASKED) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk0 = key0 + 8 * (r >> 2) + 4 * g + (r & 3), kk1 = kk0 + 32;
@@ -128,12 +130,17 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
         if (kk1 >= T || (CAUSAL && kk1 > my_q)) s1[r] = -INFINITY;
       }
     }
+    // The IEEE maximum (NaN-propagating) maps onto v_maximum3_f32 with no canonicalising
+    // moves of the matrix-core results in front of it.
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[r], s1[r]));
     // Every processed tile holds key key0 <= every row of this wave, so mx is finite.
     const float m_tile = max_halves(mx) * c;
-    if (__any(m_tile > m_run + kRescaleThreshold)) {
+    if (__builtin_expect(__any(m_tile > m_run + kRescaleThreshold), 0)) {
+      // Kept as a branch (the empty volatile asm stops the compiler from turning it into
+      // unconditional multiplies): it is taken on a row's first tile and rarely after.
+      asm volatile("");
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = exp2_fast(m_run - m_new);
       m_run = m_new;
@@ -143,17 +150,15 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
-    float rs = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p0 = exp2_fast(__builtin_fmaf(s0[r], c, -m_run));
-      const float p1 = exp2_fast(__builtin_fmaf(s1[r], c, -m_run));
-      rs += p0 + p1;
-      s0[r] = p0;
-      s1[r] = p1;
+      s0[r] = exp2_fast(__builtin_fmaf(s0[r], c, -m_run));
+      s1[r] = exp2_fast(__builtin_fmaf(s1[r], c, -m_run));
     }
-    l_run += rs;
     const bf16x8 pb0 = pack8(s0, 0), pb1 = pack8(s0, 1), pb2 = pack8(s1, 0), pb3 = pack8(s1, 1);
+    // l += the row's sum of the rounded p (the weights O is built from), one v_dot2 with
+    // (1, 1) per bf16 pair: half the instructions of adding the fp32 values.
+    l_run = sum_pairs(pb0, sum_pairs(pb1, sum_pairs(pb2, sum_pairs(pb3, l_run))));
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -163,10 +168,26 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
       o[dt] = mfma32(lds_col8<FWD_BN>(vt, L, 48, 32 * dt), pb3, o[dt]);
     }
   };
-  for (int it = 0; it < n_kv; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_kv) step(it + 1, std::integral_constant<int, 1>{});
+  // The first tiles (the workgroup's diagonal ones under the causal mask, or the ragged
+  // last key block) carry the mask; the loop over the others has no mask code at all.
+  constexpr auto B0 = std::integral_constant<int, 0>{};
+  constexpr auto B1 = std::integral_constant<int, 1>{};
+  constexpr auto MASK = std::true_type{};
+  constexpr auto NOMASK = std::false_type{};
+  const int n_mask = CAUSAL ? min(n_kv, n_kv - q0 / FWD_BN) : (T % FWD_BN != 0 ? 1 : 0);
+  int it = 0;
+  for (; it < n_mask; ++it) {
+    if (it & 1)
+      step(it, B1, MASK);
+    else
+      step(it, B0, MASK);
   }
+  if ((it & 1) && it < n_kv) step(it++, B1, NOMASK);
+  for (; it + 1 < n_kv; it += 2) {
+    step(it, B0, NOMASK);
+    step(it + 1, B1, NOMASK);
+  }
+  if (it < n_kv) step(it, B0, NOMASK);
 
   // deferred normalisation and stats
   const float l_tot = sum_halves(l_run);
