@@ -41,6 +41,7 @@ constexpr int FWD_BM = 128;
 constexpr int FWD_BN = 64;
 constexpr int FWD_NT = 256;
 constexpr float kRescaleThreshold = 8.f;  // log2 units
+constexpr float kSumLimit = 256.f;        // 2^kRescaleThreshold
 
 template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
@@ -116,31 +117,34 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
     const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
     // S^T = K Q^T for keys key0 .. key0+63 (two 32-key accumulators)
-    f32x16 s0 = zero16(), s1 = zero16();
+    f32x16 s0, s1;
+    auto scores = [&]() __attribute__((always_inline)) {
+      s0 = zero16();
+      s1 = zero16();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s0 = mfma32(lds_row8<FWD_BN>(kt, L, 0, ks), qf[ks], s0);
-      s1 = mfma32(lds_row8<FWD_BN>(kt, L, 32, ks), qf[ks], s1);
-    }
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk0 = key0 + 8 * (r >> 2) + 4 * g + (r & 3), kk1 = kk0 + 32;
-        if (kk0 >= T || (CAUSAL && kk0 > my_q)) s0[r] = -INFINITY;
-        if (kk1 >= T || (CAUSAL && kk1 > my_q)) s1[r] = -INFINITY;
+      for (int ks = 0; ks < KS; ++ks) {
+        s0 = mfma32(lds_row8<FWD_BN>(kt, L, 0, ks), qf[ks], s0);
+        s1 = mfma32(lds_row8<FWD_BN>(kt, L, 32, ks), qf[ks], s1);
       }
-    }
-    // The IEEE maximum (NaN-propagating) maps onto v_maximum3_f32 with no canonicalising
-    // moves of the matrix-core results in front of it.
-    float mx = -INFINITY;
+      if constexpr (MASKED) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[r], s1[r]));
-    // Every processed tile holds key key0 <= every row of this wave, so mx is finite.
-    const float m_tile = max_halves(mx) * c;
-    if (__builtin_expect(__any(m_tile > m_run + kRescaleThreshold), 0)) {
-      // Kept as a branch (the empty volatile asm stops the compiler from turning it into
-      // unconditional multiplies): it is taken on a row's first tile and rarely after.
-      asm volatile("");
+        for (int r = 0; r < 16; ++r) {
+          const int kk0 = key0 + 8 * (r >> 2) + 4 * g + (r & 3), kk1 = kk0 + 32;
+          if (kk0 >= T || (CAUSAL && kk0 > my_q)) s0[r] = -INFINITY;
+          if (kk1 >= T || (CAUSAL && kk1 > my_q)) s1[r] = -INFINITY;
+        }
+      }
+    };
+    // The tile's row maximum (scaled, log2 units).  The IEEE maximum (NaN-propagating)
+    // maps onto v_maximum3_f32 with no canonicalising moves of the MFMA results.  Every
+    // processed tile holds key key0 <= every row of this wave, so it is finite.
+    auto tile_max = [&]() __attribute__((always_inline)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[r], s1[r]));
+      return max_halves(mx) * c;
+    };
+    auto raise_max = [&](float m_tile) __attribute__((always_inline)) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = exp2_fast(m_run - m_new);
       m_run = m_new;
@@ -149,16 +153,48 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
+    };
+    // p = 2^(S c - m) as bf16 operands of the second product; returns this lane's sum of
+    // the rounded p (the weights O is built from), one v_dot2 with (1, 1) per bf16 pair.
+    bf16x8 pb[4];
+    auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = exp2_fast(__builtin_fmaf(s0[r], c, -m_run));
-      s1[r] = exp2_fast(__builtin_fmaf(s1[r], c, -m_run));
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = exp2_fast(__builtin_fmaf(s0[r], c, -m_run));
+        s1[r] = exp2_fast(__builtin_fmaf(s1[r], c, -m_run));
+      }
+      pb[0] = pack8(s0, 0);
+      pb[1] = pack8(s0, 1);
+      pb[2] = pack8(s1, 0);
+      pb[3] = pack8(s1, 1);
+      return sum_pairs(pb[0], sum_pairs(pb[1], sum_pairs(pb[2], sum_pairs(pb[3], 0.f))));
+    };
+    scores();
+    float rs;
+    if constexpr (MASKED) {
+      const float m_tile = tile_max();
+      // Kept as a branch (the empty volatile asm stops the compiler from turning it into
+      // unconditional multiplies): it is taken on a row's first tile and rarely after.
+      if (__builtin_expect(__any(m_tile > m_run + kRescaleThreshold), 0)) {
+        asm volatile("");
+        raise_max(m_tile);
+      }
+      rs = probs();
+    } else {
+      // No maximum at all on the common path: p is taken against the running max, and
+      // only if some lane's sum exceeds 2^8 (so that a p might) are S recomputed from the
+      // K tile still in LDS, the running max raised to the exact one and p redone.  A sum
+      // <= 2^8 bounds every p by 2^8, the same bound the masked path keeps.
+      rs = probs();
+      if (__builtin_expect(__any(rs > kSumLimit), 0)) {
+        asm volatile("");
+        scores();
+        raise_max(tile_max());
+        rs = probs();
+      }
     }
-    const bf16x8 pb0 = pack8(s0, 0), pb1 = pack8(s0, 1), pb2 = pack8(s1, 0), pb3 = pack8(s1, 1);
-    // l += the row's sum of the rounded p (the weights O is built from), one v_dot2 with
-    // (1, 1) per bf16 pair: half the instructions of adding the fp32 values.
-    l_run = sum_pairs(pb0, sum_pairs(pb1, sum_pairs(pb2, sum_pairs(pb3, l_run))));
+    l_run += rs;
+    const bf16x8 pb0 = pb[0], pb1 = pb[1], pb2 = pb[2], pb3 = pb[3];
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {

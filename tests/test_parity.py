@@ -9,7 +9,9 @@ import torch
 
 import exact_attention_53_amd as attn
 import workloads
-from tests.gpu_cases import compare, gpu_inputs, oracle, run_gpu, sample_heads, say, to_np
+from oracle import attn_ref
+from tests.gpu_cases import (check_bf16, check_lse, compare, gpu_inputs, oracle, run_gpu, sample_heads, say,
+                             to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +59,35 @@ def test_large_magnitude_scores():
         say(f"case sigma4 {w.name}")
         cpu, gpu = gpu_inputs(w)
         compare(w, run_gpu(w, gpu, False), oracle(w, cpu))
+
+
+@pytest.mark.parametrize("causal,T", [(True, 333), (False, 320)], ids=["causal", "full"])
+def test_row_maximum_found_late(causal, T):
+    """Key 0 is planted with a score far above all others (about 15 against about 1).
+    Key tiles are visited from the last one down, so key 0 comes in the last tile of
+    every row: the running maximum must be raised, and O and l rescaled, after most of
+    the row has been summed.  In the full case with T a multiple of the key tile no tile
+    carries a mask, so the first tile is met with no maximum at all.
+
+    Only the forward outputs are compared: with P_i0 close to 1 in every row, dS_i0 =
+    P_i0 (dP_i0 - D_i) cancels almost exactly, and the bf16 rounding of the stored O that
+    D_i is computed from dominates the tiny dK; large scores in the backward are covered
+    by the N(0, 4^2) case."""
+    for dims in HEADDIMS:
+        w = _small(T, dims[0], dims[1], causal, B=1, NH=2, seed=13)
+        say(f"case late max {w.name}")
+        cpu = workloads.make_inputs(w)
+        q = cpu["q"].to(torch.float32)
+        q[..., 0] += 4.0
+        k = cpu["k"].to(torch.float32)
+        k[:, 0, :, 0] = 30.0 * (w.d_qk / 64) ** 0.5
+        cpu["q"], cpu["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+        dev = torch.device("cuda:0")
+        gpu = {n: cpu[n].to(dev) for n in ("q", "k", "v")}
+        o, lse = attn.fwd(gpu["q"], gpu["k"], gpu["v"], w.causal, w.scale)
+        ref_o, ref_lse = attn_ref.attn_ref_fwd(cpu["q"], cpu["k"], cpu["v"], w.causal, w.scale)
+        check_bf16(f"{w.name} o", to_np(o), ref_o)
+        check_lse(f"{w.name} lse", to_np(lse), ref_lse)
 
 
 def test_zero_queries_closed_form():
