@@ -7,6 +7,7 @@ from .attn_ref import (  # noqa: F401
     attn_ref_bwd,
     attn_ref_bwd_loop,
     attn_ref_fwd,
+    attn_ref_varlen,
     head_backward,
     head_forward,
     to_f64,

@@ -49,6 +49,7 @@ __all__ = [
     "attn_ref_fwd",
     "attn_ref_bwd",
     "attn_ref_heads",
+    "attn_ref_varlen",
     "attn_ref_bwd_loop",
 ]
 
@@ -84,14 +85,15 @@ def _softmax_rows(S: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
                  block_rows: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """One head: q, k (T, d_qk), v (T, d_v) float64 -> O (T, d_v), LSE (T,)."""
-    T = q.shape[0]
+    """One head: q (T, d_qk), k (Tk, d_qk), v (Tk, d_v) float64 -> O (T, d_v), LSE (T,).
+    Tk >= 1 may differ from T (padded batches); the causal mask stays top-left."""
+    T, Tk = q.shape[0], k.shape[0]
     br = T if block_rows is None else block_rows
     O = np.empty((T, v.shape[1]))
     lse = np.empty(T)
     for r0 in range(0, T, br):
         r1 = min(T, r0 + br)
-        nk = r1 if causal else T          # keys past the last query are all masked
+        nk = min(r1, Tk) if causal else Tk  # keys past the last query are all masked
         S = _scores(q[r0:r1], k[:nk], scale, causal, r0)
         P, lse[r0:r1] = _softmax_rows(S)
         O[r0:r1] = P @ v[:nk]
@@ -100,8 +102,9 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
 
 def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
                   causal: bool, block_rows: Optional[int] = None):
-    """One head: returns dQ, dK, dV and also O, LSE and D = (dP * P) 1 (all float64)."""
-    T = q.shape[0]
+    """One head: returns dQ, dK, dV and also O, LSE and D = (dP * P) 1 (all float64).
+    q, do have T rows, k, v have Tk >= 1 rows (Tk may differ from T)."""
+    T, Tk = q.shape[0], k.shape[0]
     br = T if block_rows is None else block_rows
     O = np.empty((T, v.shape[1]))
     lse = np.empty(T)
@@ -111,7 +114,7 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
     dV = np.zeros_like(v)
     for r0 in range(0, T, br):
         r1 = min(T, r0 + br)
-        nk = r1 if causal else T
+        nk = min(r1, Tk) if causal else Tk
         S = _scores(q[r0:r1], k[:nk], scale, causal, r0)
         P, lse[r0:r1] = _softmax_rows(S)
         O[r0:r1] = P @ v[:nk]
@@ -188,6 +191,43 @@ def attn_ref_heads(q, k, v, do, causal: bool, scale: Optional[float] = None,
         r = head_backward(qh, kh, vh, dh, scale, causal, br)
         res[(b, h)] = dict(zip(("dq", "dk", "dv", "o", "lse", "D"), r))
     return res
+
+
+def attn_ref_varlen(q, k, v, do, seq_q, seq_k, causal: bool, scale: Optional[float] = None):
+    """Padded batches: the padding mask with per-batch lengths seq_len_q and seq_len_kv
+    among the SDPA options of [SA8 1.2].  Batch b uses query rows 0 .. seq_q[b]-1 and
+    key/value rows 0 .. seq_k[b]-1 of its (T, NH, d) slices; everything past them is
+    padding and never read.  Within a batch the result is the plain definition above on
+    the unpadded rows (causal: key j allowed for query i iff j <= i, top-left).
+
+    Readings where the page is silent: padding query rows get O = 0, LSE = -inf and
+    dQ = 0; padding key rows get dK = dV = 0; a query with no allowed key (seq_k[b] = 0)
+    gets O = 0, LSE = -inf (the logsumexp of an empty set) and zero gradients.
+    do may be None (forward only).  Returns a dict o, lse (and dq, dk, dv), float64,
+    in the (B, T, NH, d) / (B, NH, T) layouts.
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    do = None if do is None else to_f64(do)
+    B, T, NH, dqk = q.shape
+    dv_w = v.shape[3]
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    out = {"o": np.zeros((B, T, NH, dv_w)), "lse": np.full((B, NH, T), -np.inf)}
+    if do is not None:
+        out.update(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v))
+    for b in range(B):
+        lq, lk = int(seq_q[b]), int(seq_k[b])
+        if lq == 0 or lk == 0:
+            continue
+        for h in range(NH):
+            qh, kh, vh = q[b, :lq, h], k[b, :lk, h], v[b, :lk, h]
+            if do is None:
+                out["o"][b, :lq, h], out["lse"][b, h, :lq] = head_forward(qh, kh, vh, scale, causal)
+                continue
+            dq, dk, dv, o, lse, _ = head_backward(qh, kh, vh, do[b, :lq, h], scale, causal)
+            out["o"][b, :lq, h], out["lse"][b, h, :lq] = o, lse
+            out["dq"][b, :lq, h], out["dk"][b, :lk, h], out["dv"][b, :lk, h] = dq, dk, dv
+    return out
 
 
 def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None):

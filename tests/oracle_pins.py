@@ -7,7 +7,8 @@ against copies of the oracle with a planted mistake (test_oracle.py checks that
 each planted mistake trips at least one pin).
 
 Pages cited:
-  [SA8] "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析", sections 2.1, 2.2, A.1-A.3.
+  [SA8] "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析", sections 1.2 (padding mask,
+        seq_len_q, seq_len_kv), 2.1, 2.2, A.1-A.3.
 """
 from __future__ import annotations
 
@@ -251,6 +252,119 @@ def pin_torch_autograd(ref, causal: bool, B=2, T=37, NH=3, dqk=16, dv=24):
         _close(a, b.numpy(), rtol=1e-12, what=f"torch autograd {name} causal={causal}")
 
 
+# ---------------------------------------------------------------------------------
+# 6. Padded batches: the padding mask with seq_len_q / seq_len_kv   [SA8 1.2]
+# ---------------------------------------------------------------------------------
+def _check_varlen_padding(r, seq_q, seq_k, what):
+    """Padding query rows: O = 0, LSE = -inf, dQ = 0; padding key rows: dK = dV = 0;
+    a batch with no keys: O = 0, LSE = -inf everywhere."""
+    B, T = r["o"].shape[:2]
+    for b in range(B):
+        lq, lk = int(seq_q[b]), int(seq_k[b])
+        empty = lq if lk > 0 else 0
+        assert np.all(r["o"][b, empty:] == 0), f"{what}: O padding b={b}"
+        assert np.all(np.isneginf(r["lse"][b, :, empty:])), f"{what}: LSE padding b={b}"
+        assert np.all(np.isfinite(r["lse"][b, :, :empty])), f"{what}: LSE rows b={b}"
+        if "dq" in r:
+            assert np.all(r["dq"][b, empty:] == 0), f"{what}: dQ padding b={b}"
+            kept = lk if lq > 0 else 0
+            assert np.all(r["dk"][b, kept:] == 0) and np.all(r["dv"][b, kept:] == 0), f"{what}: dK/dV padding b={b}"
+
+
+def pin_varlen_full_length(ref, causal: bool):
+    """Every length equal to T: the padded-batch result is the dense one."""
+    q, k, v, do = _inputs(2, 21, 2, 16, 24, 31)
+    g = ref.attn_ref_bwd(q, k, v, do, causal, 0.4)
+    r = ref.attn_ref_varlen(q, k, v, do, [21, 21], [21, 21], causal, 0.4)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        _close(r[name], g[name], rtol=1e-12, what=f"varlen full length {name} causal={causal}")
+
+
+VARLEN_Q = [9, 4, 6, 0, 9]
+VARLEN_K = [5, 9, 0, 3, 9]
+
+
+def pin_varlen_loops(ref, causal: bool):
+    """Forward of padded batches (query and key lengths differ, one batch without keys,
+    one without queries) by scalar loops over (i, j): for i < Lq_b the allowed keys are
+    j < Lk_b (and j <= i under the causal mask); O_i = sum_j e^(s_ij - m_i) v_j /
+    sum_j e^(s_ij - m_i), LSE_i = m_i + ln sum_j e^(s_ij - m_i)."""
+    q, k, v, _ = _inputs(5, 9, 2, 4, 3, 41)
+    scale = 0.7
+    r = ref.attn_ref_varlen(q, k, v, None, VARLEN_Q, VARLEN_K, causal, scale)
+    _check_varlen_padding(r, VARLEN_Q, VARLEN_K, f"varlen loops causal={causal}")
+    for b in range(5):
+        for h in range(2):
+            for i in range(VARLEN_Q[b]):
+                js = [j for j in range(VARLEN_K[b]) if not (causal and j > i)]
+                if not js:
+                    continue
+                s_ = [scale * sum(q[b, i, h, c] * k[b, j, h, c] for c in range(4)) for j in js]
+                m = max(s_)
+                e = [math.exp(x - m) for x in s_]
+                tot = math.fsum(e)
+                o = [math.fsum(e[n] * v[b, j, h, c] for n, j in enumerate(js)) / tot for c in range(3)]
+                _close(r["o"][b, i, h], o, rtol=1e-13, what=f"varlen loops O b={b} i={i}")
+                _close([r["lse"][b, h, i]], [m + math.log(tot)], rtol=1e-14, what=f"varlen loops LSE b={b} i={i}")
+
+
+def pin_varlen_padding_ignored(ref, causal: bool):
+    """Rows past the lengths are never read: NaN there changes nothing."""
+    q, k, v, do = _inputs(5, 9, 2, 4, 3, 43)
+    a = ref.attn_ref_varlen(q, k, v, do, VARLEN_Q, VARLEN_K, causal)
+    q2, k2, v2, do2 = (x.copy() for x in (q, k, v, do))
+    for b in range(5):
+        q2[b, VARLEN_Q[b]:] = np.nan
+        do2[b, VARLEN_Q[b]:] = np.nan
+        k2[b, VARLEN_K[b]:] = np.nan
+        v2[b, VARLEN_K[b]:] = np.nan
+    c = ref.attn_ref_varlen(q2, k2, v2, do2, VARLEN_Q, VARLEN_K, causal)
+    _check_varlen_padding(c, VARLEN_Q, VARLEN_K, f"varlen NaN padding causal={causal}")
+    for name in ("o", "dq", "dk", "dv"):
+        np.testing.assert_array_equal(a[name], c[name], err_msg=f"varlen NaN padding {name}")
+    np.testing.assert_array_equal(a["lse"], c["lse"])
+
+
+def pin_varlen_finite_differences(ref, causal: bool, h: float = 1e-6):
+    """dQ, dK, dV of padded batches with different query and key lengths equal central
+    differences of sum(O * dO) over every input element (padding included, where the
+    derivative is zero)."""
+    q, k, v, do = _inputs(2, 6, 1, 3, 2, 47)
+    sq, sk = [6, 3], [4, 6]
+    g = ref.attn_ref_varlen(q, k, v, do, sq, sk, causal, 0.6)
+
+    def f(qq, kk, vv):
+        return float(np.sum(ref.attn_ref_varlen(qq, kk, vv, None, sq, sk, causal, 0.6)["o"] * do))
+
+    for pos, name in enumerate(("dq", "dk", "dv")):
+        x = (q, k, v)[pos]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args_p, args_m = [q, k, v], [q, k, v]
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args_p[pos], args_m[pos] = xp, xm
+            fd[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        _close(g[name], fd, rtol=1e-6, atol=1e-9, what=f"varlen finite differences {name} causal={causal}")
+
+
+def pin_varlen_zero_queries(ref, causal: bool):
+    """Q = 0: O_i is the mean of V over the allowed keys and LSE_i = ln(count), with
+    count = min(i + 1, Lk) under the causal mask and Lk otherwise."""
+    _, k, v, _ = _inputs(5, 9, 2, 4, 3, 53)
+    q = np.zeros((5, 9, 2, 4))
+    r = ref.attn_ref_varlen(q, k, v, None, VARLEN_Q, VARLEN_K, causal)
+    for b in range(5):
+        lk = VARLEN_K[b]
+        if lk == 0:
+            continue
+        for i in range(VARLEN_Q[b]):
+            n = min(i + 1, lk) if causal else lk
+            _close(r["o"][b, i], v[b, :n].mean(axis=0), rtol=1e-14, what=f"varlen zero queries O b={b} i={i}")
+            _close(r["lse"][b, :, i], np.full(2, math.log(n)), rtol=1e-14, atol=1e-15,
+                   what=f"varlen zero queries LSE b={b} i={i}")
+
+
 ALL_PINS = [
     ("finite_differences_causal", lambda r: pin_finite_differences(r, True)),
     ("finite_differences_full", lambda r: pin_finite_differences(r, False)),
@@ -270,4 +384,14 @@ ALL_PINS = [
     ("worked_example_causal", lambda r: pin_worked_example(r, "causal")),
     ("torch_autograd_causal", lambda r: pin_torch_autograd(r, True)),
     ("torch_autograd_full", lambda r: pin_torch_autograd(r, False)),
+    ("varlen_full_length_causal", lambda r: pin_varlen_full_length(r, True)),
+    ("varlen_full_length_full", lambda r: pin_varlen_full_length(r, False)),
+    ("varlen_loops_causal", lambda r: pin_varlen_loops(r, True)),
+    ("varlen_loops_full", lambda r: pin_varlen_loops(r, False)),
+    ("varlen_padding_ignored_causal", lambda r: pin_varlen_padding_ignored(r, True)),
+    ("varlen_padding_ignored_full", lambda r: pin_varlen_padding_ignored(r, False)),
+    ("varlen_zero_queries_causal", lambda r: pin_varlen_zero_queries(r, True)),
+    ("varlen_zero_queries_full", lambda r: pin_varlen_zero_queries(r, False)),
+    ("finite_differences_varlen_causal", lambda r: pin_varlen_finite_differences(r, True)),
+    ("finite_differences_varlen_full", lambda r: pin_varlen_finite_differences(r, False)),
 ]

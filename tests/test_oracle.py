@@ -61,6 +61,9 @@ MUTANTS = {
     "lse_no_max": ("return e / l, (m + np.log(l))[:, 0]", "return e / l, (np.log(l))[:, 0]"),
     "D_from_dP_only": ("Dr = (dP * P).sum(axis=1)", "Dr = dP.sum(axis=1)"),
     "scores_no_scale": ("S = scale * (q @ k.T)", "S = (q @ k.T)"),
+    "varlen_keys_cut_at_query_length": ("qh, kh, vh = q[b, :lq, h], k[b, :lk, h], v[b, :lk, h]",
+                                        "qh, kh, vh = q[b, :lq, h], k[b, :lq, h], v[b, :lq, h]"),
+    "varlen_padding_lse_zero": ('"lse": np.full((B, NH, T), -np.inf)}', '"lse": np.zeros((B, NH, T))}'),
 }
 
 
