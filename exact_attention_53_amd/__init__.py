@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "AttnError", "lib_path", "load", "fwd", "fwd_packed", "bwd", "bwd_packed",
-    "workspace_bytes", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
+    "workspace_bytes", "fwd_varlen", "bwd_varlen", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +68,14 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd.argtypes = bwd_args
     lib.attn_bwd_staged.restype = i
     lib.attn_bwd_staged.argtypes = bwd_args + [ctypes.c_uint]
+    lib.attn_fwd_varlen_workspace_bytes.restype = sz
+    lib.attn_fwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_fwd_varlen.restype = i
+    lib.attn_fwd_varlen.argtypes = [vp, S, vp, S, vp, S, vp, S, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_bwd_varlen_workspace_bytes.restype = sz
+    lib.attn_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_bwd_varlen.restype = i
+    lib.attn_bwd_varlen.argtypes = bwd_args[:17] + [vp, vp] + bwd_args[17:]
     _lib = lib
     return lib
 
@@ -193,3 +201,84 @@ def bwd_packed(qkv, o, lse, do, causal: bool = True, scale: Optional[float] = No
     bwd(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], o, lse, do, causal, scale, deterministic,
         dq=dqkv[:, :, 0], dk=dqkv[:, :, 1], dv=dqkv[:, :, 2], workspace=workspace)
     return dqkv
+
+
+def _lengths(x: torch.Tensor, name: str, B: int, dev: torch.device) -> torch.Tensor:
+    if x.dtype != torch.int32 or x.dim() != 1 or x.numel() != B or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor of B = {B} lengths")
+    if x.device != dev:
+        raise ValueError(f"{name} is on {x.device}, expected {dev}")
+    return x
+
+
+def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causal: bool = True,
+               scale: Optional[float] = None, return_lse: bool = True, layout: str = "bthd",
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Forward on padded batches: batch b uses the first seq_len_q[b] query rows and the
+    first seq_len_kv[b] key/value rows (int32 device tensors of B lengths); padding rows
+    of o are written as 0 and of lse as -inf.  Returns (o, lse)."""
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("fwd_varlen runs on the GPU only; got a CPU tensor")
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, n, dev)
+    B, NH, T, dqk = _dims(q, layout)
+    dv = v.shape[3]
+    _lengths(seq_len_q, "seq_len_q", B, dev)
+    _lengths(seq_len_kv, "seq_len_kv", B, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        shape = (B, T, NH, dv) if layout == "bthd" else (B, NH, T, dv)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", dev)
+    lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev) if return_lse else None
+    need = int(lib.attn_fwd_varlen_workspace_bytes(B, NH, T, dqk, dv))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_fwd_varlen(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                                   v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
+                                   lse.data_ptr() if return_lse else None, seq_len_q.data_ptr(),
+                                   seq_len_kv.data_ptr(), B, NH, T, dqk, dv, float(scale), int(bool(causal)),
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(dev)))
+    return out, lse
+
+
+def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causal: bool = True,
+               scale: Optional[float] = None, deterministic: bool = False, layout: str = "bthd",
+               workspace: Optional[torch.Tensor] = None):
+    """Backward on padded batches (see fwd_varlen).  Returns (dq, dk, dv); padding rows
+    are written as 0."""
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("bwd_varlen runs on the GPU only; got a CPU tensor")
+    for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _need(x, n, dev)
+    B, NH, T, dqk = _dims(q, layout)
+    dvd = v.shape[3]
+    _lengths(seq_len_q, "seq_len_q", B, dev)
+    _lengths(seq_len_kv, "seq_len_kv", B, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    need = int(lib.attn_bwd_varlen_workspace_bytes(B, NH, T, dqk, dvd, int(bool(deterministic))))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_bwd_varlen(
+            q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+            v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
+            lse.data_ptr(), do.data_ptr(), _strides(do, layout),
+            dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
+            dv.data_ptr(), _strides(dv, layout), seq_len_q.data_ptr(), seq_len_kv.data_ptr(),
+            B, NH, T, dqk, dvd, float(scale), int(bool(causal)), int(bool(deterministic)),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk, dv

@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libattn53.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 _CONFIGS = [(dqk, dv, mask) for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in ("causal", "full")]
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip"] + [
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_plan.hip"] + [
     f"attn_bwd_{kind}_{dqk}_{dv}_{mask}.hip" for kind in ("kv", "dq") for dqk, dv, mask in _CONFIGS
 ] + ["attn_api.cpp"]
 

@@ -59,31 +59,18 @@ size_t ws_acc_bytes(int B, int NH, int T, int dqk) { return align256((size_t)B *
 
 attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
-}  // namespace
+// Work list of a padded-batch launch: one (b, block) pair of int32 per item.
+size_t ws_list_bytes(int B, int T, int block) { return align256((size_t)B * ((T + block - 1) / block) * 8); }
 
-extern "C" {
+constexpr int kFwdBlock = 128;  // query rows per forward workgroup
+constexpr int kKvBlock = 128;   // keys per key/value workgroup
 
-const char* attn_status_string(attn_status s) {
-  switch (s) {
-    case ATTN_OK: return "ok";
-    case ATTN_ERR_NULL: return "a required pointer is NULL";
-    case ATTN_ERR_SHAPE: return "B, NH and T must be >= 1 and B*NH*T must fit in int32";
-    case ATTN_ERR_HEADDIM: return "unsupported head dims: (d_qk, d_v) must be (64,64), (128,128) or (192,128)";
-    case ATTN_ERR_STRIDE: return "strides must be non-negative multiples of 8 elements, the t stride at most 2^24";
-    case ATTN_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
-    case ATTN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than attn_bwd_workspace_bytes()";
-    case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
-    case ATTN_ERR_ARG: return "invalid argument: scale must be finite and > 0, flags 0 or 1, stage mask non-empty";
-    case ATTN_ERR_ALIAS: return "an output tensor overlaps an input tensor";
-  }
-  return "unknown attn_status";
-}
+bool int_ptr_ok(const int32_t* p) { return p != nullptr && reinterpret_cast<uintptr_t>(p) % 4 == 0; }
 
-int attn_version(void) { return 100; }
-
-attn_status attn_fwd(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
-                     attn_strides sv, void* o, attn_strides so, float* lse, int B, int NH, int T, int d_qk,
-                     int d_v, float scale, int causal, void* stream) {
+attn_status fwd_impl(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v, attn_strides sv,
+                     void* o, attn_strides so, float* lse, const int32_t* seq_q, const int32_t* seq_k, int B, int NH,
+                     int T, int d_qk, int d_v, float scale, int causal, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
@@ -94,9 +81,22 @@ attn_status attn_fwd(const void* q, attn_strides sq, const void* k, attn_strides
   if ((st = check_tensor(o, so, B, NH, T, d_v, &eo)) != ATTN_OK) return st;
   if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_ALIGN;
   if (overlaps(eo, eq) || overlaps(eo, ek) || overlaps(eo, ev)) return ATTN_ERR_ALIAS;
+  Extent el{0, 0};
   if (lse != nullptr) {
-    Extent el{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + (uintptr_t)B * NH * T * 4u};
+    el = Extent{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + (uintptr_t)B * NH * T * 4u};
     if (overlaps(el, eq) || overlaps(el, ek) || overlaps(el, ev) || overlaps(el, eo)) return ATTN_ERR_ALIAS;
+  }
+  const bool varlen = seq_q != nullptr || seq_k != nullptr;
+  if (varlen) {
+    if (seq_q == nullptr || seq_k == nullptr) return ATTN_ERR_NULL;
+    if (!int_ptr_ok(seq_q) || !int_ptr_ok(seq_k)) return ATTN_ERR_ALIGN;
+    const size_t need = ws_list_bytes(B, T, kFwdBlock);
+    if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || workspace_bytes < need)
+      return ATTN_ERR_WORKSPACE;
+    const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlaps(ew, eq) || overlaps(ew, ek) || overlaps(ew, ev) || overlaps(ew, eo) ||
+        (lse != nullptr && overlaps(ew, el)))
+      return ATTN_ERR_ALIAS;
   }
   FwdParams p{};
   p.q = q; p.sq = cvt(sq);
@@ -106,28 +106,42 @@ attn_status attn_fwd(const void* q, attn_strides sq, const void* k, attn_strides
   p.lse = lse;
   p.B = B; p.NH = NH; p.T = T;
   p.scale_log2 = scale * kLog2e;
-  return hip_status(attn53::launch_fwd(p, d_qk, d_v, causal != 0, (hipStream_t)stream));
+  const hipStream_t s = (hipStream_t)stream;
+  if (varlen) {
+    attn53::PlanParams pp{seq_q, seq_k, static_cast<int*>(workspace), B, T, kFwdBlock, attn53::PLAN_Q, causal};
+    if ((st = hip_status(attn53::launch_plan(pp, s))) != ATTN_OK) return st;
+    p.seq_q = seq_q;
+    p.seq_k = seq_k;
+    p.items = static_cast<const int*>(workspace);
+  }
+  return hip_status(attn53::launch_fwd(p, d_qk, d_v, causal != 0, s));
 }
 
-size_t attn_bwd_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic) {
+size_t bwd_ws_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic, bool varlen) {
   if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK) return 0;
   size_t n = 2 * ws_D_bytes(B, NH, T);  // D and LSE log2(e)
   if (!deterministic) n += ws_acc_bytes(B, NH, T, d_qk);
+  if (varlen) n += ws_list_bytes(B, T, kKvBlock) + ws_list_bytes(B, T, attn53::dq_block_rows(d_qk));
   return n;
 }
 
-attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
-                            attn_strides sv, const void* o, attn_strides so, const float* lse, const void* do_,
-                            attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk, void* dv,
-                            attn_strides sdv, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
-                            int deterministic, void* workspace, size_t workspace_bytes, void* stream,
-                            unsigned stages) {
+attn_status bwd_impl(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v, attn_strides sv,
+                     const void* o, attn_strides so, const float* lse, const void* do_, attn_strides sdo, void* dq,
+                     attn_strides sdq, void* dk, attn_strides sdk, void* dv, attn_strides sdv,
+                     const int32_t* seq_q, const int32_t* seq_k, int B, int NH, int T, int d_qk, int d_v,
+                     float scale, int causal, int deterministic, void* workspace, size_t workspace_bytes,
+                     void* stream, unsigned stages) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1) ||
       (deterministic != 0 && deterministic != 1))
     return ATTN_ERR_ARG;
   if (stages == 0 || (stages & ~ATTN_BWD_ALL) != 0) return ATTN_ERR_ARG;
+  const bool varlen = seq_q != nullptr || seq_k != nullptr;
+  if (varlen) {
+    if (seq_q == nullptr || seq_k == nullptr) return ATTN_ERR_NULL;
+    if (!int_ptr_ok(seq_q) || !int_ptr_ok(seq_k)) return ATTN_ERR_ALIGN;
+  }
   Extent eq, ek, ev, eo, edo, edq, edk, edv;
   if ((st = check_tensor(q, sq, B, NH, T, d_qk, &eq)) != ATTN_OK) return st;
   if ((st = check_tensor(k, sk, B, NH, T, d_qk, &ek)) != ATTN_OK) return st;
@@ -140,7 +154,7 @@ attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_
   if (lse == nullptr) return ATTN_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_ALIGN;
   const Extent el{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + (uintptr_t)B * NH * T * 4u};
-  const size_t need = attn_bwd_workspace_bytes(B, NH, T, d_qk, d_v, deterministic);
+  const size_t need = bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, varlen);
   if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || workspace_bytes < need)
     return ATTN_ERR_WORKSPACE;
   const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
@@ -164,11 +178,31 @@ attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_
   p.B = B; p.NH = NH; p.T = T; p.Tpad = (int)tpad(T);
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
-  p.D = static_cast<float*>(workspace);
-  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_D_bytes(B, NH, T));
-  p.dq_acc = deterministic ? nullptr
-                           : reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * ws_D_bytes(B, NH, T));
+  char* ws = static_cast<char*>(workspace);
+  p.D = reinterpret_cast<float*>(ws);
+  p.lse2 = reinterpret_cast<float*>(ws + ws_D_bytes(B, NH, T));
+  size_t off = 2 * ws_D_bytes(B, NH, T);
+  if (!deterministic) {
+    p.dq_acc = reinterpret_cast<float*>(ws + off);
+    off += ws_acc_bytes(B, NH, T, d_qk);
+  }
   const hipStream_t s = (hipStream_t)stream;
+  if (varlen) {
+    p.seq_q = seq_q;
+    p.seq_k = seq_k;
+    int* list_kv = reinterpret_cast<int*>(ws + off);
+    int* list_dq = reinterpret_cast<int*>(ws + off + ws_list_bytes(B, T, kKvBlock));
+    p.items_kv = list_kv;
+    p.items_dq = list_dq;
+    if (stages & ATTN_BWD_MAIN) {
+      attn53::PlanParams pp{seq_q, seq_k, list_kv, B, T, kKvBlock, attn53::PLAN_KV, causal};
+      if ((st = hip_status(attn53::launch_plan(pp, s))) != ATTN_OK) return st;
+    }
+    if ((stages & ATTN_BWD_DQ) && deterministic) {
+      attn53::PlanParams pp{seq_q, seq_k, list_dq, B, T, attn53::dq_block_rows(d_qk), attn53::PLAN_Q, causal};
+      if ((st = hip_status(attn53::launch_plan(pp, s))) != ATTN_OK) return st;
+    }
+  }
   if (stages & ATTN_BWD_PREPROCESS) {
     st = hip_status(attn53::launch_bwd_preprocess(p, d_qk, d_v, !deterministic, s));
     if (st != ATTN_OK) return st;
@@ -185,13 +219,85 @@ attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_
   return ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, NH and T must be >= 1 and B*NH*T must fit in int32";
+    case ATTN_ERR_HEADDIM: return "unsupported head dims: (d_qk, d_v) must be (64,64), (128,128) or (192,128)";
+    case ATTN_ERR_STRIDE: return "strides must be non-negative multiples of 8 elements, the t stride at most 2^24";
+    case ATTN_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
+    case ATTN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than attn_bwd_workspace_bytes()";
+    case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case ATTN_ERR_ARG: return "invalid argument: scale must be finite and > 0, flags 0 or 1, stage mask non-empty";
+    case ATTN_ERR_ALIAS: return "an output tensor overlaps an input tensor";
+  }
+  return "unknown attn_status";
+}
+
+int attn_version(void) { return 200; }
+
+attn_status attn_fwd(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                     attn_strides sv, void* o, attn_strides so, float* lse, int B, int NH, int T, int d_qk,
+                     int d_v, float scale, int causal, void* stream) {
+  return fwd_impl(q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale, causal, nullptr, 0,
+                  stream);
+}
+
+size_t attn_fwd_varlen_workspace_bytes(int B, int NH, int T, int d_qk, int d_v) {
+  if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK) return 0;
+  return ws_list_bytes(B, T, kFwdBlock);
+}
+
+attn_status attn_fwd_varlen(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                            attn_strides sv, void* o, attn_strides so, float* lse, const int32_t* seq_len_q,
+                            const int32_t* seq_len_kv, int B, int NH, int T, int d_qk, int d_v, float scale,
+                            int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (seq_len_q == nullptr || seq_len_kv == nullptr) return ATTN_ERR_NULL;
+  return fwd_impl(q, sq, k, sk, v, sv, o, so, lse, seq_len_q, seq_len_kv, B, NH, T, d_qk, d_v, scale, causal,
+                  workspace, workspace_bytes, stream);
+}
+
+size_t attn_bwd_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic) {
+  return bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, false);
+}
+
+attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                            attn_strides sv, const void* o, attn_strides so, const float* lse, const void* do_,
+                            attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk, void* dv,
+                            attn_strides sdv, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
+                            int deterministic, void* workspace, size_t workspace_bytes, void* stream,
+                            unsigned stages) {
+  return bwd_impl(q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr, nullptr, B, NH, T,
+                  d_qk, d_v, scale, causal, deterministic, workspace, workspace_bytes, stream, stages);
+}
+
 attn_status attn_bwd(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v, attn_strides sv,
                      const void* o, attn_strides so, const float* lse, const void* do_, attn_strides sdo, void* dq,
                      attn_strides sdq, void* dk, attn_strides sdk, void* dv, attn_strides sdv, int B, int NH, int T,
                      int d_qk, int d_v, float scale, int causal, int deterministic, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  return attn_bwd_staged(q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, B, NH, T, d_qk, d_v,
-                         scale, causal, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
+  return bwd_impl(q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr, nullptr, B, NH, T,
+                  d_qk, d_v, scale, causal, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
+}
+
+size_t attn_bwd_varlen_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic) {
+  return bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, true);
+}
+
+attn_status attn_bwd_varlen(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                            attn_strides sv, const void* o, attn_strides so, const float* lse, const void* do_,
+                            attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk, void* dv,
+                            attn_strides sdv, const int32_t* seq_len_q, const int32_t* seq_len_kv, int B, int NH,
+                            int T, int d_qk, int d_v, float scale, int causal, int deterministic, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (seq_len_q == nullptr || seq_len_kv == nullptr) return ATTN_ERR_NULL;
+  return bwd_impl(q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, seq_len_q, seq_len_kv, B, NH,
+                  T, d_qk, d_v, scale, causal, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
 }
 
 }  // extern "C"

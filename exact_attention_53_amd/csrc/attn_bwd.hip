@@ -38,6 +38,10 @@ hipError_t launch_bwd_dq(const BwdParams& p, int d_qk, int d_v, bool causal, hip
   return hipErrorInvalidValue;
 }
 
+int dq_block_rows(int d_qk) {
+  return d_qk == 64 ? DqShape<64>::BM : d_qk == 128 ? DqShape<128>::BM : DqShape<192>::BM;
+}
+
 hipError_t launch_bwd_finalize(const BwdParams& p, int d_qk, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.NH * p.Tpad;
   if (d_qk == 64)

@@ -57,7 +57,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int d_qk, int
     const int t = (int)(row % p.Tpad);
     const int bh = (int)(row / p.Tpad);
     const int b = bh / p.NH, h = bh % p.NH;
-    if (t < p.T) {
+    const int Lq = p.seq_q != nullptr ? batch_len(p.seq_q, b, p.T) : p.T;
+    if (t < Lq) {
       const bf16* orow = (const bf16*)p.o + b * p.so.b + h * p.so.h + (int64_t)t * p.so.t;
       const bf16* drow = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h + (int64_t)t * p.sdo.t;
       const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(orow + 8 * c));
@@ -76,8 +77,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int d_qk, int
     const int t = (int)(row % p.Tpad);
     const int bh = (int)(row / p.Tpad);
     p.D[row] = sum;
-    // LSE in base-2 units; padding rows get +inf, which makes their P exactly 0
-    p.lse2[row] = t < p.T ? p.lse[(int64_t)bh * p.T + t] * kLog2e : INFINITY;
+    // LSE in base-2 units; padding rows (past T, past the batch's query length, or
+    // without keys: LSE = -inf) get +inf, which makes their P exactly 0
+    const int Lq = p.seq_q != nullptr ? batch_len(p.seq_q, bh / p.NH, p.T) : p.T;
+    const float l = t < Lq ? p.lse[(int64_t)bh * p.T + t] : -INFINITY;
+    p.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
@@ -188,17 +192,30 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in a scalar register
   const int T = p.T;
-  const int nqb = (T + BWD_BM - 1) / BWD_BM;
-  const Item item = schedule(blockIdx.x, p.B * p.NH);
-  const int kb = item.rank;  // causal: block 0 has the most query blocks -> first
-  const int b = item.bh / p.NH, h = item.bh % p.NH;
+  // Lq / Lk: valid query / key rows of this batch (T, or the padded-batch lengths)
+  int kb, b, h, Lq = T, Lk = T;
+  if (p.items_kv == nullptr) {
+    const Item item = schedule(blockIdx.x, p.B * p.NH);
+    kb = item.rank;  // causal: block 0 has the most query blocks -> first
+    b = item.bh / p.NH;
+    h = item.bh % p.NH;
+  } else {
+    const ListItem it = list_item(blockIdx.x, p.NH, p.items_kv);
+    b = it.b;
+    h = it.h;
+    kb = it.blk;
+    Lq = batch_len(p.seq_q, b, T);
+    Lk = batch_len(p.seq_k, b, T);
+  }
+  const int bh = b * p.NH + h;
+  const int nqb = (Lq + BWD_BM - 1) / BWD_BM;
 
   const bf16* qg = (const bf16*)p.q + b * p.sq.b + h * p.sq.h;
   const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
   const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
   const bf16* dog = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h;
-  const float* lseg = p.lse2 + (int64_t)item.bh * p.Tpad;
-  const float* Dg = p.D + (int64_t)item.bh * p.Tpad;
+  const float* lseg = p.lse2 + (int64_t)bh * p.Tpad;
+  const float* Dg = p.D + (int64_t)bh * p.Tpad;
   const int64_t sqt = p.sq.t, sdot = p.sdo.t;
 
   const LdsLane L = lds_lane(lane);
@@ -206,19 +223,35 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int kw = 32 * w;
   const int my_key = key0 + kw + lq;
   const float c = p.scale_log2;
+  bf16* dkg = (bf16*)p.dk + b * p.sdk.b + h * p.sdk.h;
+  bf16* dvg = (bf16*)p.dv + b * p.sdv.b + h * p.sdv.h;
+
+  const int i0 = CAUSAL ? key0 / BWD_BM : 0;
+  const int n_q = nqb - i0;
+  if (key0 >= Lk || n_q <= 0) {  // padding keys only, or no query sees them: dK = dV = 0
+    if (my_key < T) {
+#pragma unroll
+      for (int x = 0; x < DQK / 16; ++x)
+        *reinterpret_cast<u32x4*>(dkg + (int64_t)my_key * p.sdk.t + g * (DQK / 2) + 8 * x) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int x = 0; x < DV / 16; ++x)
+        *reinterpret_cast<u32x4*>(dvg + (int64_t)my_key * p.sdv.t + g * (DV / 2) + 8 * x) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
 
   // K and V rows of this wavefront as B-operand fragments of S = Q K^T and dP = dO V^T.
   bf16x8 kf[KSQ], vf[KSV];
 #pragma unroll
   for (int ks = 0; ks < KSQ; ++ks) {
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (my_key < T) raw = *reinterpret_cast<const u32x4*>(kg + (int64_t)my_key * p.sk.t + 16 * ks + 8 * g);
+    if (my_key < Lk) raw = *reinterpret_cast<const u32x4*>(kg + (int64_t)my_key * p.sk.t + 16 * ks + 8 * g);
     kf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
 #pragma unroll
   for (int ks = 0; ks < KSV; ++ks) {
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (my_key < T) raw = *reinterpret_cast<const u32x4*>(vg + (int64_t)my_key * p.sv.t + 16 * ks + 8 * g);
+    if (my_key < Lk) raw = *reinterpret_cast<const u32x4*>(vg + (int64_t)my_key * p.sv.t + 16 * ks + 8 * g);
     vf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
 
@@ -229,8 +262,8 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   auto load_step = [&](int qb, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     const int r0 = qb * BWD_BM;
-    qload.issue(qg + r0 * sqt, sqt, T - r0, (ATTN_LDS char*)(BUF ? qbuf1 : qbuf0), w);
-    oload.issue(dog + r0 * sdot, sdot, T - r0, (ATTN_LDS char*)(BUF ? obuf1 : obuf0), w);
+    qload.issue(qg + r0 * sqt, sqt, Lq - r0, (ATTN_LDS char*)(BUF ? qbuf1 : qbuf0), w);
+    oload.issue(dog + r0 * sdot, sdot, Lq - r0, (ATTN_LDS char*)(BUF ? obuf1 : obuf0), w);
     if (w == 0) {  // 64 rows of LSE log2(e) and of D (both padded to Tpad rows)
       load_f32x64_lds(lseg + r0, BWD_BM, (ATTN_LDS float*)(BUF ? lse1 : lse0), lane);
     } else if (w == 1) {
@@ -240,12 +273,10 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
   if constexpr (ATOMIC_DQ) {
     TileStage<BWD_BN, DQK, BWD_NT> kst;
-    kst.load(kg, p.sk.t, key0, T, tid);
+    kst.load(kg, p.sk.t, key0, Lk, tid);
     kst.store((ATTN_LDS char*)kd_lds, tid);
   }
 
-  const int i0 = CAUSAL ? key0 / BWD_BM : 0;
-  const int n_q = nqb - i0;
 
   f32x16 dk[NDK], dv[NDV];
 #pragma unroll
@@ -254,7 +285,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   for (int t = 0; t < NDV; ++t) dv[t] = zero16();
   const int tq = w & 1;               // dQ: query tile of this wavefront
   const int dq_t0 = (w >> 1) * NDQ;   //     first d tile
-  float* dqacc = ATOMIC_DQ ? p.dq_acc + (int64_t)item.bh * p.Tpad * DQK : nullptr;
+  float* dqacc = ATOMIC_DQ ? p.dq_acc + (int64_t)bh * p.Tpad * DQK : nullptr;
 
   // partial dQ of the query block at q0 from the dS^T tile in `st`, added atomically
   auto dq_partial = [&](const ATTN_LDS char* st, int q0) {
@@ -330,7 +361,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             const int r = 4 * a + e;
             const int q = q0 + qi + e;
             const float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -Lv[e]));
-            s[t][r] = (my_key >= T || q >= T || (CAUSAL && my_key > q)) ? 0.f : pv;
+            s[t][r] = (my_key >= Lk || q >= Lq || (CAUSAL && my_key > q)) ? 0.f : pv;
           }
         }
 #pragma unroll
@@ -457,9 +488,9 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   constexpr auto NOMASK = std::false_type{};
   constexpr auto B0 = std::integral_constant<int, 0>{};
   constexpr auto B1 = std::integral_constant<int, 1>{};
-  const bool ragged_keys = key0 + BWD_BN > T;
+  const bool ragged_keys = key0 + BWD_BN > Lk;
   const int n_head = ragged_keys ? n_q : (CAUSAL ? min(BWD_BN / BWD_BM, n_q) : 0);  // even, or n_q
-  const int n_tail = (n_head < n_q && T % BWD_BM != 0) ? 1 : 0;
+  const int n_tail = (n_head < n_q && Lq % BWD_BM != 0) ? 1 : 0;
   const int mid_end = n_q - n_tail;
   for (int it = 0; it < n_head; it += 2) {
     step(it, B0, MASK);
@@ -485,8 +516,6 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
   // dK = scale dS^T Q, dV; element r of tile t: key key0 + kw + 8 (r / 4) + 4 g + r % 4,
   // column 32 t + lq.
-  bf16* dkg = (bf16*)p.dk + b * p.sdk.b + h * p.sdk.h;
-  bf16* dvg = (bf16*)p.dv + b * p.sdv.b + h * p.sdv.h;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = key0 + kw + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -597,9 +626,22 @@ void bwd_dq_kernel(BwdParams p) {
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the same, in a scalar register
   const int T = p.T;
   const int nqb = (T + BM - 1) / BM;
-  const Item item = schedule(blockIdx.x, p.B * p.NH);
-  const int qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
-  const int b = item.bh / p.NH, h = item.bh % p.NH;
+  // Lq / Lk: valid query / key rows of this batch (T, or the padded-batch lengths)
+  int qb, b, h, Lq = T, Lk = T;
+  if (p.items_dq == nullptr) {
+    const Item item = schedule(blockIdx.x, p.B * p.NH);
+    qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
+    b = item.bh / p.NH;
+    h = item.bh % p.NH;
+  } else {
+    const ListItem it = list_item(blockIdx.x, p.NH, p.items_dq);
+    b = it.b;
+    h = it.h;
+    qb = it.blk;
+    Lq = batch_len(p.seq_q, b, T);
+    Lk = batch_len(p.seq_k, b, T);
+  }
+  const int bh = b * p.NH + h;
 
   const bf16* qg = (const bf16*)p.q + b * p.sq.b + h * p.sq.h;
   const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
@@ -611,6 +653,20 @@ void bwd_dq_kernel(BwdParams p) {
   const LdsLane L = lds_lane(lane);
   const int q0 = qb * BM, qw = q0 + 32 * QT * w;  // first row of this wavefront
   const float c = p.scale_log2;
+  const int kv_end = CAUSAL ? min(Lk, q0 + BM) : Lk;
+  const int n_kv = (kv_end + DQ_BN - 1) / DQ_BN;
+  if (q0 >= Lq || n_kv == 0) {  // padding rows only, or no keys: dQ = 0
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      const int q = qw + 32 * u + lq;
+      if (q < T) {
+#pragma unroll
+        for (int x = 0; x < DQK / 16; ++x)
+          *reinterpret_cast<u32x4*>(dqg + (int64_t)q * p.sdq.t + g * (DQK / 2) + 8 * x) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    return;
+  }
 
   // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T
   bf16x8 qf[QT][KSQ], df[QT][KSV];
@@ -621,17 +677,17 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (q < T) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)q * p.sq.t + 16 * ks + 8 * g);
+      if (q < Lq) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)q * p.sq.t + 16 * ks + 8 * g);
       qf[u][ks] = __builtin_bit_cast(bf16x8, raw);
     }
 #pragma unroll
     for (int ks = 0; ks < KSV; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (q < T) raw = *reinterpret_cast<const u32x4*>(dog + (int64_t)q * p.sdo.t + 16 * ks + 8 * g);
+      if (q < Lq) raw = *reinterpret_cast<const u32x4*>(dog + (int64_t)q * p.sdo.t + 16 * ks + 8 * g);
       df[u][ks] = __builtin_bit_cast(bf16x8, raw);
     }
-    lse2[u] = p.lse2[(int64_t)item.bh * p.Tpad + min(q, p.Tpad - 1)];  // +inf on padding rows
-    Dq[u] = q < T ? p.D[(int64_t)item.bh * p.Tpad + q] : 0.f;
+    lse2[u] = p.lse2[(int64_t)bh * p.Tpad + min(q, p.Tpad - 1)];  // +inf on padding rows
+    Dq[u] = q < Lq ? p.D[(int64_t)bh * p.Tpad + q] : 0.f;
   }
 
   DirectTile<DQ_BN, DQK, BWD_NT / 64> kload;
@@ -640,12 +696,9 @@ void bwd_dq_kernel(BwdParams p) {
   vload.init(svt, w, lane);
   auto load_kv = [&](int key0, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    kload.issue(kg + key0 * skt, skt, T - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), wu);
-    vload.issue(vg + key0 * svt, svt, T - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), wu);
+    kload.issue(kg + key0 * skt, skt, Lk - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), wu);
+    vload.issue(vg + key0 * svt, svt, Lk - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), wu);
   };
-
-  const int kv_end = CAUSAL ? min(T, q0 + BM) : T;
-  const int n_kv = (kv_end + DQ_BN - 1) / DQ_BN;
 
   f32x16 dq[QT][NDQ];
 #pragma unroll
@@ -685,7 +738,7 @@ void bwd_dq_kernel(BwdParams p) {
           float pv = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
           if constexpr (MASKED) {
             const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            pv = (key >= T || (CAUSAL && key > qw + 32 * u + lq)) ? 0.f : pv;
+            pv = (key >= Lk || (CAUSAL && key > qw + 32 * u + lq)) ? 0.f : pv;
           }
           s[t][u][r] = pv;
         }
@@ -816,7 +869,7 @@ void bwd_dq_kernel(BwdParams p) {
     const int key0 = j * DQ_BN;
     if constexpr (decltype(maskc)::value) {
       if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
-      if ((CAUSAL && key0 + DQ_BN - 1 > qw) || key0 + DQ_BN > T)
+      if ((CAUSAL && key0 + DQ_BN - 1 > qw) || key0 + DQ_BN > Lk)
         tile_body(key0, bufc, std::true_type{});
       else
         tile_body(key0, bufc, std::false_type{});
@@ -827,7 +880,10 @@ void bwd_dq_kernel(BwdParams p) {
   // The first tiles (the workgroup's diagonal ones under the causal mask, or the ragged
   // last key block) may carry a mask for some wavefront; they run as plain code, the
   // rest as the pipeline.
-  const int n_head = CAUSAL ? min(n_kv, n_kv - q0 / DQ_BN) : (T % DQ_BN != 0 ? 1 : 0);
+  // Tiles j >= first_masked (visited first) hold keys past Lk or past some row's diagonal.
+  const int first_ragged = Lk % DQ_BN != 0 ? Lk / DQ_BN : n_kv;
+  const int first_masked = min(min(first_ragged, CAUSAL ? q0 / DQ_BN : n_kv), n_kv);
+  const int n_head = n_kv - first_masked;
   constexpr auto B0 = std::integral_constant<int, 0>{};
   constexpr auto B1 = std::integral_constant<int, 1>{};
   int it = 0;

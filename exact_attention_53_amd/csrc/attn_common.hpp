@@ -293,4 +293,26 @@ __device__ __forceinline__ Item schedule(int bid, int nbh) {
   return it;
 }
 
+// Work item of a padded-batch launch: `list` holds (b, block) pairs sorted longest
+// first (attn_plan.hip); the workgroup ids run over list entries and heads, with the
+// heads grouped per XCD as in schedule() when NH is a multiple of 8.
+struct ListItem {
+  int b, h, blk;
+};
+__device__ __forceinline__ ListItem list_item(int bid, int NH, const int* list) {
+  int h, r;
+  if ((NH & 7) == 0) {
+    const int xcd = bid & 7, local = bid >> 3, per = NH >> 3;
+    h = xcd * per + local % per;
+    r = local / per;
+  } else {
+    h = bid % NH;
+    r = bid / NH;
+  }
+  return ListItem{list[2 * r], h, list[2 * r + 1]};
+}
+
+// Valid rows of batch b, clamped to [0, T].
+__device__ __forceinline__ int batch_len(const int* seq, int b, int T) { return min(max(seq[b], 0), T); }
+
 }  // namespace attn53

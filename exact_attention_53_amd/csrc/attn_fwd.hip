@@ -58,9 +58,22 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in a scalar register
   const int T = p.T;
   const int nqb = (T + FWD_BM - 1) / FWD_BM;
-  const Item item = schedule(blockIdx.x, p.B * p.NH);
-  const int qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
-  const int b = item.bh / p.NH, h = item.bh % p.NH;
+  // Lq / Lk: valid query / key rows of this batch (T, or the padded-batch lengths)
+  int qb, b, h, Lq = T, Lk = T;
+  if (p.items == nullptr) {
+    const Item item = schedule(blockIdx.x, p.B * p.NH);
+    qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
+    b = item.bh / p.NH;
+    h = item.bh % p.NH;
+  } else {
+    const ListItem it = list_item(blockIdx.x, p.NH, p.items);
+    b = it.b;
+    h = it.h;
+    qb = it.blk;
+    Lq = batch_len(p.seq_q, b, T);
+    Lk = batch_len(p.seq_k, b, T);
+  }
+  const int bh = b * p.NH + h;
 
   const bf16* qg = (const bf16*)p.q + b * p.sq.b + h * p.sq.h;
   const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
@@ -72,13 +85,24 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int q0 = qb * FWD_BM;
   const int qw = q0 + 32 * w;
   const int my_q = qw + lq;
+  const int kv_end = CAUSAL ? min(Lk, q0 + FWD_BM) : Lk;
+  const int n_kv = (kv_end + FWD_BN - 1) / FWD_BN;
+  if (q0 >= Lq || n_kv == 0) {  // padding rows only, or no keys: O = 0, LSE = -inf
+    if (my_q < T) {
+      bf16* orow = og + (int64_t)my_q * p.so.t;
+#pragma unroll
+      for (int y = 0; y < DV / 8; ++y) *reinterpret_cast<u32x2*>(orow + 8 * y + 4 * g) = u32x2{0u, 0u};
+      if (p.lse != nullptr && g == 0) p.lse[(int64_t)bh * T + my_q] = -INFINITY;
+    }
+    return;
+  }
 
   // Q rows of this wavefront, as B-operand fragments of S^T = K Q^T.
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (my_q < T) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)my_q * p.sq.t + 16 * ks + 8 * g);
+    if (my_q < Lq) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)my_q * p.sq.t + 16 * ks + 8 * g);
     qf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
 
@@ -88,12 +112,10 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   vload.init(svt, w, lane);
   auto load_kv = [&](int key0, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    kload.issue(kg + key0 * skt, skt, T - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), w);
-    vload.issue(vg + key0 * svt, svt, T - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), w);
+    kload.issue(kg + key0 * skt, skt, Lk - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), w);
+    vload.issue(vg + key0 * svt, svt, Lk - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), w);
   };
 
-  const int kv_end = CAUSAL ? min(T, q0 + FWD_BM) : T;
-  const int n_kv = (kv_end + FWD_BN - 1) / FWD_BN;
   const float c = p.scale_log2;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -130,8 +152,8 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk0 = key0 + 8 * (r >> 2) + 4 * g + (r & 3), kk1 = kk0 + 32;
-          if (kk0 >= T || (CAUSAL && kk0 > my_q)) s0[r] = -INFINITY;
-          if (kk1 >= T || (CAUSAL && kk1 > my_q)) s1[r] = -INFINITY;
+          if (kk0 >= Lk || (CAUSAL && kk0 > my_q)) s0[r] = -INFINITY;
+          if (kk1 >= Lk || (CAUSAL && kk1 > my_q)) s1[r] = -INFINITY;
         }
       }
     };
@@ -210,7 +232,10 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr auto B1 = std::integral_constant<int, 1>{};
   constexpr auto MASK = std::true_type{};
   constexpr auto NOMASK = std::false_type{};
-  const int n_mask = CAUSAL ? min(n_kv, n_kv - q0 / FWD_BN) : (T % FWD_BN != 0 ? 1 : 0);
+  // Tiles j >= first_masked (visited first) hold keys past Lk or past some row's diagonal.
+  const int first_ragged = Lk % FWD_BN != 0 ? Lk / FWD_BN : n_kv;
+  const int first_masked = min(min(first_ragged, CAUSAL ? q0 / FWD_BN : n_kv), n_kv);
+  const int n_mask = n_kv - first_masked;
   int it = 0;
   for (; it < n_mask; ++it) {
     if (it & 1)
@@ -227,7 +252,7 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 
   // deferred normalisation and stats
   const float l_tot = sum_halves(l_run);
-  if (my_q < T) {
+  if (my_q < Lq) {
     const float inv = 1.f / l_tot;
     bf16* orow = og + (int64_t)my_q * p.so.t;
 #pragma unroll
@@ -240,7 +265,12 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
         *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * g) = v;
       }
     if (p.lse != nullptr && g == 0)
-      p.lse[(int64_t)item.bh * T + my_q] = (m_run + log2_fast(l_tot)) * kLn2;
+      p.lse[(int64_t)bh * T + my_q] = (m_run + log2_fast(l_tot)) * kLn2;
+  } else if (my_q < T) {  // padding row of a padded batch: O = 0, LSE = -inf
+    bf16* orow = og + (int64_t)my_q * p.so.t;
+#pragma unroll
+    for (int y = 0; y < DV / 8; ++y) *reinterpret_cast<u32x2*>(orow + 8 * y + 4 * g) = u32x2{0u, 0u};
+    if (p.lse != nullptr && g == 0) p.lse[(int64_t)bh * T + my_q] = -INFINITY;
   }
 }
 

@@ -18,6 +18,11 @@ struct FwdParams {
   float* lse;              // (B, NH, T) or nullptr
   int B, NH, T;
   float scale_log2;        // scale * log2(e)
+  // Padded batches (all three set, or all nullptr): valid query / key rows per batch
+  // (B int32 each; clamped to [0, T]) and the sorted work list of (b, query block).
+  const int* seq_q;
+  const int* seq_k;
+  const int* items;
 };
 
 struct BwdParams {
@@ -36,6 +41,24 @@ struct BwdParams {
   float* D;                // workspace: (B, NH, Tpad) fp32, rowsum(dO * O)
   float* lse2;             // workspace: (B, NH, Tpad) fp32, LSE * log2(e) (+inf on padding)
   float* dq_acc;           // workspace: (B, NH, Tpad, d_qk) fp32, atomic mode only
+  // Padded batches (all set, or all nullptr): valid query / key rows per batch and the
+  // sorted work lists of the key/value kernel (b, key block) and the dQ kernel
+  // (b, query block).
+  const int* seq_q;
+  const int* seq_k;
+  const int* items_kv;
+  const int* items_dq;
+};
+
+// Work lists of padded batches (see attn_plan.hip).  KIND_Q: query blocks of `block`
+// rows, costed by the key tiles of 64 they visit; KIND_KV: key blocks of `block` keys,
+// costed by the query steps of 64 rows they visit.
+enum PlanKind { PLAN_Q = 0, PLAN_KV = 1 };
+struct PlanParams {
+  const int* seq_q;
+  const int* seq_k;
+  int* items;    // out: 2 int32 per item (b, block), longest first
+  int B, T, block, kind, causal;
 };
 
 constexpr int kRowPad = 128;
@@ -46,5 +69,8 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, int d_qk, int d_v, bool zer
 hipError_t launch_bwd_main(const BwdParams& p, int d_qk, int d_v, bool causal, bool deterministic, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s);
 hipError_t launch_bwd_finalize(const BwdParams& p, int d_qk, hipStream_t s);
+hipError_t launch_plan(const PlanParams& p, hipStream_t s);
+// Query rows per workgroup of the dQ kernel (its work list uses blocks of this size).
+int dq_block_rows(int d_qk);
 
 }  // namespace attn53

@@ -165,6 +165,58 @@ attn_status attn_bwd_staged(const void* q, attn_strides sq,
                             void* workspace, size_t workspace_bytes, void* stream,
                             unsigned stages);
 
+/*
+ * Padded batches — the padding mask with per-batch query and key/value lengths
+ * (seq_len_q, seq_len_kv) among the SDPA options of [SA8 1.2] — with the work of the
+ * batch ordered by execution time, longest first, by a preprocessing kernel
+ * [2CTA 3.2].
+ *
+ * Tensors keep their (B, NH, T, d) shapes and strides; T is the padded length.  Batch b
+ * uses query rows 0 .. seq_len_q[b]-1 of q, o, do_, dq and key/value rows
+ * 0 .. seq_len_kv[b]-1 of k, v, dk, dv; rows past them are padding.  Within a batch
+ * the result is that of attn_fwd / attn_bwd on the unpadded rows, with the causal mask
+ * top-left aligned (key j allowed for query i iff j <= i) also when the two lengths
+ * differ.  Padding rows are never read and are written as: O = 0, LSE = -inf,
+ * dQ = 0 (query padding); dK = dV = 0 (key padding).  A batch with seq_len_kv[b] = 0
+ * has no keys: O = 0, LSE = -inf and zero gradients on all its rows.
+ *
+ *   seq_len_q, seq_len_kv : device pointers to B int32 each, 4-byte aligned (read);
+ *                           values are clamped to [0, T] on the device (the host
+ *                           cannot see them).  NULL: ATTN_ERR_NULL.
+ *   workspace             : device memory of at least the matching *_workspace_bytes,
+ *                           16-byte aligned, owned by the caller, clobbered; it holds
+ *                           the sorted work lists (and, backward, what attn_bwd keeps
+ *                           there).  Smaller or misaligned: ATTN_ERR_WORKSPACE.
+ * Every other argument, layout rule and error is that of attn_fwd / attn_bwd.
+ */
+size_t attn_fwd_varlen_workspace_bytes(int B, int NH, int T, int d_qk, int d_v);
+
+attn_status attn_fwd_varlen(const void* q, attn_strides sq,
+                            const void* k, attn_strides sk,
+                            const void* v, attn_strides sv,
+                            void* o, attn_strides so,
+                            float* lse,
+                            const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                            int B, int NH, int T, int d_qk, int d_v,
+                            float scale, int causal,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+size_t attn_bwd_varlen_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic);
+
+attn_status attn_bwd_varlen(const void* q, attn_strides sq,
+                            const void* k, attn_strides sk,
+                            const void* v, attn_strides sv,
+                            const void* o, attn_strides so,
+                            const float* lse,
+                            const void* do_, attn_strides sdo,
+                            void* dq, attn_strides sdq,
+                            void* dk, attn_strides sdk,
+                            void* dv, attn_strides sdv,
+                            const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                            int B, int NH, int T, int d_qk, int d_v,
+                            float scale, int causal, int deterministic,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
