@@ -143,3 +143,32 @@ def test_varlen_length_mix_sampled():
         refs[(b, h)] = {"dq": pad(r[0]), "dk": pad(r[1]), "dv": pad(r[2]), "o": pad(r[3]),
                         "lse": np.concatenate([r[4], np.full(T - lq, -np.inf)])}
     _compare("varlen mix", got, lambda b, h: refs[(b, h)], sq, sk, heads=heads)
+
+
+@pytest.mark.parametrize("dims", HEADDIMS, ids=lambda d: f"d{d[0]}x{d[1]}")
+def test_varlen_decode_shape(dims):
+    """Inference forward of one decode step per sequence: a single query row (or a few)
+    against each sequence's own key length, non-causal, without the softmax stats
+    (lse = NULL, the inference mode of [SA8 1.2, 1.3]).  O against the oracle; equal bit
+    for bit to the same call with stats."""
+    dqk, dv = dims
+    T, NH = 2500, 3
+    sq = [1, 1, 1, 4, 1, 0]
+    sk = [2500, 1, 777, 2049, 64, 300]
+    B = len(sq)
+    say(f"case varlen decode d{dqk}x{dv} seq_q={sq} seq_kv={sk}")
+    cpu, gpu, lens = _inputs(B, T, NH, dqk, dv, 83, sq, sk)
+    scale = 1.0 / np.sqrt(dqk)
+    o_inf, lse_inf = attn.fwd_varlen(gpu["q"], gpu["k"], gpu["v"], lens[0], lens[1], False, scale, return_lse=False)
+    o_tr, _ = attn.fwd_varlen(gpu["q"], gpu["k"], gpu["v"], lens[0], lens[1], False, scale)
+    torch.cuda.synchronize()
+    assert lse_inf is None
+    assert torch.equal(o_inf, o_tr)
+    ref = attn_ref.attn_ref_varlen(cpu["q"], cpu["k"], cpu["v"], None, sq, sk, False, scale)
+    for b in range(B):
+        g = to_np(o_inf[b])
+        rows = sq[b] if sk[b] > 0 else 0
+        for h in range(NH):
+            if rows:
+                check_bf16(f"decode b={b} h={h} o", g[:rows, h], ref["o"][b, :rows, h])
+        assert np.all(g[rows:] == 0), f"decode b={b}: padding rows not zero"
