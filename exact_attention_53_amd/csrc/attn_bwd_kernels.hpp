@@ -535,7 +535,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 // DQ_QT tiles of 32 rows, held in registers as B operands together with their dO rows,
 // LSE and D.  With two tiles per wavefront (d_qk <= 128; one wavefront per SIMD) every
 // K or V fragment read from LDS feeds two products; with d_qk = 192 a wavefront owns
-// one tile and two workgroups share a CU.  Key/value tiles of 64 rows stream through
+// one tile (two do not fit in 512 registers).  Key/value tiles of 64 rows stream through
 // double-buffered LDS by direct loads, in descending order.  Per tile:
 // S^T = K Q^T and dP^T = V dO^T, P^T = 2^(S^T c - LSE log2 e), dS^T = P^T (dP^T - D),
 // dQ^T += K^T dS^T with the K^T operand read column-wise.  Every dQ row is summed over
@@ -607,7 +607,9 @@ template <int DQK>
 struct DqShape {
   static constexpr int QT = DQK <= 128 ? 2 : 1;  // 32-row query tiles per wavefront
   static constexpr int BM = 128 * QT;            // query rows per workgroup
-  static constexpr int WAVES_PER_EU = QT == 2 ? 1 : 2;
+  // one wavefront per SIMD (up to 512 registers): with d_qk = 192 and one tile, two
+  // wavefronts per SIMD (256 registers each) spill about 370 registers per lane
+  static constexpr int WAVES_PER_EU = 1;
 };
 
 template <int DQK, int DV, bool CAUSAL>
