@@ -4,7 +4,7 @@ A step is one forward and one backward pass (every stage of the hot path) over o
 batch of synthetic input already resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--dq-mode deterministic|atomic] [--no-cpu-baseline]
+                  [--dq-mode deterministic|atomic] [--no-cpu-baseline] [--cold]
 
 FLOP convention: per unmasked (query, key) pair and head, the forward counts
 2 (d_qk + d_v) (S = QK^T, O = PV) and the backward 2 (3 d_qk + 2 d_v) (S recomputed,
@@ -72,6 +72,16 @@ def flops(w):
     return 2.0 * (w.d_qk + w.d_v) * pairs, 2.0 * (3 * w.d_qk + 2 * w.d_v) * pairs
 
 
+def alg_bytes(w):
+    """HBM bytes the method must move (each tensor read or written once): the forward
+    reads Q, K, V and writes O and LSE; the backward reads Q, K, V, O, dO and LSE and writes
+    dQ, dK, dV (D is its own intermediate: written and read once, 8 bytes per row)."""
+    rows = w.B * w.NH * w.T
+    fwd = rows * (2 * (2 * w.d_qk + w.d_v) + 2 * w.d_v + 4)
+    bwd = rows * (2 * (2 * w.d_qk + 3 * w.d_v) + 4 + 8 + 2 * (2 * w.d_qk + w.d_v))
+    return float(fwd), float(bwd)
+
+
 def cpu_baseline(w, seconds_budget: float = 20.0):
     """Times the CPU oracle (numpy float64) on a bounded sample of the same workload:
     complete forward + backward of whole (b, h) heads."""
@@ -127,6 +137,9 @@ def main():
     ap.add_argument("--dq-mode", choices=["deterministic", "atomic"], default="deterministic",
                     help="dQ summed in a fixed order without atomics (default) or by fp32 atomics")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 1 GiB buffer before every step (evicts the 256 MB last-level cache); "
+                         "the step time is then the sum of the kernel intervals, without the eviction")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -164,7 +177,11 @@ def main():
     det = args.dq_mode == "deterministic"
     ws = torch.empty(attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, det), dtype=torch.uint8, device=dev)
 
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
+
     def step(ev=None):
+        if flush is not None:
+            flush.fill_(1.0)
         if ev is not None:
             ev[0].record()
         attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse)
@@ -202,6 +219,8 @@ def main():
         return sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
 
     t_fwd, t_pre, t_main, t_dq = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    if args.cold:  # the eviction between steps is not part of the step
+        ms_step = t_fwd + t_pre + t_main + t_dq
     f_fwd, f_bwd = flops(w)
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     # Algorithmic flops carried by each kernel (recomputation is not counted): the
@@ -245,6 +264,9 @@ def main():
         "bwd_tflops": round(f_bwd / ((t_pre + t_main + t_dq) * 1e-3) / 1e12, 2),
         "kernels_ms": {n: round(v["ms"], 4) for n, v in kernels.items()},
         "kernels_tflops": {n: round(v["tflops"], 1) for n, v in kernels.items() if v["flops"] > 0},
+        "alg_gbs": {"fwd": round(alg_bytes(w)[0] / (t_fwd * 1e-3) / 1e9, 1),
+                    "bwd": round(alg_bytes(w)[1] / ((t_pre + t_main + t_dq) * 1e-3) / 1e9, 1)},
+        "cache": "cold (1 GiB written before each step)" if args.cold else "warm",
         "wall_s_timed": round(t_wall, 3),
         "roofline": {
             "kernel": dom,
