@@ -56,10 +56,10 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def hbm_traffic(kernel: str, w, dq_mode: str):
+def hbm_traffic(kernel: str, w, dq_mode: str, dtype: str = "bf16"):
     """Measured HBM bytes per launch of `kernel`, or None where no measurement of the
     current sources on this workload exists."""
-    if w.name != "headline" or dq_mode != "deterministic" or kernel not in TRAFFIC_KIB:
+    if w.name != "headline" or dq_mode != "deterministic" or dtype != "bf16" or kernel not in TRAFFIC_KIB:
         return None
     if kernel_sources_hash() != TRAFFIC_SOURCES:
         return None
@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--dq-mode", choices=["deterministic", "atomic"], default="deterministic",
                     help="dQ summed in a fixed order without atomics (default) or by fp32 atomics")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
+                    help="16-bit element type of Q, K, V, O and the gradients (the metric is quoted for bf16)")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB buffer before every step (evicts the 256 MB last-level cache); "
                          "the step time is then the sum of the kernel intervals, without the eviction")
@@ -160,7 +162,8 @@ def main():
 
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    cpu = workloads.make_inputs(w)
+    et = torch.bfloat16 if args.dtype == "bf16" else torch.float16
+    cpu = workloads.make_inputs(w, et)
     if w.packed:
         qkv = cpu["qkv"].to(dev)
         q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
@@ -169,11 +172,11 @@ def main():
     do = cpu["do"].to(dev)
     del cpu
     B, T, NH = w.B, w.T, w.NH
-    o = torch.empty((B, T, NH, w.d_v), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((B, T, NH, w.d_v), dtype=et, device=dev)
     lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
-    dq = torch.empty((B, T, NH, w.d_qk), dtype=torch.bfloat16, device=dev)
+    dq = torch.empty((B, T, NH, w.d_qk), dtype=et, device=dev)
     dk = torch.empty_like(dq)
-    dv = torch.empty((B, T, NH, w.d_v), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((B, T, NH, w.d_v), dtype=et, device=dev)
     det = args.dq_mode == "deterministic"
     ws = torch.empty(attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, det), dtype=torch.uint8, device=dev)
 
@@ -250,7 +253,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: B={B} NH={NH} T={T} d_qk={w.d_qk} d_v={w.d_v} "
@@ -275,7 +278,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": hbm_traffic(dom, w, args.dq_mode),
+            "traffic": hbm_traffic(dom, w, args.dq_mode, args.dtype),
             "traffic_unit": "bytes per launch",
         },
     }

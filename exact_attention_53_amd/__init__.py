@@ -7,7 +7,11 @@ allocates outputs and the workspace with torch, and passes torch's current HIP
 stream.  Every step of the computation runs in the library's HIP kernels; there is
 no fallback path, and a missing library raises.
 
-Tensor layout: 4-D bf16 tensors in (B, T, NH, d) order by default (``layout="bthd"``,
+Element type: bf16, or fp16 (the same dtype for every 16-bit tensor of a call; bf16
+calls go through attn_fwd / attn_bwd / *_varlen, fp16 calls through attn_fwd_typed /
+attn_bwd_typed).
+
+Tensor layout: 4-D tensors in (B, T, NH, d) order by default (``layout="bthd"``,
 the layout of the pages' output O), or (B, NH, T, d) (``layout="bhtd"``); any strides
 whose last one is 1 and whose others are multiples of 8 elements.  Packed QKV blocks
 (B, T, 3, NH, HS) are accepted through ``qkv[:, :, 0]`` etc. or ``fwd_packed``.
@@ -76,6 +80,10 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_varlen.restype = i
     lib.attn_bwd_varlen.argtypes = bwd_args[:17] + [vp, vp] + bwd_args[17:]
+    lib.attn_fwd_typed.restype = i
+    lib.attn_fwd_typed.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_bwd_typed.restype = i
+    lib.attn_bwd_typed.argtypes = [i] + bwd_args[:17] + [vp, vp] + bwd_args[17:] + [ctypes.c_uint]
     _lib = lib
     return lib
 
@@ -106,11 +114,20 @@ def _dims(x: torch.Tensor, layout: str) -> Tuple[int, int, int, int]:
     return (B, c, a, d) if layout == "bthd" else (B, a, c, d)  # -> B, NH, T, d
 
 
-def _need(x: torch.Tensor, name: str, dev: torch.device):
-    if x.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16, got {x.dtype}")
+_DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1}  # attn_dtype of the C ABI
+
+
+def _need(x: torch.Tensor, name: str, dev: torch.device, dtype: torch.dtype = torch.bfloat16):
+    if x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (the dtype of q), got {x.dtype}")
     if x.device != dev:
         raise ValueError(f"{name} is on {x.device}, expected {dev}")
+
+
+def _elem(q: torch.Tensor) -> torch.dtype:
+    if q.dtype not in _DTYPE_CODE:
+        raise TypeError(f"q must be bfloat16 or float16, got {q.dtype}")
+    return q.dtype
 
 
 def _stream(dev: torch.device) -> int:
@@ -126,25 +143,30 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("fwd runs on the GPU only; got a CPU tensor")
+    et = _elem(q)
     for n, x in (("q", q), ("k", k), ("v", v)):
-        _need(x, n, dev)
+        _need(x, n, dev, et)
     B, NH, T, dqk = _dims(q, layout)
     dv = v.shape[3]
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
     if out is None:
         shape = (B, T, NH, dv) if layout == "bthd" else (B, NH, T, dv)
-        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-    _need(out, "out", dev)
+        out = torch.empty(shape, dtype=et, device=dev)
+    _need(out, "out", dev, et)
     if return_lse and lse is None:
         lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
         raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    tensors = (q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+               v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
+               lse.data_ptr() if return_lse else None)
     with torch.cuda.device(dev):
-        _check(lib.attn_fwd(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
-                            v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
-                            lse.data_ptr() if return_lse else None, B, NH, T, dqk, dv, float(scale),
-                            int(bool(causal)), _stream(dev)))
+        if et == torch.bfloat16:
+            _check(lib.attn_fwd(*tensors, B, NH, T, dqk, dv, float(scale), int(bool(causal)), _stream(dev)))
+        else:
+            _check(lib.attn_fwd_typed(_DTYPE_CODE[et], *tensors, None, None, B, NH, T, dqk, dv, float(scale),
+                                      int(bool(causal)), None, 0, _stream(dev)))
     return out, (lse if return_lse else None)
 
 
@@ -167,8 +189,9 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("bwd runs on the GPU only; got a CPU tensor")
+    et = _elem(q)
     for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        _need(x, n, dev)
+        _need(x, n, dev, et)
     B, NH, T, dqk = _dims(q, layout)
     dvd = v.shape[3]
     if scale is None:
@@ -181,15 +204,20 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
     need = workspace_bytes(B, NH, T, dqk, dvd, deterministic)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(x, n, dev, et)
+    tensors = (q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+               v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
+               lse.data_ptr(), do.data_ptr(), _strides(do, layout),
+               dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
+               dv.data_ptr(), _strides(dv, layout))
+    rest = (B, NH, T, dqk, dvd, float(scale), int(bool(causal)), int(bool(deterministic)), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(dev), int(stages))
     with torch.cuda.device(dev):
-        _check(lib.attn_bwd_staged(
-            q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
-            v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
-            lse.data_ptr(), do.data_ptr(), _strides(do, layout),
-            dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
-            dv.data_ptr(), _strides(dv, layout), B, NH, T, dqk, dvd, float(scale),
-            int(bool(causal)), int(bool(deterministic)), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), _stream(dev), int(stages)))
+        if et == torch.bfloat16:
+            _check(lib.attn_bwd_staged(*tensors, *rest))
+        else:
+            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *tensors, None, None, *rest))
     return dq, dk, dv
 
 
@@ -221,8 +249,9 @@ def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causa
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("fwd_varlen runs on the GPU only; got a CPU tensor")
+    et = _elem(q)
     for n, x in (("q", q), ("k", k), ("v", v)):
-        _need(x, n, dev)
+        _need(x, n, dev, et)
     B, NH, T, dqk = _dims(q, layout)
     dv = v.shape[3]
     _lengths(seq_len_q, "seq_len_q", B, dev)
@@ -231,19 +260,22 @@ def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causa
         scale = 1.0 / math.sqrt(dqk)
     if out is None:
         shape = (B, T, NH, dv) if layout == "bthd" else (B, NH, T, dv)
-        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-    _need(out, "out", dev)
+        out = torch.empty(shape, dtype=et, device=dev)
+    _need(out, "out", dev, et)
     lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev) if return_lse else None
     need = int(lib.attn_fwd_varlen_workspace_bytes(B, NH, T, dqk, dv))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = (q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+            v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
+            lse.data_ptr() if return_lse else None, seq_len_q.data_ptr(), seq_len_kv.data_ptr(),
+            B, NH, T, dqk, dv, float(scale), int(bool(causal)),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev))
     with torch.cuda.device(dev):
-        _check(lib.attn_fwd_varlen(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
-                                   v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
-                                   lse.data_ptr() if return_lse else None, seq_len_q.data_ptr(),
-                                   seq_len_kv.data_ptr(), B, NH, T, dqk, dv, float(scale), int(bool(causal)),
-                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                   _stream(dev)))
+        if et == torch.bfloat16:
+            _check(lib.attn_fwd_varlen(*args))
+        else:
+            _check(lib.attn_fwd_typed(_DTYPE_CODE[et], *args))
     return out, lse
 
 
@@ -256,8 +288,9 @@ def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.T
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("bwd_varlen runs on the GPU only; got a CPU tensor")
+    et = _elem(q)
     for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        _need(x, n, dev)
+        _need(x, n, dev, et)
     B, NH, T, dqk = _dims(q, layout)
     dvd = v.shape[3]
     _lengths(seq_len_q, "seq_len_q", B, dev)
@@ -272,13 +305,16 @@ def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.T
     need = int(lib.attn_bwd_varlen_workspace_bytes(B, NH, T, dqk, dvd, int(bool(deterministic))))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    with torch.cuda.device(dev):
-        _check(lib.attn_bwd_varlen(
-            q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+    args = (q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
             v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
             lse.data_ptr(), do.data_ptr(), _strides(do, layout),
             dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
             dv.data_ptr(), _strides(dv, layout), seq_len_q.data_ptr(), seq_len_kv.data_ptr(),
             B, NH, T, dqk, dvd, float(scale), int(bool(causal)), int(bool(deterministic)),
-            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev)))
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev))
+    with torch.cuda.device(dev):
+        if et == torch.bfloat16:
+            _check(lib.attn_bwd_varlen(*args))
+        else:
+            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *args, ALL_STAGES))
     return dq, dk, dv

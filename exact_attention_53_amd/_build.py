@@ -17,10 +17,11 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libattn53.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-_CONFIGS = [(dqk, dv, mask) for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in ("causal", "full")]
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_plan.hip"] + [
-    f"attn_bwd_{kind}_{dqk}_{dv}_{mask}.hip" for kind in ("kv", "dq") for dqk, dv, mask in _CONFIGS
-] + ["attn_api.cpp"]
+# Each backward launcher configuration (kernel, element type, head dims, mask) is one
+# compilation of attn_bwd_inst.hip, so that they compile in parallel.
+INSTANCES = [(kind, elem, dqk, dv, causal) for kind in ("kv", "dq") for elem in ("bf16", "f16")
+             for dqk, dv in ((64, 64), (128, 128), (192, 128)) for causal in (True, False)]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_plan.hip", "attn_api.cpp"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU instructions.
 FLAGS = [
@@ -58,7 +59,14 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
         lang = [] if src.endswith(".hip") else ["-x", "hip"]
         cmds.append([hipcc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
-    with cf.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+    for kind, elem, dqk, dv, causal in INSTANCES:
+        obj = os.path.join(BUILD_DIR, f"attn_bwd_{kind}_{elem}_{dqk}_{dv}_{'causal' if causal else 'full'}.o")
+        objs.append(obj)
+        defs = [f"-DATTN_INST_DQ={int(kind == 'dq')}", f"-DATTN_INST_ELEM={elem}", f"-DATTN_INST_DQK={dqk}",
+                f"-DATTN_INST_DV={dv}", f"-DATTN_INST_CAUSAL={'true' if causal else 'false'}"]
+        cmds.append([hipcc, *FLAGS, *defs, "-c", os.path.join(CSRC, "attn_bwd_inst.hip"), "-o", obj])
+    cmds.sort(key=lambda c: "attn_bwd_inst.hip" not in c[-3])  # longest compilations first
+    with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 8)) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)

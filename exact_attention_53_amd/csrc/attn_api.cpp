@@ -59,6 +59,8 @@ size_t ws_acc_bytes(int B, int NH, int T, int dqk) { return align256((size_t)B *
 
 attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+attn53::ElemType elem_type(attn_dtype d) { return d == ATTN_DTYPE_F16 ? attn53::ELEM_F16 : attn53::ELEM_BF16; }
+
 // Work list of a padded-batch launch: one (b, block) pair of int32 per item.
 size_t ws_list_bytes(int B, int T, int block) { return align256((size_t)B * ((T + block - 1) / block) * 8); }
 
@@ -67,10 +69,10 @@ constexpr int kKvBlock = 128;   // keys per key/value workgroup
 
 bool int_ptr_ok(const int32_t* p) { return p != nullptr && reinterpret_cast<uintptr_t>(p) % 4 == 0; }
 
-attn_status fwd_impl(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v, attn_strides sv,
-                     void* o, attn_strides so, float* lse, const int32_t* seq_q, const int32_t* seq_k, int B, int NH,
-                     int T, int d_qk, int d_v, float scale, int causal, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const void* k, attn_strides sk,
+                     const void* v, attn_strides sv, void* o, attn_strides so, float* lse, const int32_t* seq_q,
+                     const int32_t* seq_k, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
@@ -114,7 +116,7 @@ attn_status fwd_impl(const void* q, attn_strides sq, const void* k, attn_strides
     p.seq_k = seq_k;
     p.items = static_cast<const int*>(workspace);
   }
-  return hip_status(attn53::launch_fwd(p, d_qk, d_v, causal != 0, s));
+  return hip_status(attn53::launch_fwd(p, et, d_qk, d_v, causal != 0, s));
 }
 
 size_t bwd_ws_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic, bool varlen) {
@@ -125,7 +127,7 @@ size_t bwd_ws_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic, 
   return n;
 }
 
-attn_status bwd_impl(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v, attn_strides sv,
+attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v, attn_strides sv,
                      const void* o, attn_strides so, const float* lse, const void* do_, attn_strides sdo, void* dq,
                      attn_strides sdq, void* dk, attn_strides sdk, void* dv, attn_strides sdv,
                      const int32_t* seq_q, const int32_t* seq_k, int B, int NH, int T, int d_qk, int d_v,
@@ -204,16 +206,16 @@ attn_status bwd_impl(const void* q, attn_strides sq, const void* k, attn_strides
     }
   }
   if (stages & ATTN_BWD_PREPROCESS) {
-    st = hip_status(attn53::launch_bwd_preprocess(p, d_qk, d_v, !deterministic, s));
+    st = hip_status(attn53::launch_bwd_preprocess(p, et, d_qk, d_v, !deterministic, s));
     if (st != ATTN_OK) return st;
   }
   if (stages & ATTN_BWD_MAIN) {
-    st = hip_status(attn53::launch_bwd_main(p, d_qk, d_v, causal != 0, deterministic != 0, s));
+    st = hip_status(attn53::launch_bwd_main(p, et, d_qk, d_v, causal != 0, deterministic != 0, s));
     if (st != ATTN_OK) return st;
   }
   if (stages & ATTN_BWD_DQ) {
-    st = hip_status(deterministic ? attn53::launch_bwd_dq(p, d_qk, d_v, causal != 0, s)
-                                  : attn53::launch_bwd_finalize(p, d_qk, s));
+    st = hip_status(deterministic ? attn53::launch_bwd_dq(p, et, d_qk, d_v, causal != 0, s)
+                                  : attn53::launch_bwd_finalize(p, et, d_qk, s));
     if (st != ATTN_OK) return st;
   }
   return ATTN_OK;
@@ -233,18 +235,19 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
-    case ATTN_ERR_ARG: return "invalid argument: scale must be finite and > 0, flags 0 or 1, stage mask non-empty";
+    case ATTN_ERR_ARG:
+      return "invalid argument: scale must be finite and > 0, flags 0 or 1, stage mask non-empty, dtype known";
     case ATTN_ERR_ALIAS: return "an output tensor overlaps an input tensor";
   }
   return "unknown attn_status";
 }
 
-int attn_version(void) { return 200; }
+int attn_version(void) { return 300; }
 
 attn_status attn_fwd(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
                      attn_strides sv, void* o, attn_strides so, float* lse, int B, int NH, int T, int d_qk,
                      int d_v, float scale, int causal, void* stream) {
-  return fwd_impl(q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale, causal, nullptr, 0,
+  return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale, causal, nullptr, 0,
                   stream);
 }
 
@@ -258,7 +261,7 @@ attn_status attn_fwd_varlen(const void* q, attn_strides sq, const void* k, attn_
                             const int32_t* seq_len_kv, int B, int NH, int T, int d_qk, int d_v, float scale,
                             int causal, void* workspace, size_t workspace_bytes, void* stream) {
   if (seq_len_q == nullptr || seq_len_kv == nullptr) return ATTN_ERR_NULL;
-  return fwd_impl(q, sq, k, sk, v, sv, o, so, lse, seq_len_q, seq_len_kv, B, NH, T, d_qk, d_v, scale, causal,
+  return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, seq_len_q, seq_len_kv, B, NH, T, d_qk, d_v, scale, causal,
                   workspace, workspace_bytes, stream);
 }
 
@@ -272,7 +275,7 @@ attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_
                             attn_strides sdv, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
                             int deterministic, void* workspace, size_t workspace_bytes, void* stream,
                             unsigned stages) {
-  return bwd_impl(q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr, nullptr, B, NH, T,
+  return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr, nullptr, B, NH, T,
                   d_qk, d_v, scale, causal, deterministic, workspace, workspace_bytes, stream, stages);
 }
 
@@ -281,7 +284,7 @@ attn_status attn_bwd(const void* q, attn_strides sq, const void* k, attn_strides
                      attn_strides sdq, void* dk, attn_strides sdk, void* dv, attn_strides sdv, int B, int NH, int T,
                      int d_qk, int d_v, float scale, int causal, int deterministic, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  return bwd_impl(q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr, nullptr, B, NH, T,
+  return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr, nullptr, B, NH, T,
                   d_qk, d_v, scale, causal, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
 }
 
@@ -296,8 +299,29 @@ attn_status attn_bwd_varlen(const void* q, attn_strides sq, const void* k, attn_
                             int T, int d_qk, int d_v, float scale, int causal, int deterministic, void* workspace,
                             size_t workspace_bytes, void* stream) {
   if (seq_len_q == nullptr || seq_len_kv == nullptr) return ATTN_ERR_NULL;
-  return bwd_impl(q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, seq_len_q, seq_len_kv, B, NH,
+  return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, seq_len_q, seq_len_kv, B, NH,
                   T, d_qk, d_v, scale, causal, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
+}
+
+attn_status attn_fwd_typed(attn_dtype dtype, const void* q, attn_strides sq, const void* k, attn_strides sk,
+                           const void* v, attn_strides sv, void* o, attn_strides so, float* lse,
+                           const int32_t* seq_len_q, const int32_t* seq_len_kv, int B, int NH, int T, int d_qk,
+                           int d_v, float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_ARG;
+  return fwd_impl(elem_type(dtype), q, sq, k, sk, v, sv, o, so, lse, seq_len_q, seq_len_kv, B, NH, T, d_qk, d_v,
+                  scale, causal, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_bwd_typed(attn_dtype dtype, const void* q, attn_strides sq, const void* k, attn_strides sk,
+                           const void* v, attn_strides sv, const void* o, attn_strides so, const float* lse,
+                           const void* do_, attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk,
+                           void* dv, attn_strides sdv, const int32_t* seq_len_q, const int32_t* seq_len_kv, int B,
+                           int NH, int T, int d_qk, int d_v, float scale, int causal, int deterministic,
+                           void* workspace, size_t workspace_bytes, void* stream, unsigned stages) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_ARG;
+  return bwd_impl(elem_type(dtype), q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, seq_len_q,
+                  seq_len_kv, B, NH, T, d_qk, d_v, scale, causal, deterministic, workspace, workspace_bytes, stream,
+                  stages);
 }
 
 }  // extern "C"

@@ -10,49 +10,73 @@ namespace attn53 {
 // ---------------------------------------------------------------------------------
 static inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
-hipError_t launch_bwd_preprocess(const BwdParams& p, int d_qk, int d_v, bool zero_acc, hipStream_t s) {
+template <class E>
+static hipError_t pre_t(const BwdParams& p, int d_qk, int d_v, bool zero_acc, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.NH * p.Tpad;
   if (d_v == 64)
-    hipLaunchKernelGGL((bwd_pre_kernel<64>), dim3(blocks_for(rows * 8)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
+    hipLaunchKernelGGL((bwd_pre_kernel<E, 64>), dim3(blocks_for(rows * 8)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
   else if (d_v == 128)
-    hipLaunchKernelGGL((bwd_pre_kernel<128>), dim3(blocks_for(rows * 16)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
+    hipLaunchKernelGGL((bwd_pre_kernel<E, 128>), dim3(blocks_for(rows * 16)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const BwdParams& p, int d_qk, int d_v, bool causal, bool deterministic, hipStream_t s) {
+hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int d_v, bool zero_acc, hipStream_t s) {
+  return et == ELEM_F16 ? pre_t<f16>(p, d_qk, d_v, zero_acc, s) : pre_t<bf16>(p, d_qk, d_v, zero_acc, s);
+}
+
+template <class E>
+static hipError_t main_t(const BwdParams& p, int d_qk, int d_v, bool causal, bool det, hipStream_t s) {
   if (d_qk == 64 && d_v == 64)
-    return causal ? bwd_main_t<64, 64, true>(p, deterministic, s) : bwd_main_t<64, 64, false>(p, deterministic, s);
+    return causal ? bwd_main_t<E, 64, 64, true>(p, det, s) : bwd_main_t<E, 64, 64, false>(p, det, s);
   if (d_qk == 128 && d_v == 128)
-    return causal ? bwd_main_t<128, 128, true>(p, deterministic, s) : bwd_main_t<128, 128, false>(p, deterministic, s);
+    return causal ? bwd_main_t<E, 128, 128, true>(p, det, s) : bwd_main_t<E, 128, 128, false>(p, det, s);
   if (d_qk == 192 && d_v == 128)
-    return causal ? bwd_main_t<192, 128, true>(p, deterministic, s) : bwd_main_t<192, 128, false>(p, deterministic, s);
+    return causal ? bwd_main_t<E, 192, 128, true>(p, det, s) : bwd_main_t<E, 192, 128, false>(p, det, s);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
-  if (d_qk == 64 && d_v == 64) return causal ? bwd_dq_t<64, 64, true>(p, s) : bwd_dq_t<64, 64, false>(p, s);
-  if (d_qk == 128 && d_v == 128) return causal ? bwd_dq_t<128, 128, true>(p, s) : bwd_dq_t<128, 128, false>(p, s);
-  if (d_qk == 192 && d_v == 128) return causal ? bwd_dq_t<192, 128, true>(p, s) : bwd_dq_t<192, 128, false>(p, s);
+hipError_t launch_bwd_main(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, bool deterministic,
+                           hipStream_t s) {
+  return et == ELEM_F16 ? main_t<f16>(p, d_qk, d_v, causal, deterministic, s)
+                        : main_t<bf16>(p, d_qk, d_v, causal, deterministic, s);
+}
+
+template <class E>
+static hipError_t dq_t(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
+  if (d_qk == 64 && d_v == 64) return causal ? bwd_dq_t<E, 64, 64, true>(p, s) : bwd_dq_t<E, 64, 64, false>(p, s);
+  if (d_qk == 128 && d_v == 128)
+    return causal ? bwd_dq_t<E, 128, 128, true>(p, s) : bwd_dq_t<E, 128, 128, false>(p, s);
+  if (d_qk == 192 && d_v == 128)
+    return causal ? bwd_dq_t<E, 192, 128, true>(p, s) : bwd_dq_t<E, 192, 128, false>(p, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s) {
+  return et == ELEM_F16 ? dq_t<f16>(p, d_qk, d_v, causal, s) : dq_t<bf16>(p, d_qk, d_v, causal, s);
 }
 
 int dq_block_rows(int d_qk) {
   return d_qk == 64 ? DqShape<64>::BM : d_qk == 128 ? DqShape<128>::BM : DqShape<192>::BM;
 }
 
-hipError_t launch_bwd_finalize(const BwdParams& p, int d_qk, hipStream_t s) {
+template <class E>
+static hipError_t finalize_t(const BwdParams& p, int d_qk, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.NH * p.Tpad;
   if (d_qk == 64)
-    hipLaunchKernelGGL((bwd_finalize_kernel<64>), dim3(blocks_for(rows * 8)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_finalize_kernel<E, 64>), dim3(blocks_for(rows * 8)), dim3(256), 0, s, p);
   else if (d_qk == 128)
-    hipLaunchKernelGGL((bwd_finalize_kernel<128>), dim3(blocks_for(rows * 16)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_finalize_kernel<E, 128>), dim3(blocks_for(rows * 16)), dim3(256), 0, s, p);
   else if (d_qk == 192)
-    hipLaunchKernelGGL((bwd_finalize_kernel<192>), dim3(blocks_for(rows * 24)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_finalize_kernel<E, 192>), dim3(blocks_for(rows * 24)), dim3(256), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_finalize(const BwdParams& p, ElemType et, int d_qk, hipStream_t s) {
+  return et == ELEM_F16 ? finalize_t<f16>(p, d_qk, s) : finalize_t<bf16>(p, d_qk, s);
 }
 
 }  // namespace attn53

@@ -1,0 +1,16 @@
+// One configuration of the backward launchers per compilation, so that the
+// configurations compile in parallel.  The build defines
+//   ATTN_INST_DQ     0: key/value kernel (bwd_main_t), 1: dQ kernel (bwd_dq_t)
+//   ATTN_INST_ELEM   bf16 or f16
+//   ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_CAUSAL (true / false)
+#include "attn_bwd_kernels.hpp"
+
+namespace attn53 {
+#if ATTN_INST_DQ
+template hipError_t bwd_dq_t<ATTN_INST_ELEM, ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_CAUSAL>(const BwdParams&,
+                                                                                          hipStream_t);
+#else
+template hipError_t bwd_main_t<ATTN_INST_ELEM, ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_CAUSAL>(const BwdParams&, bool,
+                                                                                            hipStream_t);
+#endif
+}  // namespace attn53

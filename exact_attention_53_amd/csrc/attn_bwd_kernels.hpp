@@ -45,7 +45,7 @@ constexpr int DQ_BN = 64;    // dQ kernel: keys per step
 // ---------------------------------------------------------------------------------
 // preprocess: D = rowsum(dO * O); optional clear of the dQ accumulator
 // ---------------------------------------------------------------------------------
-template <int DV>
+template <class E, int DV>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int d_qk, int zero_acc) {
   constexpr int G = DV / 8;  // lanes per row
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -59,10 +59,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int d_qk, int
     const int b = bh / p.NH, h = bh % p.NH;
     const int Lq = p.seq_q != nullptr ? batch_len(p.seq_q, b, p.T) : p.T;
     if (t < Lq) {
-      const bf16* orow = (const bf16*)p.o + b * p.so.b + h * p.so.h + (int64_t)t * p.so.t;
-      const bf16* drow = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h + (int64_t)t * p.sdo.t;
-      const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(orow + 8 * c));
-      const bf16x8 dv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(drow + 8 * c));
+      const E* orow = (const E*)p.o + b * p.so.b + h * p.so.h + (int64_t)t * p.so.t;
+      const E* drow = (const E*)p.dO + b * p.sdo.b + h * p.sdo.h + (int64_t)t * p.sdo.t;
+      const vec8<E> ov = __builtin_bit_cast(vec8<E>, *reinterpret_cast<const u32x4*>(orow + 8 * c));
+      const vec8<E> dv = __builtin_bit_cast(vec8<E>, *reinterpret_cast<const u32x4*>(drow + 8 * c));
 #pragma unroll
       for (int e = 0; e < 8; ++e) sum += (float)ov[e] * (float)dv[e];
     }
@@ -173,7 +173,7 @@ struct KvPlan {
   static_assert(plan.ok, "no feasible placement of the step's VALU work");
 };
 
-template <int DQK, int DV, bool CAUSAL, bool ATOMIC_DQ>
+template <class E, int DQK, int DV, bool CAUSAL, bool ATOMIC_DQ>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
@@ -210,10 +210,10 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int bh = b * p.NH + h;
   const int nqb = (Lq + BWD_BM - 1) / BWD_BM;
 
-  const bf16* qg = (const bf16*)p.q + b * p.sq.b + h * p.sq.h;
-  const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
-  const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
-  const bf16* dog = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h;
+  const E* qg = (const E*)p.q + b * p.sq.b + h * p.sq.h;
+  const E* kg = (const E*)p.k + b * p.sk.b + h * p.sk.h;
+  const E* vg = (const E*)p.v + b * p.sv.b + h * p.sv.h;
+  const E* dog = (const E*)p.dO + b * p.sdo.b + h * p.sdo.h;
   const float* lseg = p.lse2 + (int64_t)bh * p.Tpad;
   const float* Dg = p.D + (int64_t)bh * p.Tpad;
   const int64_t sqt = p.sq.t, sdot = p.sdo.t;
@@ -223,8 +223,8 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int kw = 32 * w;
   const int my_key = key0 + kw + lq;
   const float c = p.scale_log2;
-  bf16* dkg = (bf16*)p.dk + b * p.sdk.b + h * p.sdk.h;
-  bf16* dvg = (bf16*)p.dv + b * p.sdv.b + h * p.sdv.h;
+  E* dkg = (E*)p.dk + b * p.sdk.b + h * p.sdk.h;
+  E* dvg = (E*)p.dv + b * p.sdv.b + h * p.sdv.h;
 
   const int i0 = CAUSAL ? key0 / BWD_BM : 0;
   const int n_q = nqb - i0;
@@ -241,18 +241,18 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   }
 
   // K and V rows of this wavefront as B-operand fragments of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[KSQ], vf[KSV];
+  vec8<E> kf[KSQ], vf[KSV];
 #pragma unroll
   for (int ks = 0; ks < KSQ; ++ks) {
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (my_key < Lk) raw = *reinterpret_cast<const u32x4*>(kg + (int64_t)my_key * p.sk.t + 16 * ks + 8 * g);
-    kf[ks] = __builtin_bit_cast(bf16x8, raw);
+    kf[ks] = __builtin_bit_cast(vec8<E>, raw);
   }
 #pragma unroll
   for (int ks = 0; ks < KSV; ++ks) {
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (my_key < Lk) raw = *reinterpret_cast<const u32x4*>(vg + (int64_t)my_key * p.sv.t + 16 * ks + 8 * g);
-    vf[ks] = __builtin_bit_cast(bf16x8, raw);
+    vf[ks] = __builtin_bit_cast(vec8<E>, raw);
   }
 
   DirectTile<BWD_BM, DQK, BWD_NT / 64> qload;
@@ -295,9 +295,9 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const ATTN_LDS char* kd = (const ATTN_LDS char*)kd_lds;
 #pragma unroll
     for (int m = 0; m < BWD_BN / 16; ++m) {
-      const bf16x8 a = lds_col8<BWD_BN>(st, L, 16 * m, 32 * tq);
+      const vec8<E> a = lds_col8<E, BWD_BN>(st, L, 16 * m, 32 * tq);
 #pragma unroll
-      for (int n = 0; n < NDQ; ++n) dq[n] = mfma32(a, lds_col8<BWD_BN>(kd, L, 16 * m, 32 * (dq_t0 + n)), dq[n]);
+      for (int n = 0; n < NDQ; ++n) dq[n] = mfma32(a, lds_col8<E, BWD_BN>(kd, L, 16 * m, 32 * (dq_t0 + n)), dq[n]);
     }
 #pragma unroll
     for (int n = 0; n < NDQ; ++n) {
@@ -336,19 +336,19 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       return;
     }
     f32x16 s[2], dp[2];
-    bf16x8 pb[4], sb[4];
+    vec8<E> pb[4], sb[4];
     if constexpr (MASKED) {
       // S = Q K^T and dP = dO V^T for 64 queries x this wavefront's 32 keys
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          s[t] = mfma32(lds_row8<BWD_BM>(qt, L, 32 * t, ks), kf[ks], ks == 0 ? zero16() : s[t]);
+          s[t] = mfma32(lds_row8<E, BWD_BM>(qt, L, 32 * t, ks), kf[ks], ks == 0 ? zero16() : s[t]);
 #pragma unroll
       for (int ks = 0; ks < KSV; ++ks)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          dp[t] = mfma32(lds_row8<BWD_BM>(ot, L, 32 * t, ks), vf[ks], ks == 0 ? zero16() : dp[t]);
+          dp[t] = mfma32(lds_row8<E, BWD_BM>(ot, L, 32 * t, ks), vf[ks], ks == 0 ? zero16() : dp[t]);
       // P = 2^(S c - LSE log2 e); element r of tile t: query q0 + 32 t + 8 (r / 4) + 4 g + r % 4
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -365,12 +365,12 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
           }
         }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) pb[m] = pack8(s[m >> 1], m & 1);
+      for (int m = 0; m < 4; ++m) pb[m] = pack8<E>(s[m >> 1], m & 1);
       // dV += P^T dO  (contraction over the 64 queries)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int t = 0; t < NDV; ++t) dv[t] = mfma32(pb[m], lds_col8<BWD_BM>(ot, L, 16 * m, 32 * t), dv[t]);
+        for (int t = 0; t < NDV; ++t) dv[t] = mfma32(pb[m], lds_col8<E, BWD_BM>(ot, L, 16 * m, 32 * t), dv[t]);
       // dS = P (dP - D)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -381,31 +381,31 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
           for (int e = 0; e < 4; ++e) dp[t][4 * a + e] = s[t][4 * a + e] * (dp[t][4 * a + e] - Dd[e]);
         }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) sb[m] = pack8(dp[m >> 1], m & 1);
+      for (int m = 0; m < 4; ++m) sb[m] = pack8<E>(dp[m >> 1], m & 1);
       // dK += dS^T Q
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int t = 0; t < NDK; ++t) dk[t] = mfma32(sb[m], lds_col8<BWD_BM>(qt, L, 16 * m, 32 * t), dk[t]);
+        for (int t = 0; t < NDK; ++t) dk[t] = mfma32(sb[m], lds_col8<E, BWD_BM>(qt, L, 16 * m, 32 * t), dk[t]);
     } else {
       // The same work as an explicit pipeline (KvPlan): bundle i issues MFMA i, the
       // operand read of MFMA i + LA and its share of the VALU work; the compiler may
       // reorder only within a bundle.
       using Plan = KvPlan<DQK, DV>;
       constexpr int NS = Plan::NS, NP = Plan::NP, NV = Plan::NV, LA = Plan::LA, RING = Plan::RING;
-      bf16x8 fr[RING];
+      vec8<E> fr[RING];
       f32x4 lsev[2][4], ddv[2][4];
       f32x16 pv[2], dsv[2];  // P and dS, apart from the S and dP accumulators
-      auto read_frag = [&](auto jc) -> bf16x8 {
+      auto read_frag = [&](auto jc) -> vec8<E> {
         constexpr int j = decltype(jc)::value;
         if constexpr (j < NS) {
-          return lds_row8<BWD_BM>(qt, L, 32 * (j / KSQ), j % KSQ);
+          return lds_row8<E, BWD_BM>(qt, L, 32 * (j / KSQ), j % KSQ);
         } else if constexpr (j < NS + NP) {
-          return lds_row8<BWD_BM>(ot, L, 32 * ((j - NS) / KSV), (j - NS) % KSV);
+          return lds_row8<E, BWD_BM>(ot, L, 32 * ((j - NS) / KSV), (j - NS) % KSV);
         } else if constexpr (j < NS + NP + NV) {
-          return lds_col8<BWD_BM>(ot, L, 16 * ((j - NS - NP) / NDV), 32 * ((j - NS - NP) % NDV));
+          return lds_col8<E, BWD_BM>(ot, L, 16 * ((j - NS - NP) / NDV), 32 * ((j - NS - NP) % NDV));
         } else {
-          return lds_col8<BWD_BM>(qt, L, 16 * ((j - NS - NP - NV) / NDK), 32 * ((j - NS - NP - NV) % NDK));
+          return lds_col8<E, BWD_BM>(qt, L, 16 * ((j - NS - NP - NV) / NDK), 32 * ((j - NS - NP - NV) % NDK));
         }
       };
       auto valu_op = [&](auto oc) {
@@ -414,12 +414,12 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         constexpr int h = k < 9 ? 0 : 1, r = k < 8 ? k : k - 1;
         if constexpr (grp < 2) {
           if constexpr (Plan::is_pack(o))
-            pb[2 * t + h] = pack8(pv[t], h);
+            pb[2 * t + h] = pack8<E>(pv[t], h);
           else
             pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, -lsev[t][r >> 2][r & 3]));
         } else {
           if constexpr (Plan::is_pack(o))
-            sb[2 * t + h] = pack8(dsv[t], h);
+            sb[2 * t + h] = pack8<E>(dsv[t], h);
           else
             dsv[t][r] = pv[t][r] * (dp[t][r] - ddv[t][r >> 2][r & 3]);
         }
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       ATTN_SCHED_FENCE();
       static_for<0, Plan::N>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        const bf16x8 f = fr[i % RING];
+        const vec8<E> f = fr[i % RING];
         if constexpr (i < NS) {
           constexpr int t = i / KSQ, ks = i % KSQ;
           s[t] = mfma32(f, kf[ks], ks == 0 ? zero16() : s[t]);
@@ -521,9 +521,9 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int key = key0 + kw + 8 * (r >> 2) + 4 * g + (r & 3);
     if (key < T) {
 #pragma unroll
-      for (int t = 0; t < NDK; ++t) dkg[(int64_t)key * p.sdk.t + 32 * t + lq] = (bf16)(dk[t][r] * p.scale);
+      for (int t = 0; t < NDK; ++t) dkg[(int64_t)key * p.sdk.t + 32 * t + lq] = (E)(dk[t][r] * p.scale);
 #pragma unroll
-      for (int t = 0; t < NDV; ++t) dvg[(int64_t)key * p.sdv.t + 32 * t + lq] = (bf16)dv[t][r];
+      for (int t = 0; t < NDV; ++t) dvg[(int64_t)key * p.sdv.t + 32 * t + lq] = (E)dv[t][r];
     }
   }
 }
@@ -612,7 +612,7 @@ struct DqShape {
   static constexpr int WAVES_PER_EU = 1;
 };
 
-template <int DQK, int DV, bool CAUSAL>
+template <class E, int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
                                                                          DqShape<DQK>::WAVES_PER_EU)))
 void bwd_dq_kernel(BwdParams p) {
@@ -645,11 +645,11 @@ void bwd_dq_kernel(BwdParams p) {
   }
   const int bh = b * p.NH + h;
 
-  const bf16* qg = (const bf16*)p.q + b * p.sq.b + h * p.sq.h;
-  const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
-  const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
-  const bf16* dog = (const bf16*)p.dO + b * p.sdo.b + h * p.sdo.h;
-  bf16* dqg = (bf16*)p.dq + b * p.sdq.b + h * p.sdq.h;
+  const E* qg = (const E*)p.q + b * p.sq.b + h * p.sq.h;
+  const E* kg = (const E*)p.k + b * p.sk.b + h * p.sk.h;
+  const E* vg = (const E*)p.v + b * p.sv.b + h * p.sv.h;
+  const E* dog = (const E*)p.dO + b * p.sdo.b + h * p.sdo.h;
+  E* dqg = (E*)p.dq + b * p.sdq.b + h * p.sdq.h;
   const int64_t skt = p.sk.t, svt = p.sv.t;
 
   const LdsLane L = lds_lane(lane);
@@ -671,7 +671,7 @@ void bwd_dq_kernel(BwdParams p) {
   }
 
   // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T
-  bf16x8 qf[QT][KSQ], df[QT][KSV];
+  vec8<E> qf[QT][KSQ], df[QT][KSV];
   float lse2[QT], Dq[QT];
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
@@ -680,13 +680,13 @@ void bwd_dq_kernel(BwdParams p) {
     for (int ks = 0; ks < KSQ; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
       if (q < Lq) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)q * p.sq.t + 16 * ks + 8 * g);
-      qf[u][ks] = __builtin_bit_cast(bf16x8, raw);
+      qf[u][ks] = __builtin_bit_cast(vec8<E>, raw);
     }
 #pragma unroll
     for (int ks = 0; ks < KSV; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
       if (q < Lq) raw = *reinterpret_cast<const u32x4*>(dog + (int64_t)q * p.sdo.t + 16 * ks + 8 * g);
-      df[u][ks] = __builtin_bit_cast(bf16x8, raw);
+      df[u][ks] = __builtin_bit_cast(vec8<E>, raw);
     }
     lse2[u] = p.lse2[(int64_t)bh * p.Tpad + min(q, p.Tpad - 1)];  // +inf on padding rows
     Dq[u] = q < Lq ? p.D[(int64_t)bh * p.Tpad + q] : 0.f;
@@ -718,7 +718,7 @@ void bwd_dq_kernel(BwdParams p) {
     for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 a = lds_row8<DQ_BN>(kt, L, 32 * t, ks);
+        const vec8<E> a = lds_row8<E, DQ_BN>(kt, L, 32 * t, ks);
 #pragma unroll
         for (int u = 0; u < QT; ++u) s[t][u] = mfma32(a, qf[u][ks], ks == 0 ? zero16() : s[t][u]);
       }
@@ -726,7 +726,7 @@ void bwd_dq_kernel(BwdParams p) {
     for (int ks = 0; ks < KSV; ++ks)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 a = lds_row8<DQ_BN>(vt, L, 32 * t, ks);
+        const vec8<E> a = lds_row8<E, DQ_BN>(vt, L, 32 * t, ks);
 #pragma unroll
         for (int u = 0; u < QT; ++u) dp[t][u] = mfma32(a, df[u][ks], ks == 0 ? zero16() : dp[t][u]);
       }
@@ -747,19 +747,19 @@ void bwd_dq_kernel(BwdParams p) {
     // dS^T = P^T (dP^T - D); dQ^T += K^T dS^T, one 32-key half at a time
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      bf16x8 sb[QT][2];
+      vec8<E> sb[QT][2];
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dp[t][u][r] = s[t][u][r] * (dp[t][u][r] - Dq[u]);
-        sb[u][0] = pack8(dp[t][u], 0);
-        sb[u][1] = pack8(dp[t][u], 1);
+        sb[u][0] = pack8<E>(dp[t][u], 0);
+        sb[u][1] = pack8<E>(dp[t][u], 1);
       }
 #pragma unroll
       for (int n = 0; n < NDQ; ++n)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8 a = lds_col8<DQ_BN>(kt, L, 32 * t + 16 * hh, 32 * n);
+          const vec8<E> a = lds_col8<E, DQ_BN>(kt, L, 32 * t + 16 * hh, 32 * n);
 #pragma unroll
           for (int u = 0; u < QT; ++u) dq[u][n] = mfma32(a, sb[u][hh], dq[u][n]);
         }
@@ -801,21 +801,21 @@ void bwd_dq_kernel(BwdParams p) {
     const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
     f32x16 s[2][QT], dp[2][QT];
     f32x16 pv[QT];         // P, then dS, of the half being worked on
-    bf16x8 sb[2][QT][2];
-    bf16x8 fr[Plan::RING];
-    auto read_at = [&](auto bc) __attribute__((always_inline)) -> bf16x8 {
+    vec8<E> sb[2][QT][2];
+    vec8<E> fr[Plan::RING];
+    auto read_at = [&](auto bc) __attribute__((always_inline)) -> vec8<E> {
       constexpr int b = decltype(bc)::value;
       if constexpr (b < Plan::P0)
-        return lds_row8<DQ_BN>(kt, L, 0, b);
+        return lds_row8<E, DQ_BN>(kt, L, 0, b);
       else if constexpr (b < Plan::S1)
-        return lds_row8<DQ_BN>(vt, L, 0, b - Plan::P0);
+        return lds_row8<E, DQ_BN>(vt, L, 0, b - Plan::P0);
       else if constexpr (b < Plan::P1)
-        return lds_row8<DQ_BN>(kt, L, 32, b - Plan::S1);
+        return lds_row8<E, DQ_BN>(kt, L, 32, b - Plan::S1);
       else if constexpr (b < Plan::Q0)
-        return lds_row8<DQ_BN>(vt, L, 32, b - Plan::P1);
+        return lds_row8<E, DQ_BN>(vt, L, 32, b - Plan::P1);
       else {
         constexpr int t = b < Plan::Q1 ? 0 : 1, jj = b - (t ? Plan::Q1 : Plan::Q0);
-        return lds_col8<DQ_BN>(kt, L, 32 * t + 16 * (jj % 2), 32 * (jj / 2));
+        return lds_col8<E, DQ_BN>(kt, L, 32 * t + 16 * (jj % 2), 32 * (jj / 2));
       }
     };
     auto valu_op = [&](auto oc) __attribute__((always_inline)) {
@@ -826,7 +826,7 @@ void bwd_dq_kernel(BwdParams p) {
       } else {
         constexpr int kk = k - 16 * QT, u = kk / 18, e = kk % 18;
         if constexpr (e == 8 || e == 17) {
-          sb[t][u][e == 8 ? 0 : 1] = pack8(pv[u], e == 8 ? 0 : 1);
+          sb[t][u][e == 8 ? 0 : 1] = pack8<E>(pv[u], e == 8 ? 0 : 1);
         } else {
           constexpr int r = e < 8 ? e : e - 1;
           pv[u][r] = pv[u][r] * (dp[t][u][r] - Dq[u]);
@@ -837,7 +837,7 @@ void bwd_dq_kernel(BwdParams p) {
     ATTN_SCHED_FENCE();
     static_for<0, Plan::N>([&](auto bc) __attribute__((always_inline)) {
       constexpr int b = decltype(bc)::value;
-      const bf16x8 f = fr[b % Plan::RING];
+      const vec8<E> f = fr[b % Plan::RING];
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
         if constexpr (b < Plan::P0)
@@ -906,15 +906,15 @@ void bwd_dq_kernel(BwdParams p) {
   for (int u = 0; u < QT; ++u) {
     const int q = qw + 32 * u + lq;
     if (q < T) {
-      bf16* row = dqg + (int64_t)q * p.sdq.t;
+      E* row = dqg + (int64_t)q * p.sdq.t;
 #pragma unroll
       for (int t = 0; t < NDQ; ++t)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          bf16x4 v;
+          vec4<E> v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (bf16)(dq[u][t][4 * a + e] * p.scale);
-          *reinterpret_cast<bf16x4*>(row + 32 * t + 8 * a + 4 * g) = v;
+          for (int e = 0; e < 4; ++e) v[e] = (E)(dq[u][t][4 * a + e] * p.scale);
+          *reinterpret_cast<vec4<E>*>(row + 32 * t + 8 * a + 4 * g) = v;
         }
     }
   }
@@ -923,7 +923,7 @@ void bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------------
 // finalize: dQ = scale * accumulator -> bf16
 // ---------------------------------------------------------------------------------
-template <int DQK>
+template <class E, int DQK>
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
   constexpr int G = DQK / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -937,42 +937,43 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
   const float* src = p.dq_acc + row * DQK + 8 * c;
   const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
   const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-  bf16x8 v;
+  vec8<E> v;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    v[e] = (bf16)(x0[e] * p.scale);
-    v[4 + e] = (bf16)(x1[e] * p.scale);
+    v[e] = (E)(x0[e] * p.scale);
+    v[4 + e] = (E)(x1[e] * p.scale);
   }
-  bf16* dst = (bf16*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)t * p.sdq.t + 8 * c;
+  E* dst = (E*)p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)t * p.sdq.t + 8 * c;
   *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, v);
 }
 
 // ---------------------------------------------------------------------------------
-// per-configuration launchers (instantiated in attn_bwd_kv_*.hip and attn_bwd_dq.hip)
+// per-configuration launchers (each instantiated by one compilation of attn_bwd_inst.hip)
 // ---------------------------------------------------------------------------------
-template <int DQK, int DV, bool CAUSAL>
+template <class E, int DQK, int DV, bool CAUSAL>
 hipError_t bwd_main_t(const BwdParams& p, bool deterministic, hipStream_t s) {
   const int nkb = (p.T + BWD_BN - 1) / BWD_BN;
   const dim3 grid_kv(nkb * p.B * p.NH);
   if (deterministic)
-    hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, CAUSAL, false>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, false>), grid_kv, dim3(BWD_NT), 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, CAUSAL, true>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, true>), grid_kv, dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
-template <int DQK, int DV, bool CAUSAL>
+template <class E, int DQK, int DV, bool CAUSAL>
 hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
   const int nqb = (p.T + DqShape<DQK>::BM - 1) / DqShape<DQK>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
 #define ATTN_BWD_CONFIGS(X) \
   X(64, 64, true) X(64, 64, false) X(128, 128, true) X(128, 128, false) X(192, 128, true) X(192, 128, false)
-#define ATTN_EXTERN_BWD(DQK, DV, CAUSAL)                                                         \
-  extern template hipError_t bwd_main_t<DQK, DV, CAUSAL>(const BwdParams&, bool, hipStream_t); \
-  extern template hipError_t bwd_dq_t<DQK, DV, CAUSAL>(const BwdParams&, hipStream_t);
+#define ATTN_EXTERN_BWD_E(E, DQK, DV, CAUSAL)                                                       \
+  extern template hipError_t bwd_main_t<E, DQK, DV, CAUSAL>(const BwdParams&, bool, hipStream_t); \
+  extern template hipError_t bwd_dq_t<E, DQK, DV, CAUSAL>(const BwdParams&, hipStream_t);
+#define ATTN_EXTERN_BWD(DQK, DV, CAUSAL) ATTN_EXTERN_BWD_E(bf16, DQK, DV, CAUSAL) ATTN_EXTERN_BWD_E(f16, DQK, DV, CAUSAL)
 ATTN_BWD_CONFIGS(ATTN_EXTERN_BWD)
 
 }  // namespace attn53

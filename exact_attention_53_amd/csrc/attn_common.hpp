@@ -5,7 +5,12 @@
 //   [2CTA] "深度学习反向传播优化：2-CTA MMA模式与内存访问优化"
 //   [FAT]  "FlashAttention Triton实现中的内存访问模式优化与寄存器分配策略"
 //
-// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, one 64-lane wavefront; lane l,
+// Element types.  Every kernel is a template over its 16-bit element type E: bf16
+// (__bf16) or fp16 (_Float16), the two 16-bit input formats of [SA8 1.3].  Loads, LDS
+// tiles and transposed reads move 16-bit words and do not depend on E; only the matrix
+// instruction, the fp32 -> E roundings and the dot products used for row sums do.
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16 / _f16, one 64-lane wavefront; lane l,
 // half g = l / 32):
 //   A operand (32 x 16): lane l holds A[l % 32][8g .. 8g+7]
 //   B operand (16 x 32): lane l holds B[8g .. 8g+7][l % 32]
@@ -18,7 +23,7 @@
 // contraction index in the same order, {16m + 4g + 0..3, 16m + 4g + 8..11}.  The
 // transposed LDS reads below produce exactly that order.
 //
-// LDS tiles.  A tile of R rows x C columns of bf16 (C a multiple of 64) is stored as
+// LDS tiles.  A tile of R rows x C columns of 16-bit elements (C a multiple of 64) is stored as
 // C/64 panels, each R rows of 128 bytes.  Within a row the eight 16-byte chunks are
 // permuted by XOR with swz(row).  With 64 LDS banks of 4 bytes this makes both access
 // patterns conflict-free:
@@ -36,8 +41,14 @@
 namespace attn53 {
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <class E>
+using vec8 = E __attribute__((ext_vector_type(8)));
+template <class E>
+using vec4 = E __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -56,6 +67,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -64,8 +78,7 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// 8 consecutive accumulator values (r = 8m .. 8m+7) rounded to bf16 (RNE).
-// acc + the sum of the eight values of x, by four v_dot2_f32_bf16 with (1, 1).
+// acc + the sum of the eight values of x, by four v_dot2_f32_bf16 / _f16 with (1, 1).
 __device__ __forceinline__ float sum_pairs(const bf16x8& x, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {(bf16)1.f, (bf16)1.f};
@@ -74,11 +87,21 @@ __device__ __forceinline__ float sum_pairs(const bf16x8& x, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
 }
+__device__ __forceinline__ float sum_pairs(const f16x8& x, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 one = {(f16)1.f, (f16)1.f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
+}
 
-__device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int m) {
-  bf16x8 r;
+// 8 consecutive accumulator values (r = 8m .. 8m+7) rounded to E (nearest even).
+template <class E>
+__device__ __forceinline__ vec8<E> pack8(const f32x16& acc, int m) {
+  vec8<E> r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (bf16)acc[8 * m + e];
+  for (int e = 0; e < 8; ++e) r[e] = (E)acc[8 * m + e];
   return r;
 }
 
@@ -155,10 +178,10 @@ __device__ __forceinline__ LdsLane lds_lane(uint32_t lane) {
 }
 
 // Row read: lane l gets columns 16 ks + 8 g .. +7 of row R0 + l % 32 (R0 % 16 == 0).
-template <int ROWS>
-__device__ __forceinline__ bf16x8 lds_row8(const ATTN_LDS char* tile, const LdsLane& L, int R0, int ks) {
+template <class E, int ROWS>
+__device__ __forceinline__ vec8<E> lds_row8(const ATTN_LDS char* tile, const LdsLane& L, int R0, int ks) {
   const uint32_t off = (uint32_t)(ks >> 2) * (ROWS * 128u) + (uint32_t)R0 * 128u + (L.row ^ ((uint32_t)(ks & 3) << 5));
-  return *reinterpret_cast<const ATTN_LDS bf16x8*>(tile + off);
+  return *reinterpret_cast<const ATTN_LDS vec8<E>*>(tile + off);
 }
 
 // Column read for an MFMA operand whose contraction index runs along the tile's rows.
@@ -166,21 +189,21 @@ __device__ __forceinline__ bf16x8 lds_row8(const ATTN_LDS char* tile, const LdsL
 // k = k0 + 4 g + {0..3, 8..11} (g = l / 32), k0 % 16 == 0, j0 % 32 == 0: two
 // ds_read_b64_tr_b16.  Within each 16-lane group, lane p supplies the address of row
 // (k0 + 4g + 8h + p / 4), columns j0 + 16 * ((l / 16) % 2) + 4 (p % 4) .. +3.
-template <int ROWS>
-__device__ __forceinline__ bf16x8 lds_col8(const ATTN_LDS char* tile, const LdsLane& L, int k0, int j0) {
+template <class E, int ROWS>
+__device__ __forceinline__ vec8<E> lds_col8(const ATTN_LDS char* tile, const LdsLane& L, int k0, int j0) {
   const uint32_t x = (uint32_t)((j0 >> 5) & 1) << 6;
   const uint32_t base = (uint32_t)(j0 >> 6) * (ROWS * 128u) + (uint32_t)k0 * 128u;
   i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(tile + base + (L.col0 ^ x)));
   i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(tile + base + (L.col1 ^ x)));
   i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(vec8<E>, v);
 }
 
 // ---------------------------------------------------------------------------------
 // direct global -> LDS tile loads (buffer_load_dwordx4 ... lds)
 // ---------------------------------------------------------------------------------
-// A tile of ROWS x COLS bf16 (rows of a matrix with row stride `ld` elements) is
-// written to LDS in the swizzled panel layout by NW wavefronts.  Wavefront w fills the
+// A tile of ROWS x COLS 16-bit elements (rows of a matrix with row stride `ld`
+// elements) is written to LDS in the swizzled panel layout by NW wavefronts.  Wavefront w fills the
 // 1 KB blocks w, w + NW, ...; a block is 8 rows x 128 bytes of one panel, and lane l
 // of the wavefront lands at byte 16 l of it, so the lane fetches the global chunk that
 // the swizzle puts there.  Each lane keeps one 32-bit byte offset per block; the tile
@@ -205,7 +228,7 @@ struct DirectTile {
     }
   }
   // tile = matrix + row0 * ld (uniform); valid = number of matrix rows from row0 on (>= 1).
-  __device__ __forceinline__ void issue(const bf16* tile, int64_t ld, int valid, ATTN_LDS char* dst, int w) const {
+  __device__ __forceinline__ void issue(const void* tile, int64_t ld, int valid, ATTN_LDS char* dst, int w) const {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer-resource builtins exist only for the GPU target
     const int64_t rows = valid < ROWS ? valid : ROWS;
     const int64_t bytes = ((rows - 1) * ld + COLS) * 2;
@@ -233,7 +256,7 @@ __device__ __forceinline__ void load_f32x64_lds(const float* src, int valid, ATT
 // ---------------------------------------------------------------------------------
 // global <-> LDS tile staging through registers
 // ---------------------------------------------------------------------------------
-// A tile of ROWS x COLS bf16 starting at global row `row0` of a (T, COLS) matrix with
+// A tile of ROWS x COLS 16-bit elements starting at global row `row0` of a (T, COLS) matrix with
 // row stride `ld` elements.  Rows >= T are filled with zeros.  NT threads cooperate;
 // each holds CHUNKS 16-byte chunks.  Chunk x -> panel x / (ROWS * 8), row (x / 8) %
 // ROWS, chunk-in-row x % 8: eight consecutive lanes read one 128-byte row segment.
@@ -243,7 +266,8 @@ struct TileStage {
   static_assert(ROWS * COLS / 8 % NT == 0, "tile not divisible among threads");
   u32x4 v[CHUNKS];
 
-  __device__ __forceinline__ void load(const bf16* __restrict__ g, int64_t ld, int row0, int T, int tid) {
+  template <class E>
+  __device__ __forceinline__ void load(const E* __restrict__ g, int64_t ld, int row0, int T, int tid) {
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
       const int x = tid + NT * i;

@@ -43,7 +43,7 @@ constexpr int FWD_NT = 256;
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 constexpr float kSumLimit = 256.f;        // 2^kRescaleThreshold
 
-template <int DQK, int DV, bool CAUSAL>
+template <class E, int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr int KS = DQK / 16;
   constexpr int NDT = DV / 32;
@@ -75,10 +75,10 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   }
   const int bh = b * p.NH + h;
 
-  const bf16* qg = (const bf16*)p.q + b * p.sq.b + h * p.sq.h;
-  const bf16* kg = (const bf16*)p.k + b * p.sk.b + h * p.sk.h;
-  const bf16* vg = (const bf16*)p.v + b * p.sv.b + h * p.sv.h;
-  bf16* og = (bf16*)p.o + b * p.so.b + h * p.so.h;
+  const E* qg = (const E*)p.q + b * p.sq.b + h * p.sq.h;
+  const E* kg = (const E*)p.k + b * p.sk.b + h * p.sk.h;
+  const E* vg = (const E*)p.v + b * p.sv.b + h * p.sv.h;
+  E* og = (E*)p.o + b * p.so.b + h * p.so.h;
   const int64_t skt = p.sk.t, svt = p.sv.t;
 
   const LdsLane L = lds_lane(lane);
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int n_kv = (kv_end + FWD_BN - 1) / FWD_BN;
   if (q0 >= Lq || n_kv == 0) {  // padding rows only, or no keys: O = 0, LSE = -inf
     if (my_q < T) {
-      bf16* orow = og + (int64_t)my_q * p.so.t;
+      E* orow = og + (int64_t)my_q * p.so.t;
 #pragma unroll
       for (int y = 0; y < DV / 8; ++y) *reinterpret_cast<u32x2*>(orow + 8 * y + 4 * g) = u32x2{0u, 0u};
       if (p.lse != nullptr && g == 0) p.lse[(int64_t)bh * T + my_q] = -INFINITY;
@@ -98,12 +98,12 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   }
 
   // Q rows of this wavefront, as B-operand fragments of S^T = K Q^T.
-  bf16x8 qf[KS];
+  vec8<E> qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (my_q < Lq) raw = *reinterpret_cast<const u32x4*>(qg + (int64_t)my_q * p.sq.t + 16 * ks + 8 * g);
-    qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    qf[ks] = __builtin_bit_cast(vec8<E>, raw);
   }
 
   DirectTile<FWD_BN, DQK, FWD_NT / 64> kload;
@@ -145,8 +145,8 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
       s1 = zero16();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s0 = mfma32(lds_row8<FWD_BN>(kt, L, 0, ks), qf[ks], s0);
-        s1 = mfma32(lds_row8<FWD_BN>(kt, L, 32, ks), qf[ks], s1);
+        s0 = mfma32(lds_row8<E, FWD_BN>(kt, L, 0, ks), qf[ks], s0);
+        s1 = mfma32(lds_row8<E, FWD_BN>(kt, L, 32, ks), qf[ks], s1);
       }
       if constexpr (MASKED) {
 #pragma unroll
@@ -178,17 +178,17 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     };
     // p = 2^(S c - m) as bf16 operands of the second product; returns this lane's sum of
     // the rounded p (the weights O is built from), one v_dot2 with (1, 1) per bf16 pair.
-    bf16x8 pb[4];
+    vec8<E> pb[4];
     auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s0[r] = exp2_fast(__builtin_fmaf(s0[r], c, -m_run));
         s1[r] = exp2_fast(__builtin_fmaf(s1[r], c, -m_run));
       }
-      pb[0] = pack8(s0, 0);
-      pb[1] = pack8(s0, 1);
-      pb[2] = pack8(s1, 0);
-      pb[3] = pack8(s1, 1);
+      pb[0] = pack8<E>(s0, 0);
+      pb[1] = pack8<E>(s0, 1);
+      pb[2] = pack8<E>(s1, 0);
+      pb[3] = pack8<E>(s1, 1);
       return sum_pairs(pb[0], sum_pairs(pb[1], sum_pairs(pb[2], sum_pairs(pb[3], 0.f))));
     };
     scores();
@@ -216,14 +216,14 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
       }
     }
     l_run += rs;
-    const bf16x8 pb0 = pb[0], pb1 = pb[1], pb2 = pb[2], pb3 = pb[3];
+    const vec8<E> pb0 = pb[0], pb1 = pb[1], pb2 = pb[2], pb3 = pb[3];
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] = mfma32(lds_col8<FWD_BN>(vt, L, 0, 32 * dt), pb0, o[dt]);
-      o[dt] = mfma32(lds_col8<FWD_BN>(vt, L, 16, 32 * dt), pb1, o[dt]);
-      o[dt] = mfma32(lds_col8<FWD_BN>(vt, L, 32, 32 * dt), pb2, o[dt]);
-      o[dt] = mfma32(lds_col8<FWD_BN>(vt, L, 48, 32 * dt), pb3, o[dt]);
+      o[dt] = mfma32(lds_col8<E, FWD_BN>(vt, L, 0, 32 * dt), pb0, o[dt]);
+      o[dt] = mfma32(lds_col8<E, FWD_BN>(vt, L, 16, 32 * dt), pb1, o[dt]);
+      o[dt] = mfma32(lds_col8<E, FWD_BN>(vt, L, 32, 32 * dt), pb2, o[dt]);
+      o[dt] = mfma32(lds_col8<E, FWD_BN>(vt, L, 48, 32 * dt), pb3, o[dt]);
     }
   };
   // The first tiles (the workgroup's diagonal ones under the causal mask, or the ragged
@@ -254,38 +254,45 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const float l_tot = sum_halves(l_run);
   if (my_q < Lq) {
     const float inv = 1.f / l_tot;
-    bf16* orow = og + (int64_t)my_q * p.so.t;
+    E* orow = og + (int64_t)my_q * p.so.t;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        bf16x4 v;
+        vec4<E> v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[dt][4 * a + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * g) = v;
+        for (int e = 0; e < 4; ++e) v[e] = (E)(o[dt][4 * a + e] * inv);
+        *reinterpret_cast<vec4<E>*>(orow + 32 * dt + 8 * a + 4 * g) = v;
       }
     if (p.lse != nullptr && g == 0)
       p.lse[(int64_t)bh * T + my_q] = (m_run + log2_fast(l_tot)) * kLn2;
   } else if (my_q < T) {  // padding row of a padded batch: O = 0, LSE = -inf
-    bf16* orow = og + (int64_t)my_q * p.so.t;
+    E* orow = og + (int64_t)my_q * p.so.t;
 #pragma unroll
     for (int y = 0; y < DV / 8; ++y) *reinterpret_cast<u32x2*>(orow + 8 * y + 4 * g) = u32x2{0u, 0u};
     if (p.lse != nullptr && g == 0) p.lse[(int64_t)bh * T + my_q] = -INFINITY;
   }
 }
 
-template <int DQK, int DV, bool CAUSAL>
+template <class E, int DQK, int DV, bool CAUSAL>
 static hipError_t fwd_launch(const FwdParams& p, hipStream_t s) {
   const int nqb = (p.T + FWD_BM - 1) / FWD_BM;
-  hipLaunchKernelGGL((fwd_kernel<DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(FWD_NT), 0, s, p);
+  hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(FWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
-  if (d_qk == 64 && d_v == 64) return causal ? fwd_launch<64, 64, true>(p, s) : fwd_launch<64, 64, false>(p, s);
-  if (d_qk == 128 && d_v == 128) return causal ? fwd_launch<128, 128, true>(p, s) : fwd_launch<128, 128, false>(p, s);
-  if (d_qk == 192 && d_v == 128) return causal ? fwd_launch<192, 128, true>(p, s) : fwd_launch<192, 128, false>(p, s);
+template <class E>
+static hipError_t fwd_dispatch(const FwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
+  if (d_qk == 64 && d_v == 64) return causal ? fwd_launch<E, 64, 64, true>(p, s) : fwd_launch<E, 64, 64, false>(p, s);
+  if (d_qk == 128 && d_v == 128)
+    return causal ? fwd_launch<E, 128, 128, true>(p, s) : fwd_launch<E, 128, 128, false>(p, s);
+  if (d_qk == 192 && d_v == 128)
+    return causal ? fwd_launch<E, 192, 128, true>(p, s) : fwd_launch<E, 192, 128, false>(p, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(const FwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s) {
+  return et == ELEM_F16 ? fwd_dispatch<f16>(p, d_qk, d_v, causal, s) : fwd_dispatch<bf16>(p, d_qk, d_v, causal, s);
 }
 
 }  // namespace attn53

@@ -63,12 +63,16 @@ struct PlanParams {
 
 constexpr int kRowPad = 128;
 
+// 16-bit element type of Q, K, V, O, dO, dQ, dK, dV (one type per call).
+enum ElemType { ELEM_BF16 = 0, ELEM_F16 = 1 };
+
 // Launchers: return hipSuccess or the launch error.  d_qk/d_v already validated.
-hipError_t launch_fwd(const FwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s);
-hipError_t launch_bwd_preprocess(const BwdParams& p, int d_qk, int d_v, bool zero_acc, hipStream_t s);
-hipError_t launch_bwd_main(const BwdParams& p, int d_qk, int d_v, bool causal, bool deterministic, hipStream_t s);
-hipError_t launch_bwd_dq(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s);
-hipError_t launch_bwd_finalize(const BwdParams& p, int d_qk, hipStream_t s);
+hipError_t launch_fwd(const FwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s);
+hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int d_v, bool zero_acc, hipStream_t s);
+hipError_t launch_bwd_main(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, bool deterministic,
+                           hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s);
+hipError_t launch_bwd_finalize(const BwdParams& p, ElemType et, int d_qk, hipStream_t s);
 hipError_t launch_plan(const PlanParams& p, hipStream_t s);
 // Query rows per workgroup of the dQ kernel (its work list uses blocks of this size).
 int dq_block_rows(int d_qk);

@@ -217,6 +217,60 @@ attn_status attn_bwd_varlen(const void* q, attn_strides sq,
                             float scale, int causal, int deterministic,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * 16-bit element types.  The pages run attention with 16-bit inputs and outputs and
+ * fp32 accumulation, naming both fp16 and bf16 [SA8 1.3]; every entry point above takes
+ * bf16.  The two entry points below take either type, named by `dtype`, for all of q, k,
+ * v, o, do_, dq, dk and dv of one call (LSE, D and the workspace stay fp32).  With fp16,
+ * P and dS are rounded to fp16 (nearest even) before their products, as they are to bf16
+ * in the bf16 path; the arithmetic is otherwise the same.
+ */
+typedef enum {
+  ATTN_DTYPE_BF16 = 0,  /* bfloat16 (8-bit exponent, 8-bit significand) */
+  ATTN_DTYPE_F16 = 1    /* IEEE binary16 (5-bit exponent, 11-bit significand) */
+} attn_dtype;
+
+/*
+ * attn_fwd_typed — attn_fwd (seq_len_q == seq_len_kv == NULL; workspace unused and may
+ * be NULL) or attn_fwd_varlen (both lengths given; workspace as for attn_fwd_varlen) on
+ * tensors of element type `dtype`.  An unknown dtype returns ATTN_ERR_ARG; every other
+ * argument, layout rule and error is that of attn_fwd / attn_fwd_varlen.
+ */
+attn_status attn_fwd_typed(attn_dtype dtype,
+                           const void* q, attn_strides sq,
+                           const void* k, attn_strides sk,
+                           const void* v, attn_strides sv,
+                           void* o, attn_strides so,
+                           float* lse,
+                           const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                           int B, int NH, int T, int d_qk, int d_v,
+                           float scale, int causal,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_typed — attn_bwd_staged (seq_len_q == seq_len_kv == NULL) or the padded-batch
+ * backward (both lengths given) on tensors of element type `dtype`, restricted to the
+ * stages in `stages` (ATTN_BWD_ALL for the whole backward).  The workspace is sized by
+ * attn_bwd_workspace_bytes / attn_bwd_varlen_workspace_bytes, which do not depend on the
+ * element type.  An unknown dtype returns ATTN_ERR_ARG; every other argument, layout rule
+ * and error is that of attn_bwd_staged / attn_bwd_varlen.
+ */
+attn_status attn_bwd_typed(attn_dtype dtype,
+                           const void* q, attn_strides sq,
+                           const void* k, attn_strides sk,
+                           const void* v, attn_strides sv,
+                           const void* o, attn_strides so,
+                           const float* lse,
+                           const void* do_, attn_strides sdo,
+                           void* dq, attn_strides sdq,
+                           void* dk, attn_strides sdk,
+                           void* dv, attn_strides sdv,
+                           const int32_t* seq_len_q, const int32_t* seq_len_kv,
+                           int B, int NH, int T, int d_qk, int d_v,
+                           float scale, int causal, int deterministic,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           unsigned stages);
+
 #ifdef __cplusplus
 }
 #endif

@@ -126,3 +126,29 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.fwd(x, x, x)
+
+
+def test_typed_validation(lib):
+    """attn_fwd_typed / attn_bwd_typed: an unknown element type is rejected on the host;
+    known types reach the same validation as the bf16 entry points."""
+    st, sv = strides(64, 2, 64), strides(64, 2, 64)
+
+    def tfwd(dtype, q=GOOD, o=GOOD + 0x300000, lq=None, lk=None):
+        return lib.attn_fwd_typed(dtype, q, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, o, sv, None, lq, lk,
+                                  1, 2, 64, 64, 64, 0.125, 1, None, 0, None)
+
+    def tbwd(dtype, dq=GOOD + 0x600000, stages=7):
+        return lib.attn_bwd_typed(dtype, GOOD, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, GOOD + 0x300000, sv,
+                                  GOOD + 0x400000, GOOD + 0x500000, sv, dq, st, GOOD + 0x700000, st,
+                                  GOOD + 0x800000, sv, None, None, 1, 2, 64, 64, 64, 0.125, 1, 0,
+                                  GOOD + 0x900000, 1 << 30, None, stages)
+
+    for bad in (2, -1, 99):
+        assert tfwd(bad) == ARG
+        assert tbwd(bad) == ARG
+    for dt in (0, 1):
+        assert tfwd(dt, q=None) == NULL
+        assert tfwd(dt, o=GOOD) == ALIAS
+        assert tfwd(dt, lq=GOOD + 0xa00000) == NULL   # one length pointer without the other
+        assert tbwd(dt, dq=None) == NULL
+        assert tbwd(dt, stages=0) == ARG

@@ -12,7 +12,8 @@ configurations below stand in for those sweeps.
 
 Recipe (every workload):
   * values are float32 standard normals from ``torch.Generator().manual_seed(seed + k)``,
-    multiplied by sigma, then rounded to bfloat16 (round-to-nearest-even);
+    multiplied by sigma, then rounded to bfloat16 (round-to-nearest-even), or to
+    float16 for the fp16 element type;
   * k = 0, 1, 2, 3 draw Q, K, V, dO in that order (separate layout), or
     k = 0 draws the packed QKV block and k = 1 draws dO (packed layout);
   * sigma is a standard deviation (the GPT-2 case uses 0.5 for QKV, 1 for dO).
@@ -64,13 +65,13 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
-def _randn(shape, seed: int, sigma: float) -> torch.Tensor:
+def _randn(shape, seed: int, sigma: float, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     g = torch.Generator().manual_seed(seed)
-    return (torch.randn(shape, generator=g, dtype=torch.float32) * sigma).to(torch.bfloat16)
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * sigma).to(dtype)
 
 
-def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
-    """CPU bf16 tensors for one workload.
+def make_inputs(w: Workload, dtype: torch.dtype = torch.bfloat16) -> Dict[str, torch.Tensor]:
+    """CPU tensors of element type `dtype` (bf16 or fp16) for one workload.
 
     Returns q, k, v of shape (B, T, NH, d) (possibly strided views of a packed block,
     which is then also returned as ``qkv``) and do of shape (B, T, NH, d_v).
@@ -79,11 +80,11 @@ def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
     if w.packed:
         if w.d_qk != w.d_v:
             raise ValueError("packed QKV needs d_qk == d_v")
-        qkv = _randn((B, T, 3, NH, w.d_qk), w.seed + 0, w.sigma)
-        do = _randn((B, T, NH, w.d_v), w.seed + 1, w.sigma_do)
+        qkv = _randn((B, T, 3, NH, w.d_qk), w.seed + 0, w.sigma, dtype)
+        do = _randn((B, T, NH, w.d_v), w.seed + 1, w.sigma_do, dtype)
         return {"qkv": qkv, "q": qkv[:, :, 0], "k": qkv[:, :, 1], "v": qkv[:, :, 2], "do": do}
-    q = _randn((B, T, NH, w.d_qk), w.seed + 0, w.sigma)
-    k = _randn((B, T, NH, w.d_qk), w.seed + 1, w.sigma)
-    v = _randn((B, T, NH, w.d_v), w.seed + 2, w.sigma)
-    do = _randn((B, T, NH, w.d_v), w.seed + 3, w.sigma_do)
+    q = _randn((B, T, NH, w.d_qk), w.seed + 0, w.sigma, dtype)
+    k = _randn((B, T, NH, w.d_qk), w.seed + 1, w.sigma, dtype)
+    v = _randn((B, T, NH, w.d_v), w.seed + 2, w.sigma, dtype)
+    do = _randn((B, T, NH, w.d_v), w.seed + 3, w.sigma_do, dtype)
     return {"q": q, "k": k, "v": v, "do": do}
