@@ -9,6 +9,8 @@ each planted mistake trips at least one pin).
 Pages cited:
   [SA8] "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析", sections 1.2 (padding mask,
         seq_len_q, seq_len_kv), 2.1, 2.2, A.1-A.3.
+  [2CTA] "深度学习反向传播优化：2-CTA MMA模式与内存访问优化", sections 5.1, 5.2 (causal and
+        block-sparse mask patterns).
 """
 from __future__ import annotations
 
@@ -365,6 +367,79 @@ def pin_varlen_zero_queries(ref, causal: bool):
                    what=f"varlen zero queries LSE b={b} i={i}")
 
 
+# ---------------------------------------------------------------------------------
+# Sliding-window (banded causal) mask: query i sees keys i-W+1 .. i.  A mask pattern of
+# the block-sparse family of [2CTA 5.1, 5.2]; pinned by reductions and closed forms.
+# ---------------------------------------------------------------------------------
+def pin_window_wide_is_causal(ref):
+    """A window at least T wide masks nothing beyond the causal mask."""
+    q, k, v, do = _inputs(2, 21, 2, 16, 24, 861)
+    a = ref.attn_ref_bwd(q, k, v, do, True)
+    for W in (21, 40):
+        b = ref.attn_ref_bwd(q, k, v, do, True, window=W)
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            _close(b[n], a[n], rtol=1e-15, atol=1e-15, what=f"window {W} = causal {n}")
+
+
+def pin_window_one(ref):
+    """W = 1: every query sees only its own key, so P = I: O = V, LSE_i = scale <q_i, k_i>,
+    dV = dO, and dS = 0 (a softmax over one entry has zero derivative): dQ = dK = 0."""
+    q, k, v, do = _inputs(1, 17, 2, 16, 24, 863)
+    scale = 0.37
+    r = ref.attn_ref_bwd(q, k, v, do, True, scale, window=1)
+    _close(r["o"], v, rtol=1e-15, what="window 1 O")
+    _close(r["dv"], do, rtol=1e-15, what="window 1 dV")
+    _close(r["lse"], scale * np.einsum("bthd,bthd->bht", q, k), rtol=1e-14, what="window 1 LSE")
+    assert np.max(np.abs(r["dq"])) < 1e-13 and np.max(np.abs(r["dk"])) < 1e-13, "window 1: dQ, dK not zero"
+
+
+def pin_window_zero_queries(ref):
+    """Q = 0: P is uniform over the W most recent keys: O_i = mean of V rows
+    max(0, i-W+1) .. i, LSE_i = ln(min(i + 1, W))."""
+    _, k, v, _ = _inputs(1, 30, 2, 16, 24, 865)
+    q = np.zeros_like(k)
+    for W in (1, 4, 7):
+        o, lse = ref.attn_ref_fwd(q, k, v, True, window=W)
+        for i in range(30):
+            lo = max(0, i - W + 1)
+            _close(o[0, i], v[0, lo:i + 1].mean(axis=0), rtol=1e-14, what=f"window {W} zero queries O row {i}")
+            _close(lse[0, :, i], np.full(2, math.log(i + 1 - lo)), rtol=1e-14, atol=1e-15,
+                   what=f"window {W} zero queries LSE row {i}")
+
+
+def pin_window_loops(ref):
+    """Matrix form against the scalar loop nest, with the window in the loop bounds."""
+    q, k, v, do = _inputs(2, 23, 2, 16, 24, 867)
+    for W in (2, 5, 11):
+        dq, dk, dv, o, lse = ref.attn_ref_bwd_loop(q, k, v, do, True, window=W)
+        r = ref.attn_ref_bwd(q, k, v, do, True, window=W)
+        for n, x in (("dq", dq), ("dk", dk), ("dv", dv), ("o", o), ("lse", lse)):
+            _close(r[n], x, rtol=1e-12, atol=1e-14, what=f"window {W} loop form {n}")
+
+
+def pin_window_finite_differences(ref, h: float = 1e-6):
+    """dQ, dK, dV under the window equal central differences of sum(O * dO)."""
+    q, k, v, do = _inputs(1, 12, 1, 8, 8, 869)
+    W = 4
+    r = ref.attn_ref_bwd(q, k, v, do, True, window=W)
+
+    def f(qq, kk, vv):
+        return float(np.sum(ref.attn_ref_fwd(qq, kk, vv, True, window=W)[0] * do))
+
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        g = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if n == name else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+            args_m = [xm if n == name else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+            g[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        _close(r[name], g, rtol=1e-6, atol=1e-8, what=f"window finite differences {name}")
+
+
 ALL_PINS = [
     ("finite_differences_causal", lambda r: pin_finite_differences(r, True)),
     ("finite_differences_full", lambda r: pin_finite_differences(r, False)),
@@ -394,4 +469,9 @@ ALL_PINS = [
     ("varlen_zero_queries_full", lambda r: pin_varlen_zero_queries(r, False)),
     ("finite_differences_varlen_causal", lambda r: pin_varlen_finite_differences(r, True)),
     ("finite_differences_varlen_full", lambda r: pin_varlen_finite_differences(r, False)),
+    ("window_wide_is_causal", pin_window_wide_is_causal),
+    ("window_one", pin_window_one),
+    ("window_zero_queries", pin_window_zero_queries),
+    ("window_loops", pin_window_loops),
+    ("finite_differences_window", pin_window_finite_differences),
 ]

@@ -64,6 +64,8 @@ MUTANTS = {
     "varlen_keys_cut_at_query_length": ("qh, kh, vh = q[b, :lq, h], k[b, :lk, h], v[b, :lk, h]",
                                         "qh, kh, vh = q[b, :lq, h], k[b, :lq, h], v[b, :lq, h]"),
     "varlen_padding_lse_zero": ('"lse": np.full((B, NH, T), -np.inf)}', '"lse": np.zeros((B, NH, T))}'),
+    "window_off_by_one": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = np.where(qi - kj > window, -np.inf, S)"),
+    "window_ignored": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = S"),
 }
 
 
