@@ -81,9 +81,9 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_varlen.restype = i
     lib.attn_bwd_varlen.argtypes = bwd_args[:17] + [vp, vp] + bwd_args[17:]
     lib.attn_fwd_typed.restype = i
-    lib.attn_fwd_typed.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_fwd_typed.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.attn_bwd_typed.restype = i
-    lib.attn_bwd_typed.argtypes = [i] + bwd_args[:17] + [vp, vp] + bwd_args[17:] + [ctypes.c_uint]
+    lib.attn_bwd_typed.argtypes = [i] + bwd_args[:17] + [vp, vp] + bwd_args[17:24] + [i] + bwd_args[24:] + [ctypes.c_uint]
     _lib = lib
     return lib
 
@@ -136,9 +136,10 @@ def _stream(dev: torch.device) -> int:
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
         scale: Optional[float] = None, return_lse: bool = True, layout: str = "bthd",
-        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, window: int = 0):
     """Exact attention forward.  Returns (o, lse); lse is None when return_lse is False
-    (inference mode: the kernel skips the stats)."""
+    (inference mode: the kernel skips the stats).  window > 0 (causal only): query i sees
+    keys i-window+1 .. i."""
     lib = load()
     dev = q.device
     if dev.type != "cuda":
@@ -162,11 +163,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
                v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
                lse.data_ptr() if return_lse else None)
     with torch.cuda.device(dev):
-        if et == torch.bfloat16:
+        if et == torch.bfloat16 and window == 0:
             _check(lib.attn_fwd(*tensors, B, NH, T, dqk, dv, float(scale), int(bool(causal)), _stream(dev)))
         else:
             _check(lib.attn_fwd_typed(_DTYPE_CODE[et], *tensors, None, None, B, NH, T, dqk, dv, float(scale),
-                                      int(bool(causal)), None, 0, _stream(dev)))
+                                      int(bool(causal)), int(window), None, 0, _stream(dev)))
     return out, (lse if return_lse else None)
 
 
@@ -183,8 +184,9 @@ def workspace_bytes(B: int, NH: int, T: int, d_qk: int, d_v: int, deterministic:
 
 def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
         deterministic: bool = False, layout: str = "bthd", dq=None, dk=None, dv=None,
-        workspace: Optional[torch.Tensor] = None, stages: int = ALL_STAGES):
-    """Exact attention backward.  Returns (dq, dk, dv)."""
+        workspace: Optional[torch.Tensor] = None, stages: int = ALL_STAGES, window: int = 0):
+    """Exact attention backward.  Returns (dq, dk, dv).  window: the forward's sliding
+    window (0 = none)."""
     lib = load()
     dev = q.device
     if dev.type != "cuda":
@@ -211,13 +213,14 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
                lse.data_ptr(), do.data_ptr(), _strides(do, layout),
                dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
                dv.data_ptr(), _strides(dv, layout))
-    rest = (B, NH, T, dqk, dvd, float(scale), int(bool(causal)), int(bool(deterministic)), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), _stream(dev), int(stages))
+    dims = (B, NH, T, dqk, dvd, float(scale), int(bool(causal)))
+    rest = (int(bool(deterministic)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream(dev), int(stages))
     with torch.cuda.device(dev):
-        if et == torch.bfloat16:
-            _check(lib.attn_bwd_staged(*tensors, *rest))
+        if et == torch.bfloat16 and window == 0:
+            _check(lib.attn_bwd_staged(*tensors, *dims, *rest))
         else:
-            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *tensors, None, None, *rest))
+            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *tensors, None, None, *dims, int(window), *rest))
     return dq, dk, dv
 
 
@@ -275,7 +278,7 @@ def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causa
         if et == torch.bfloat16:
             _check(lib.attn_fwd_varlen(*args))
         else:
-            _check(lib.attn_fwd_typed(_DTYPE_CODE[et], *args))
+            _check(lib.attn_fwd_typed(_DTYPE_CODE[et], *args[:18], 0, *args[18:]))
     return out, lse
 
 
@@ -316,5 +319,5 @@ def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.T
         if et == torch.bfloat16:
             _check(lib.attn_bwd_varlen(*args))
         else:
-            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *args, ALL_STAGES))
+            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *args[:26], 0, *args[26:], ALL_STAGES))
     return dq, dk, dv

@@ -19,8 +19,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 # Each backward launcher configuration (kernel, element type, head dims, mask) is one
 # compilation of attn_bwd_inst.hip, so that they compile in parallel.
-INSTANCES = [(kind, elem, dqk, dv, causal) for kind in ("kv", "dq") for elem in ("bf16", "f16")
-             for dqk, dv in ((64, 64), (128, 128), (192, 128)) for causal in (True, False)]
+INSTANCES = [(kind, elem, dqk, dv, mask) for kind in ("kv", "dq") for elem in ("bf16", "f16")
+             for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in (0, 1, 2)]
 SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_plan.hip", "attn_api.cpp"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU instructions.
@@ -59,11 +59,11 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
         lang = [] if src.endswith(".hip") else ["-x", "hip"]
         cmds.append([hipcc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
-    for kind, elem, dqk, dv, causal in INSTANCES:
-        obj = os.path.join(BUILD_DIR, f"attn_bwd_{kind}_{elem}_{dqk}_{dv}_{'causal' if causal else 'full'}.o")
+    for kind, elem, dqk, dv, mask in INSTANCES:
+        obj = os.path.join(BUILD_DIR, f"attn_bwd_{kind}_{elem}_{dqk}_{dv}_{('full', 'causal', 'window')[mask]}.o")
         objs.append(obj)
         defs = [f"-DATTN_INST_DQ={int(kind == 'dq')}", f"-DATTN_INST_ELEM={elem}", f"-DATTN_INST_DQK={dqk}",
-                f"-DATTN_INST_DV={dv}", f"-DATTN_INST_CAUSAL={'true' if causal else 'false'}"]
+                f"-DATTN_INST_DV={dv}", f"-DATTN_INST_MASK={mask}"]
         cmds.append([hipcc, *FLAGS, *defs, "-c", os.path.join(CSRC, "attn_bwd_inst.hip"), "-o", obj])
     cmds.sort(key=lambda c: "attn_bwd_inst.hip" not in c[-3])  # longest compilations first
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 8)) as ex:

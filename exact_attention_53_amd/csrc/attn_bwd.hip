@@ -26,14 +26,23 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int 
   return et == ELEM_F16 ? pre_t<f16>(p, d_qk, d_v, zero_acc, s) : pre_t<bf16>(p, d_qk, d_v, zero_acc, s);
 }
 
+// mask mode of the launchers: 0 none, 1 causal, 2 causal with a sliding window
+static inline int mask_mode(const BwdParams& p, bool causal) { return !causal ? 0 : p.win < kNoWindow ? 2 : 1; }
+
+template <class E, int DQK, int DV>
+static hipError_t main_m(const BwdParams& p, bool causal, bool det, hipStream_t s) {
+  switch (mask_mode(p, causal)) {
+    case 0: return bwd_main_t<E, DQK, DV, 0>(p, det, s);
+    case 1: return bwd_main_t<E, DQK, DV, 1>(p, det, s);
+    default: return bwd_main_t<E, DQK, DV, 2>(p, det, s);
+  }
+}
+
 template <class E>
 static hipError_t main_t(const BwdParams& p, int d_qk, int d_v, bool causal, bool det, hipStream_t s) {
-  if (d_qk == 64 && d_v == 64)
-    return causal ? bwd_main_t<E, 64, 64, true>(p, det, s) : bwd_main_t<E, 64, 64, false>(p, det, s);
-  if (d_qk == 128 && d_v == 128)
-    return causal ? bwd_main_t<E, 128, 128, true>(p, det, s) : bwd_main_t<E, 128, 128, false>(p, det, s);
-  if (d_qk == 192 && d_v == 128)
-    return causal ? bwd_main_t<E, 192, 128, true>(p, det, s) : bwd_main_t<E, 192, 128, false>(p, det, s);
+  if (d_qk == 64 && d_v == 64) return main_m<E, 64, 64>(p, causal, det, s);
+  if (d_qk == 128 && d_v == 128) return main_m<E, 128, 128>(p, causal, det, s);
+  if (d_qk == 192 && d_v == 128) return main_m<E, 192, 128>(p, causal, det, s);
   return hipErrorInvalidValue;
 }
 
@@ -43,13 +52,20 @@ hipError_t launch_bwd_main(const BwdParams& p, ElemType et, int d_qk, int d_v, b
                         : main_t<bf16>(p, d_qk, d_v, causal, deterministic, s);
 }
 
+template <class E, int DQK, int DV>
+static hipError_t dq_m(const BwdParams& p, bool causal, hipStream_t s) {
+  switch (mask_mode(p, causal)) {
+    case 0: return bwd_dq_t<E, DQK, DV, 0>(p, s);
+    case 1: return bwd_dq_t<E, DQK, DV, 1>(p, s);
+    default: return bwd_dq_t<E, DQK, DV, 2>(p, s);
+  }
+}
+
 template <class E>
 static hipError_t dq_t(const BwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
-  if (d_qk == 64 && d_v == 64) return causal ? bwd_dq_t<E, 64, 64, true>(p, s) : bwd_dq_t<E, 64, 64, false>(p, s);
-  if (d_qk == 128 && d_v == 128)
-    return causal ? bwd_dq_t<E, 128, 128, true>(p, s) : bwd_dq_t<E, 128, 128, false>(p, s);
-  if (d_qk == 192 && d_v == 128)
-    return causal ? bwd_dq_t<E, 192, 128, true>(p, s) : bwd_dq_t<E, 192, 128, false>(p, s);
+  if (d_qk == 64 && d_v == 64) return dq_m<E, 64, 64>(p, causal, s);
+  if (d_qk == 128 && d_v == 128) return dq_m<E, 128, 128>(p, causal, s);
+  if (d_qk == 192 && d_v == 128) return dq_m<E, 192, 128>(p, causal, s);
   return hipErrorInvalidValue;
 }
 

@@ -2,15 +2,15 @@
 // configurations compile in parallel.  The build defines
 //   ATTN_INST_DQ     0: key/value kernel (bwd_main_t), 1: dQ kernel (bwd_dq_t)
 //   ATTN_INST_ELEM   bf16 or f16
-//   ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_CAUSAL (true / false)
+//   ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_MASK (0 none, 1 causal, 2 causal + sliding window)
 #include "attn_bwd_kernels.hpp"
 
 namespace attn53 {
 #if ATTN_INST_DQ
-template hipError_t bwd_dq_t<ATTN_INST_ELEM, ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_CAUSAL>(const BwdParams&,
+template hipError_t bwd_dq_t<ATTN_INST_ELEM, ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_MASK>(const BwdParams&,
                                                                                           hipStream_t);
 #else
-template hipError_t bwd_main_t<ATTN_INST_ELEM, ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_CAUSAL>(const BwdParams&, bool,
+template hipError_t bwd_main_t<ATTN_INST_ELEM, ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_MASK>(const BwdParams&, bool,
                                                                                             hipStream_t);
 #endif
 }  // namespace attn53

@@ -173,7 +173,8 @@ struct KvPlan {
   static_assert(plan.ok, "no feasible placement of the step's VALU work");
 };
 
-template <class E, int DQK, int DV, bool CAUSAL, bool ATOMIC_DQ>
+// WIN (with CAUSAL only): sliding window of p.win keys.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ATOMIC_DQ>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
@@ -226,8 +227,11 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   E* dkg = (E*)p.dk + b * p.sdk.b + h * p.sdk.h;
   E* dvg = (E*)p.dv + b * p.sdv.b + h * p.sdv.h;
 
+  const int W = WIN ? p.win : kNoWindow;
   const int i0 = CAUSAL ? key0 / BWD_BM : 0;
-  const int n_q = nqb - i0;
+  // sliding window: query blocks past i_end hold no query whose window reaches this block
+  const int i_end = WIN ? min(nqb, (key0 + BWD_BN - 1 + W - 1) / BWD_BM + 1) : nqb;
+  const int n_q = i_end - i0;
   if (key0 >= Lk || n_q <= 0) {  // padding keys only, or no query sees them: dK = dV = 0
     if (my_key < T) {
 #pragma unroll
@@ -323,8 +327,9 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const ATTN_LDS char* ot = (const ATTN_LDS char*)(BUF ? obuf1 : obuf0);
     const float* lb = BUF ? lse1 : lse0;
     const float* db = BUF ? dd1 : dd0;
-    if (MASKED && CAUSAL && key0 + kw > q0 + BWD_BM - 1) {
-      // every key of this wavefront lies above every query of the block: P = dS = 0
+    if (MASKED && CAUSAL && (key0 + kw > q0 + BWD_BM - 1 || (WIN && q0 - (key0 + kw + 31) >= W))) {
+      // every key of this wavefront lies above every query of the block, or below every
+      // query's window: P = dS = 0
       if constexpr (ATOMIC_DQ) {
         if constexpr (!ST_DOUBLE) __syncthreads();
 #pragma unroll
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             const int r = 4 * a + e;
             const int q = q0 + qi + e;
             const float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -Lv[e]));
-            s[t][r] = (my_key >= Lk || q >= Lq || (CAUSAL && my_key > q)) ? 0.f : pv;
+            s[t][r] = (my_key >= Lk || q >= Lq || (CAUSAL && (my_key > q || (WIN && q - my_key >= W)))) ? 0.f : pv;
           }
         }
 #pragma unroll
@@ -491,7 +496,10 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const bool ragged_keys = key0 + BWD_BN > Lk;
   const int n_head = ragged_keys ? n_q : (CAUSAL ? min(BWD_BN / BWD_BM, n_q) : 0);  // even, or n_q
   const int n_tail = (n_head < n_q && Lq % BWD_BM != 0) ? 1 : 0;
-  const int mid_end = n_q - n_tail;
+  // sliding window: steps from win_start on hold a query past the window of key0
+  const int x_win = key0 + W - BWD_BM + 1;
+  const int win_start = WIN ? max(n_head, (x_win <= 0 ? 0 : (x_win + BWD_BM - 1) / BWD_BM) - i0) : n_q;
+  const int mid_end = WIN ? min(n_q - n_tail, win_start) : n_q - n_tail;
   for (int it = 0; it < n_head; it += 2) {
     step(it, B0, MASK);
     if (it + 1 < n_head) step(it + 1, B1, MASK);
@@ -502,7 +510,14 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     step(it + 1, B1, NOMASK);
   }
   if (it < mid_end) step(it++, B0, NOMASK);
-  if (it < n_q) {
+  if constexpr (WIN) {
+    for (; it < n_q; ++it) {
+      if (it & 1)
+        step(it, B1, MASK);
+      else
+        step(it, B0, MASK);
+    }
+  } else if (it < n_q) {
     if (it & 1)
       step(it, B1, MASK);
     else
@@ -612,7 +627,8 @@ struct DqShape {
   static constexpr int WAVES_PER_EU = 1;
 };
 
-template <class E, int DQK, int DV, bool CAUSAL>
+// WIN (with CAUSAL only): sliding window of p.win keys.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
                                                                          DqShape<DQK>::WAVES_PER_EU)))
 void bwd_dq_kernel(BwdParams p) {
@@ -655,8 +671,12 @@ void bwd_dq_kernel(BwdParams p) {
   const LdsLane L = lds_lane(lane);
   const int q0 = qb * BM, qw = q0 + 32 * QT * w;  // first row of this wavefront
   const float c = p.scale_log2;
+  const int W = WIN ? p.win : kNoWindow;
   const int kv_end = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int n_kv = (kv_end + DQ_BN - 1) / DQ_BN;
+  // sliding window: tiles below j_lo hold no key of any row's window
+  const int j_lo = WIN ? max(0, q0 - W + 1) / DQ_BN : 0;
+  const int n_tiles = n_kv - j_lo;
   if (q0 >= Lq || n_kv == 0) {  // padding rows only, or no keys: dQ = 0
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
@@ -740,7 +760,8 @@ void bwd_dq_kernel(BwdParams p) {
           float pv = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
           if constexpr (MASKED) {
             const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            pv = (key >= Lk || (CAUSAL && key > qw + 32 * u + lq)) ? 0.f : pv;
+            const int q = qw + 32 * u + lq;
+            pv = (key >= Lk || (CAUSAL && (key > q || (WIN && q - key >= W)))) ? 0.f : pv;
           }
           s[t][u][r] = pv;
         }
@@ -861,17 +882,33 @@ void bwd_dq_kernel(BwdParams p) {
     });
   };
 
-  load_kv((n_kv - 1) * DQ_BN, std::integral_constant<int, 0>{});
+  // Fixed visiting order: the masked tiles first (those at or above the diagonal or past
+  // Lk, then those under the window's lower edge, each descending), then the unmasked
+  // ones, descending.  Tiles j >= first_masked hold keys past Lk or past some row's
+  // diagonal; tiles j_lo <= j < j_mid hold keys below some row's window.
+  const int first_ragged = Lk % DQ_BN != 0 ? Lk / DQ_BN : n_kv;
+  const int first_masked = min(min(first_ragged, CAUSAL ? q0 / DQ_BN : n_kv), n_kv);
+  const int j_mid = WIN ? max(j_lo, min((max(0, q0 + BM - W) + DQ_BN - 1) / DQ_BN, first_masked)) : j_lo;
+  const int n_head = n_kv - first_masked;
+  const int n_msk = n_head + (j_mid - j_lo);
+  auto tile_of = [&](int it) {
+    if constexpr (WIN)
+      return it < n_head ? n_kv - 1 - it : it < n_msk ? j_mid - 1 - (it - n_head) : first_masked - 1 - (it - n_msk);
+    else
+      return n_kv - 1 - it;
+  };
+  load_kv(tile_of(0) * DQ_BN, std::integral_constant<int, 0>{});
   auto step = [&](int it, auto bufc, auto maskc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
-    const int j = n_kv - 1 - it;  // fixed order: descending key block
+    const int j = tile_of(it);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + 1 < n_kv) load_kv((j - 1) * DQ_BN, std::integral_constant<int, 1 - BUF>{});
+    if (it + 1 < n_tiles) load_kv(tile_of(it + 1) * DQ_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * DQ_BN;
     if constexpr (decltype(maskc)::value) {
       if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
-      if ((CAUSAL && key0 + DQ_BN - 1 > qw) || key0 + DQ_BN > Lk)
+      if (WIN && key0 + DQ_BN <= qw - W + 1) return;  // tile wholly below its rows' windows
+      if ((CAUSAL && (key0 + DQ_BN - 1 > qw || (WIN && key0 < qw + 32 * QT - W))) || key0 + DQ_BN > Lk)
         tile_body(key0, bufc, std::true_type{});
       else
         tile_body(key0, bufc, std::false_type{});
@@ -882,25 +919,21 @@ void bwd_dq_kernel(BwdParams p) {
   // The first tiles (the workgroup's diagonal ones under the causal mask, or the ragged
   // last key block) may carry a mask for some wavefront; they run as plain code, the
   // rest as the pipeline.
-  // Tiles j >= first_masked (visited first) hold keys past Lk or past some row's diagonal.
-  const int first_ragged = Lk % DQ_BN != 0 ? Lk / DQ_BN : n_kv;
-  const int first_masked = min(min(first_ragged, CAUSAL ? q0 / DQ_BN : n_kv), n_kv);
-  const int n_head = n_kv - first_masked;
   constexpr auto B0 = std::integral_constant<int, 0>{};
   constexpr auto B1 = std::integral_constant<int, 1>{};
   int it = 0;
-  for (; it < n_head; ++it) {
+  for (; it < n_msk; ++it) {
     if (it & 1)
       step(it, B1, std::true_type{});
     else
       step(it, B0, std::true_type{});
   }
-  if ((it & 1) && it < n_kv) step(it++, B1, std::false_type{});
-  for (; it + 1 < n_kv; it += 2) {
+  if ((it & 1) && it < n_tiles) step(it++, B1, std::false_type{});
+  for (; it + 1 < n_tiles; it += 2) {
     step(it, B0, std::false_type{});
     step(it + 1, B1, std::false_type{});
   }
-  if (it < n_kv) step(it, B0, std::false_type{});
+  if (it < n_tiles) step(it, B0, std::false_type{});
 
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
@@ -950,30 +983,34 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------------
 // per-configuration launchers (each instantiated by one compilation of attn_bwd_inst.hip)
 // ---------------------------------------------------------------------------------
-template <class E, int DQK, int DV, bool CAUSAL>
+// MASK: 0 none, 1 causal, 2 causal with a sliding window of p.win keys.
+template <class E, int DQK, int DV, int MASK>
 hipError_t bwd_main_t(const BwdParams& p, bool deterministic, hipStream_t s) {
+  constexpr bool CAUSAL = MASK >= 1, WIN = MASK == 2;
   const int nkb = (p.T + BWD_BN - 1) / BWD_BN;
   const dim3 grid_kv(nkb * p.B * p.NH);
   if (deterministic)
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, false>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, false>), grid_kv, dim3(BWD_NT), 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, true>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, true>), grid_kv, dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
-template <class E, int DQK, int DV, bool CAUSAL>
+template <class E, int DQK, int DV, int MASK>
 hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
+  constexpr bool CAUSAL = MASK >= 1, WIN = MASK == 2;
   const int nqb = (p.T + DqShape<DQK>::BM - 1) / DqShape<DQK>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, CAUSAL, WIN>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
 #define ATTN_BWD_CONFIGS(X) \
-  X(64, 64, true) X(64, 64, false) X(128, 128, true) X(128, 128, false) X(192, 128, true) X(192, 128, false)
-#define ATTN_EXTERN_BWD_E(E, DQK, DV, CAUSAL)                                                       \
-  extern template hipError_t bwd_main_t<E, DQK, DV, CAUSAL>(const BwdParams&, bool, hipStream_t); \
-  extern template hipError_t bwd_dq_t<E, DQK, DV, CAUSAL>(const BwdParams&, hipStream_t);
-#define ATTN_EXTERN_BWD(DQK, DV, CAUSAL) ATTN_EXTERN_BWD_E(bf16, DQK, DV, CAUSAL) ATTN_EXTERN_BWD_E(f16, DQK, DV, CAUSAL)
+  X(64, 64, 0) X(64, 64, 1) X(64, 64, 2) X(128, 128, 0) X(128, 128, 1) X(128, 128, 2) \
+  X(192, 128, 0) X(192, 128, 1) X(192, 128, 2)
+#define ATTN_EXTERN_BWD_E(E, DQK, DV, MASK)                                                       \
+  extern template hipError_t bwd_main_t<E, DQK, DV, MASK>(const BwdParams&, bool, hipStream_t); \
+  extern template hipError_t bwd_dq_t<E, DQK, DV, MASK>(const BwdParams&, hipStream_t);
+#define ATTN_EXTERN_BWD(DQK, DV, MASK) ATTN_EXTERN_BWD_E(bf16, DQK, DV, MASK) ATTN_EXTERN_BWD_E(f16, DQK, DV, MASK)
 ATTN_BWD_CONFIGS(ATTN_EXTERN_BWD)
 
 }  // namespace attn53

@@ -29,7 +29,10 @@
 // only rescaled, when a row's maximum grows by more than 2^8; between raises p <= 2^8.
 // The result O = O^T / l and LSE = ln 2 (m + log2 l) do not depend on when m was raised.
 // Causal: tiles wholly above the diagonal are never loaded; the diagonal tile(s) come
-// first; a wavefront skips tiles that lie wholly above its rows.
+// first; a wavefront skips tiles that lie wholly above its rows.  With a sliding window
+// (query i sees keys i-W+1 .. i) the tiles wholly below the band are never loaded
+// either; the band's lower edge is masked on the last tiles, which run after the
+// unmasked ones, and a wavefront skips tiles wholly below its rows' windows.
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -43,7 +46,8 @@ constexpr int FWD_NT = 256;
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 constexpr float kSumLimit = 256.f;        // 2^kRescaleThreshold
 
-template <class E, int DQK, int DV, bool CAUSAL>
+// WIN (with CAUSAL only): sliding window of p.win keys.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr int KS = DQK / 16;
   constexpr int NDT = DV / 32;
@@ -85,8 +89,12 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int q0 = qb * FWD_BM;
   const int qw = q0 + 32 * w;
   const int my_q = qw + lq;
+  const int W = WIN ? p.win : kNoWindow;
   const int kv_end = CAUSAL ? min(Lk, q0 + FWD_BM) : Lk;
   const int n_kv = (kv_end + FWD_BN - 1) / FWD_BN;
+  // sliding window: tiles below j_lo hold no key of any row's window
+  const int j_lo = WIN ? max(0, q0 - W + 1) / FWD_BN : 0;
+  const int n_tiles = n_kv - j_lo;
   if (q0 >= Lq || n_kv == 0) {  // padding rows only, or no keys: O = 0, LSE = -inf
     if (my_q < T) {
       E* orow = og + (int64_t)my_q * p.so.t;
@@ -133,9 +141,10 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     const int j = n_kv - 1 - it;  // diagonal / tail tile first
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile j has landed in LDS
     __syncthreads();                // ... and every other wave's; the other buffer is free
-    if (it + 1 < n_kv) load_kv((j - 1) * FWD_BN, std::integral_constant<int, 1 - BUF>{});
+    if (it + 1 < n_tiles) load_kv((j - 1) * FWD_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * FWD_BN;
     if (MASKED && CAUSAL && key0 > qw + 31) return;  // tile wholly above this wavefront's rows
+    if (MASKED && WIN && key0 + FWD_BN <= qw - W + 1) return;  // wholly below its windows
     const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
     const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
     // S^T = K Q^T for keys key0 .. key0+63 (two 32-key accumulators)
@@ -152,14 +161,16 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk0 = key0 + 8 * (r >> 2) + 4 * g + (r & 3), kk1 = kk0 + 32;
-          if (kk0 >= Lk || (CAUSAL && kk0 > my_q)) s0[r] = -INFINITY;
-          if (kk1 >= Lk || (CAUSAL && kk1 > my_q)) s1[r] = -INFINITY;
+          if (kk0 >= Lk || (CAUSAL && (kk0 > my_q || (WIN && my_q - kk0 >= W)))) s0[r] = -INFINITY;
+          if (kk1 >= Lk || (CAUSAL && (kk1 > my_q || (WIN && my_q - kk1 >= W)))) s1[r] = -INFINITY;
         }
       }
     };
     // The tile's row maximum (scaled, log2 units).  The IEEE maximum (NaN-propagating)
-    // maps onto v_maximum3_f32 with no canonicalising moves of the MFMA results.  Every
-    // processed tile holds key key0 <= every row of this wave, so it is finite.
+    // maps onto v_maximum3_f32 with no canonicalising moves of the MFMA results.  The
+    // first tile a wave processes holds every one of its rows' own keys, so the running
+    // max is finite from then on; a later tile under the window's lower edge may hold no
+    // key of a row (its maximum is -inf, which never raises the running max).
     auto tile_max = [&]() __attribute__((always_inline)) {
       float mx = -INFINITY;
 #pragma unroll
@@ -232,10 +243,13 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr auto B1 = std::integral_constant<int, 1>{};
   constexpr auto MASK = std::true_type{};
   constexpr auto NOMASK = std::false_type{};
-  // Tiles j >= first_masked (visited first) hold keys past Lk or past some row's diagonal.
+  // Tiles j >= first_masked (visited first) hold keys past Lk or past some row's diagonal;
+  // tiles j < j_full (visited last) hold keys below some row's window.
   const int first_ragged = Lk % FWD_BN != 0 ? Lk / FWD_BN : n_kv;
   const int first_masked = min(min(first_ragged, CAUSAL ? q0 / FWD_BN : n_kv), n_kv);
+  const int j_full = WIN ? min((max(0, q0 + FWD_BM - W) + FWD_BN - 1) / FWD_BN, first_masked) : 0;
   const int n_mask = n_kv - first_masked;
+  const int mid_end = WIN ? n_tiles - max(0, j_full - j_lo) : n_kv;
   int it = 0;
   for (; it < n_mask; ++it) {
     if (it & 1)
@@ -243,12 +257,20 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     else
       step(it, B0, MASK);
   }
-  if ((it & 1) && it < n_kv) step(it++, B1, NOMASK);
-  for (; it + 1 < n_kv; it += 2) {
+  if ((it & 1) && it < mid_end) step(it++, B1, NOMASK);
+  for (; it + 1 < mid_end; it += 2) {
     step(it, B0, NOMASK);
     step(it + 1, B1, NOMASK);
   }
-  if (it < n_kv) step(it, B0, NOMASK);
+  if (it < mid_end) step(it++, B0, NOMASK);
+  if constexpr (WIN) {
+    for (; it < n_tiles; ++it) {
+      if (it & 1)
+        step(it, B1, MASK);
+      else
+        step(it, B0, MASK);
+    }
+  }
 
   // deferred normalisation and stats
   const float l_tot = sum_halves(l_run);
@@ -274,20 +296,23 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   }
 }
 
-template <class E, int DQK, int DV, bool CAUSAL>
-static hipError_t fwd_launch(const FwdParams& p, hipStream_t s) {
-  const int nqb = (p.T + FWD_BM - 1) / FWD_BM;
-  hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, CAUSAL>), dim3(nqb * p.B * p.NH), dim3(FWD_NT), 0, s, p);
+template <class E, int DQK, int DV>
+static hipError_t fwd_launch(const FwdParams& p, bool causal, hipStream_t s) {
+  const dim3 grid((p.T + FWD_BM - 1) / FWD_BM * p.B * p.NH);
+  if (!causal)
+    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, false, false>), grid, dim3(FWD_NT), 0, s, p);
+  else if (p.win < kNoWindow)
+    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, true>), grid, dim3(FWD_NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, false>), grid, dim3(FWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
 template <class E>
 static hipError_t fwd_dispatch(const FwdParams& p, int d_qk, int d_v, bool causal, hipStream_t s) {
-  if (d_qk == 64 && d_v == 64) return causal ? fwd_launch<E, 64, 64, true>(p, s) : fwd_launch<E, 64, 64, false>(p, s);
-  if (d_qk == 128 && d_v == 128)
-    return causal ? fwd_launch<E, 128, 128, true>(p, s) : fwd_launch<E, 128, 128, false>(p, s);
-  if (d_qk == 192 && d_v == 128)
-    return causal ? fwd_launch<E, 192, 128, true>(p, s) : fwd_launch<E, 192, 128, false>(p, s);
+  if (d_qk == 64 && d_v == 64) return fwd_launch<E, 64, 64>(p, causal, s);
+  if (d_qk == 128 && d_v == 128) return fwd_launch<E, 128, 128>(p, causal, s);
+  if (d_qk == 192 && d_v == 128) return fwd_launch<E, 192, 128>(p, causal, s);
   return hipErrorInvalidValue;
 }
 

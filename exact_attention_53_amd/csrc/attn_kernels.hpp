@@ -18,6 +18,8 @@ struct FwdParams {
   float* lse;              // (B, NH, T) or nullptr
   int B, NH, T;
   float scale_log2;        // scale * log2(e)
+  int win;                 // causal sliding window: query i sees keys i-win+1 .. i
+                           // (1 << 30 when there is no window)
   // Padded batches (all three set, or all nullptr): valid query / key rows per batch
   // (B int32 each; clamped to [0, T]) and the sorted work list of (b, query block).
   const int* seq_q;
@@ -38,6 +40,7 @@ struct BwdParams {
   int B, NH, T, Tpad;      // Tpad = T rounded up to kRowPad
   float scale;
   float scale_log2;
+  int win;                 // causal sliding window as in FwdParams
   float* D;                // workspace: (B, NH, Tpad) fp32, rowsum(dO * O)
   float* lse2;             // workspace: (B, NH, Tpad) fp32, LSE * log2(e) (+inf on padding)
   float* dq_acc;           // workspace: (B, NH, Tpad, d_qk) fp32, atomic mode only
@@ -62,6 +65,7 @@ struct PlanParams {
 };
 
 constexpr int kRowPad = 128;
+constexpr int kNoWindow = 1 << 30;  // a window wider than any sequence
 
 // 16-bit element type of Q, K, V, O, dO, dQ, dK, dV (one type per call).
 enum ElemType { ELEM_BF16 = 0, ELEM_F16 = 1 };

@@ -231,10 +231,21 @@ typedef enum {
 } attn_dtype;
 
 /*
+ * Sliding window (`window` argument of the two entry points below).  0: no window.
+ * W >= 1: a banded causal mask, query i sees keys i-W+1 .. i only — the simplest of the
+ * block-sparse mask patterns that the FA4 framework composes with causal masking
+ * [2CTA 5.1, 5.2].  Tiles wholly outside the band are never loaded; only tiles that the
+ * band's edges cross carry a mask.  W >= 1 needs causal = 1 and no padded-batch lengths,
+ * W < 0 is invalid: otherwise ATTN_ERR_ARG.  Every row keeps at least its own key, so
+ * the LSE and the outputs stay finite; the backward must get the forward's window.
+ */
+
+/*
  * attn_fwd_typed — attn_fwd (seq_len_q == seq_len_kv == NULL; workspace unused and may
  * be NULL) or attn_fwd_varlen (both lengths given; workspace as for attn_fwd_varlen) on
- * tensors of element type `dtype`.  An unknown dtype returns ATTN_ERR_ARG; every other
- * argument, layout rule and error is that of attn_fwd / attn_fwd_varlen.
+ * tensors of element type `dtype`, with an optional sliding window.  An unknown dtype
+ * returns ATTN_ERR_ARG; every other argument, layout rule and error is that of
+ * attn_fwd / attn_fwd_varlen.
  */
 attn_status attn_fwd_typed(attn_dtype dtype,
                            const void* q, attn_strides sq,
@@ -244,12 +255,13 @@ attn_status attn_fwd_typed(attn_dtype dtype,
                            float* lse,
                            const int32_t* seq_len_q, const int32_t* seq_len_kv,
                            int B, int NH, int T, int d_qk, int d_v,
-                           float scale, int causal,
+                           float scale, int causal, int window,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_bwd_typed — attn_bwd_staged (seq_len_q == seq_len_kv == NULL) or the padded-batch
- * backward (both lengths given) on tensors of element type `dtype`, restricted to the
+ * backward (both lengths given) on tensors of element type `dtype`, with the forward's
+ * sliding window (0 = none), restricted to the
  * stages in `stages` (ATTN_BWD_ALL for the whole backward).  The workspace is sized by
  * attn_bwd_workspace_bytes / attn_bwd_varlen_workspace_bytes, which do not depend on the
  * element type.  An unknown dtype returns ATTN_ERR_ARG; every other argument, layout rule
@@ -267,7 +279,7 @@ attn_status attn_bwd_typed(attn_dtype dtype,
                            void* dv, attn_strides sdv,
                            const int32_t* seq_len_q, const int32_t* seq_len_kv,
                            int B, int NH, int T, int d_qk, int d_v,
-                           float scale, int causal, int deterministic,
+                           float scale, int causal, int window, int deterministic,
                            void* workspace, size_t workspace_bytes, void* stream,
                            unsigned stages);
 

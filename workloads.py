@@ -40,6 +40,7 @@ class Workload:
     sigma: float = 1.0       # std of Q, K, V
     sigma_do: float = 1.0    # std of dO
     packed: bool = False     # Q, K, V are views of one (B, T, 3, NH, HS) tensor
+    window: int = 0          # causal sliding window: query i sees keys i-window+1 .. i (0 = none)
 
     @property
     def scale(self) -> float:
@@ -47,7 +48,11 @@ class Workload:
 
     def pairs(self) -> int:
         """Unmasked (query, key) pairs over all heads."""
-        per_head = self.T * (self.T + 1) // 2 if self.causal else self.T * self.T
+        T, W = self.T, self.window
+        if self.causal and 0 < W < T:  # rows i < W see i + 1 keys, the others W
+            per_head = W * (W + 1) // 2 + (T - W) * W
+        else:
+            per_head = T * (T + 1) // 2 if self.causal else T * T
         return self.B * self.NH * per_head
 
     def with_(self, **kw) -> "Workload":
@@ -62,6 +67,8 @@ WORKLOADS: Dict[str, Workload] = {
     "long": Workload("long", 1, 16, 32768, 128, 128, True, 53004),
     "asym": Workload("asym", 4, 16, 8192, 192, 128, True, 53005),
     "headline": Workload("headline", 4, 16, 8192, 128, 128, True, 53006),
+    # the headline shape under a 1024-key sliding window (local attention)
+    "window": Workload("window", 4, 16, 8192, 128, 128, True, 53007, window=1024),
 }
 
 
