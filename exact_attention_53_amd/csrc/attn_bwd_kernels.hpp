@@ -175,7 +175,7 @@ struct KvPlan {
 
 // WIN (with CAUSAL only): sliding window of p.win keys.
 template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ATOMIC_DQ>
-__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_kernel(BwdParams p) {
+__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 64 ? 2 : 1, DQK == 64 ? 2 : 1))) void bwd_kv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
   constexpr int NDQ = DQK / 32 / 2;  // dQ tiles per wavefront
@@ -548,9 +548,11 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 // ---------------------------------------------------------------------------------
 // One workgroup of 4 wavefronts per DQ_QT * 128 query rows; each wavefront owns
 // DQ_QT tiles of 32 rows, held in registers as B operands together with their dO rows,
-// LSE and D.  With two tiles per wavefront (d_qk <= 128; one wavefront per SIMD) every
+// LSE and D.  With two tiles per wavefront (d_qk = 128; one wavefront per SIMD) every
 // K or V fragment read from LDS feeds two products; with d_qk = 192 a wavefront owns
-// one tile (two do not fit in 512 registers).  Key/value tiles of 64 rows stream through
+// one tile (two do not fit in 512 registers); with d_qk = 64 a wavefront owns one tile
+// and two wavefronts share a SIMD (short sequences: twice the workgroups, half the
+// work per workgroup).  Key/value tiles of 64 rows stream through
 // double-buffered LDS by direct loads, in descending order.  Per tile:
 // S^T = K Q^T and dP^T = V dO^T, P^T = 2^(S^T c - LSE log2 e), dS^T = P^T (dP^T - D),
 // dQ^T += K^T dS^T with the K^T operand read column-wise.  Every dQ row is summed over
@@ -620,11 +622,12 @@ struct DqPlan {
 
 template <int DQK>
 struct DqShape {
-  static constexpr int QT = DQK <= 128 ? 2 : 1;  // 32-row query tiles per wavefront
+  static constexpr int QT = DQK == 128 ? 2 : 1;  // 32-row query tiles per wavefront
   static constexpr int BM = 128 * QT;            // query rows per workgroup
-  // one wavefront per SIMD (up to 512 registers): with d_qk = 192 and one tile, two
-  // wavefronts per SIMD (256 registers each) spill about 370 registers per lane
-  static constexpr int WAVES_PER_EU = 1;
+  // d_qk = 128, 192: one wavefront per SIMD (up to 512 registers; with d_qk = 192 and
+  // one tile, two wavefronts per SIMD of 256 registers each spill about 370 registers per
+  // lane); d_qk = 64 with one tile fits 256 registers, so two wavefronts share a SIMD
+  static constexpr int WAVES_PER_EU = DQK == 64 ? 2 : 1;
 };
 
 // WIN (with CAUSAL only): sliding window of p.win keys.
