@@ -4,6 +4,7 @@ Only the test suite, the smoke check and the bench's CPU-baseline leg may import
 this package; the GPU library never does.
 """
 from .attn_ref import (  # noqa: F401
+    alibi_slopes,
     attn_ref_bwd,
     attn_ref_bwd_loop,
     attn_ref_fwd,

@@ -21,6 +21,10 @@ What is computed (the plain definition, S and P materialised, float64 throughout
             sliding window (causal only, window W >= 1): additionally S[i, j] = -inf
             for i - j >= W, so query i sees keys i-W+1 .. i — a banded mask, the
             simplest of the block-sparse mask patterns of [2CTA 5.1, 5.2]
+            ALiBi (causal only; the use_alibi_mask option of [SA8 1.2]): additionally
+            S[i, j] -= m_h (i - j) with the head slopes m_h = 2^(-8 (h+1) / NH) of the
+            linear-bias scheme (the page names the option but not its slopes; this
+            geometric sequence is the reading taken)
             O = P V                                  [SA8 2.1, A.1]
             LSE_i = m_i + ln(sum_j exp(S_ij - m_i)),  m_i = max_j S_ij
             (the pages' "softmax stats" [SA8 1.2, 1.3] are never defined; this
@@ -57,6 +61,7 @@ __all__ = [
     "attn_ref_heads",
     "attn_ref_varlen",
     "attn_ref_bwd_loop",
+    "alibi_slopes",
 ]
 
 
@@ -70,23 +75,34 @@ def to_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, row0: int, window: int = 0) -> np.ndarray:
+def _scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, row0: int, window: int = 0,
+            slope: float = 0.0) -> np.ndarray:
     """S = scale * Q K^T for query rows row0 .. row0+len(q)-1 against all given keys,
-    with the causal mask (key index > query index -> -inf) and, when window > 0, the
-    sliding-window mask (query index - key index >= window -> -inf)."""
+    with the causal mask (key index > query index -> -inf), when window > 0 the
+    sliding-window mask (query index - key index >= window -> -inf), and when slope > 0
+    the linear bias -slope * (query index - key index)."""
     S = scale * (q @ k.T)
     if causal:
         qi = np.arange(row0, row0 + q.shape[0])[:, None]
         kj = np.arange(k.shape[0])[None, :]
+        if slope:
+            S = S - slope * (qi - kj)
         S = np.where(kj > qi, -np.inf, S)
         if window > 0:
             S = np.where(qi - kj >= window, -np.inf, S)
     return S
 
 
-def _check_window(causal: bool, window: int):
+def alibi_slopes(NH: int) -> np.ndarray:
+    """Head slopes of the linear-bias (ALiBi) mask: m_h = 2^(-8 (h + 1) / NH)."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / NH) for h in range(NH)])
+
+
+def _check_window(causal: bool, window: int, slope: float = 0.0):
     if window < 0 or (window > 0 and not causal):
         raise ValueError("a sliding window needs the causal mask and window >= 1 (0 = none)")
+    if slope < 0 or (slope > 0 and not causal):
+        raise ValueError("the ALiBi bias needs the causal mask and a slope > 0")
 
 
 def _softmax_rows(S: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
@@ -98,10 +114,11 @@ def _softmax_rows(S: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
-                 block_rows: Optional[int] = None, window: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+                 block_rows: Optional[int] = None, window: int = 0,
+                 slope: float = 0.0) -> Tuple[np.ndarray, np.ndarray]:
     """One head: q (T, d_qk), k (Tk, d_qk), v (Tk, d_v) float64 -> O (T, d_v), LSE (T,).
     Tk >= 1 may differ from T (padded batches); the causal mask stays top-left."""
-    _check_window(causal, window)
+    _check_window(causal, window, slope)
     T, Tk = q.shape[0], k.shape[0]
     br = T if block_rows is None else block_rows
     O = np.empty((T, v.shape[1]))
@@ -109,17 +126,18 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
     for r0 in range(0, T, br):
         r1 = min(T, r0 + br)
         nk = min(r1, Tk) if causal else Tk  # keys past the last query are all masked
-        S = _scores(q[r0:r1], k[:nk], scale, causal, r0, window)
+        S = _scores(q[r0:r1], k[:nk], scale, causal, r0, window, slope)
         P, lse[r0:r1] = _softmax_rows(S)
         O[r0:r1] = P @ v[:nk]
     return O, lse
 
 
 def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
-                  causal: bool, block_rows: Optional[int] = None, window: int = 0):
+                  causal: bool, block_rows: Optional[int] = None, window: int = 0, slope: float = 0.0):
     """One head: returns dQ, dK, dV and also O, LSE and D = (dP * P) 1 (all float64).
-    q, do have T rows, k, v have Tk >= 1 rows (Tk may differ from T)."""
-    _check_window(causal, window)
+    q, do have T rows, k, v have Tk >= 1 rows (Tk may differ from T).  The bias is a
+    constant of the inputs: it changes P but adds no term to the gradients."""
+    _check_window(causal, window, slope)
     T, Tk = q.shape[0], k.shape[0]
     br = T if block_rows is None else block_rows
     O = np.empty((T, v.shape[1]))
@@ -131,7 +149,7 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
     for r0 in range(0, T, br):
         r1 = min(T, r0 + br)
         nk = min(r1, Tk) if causal else Tk
-        S = _scores(q[r0:r1], k[:nk], scale, causal, r0, window)
+        S = _scores(q[r0:r1], k[:nk], scale, causal, r0, window, slope)
         P, lse[r0:r1] = _softmax_rows(S)
         O[r0:r1] = P @ v[:nk]
         dV[:nk] += P.T @ do[r0:r1]                      # dV = P^T dO
@@ -149,29 +167,32 @@ def _block_rows(T: int, width: int) -> int:
     return max(1, min(T, (1 << 25) // max(T, 1) // max(1, width // 64)))
 
 
-def attn_ref_fwd(q, k, v, causal: bool, scale: Optional[float] = None, window: int = 0):
+def attn_ref_fwd(q, k, v, causal: bool, scale: Optional[float] = None, window: int = 0, alibi: bool = False):
     """Forward over (B, T, NH, d) tensors.  Returns O (B, T, NH, d_v) and LSE (B, NH, T)
     in float64."""
     q, k, v = to_f64(q), to_f64(k), to_f64(v)
     B, T, NH, dqk = q.shape
     if scale is None:
         scale = 1.0 / np.sqrt(dqk)
+    slopes = alibi_slopes(NH) if alibi else np.zeros(NH)
     O = np.empty((B, T, NH, v.shape[3]))
     lse = np.empty((B, NH, T))
     br = _block_rows(T, dqk)
     for b in range(B):
         for h in range(NH):
-            O[b, :, h], lse[b, h] = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, br, window)
+            O[b, :, h], lse[b, h] = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, br, window,
+                                                 slopes[h])
     return O, lse
 
 
-def attn_ref_bwd(q, k, v, do, causal: bool, scale: Optional[float] = None, window: int = 0):
+def attn_ref_bwd(q, k, v, do, causal: bool, scale: Optional[float] = None, window: int = 0, alibi: bool = False):
     """Backward over (B, T, NH, d) tensors.  Returns a dict with dq, dk, dv
     (B, T, NH, d), o (B, T, NH, d_v), lse and D (B, NH, T), all float64."""
     q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
     B, T, NH, dqk = q.shape
     if scale is None:
         scale = 1.0 / np.sqrt(dqk)
+    slopes = alibi_slopes(NH) if alibi else np.zeros(NH)
     out = {
         "dq": np.empty((B, T, NH, dqk)),
         "dk": np.empty((B, T, NH, dqk)),
@@ -183,7 +204,7 @@ def attn_ref_bwd(q, k, v, do, causal: bool, scale: Optional[float] = None, windo
     br = _block_rows(T, dqk)
     for b in range(B):
         for h in range(NH):
-            r = head_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal, br, window)
+            r = head_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal, br, window, slopes[h])
             for name, x in zip(("dq", "dk", "dv", "o"), r[:4]):
                 out[name][b, :, h] = x
             out["lse"][b, h], out["D"][b, h] = r[4], r[5]
@@ -191,7 +212,7 @@ def attn_ref_bwd(q, k, v, do, causal: bool, scale: Optional[float] = None, windo
 
 
 def attn_ref_heads(q, k, v, do, causal: bool, scale: Optional[float] = None,
-                   heads: Sequence[Tuple[int, int]] = (), window: int = 0):
+                   heads: Sequence[Tuple[int, int]] = (), window: int = 0, alibi: bool = False):
     """Forward and backward of selected (b, h) heads of (B, T, NH, d) tensors; only
     those heads are converted to float64.  Returns {(b, h): {"dq", "dk", "dv", "o":
     (T, d) arrays, "lse", "D": (T,) arrays}}."""
@@ -200,11 +221,12 @@ def attn_ref_heads(q, k, v, do, causal: bool, scale: Optional[float] = None,
         scale = 1.0 / np.sqrt(dqk)
     T = q.shape[1]
     br = _block_rows(T, dqk)
+    slopes = alibi_slopes(q.shape[2]) if alibi else np.zeros(q.shape[2])
     res = {}
     for b, h in heads:
         b, h = int(b), int(h)
         qh, kh, vh, dh = (np.ascontiguousarray(to_f64(x[b, :, h])) for x in (q, k, v, do))
-        r = head_backward(qh, kh, vh, dh, scale, causal, br, window)
+        r = head_backward(qh, kh, vh, dh, scale, causal, br, window, slopes[h])
         res[(b, h)] = dict(zip(("dq", "dk", "dv", "o", "lse", "D"), r))
     return res
 
@@ -246,14 +268,16 @@ def attn_ref_varlen(q, k, v, do, seq_q, seq_k, causal: bool, scale: Optional[flo
     return out
 
 
-def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, window: int = 0):
+def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, window: int = 0,
+                      alibi: bool = False):
     """Independent loop formulation for small T (T <= 64), written from the softmax
     Jacobian dy_i/dx_j = y_i (delta_ij - y_j) [SA8 2.1, A.3] and the per-(b, t, h)
     loop nest of the CPU reference in [SA8 2.2]:
 
       for each (b, t, h):
         att[t2]      = softmax over t2 (t2 <= t when causal; also t2 > t - window
-                       when window > 0) of scale * <q_t, k_t2>
+                       when window > 0) of scale * <q_t, k_t2> - m_h (t - t2)
+                       (m_h = 0 without the ALiBi bias)
         datt[t2]     = <v_t2, do_t>                       (gradient w.r.t. att)
         dv_t2       += att[t2] * do_t
         dpreatt[t3]  = scale * sum_t2 att[t2] (delta(t2, t3) - att[t3]) datt[t2]
@@ -264,11 +288,12 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
     share a line with head_forward/head_backward and serves to pin them.
     Returns dq, dk, dv, o (B, T, NH, d) and lse (B, NH, T) in float64.
     """
-    _check_window(causal, window)
+    _check_window(causal, window, 1.0 if alibi else 0.0)
     q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
     B, T, NH, dqk = q.shape
     if scale is None:
         scale = 1.0 / np.sqrt(dqk)
+    slopes = alibi_slopes(NH) if alibi else np.zeros(NH)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -281,8 +306,8 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
                 first = max(0, t - window + 1) if window > 0 else 0
                 # forward row by loops: preatt, max, exp, sum, normalise (keys before
                 # `first` get -inf scores: exp gives exactly 0, so they add nothing)
-                pre = [scale * float(np.dot(q[b, t, h], k[b, t2, h])) if t2 >= first else -math.inf
-                       for t2 in range(last)]
+                pre = [scale * float(np.dot(q[b, t, h], k[b, t2, h])) - slopes[h] * (t - t2) if t2 >= first
+                       else -math.inf for t2 in range(last)]
                 mx = max(pre)
                 ex = [np.exp(p - mx) for p in pre]
                 tot = sum(ex)

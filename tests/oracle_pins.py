@@ -8,7 +8,7 @@ each planted mistake trips at least one pin).
 
 Pages cited:
   [SA8] "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析", sections 1.2 (padding mask,
-        seq_len_q, seq_len_kv), 2.1, 2.2, A.1-A.3.
+        seq_len_q, seq_len_kv; ALiBi mask), 2.1, 2.2, A.1-A.3.
   [2CTA] "深度学习反向传播优化：2-CTA MMA模式与内存访问优化", sections 5.1, 5.2 (causal and
         block-sparse mask patterns).
 """
@@ -440,6 +440,63 @@ def pin_window_finite_differences(ref, h: float = 1e-6):
         _close(r[name], g, rtol=1e-6, atol=1e-8, what=f"window finite differences {name}")
 
 
+# ---------------------------------------------------------------------------------
+# ALiBi bias (use_alibi_mask of [SA8 1.2]): S_ij -= m_h (i - j) under the causal mask.
+# ---------------------------------------------------------------------------------
+def pin_alibi_slopes(ref):
+    """The linear-bias slopes for 8 heads are 1/2, 1/4, ..., 1/256; for 16 heads the
+    sequence 2^-0.5, 2^-1, ..., 2^-8."""
+    _close(ref.alibi_slopes(8), [1 / 2 ** (h + 1) for h in range(8)], rtol=1e-15, what="alibi slopes NH=8")
+    _close(ref.alibi_slopes(16), [2 ** (-(h + 1) / 2) for h in range(16)], rtol=1e-15, what="alibi slopes NH=16")
+
+
+def pin_alibi_zero_queries(ref):
+    """Q = 0: row i weighs key i - d by r^d with r = e^(-m_h), so O_i = sum_d r^d V_(i-d) / Z_i
+    and LSE_i = ln Z_i with the geometric sum Z_i = (1 - r^(i+1)) / (1 - r)."""
+    _, k, v, _ = _inputs(1, 25, 4, 16, 24, 871)
+    q = np.zeros_like(k)
+    o, lse = ref.attn_ref_fwd(q, k, v, True, alibi=True)
+    for h in range(4):
+        r = math.exp(-(2.0 ** (-8.0 * (h + 1) / 4)))
+        for i in range(25):
+            z = (1 - r ** (i + 1)) / (1 - r)
+            num = sum(r ** d * v[0, i - d, h] for d in range(i + 1))
+            _close(o[0, i, h], num / z, rtol=1e-13, what=f"alibi zero queries O h={h} row {i}")
+            _close(lse[0, h, i], math.log(z), rtol=1e-13, atol=1e-15, what=f"alibi zero queries LSE h={h} row {i}")
+
+
+def pin_alibi_loops(ref):
+    """Matrix form against the scalar loop nest with the bias in the scores."""
+    q, k, v, do = _inputs(2, 23, 4, 16, 24, 873)
+    dq, dk, dv, o, lse = ref.attn_ref_bwd_loop(q, k, v, do, True, alibi=True)
+    r = ref.attn_ref_bwd(q, k, v, do, True, alibi=True)
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv), ("o", o), ("lse", lse)):
+        _close(r[n], x, rtol=1e-12, atol=1e-14, what=f"alibi loop form {n}")
+
+
+def pin_alibi_finite_differences(ref, h: float = 1e-6):
+    """dQ, dK, dV with the bias equal central differences of sum(O * dO): the bias is a
+    constant, so it changes P but adds no gradient term."""
+    q, k, v, do = _inputs(1, 12, 2, 8, 8, 875)
+    r = ref.attn_ref_bwd(q, k, v, do, True, alibi=True)
+
+    def f(qq, kk, vv):
+        return float(np.sum(ref.attn_ref_fwd(qq, kk, vv, True, alibi=True)[0] * do))
+
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        g = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if n == name else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+            args_m = [xm if n == name else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+            g[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        _close(r[name], g, rtol=1e-6, atol=1e-8, what=f"alibi finite differences {name}")
+
+
 ALL_PINS = [
     ("finite_differences_causal", lambda r: pin_finite_differences(r, True)),
     ("finite_differences_full", lambda r: pin_finite_differences(r, False)),
@@ -474,4 +531,8 @@ ALL_PINS = [
     ("window_zero_queries", pin_window_zero_queries),
     ("window_loops", pin_window_loops),
     ("finite_differences_window", pin_window_finite_differences),
+    ("alibi_slopes", pin_alibi_slopes),
+    ("alibi_zero_queries", pin_alibi_zero_queries),
+    ("alibi_loops", pin_alibi_loops),
+    ("finite_differences_alibi", pin_alibi_finite_differences),
 ]

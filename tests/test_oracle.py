@@ -66,6 +66,8 @@ MUTANTS = {
     "varlen_padding_lse_zero": ('"lse": np.full((B, NH, T), -np.inf)}', '"lse": np.zeros((B, NH, T))}'),
     "window_off_by_one": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = np.where(qi - kj > window, -np.inf, S)"),
     "window_ignored": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = S"),
+    "alibi_sign": ("S = S - slope * (qi - kj)", "S = S + slope * (qi - kj)"),
+    "alibi_slope_index": ("2.0 ** (-8.0 * (h + 1) / NH)", "2.0 ** (-8.0 * h / NH)"),
 }
 
 
