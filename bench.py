@@ -99,7 +99,7 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
         hd = all_heads[done]
         t0 = time.perf_counter()
         attn_ref.attn_ref_heads(cpu["q"], cpu["k"], cpu["v"], cpu["do"], w.causal, w.scale, heads=[hd],
-                                window=w.window)
+                                window=w.window, alibi=w.alibi)
         t_total += time.perf_counter() - t0
         heads.append(hd)
         done += 1
@@ -188,19 +188,19 @@ def main():
             flush.fill_(1.0)
         if ev is not None:
             ev[0].record()
-        attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse, window=w.window)
+        attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse, window=w.window, alibi=w.alibi)
         if ev is not None:
             ev[1].record()
         attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws,
-                 stages=attn.PREPROCESS, window=w.window)
+                 stages=attn.PREPROCESS, window=w.window, alibi=w.alibi)
         if ev is not None:
             ev[2].record()
         attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws, stages=attn.MAIN,
-                 window=w.window)
+                 window=w.window, alibi=w.alibi)
         if ev is not None:
             ev[3].record()
         attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws,
-                 stages=attn.DQ, window=w.window)
+                 stages=attn.DQ, window=w.window, alibi=w.alibi)
         if ev is not None:
             ev[4].record()
 
@@ -260,9 +260,10 @@ def main():
         "config": {
             "workload": f"{w.name}: B={B} NH={NH} T={T} d_qk={w.d_qk} d_v={w.d_v} "
                         f"{'causal' if w.causal else 'non-causal'}"
-                        f"{f' window {w.window}' if w.window else ''}, {'packed QKV' if w.packed else 'BTHD'}, "
+                        f"{f' window {w.window}' if w.window else ''}{' ALiBi' if w.alibi else ''}, "
+                        f"{'packed QKV' if w.packed else 'BTHD'}, "
                         f"dQ mode {args.dq_mode}",
-            "B": B, "NH": NH, "T": T, "d_qk": w.d_qk, "d_v": w.d_v, "causal": w.causal, "window": w.window,
+            "B": B, "NH": NH, "T": T, "d_qk": w.d_qk, "d_v": w.d_v, "causal": w.causal, "window": w.window, "alibi": w.alibi,
             "dq_mode": args.dq_mode,
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -81,9 +81,9 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_varlen.restype = i
     lib.attn_bwd_varlen.argtypes = bwd_args[:17] + [vp, vp] + bwd_args[17:]
     lib.attn_fwd_typed.restype = i
-    lib.attn_fwd_typed.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_fwd_typed.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.attn_bwd_typed.restype = i
-    lib.attn_bwd_typed.argtypes = [i] + bwd_args[:17] + [vp, vp] + bwd_args[17:24] + [i] + bwd_args[24:] + [ctypes.c_uint]
+    lib.attn_bwd_typed.argtypes = [i] + bwd_args[:17] + [vp, vp] + bwd_args[17:24] + [i, i] + bwd_args[24:] + [ctypes.c_uint]
     _lib = lib
     return lib
 
@@ -136,10 +136,12 @@ def _stream(dev: torch.device) -> int:
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
         scale: Optional[float] = None, return_lse: bool = True, layout: str = "bthd",
-        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, window: int = 0):
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, window: int = 0,
+        alibi: bool = False):
     """Exact attention forward.  Returns (o, lse); lse is None when return_lse is False
     (inference mode: the kernel skips the stats).  window > 0 (causal only): query i sees
-    keys i-window+1 .. i."""
+    keys i-window+1 .. i.  alibi (causal only): linear bias -m_h (i - j) on the scaled
+    scores, m_h = 2^(-8 (h+1) / NH)."""
     lib = load()
     dev = q.device
     if dev.type != "cuda":
@@ -163,11 +165,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
                v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
                lse.data_ptr() if return_lse else None)
     with torch.cuda.device(dev):
-        if et == torch.bfloat16 and window == 0:
+        if et == torch.bfloat16 and window == 0 and not alibi:
             _check(lib.attn_fwd(*tensors, B, NH, T, dqk, dv, float(scale), int(bool(causal)), _stream(dev)))
         else:
             _check(lib.attn_fwd_typed(_DTYPE_CODE[et], *tensors, None, None, B, NH, T, dqk, dv, float(scale),
-                                      int(bool(causal)), int(window), None, 0, _stream(dev)))
+                                      int(bool(causal)), int(window), int(bool(alibi)), None, 0, _stream(dev)))
     return out, (lse if return_lse else None)
 
 
@@ -184,9 +186,10 @@ def workspace_bytes(B: int, NH: int, T: int, d_qk: int, d_v: int, deterministic:
 
 def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
         deterministic: bool = False, layout: str = "bthd", dq=None, dk=None, dv=None,
-        workspace: Optional[torch.Tensor] = None, stages: int = ALL_STAGES, window: int = 0):
-    """Exact attention backward.  Returns (dq, dk, dv).  window: the forward's sliding
-    window (0 = none)."""
+        workspace: Optional[torch.Tensor] = None, stages: int = ALL_STAGES, window: int = 0,
+        alibi: bool = False):
+    """Exact attention backward.  Returns (dq, dk, dv).  window, alibi: the forward's
+    sliding window (0 = none) and ALiBi flag."""
     lib = load()
     dev = q.device
     if dev.type != "cuda":
@@ -217,10 +220,11 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
     rest = (int(bool(deterministic)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             _stream(dev), int(stages))
     with torch.cuda.device(dev):
-        if et == torch.bfloat16 and window == 0:
+        if et == torch.bfloat16 and window == 0 and not alibi:
             _check(lib.attn_bwd_staged(*tensors, *dims, *rest))
         else:
-            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *tensors, None, None, *dims, int(window), *rest))
+            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *tensors, None, None, *dims, int(window), int(bool(alibi)),
+                                      *rest))
     return dq, dk, dv
 
 
@@ -278,7 +282,7 @@ def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causa
         if et == torch.bfloat16:
             _check(lib.attn_fwd_varlen(*args))
         else:
-            _check(lib.attn_fwd_typed(_DTYPE_CODE[et], *args[:18], 0, *args[18:]))
+            _check(lib.attn_fwd_typed(_DTYPE_CODE[et], *args[:18], 0, 0, *args[18:]))
     return out, lse
 
 
@@ -319,5 +323,5 @@ def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.T
         if et == torch.bfloat16:
             _check(lib.attn_bwd_varlen(*args))
         else:
-            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *args[:26], 0, *args[26:], ALL_STAGES))
+            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *args[:26], 0, 0, *args[26:], ALL_STAGES))
     return dq, dk, dv

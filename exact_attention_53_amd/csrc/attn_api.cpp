@@ -61,10 +61,11 @@ attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E
 
 attn53::ElemType elem_type(attn_dtype d) { return d == ATTN_DTYPE_F16 ? attn53::ELEM_F16 : attn53::ELEM_BF16; }
 
-// Sliding window: 0 = none; >= 1 needs the causal mask and a dense (unpadded) batch.
-bool window_ok(int window, int causal, const int32_t* seq_q, const int32_t* seq_k) {
-  if (window < 0) return false;
-  return window == 0 || (causal == 1 && seq_q == nullptr && seq_k == nullptr);
+// Sliding window (0 = none; >= 1) and ALiBi bias (0 / 1): each needs the causal mask and a
+// dense (unpadded) batch; they do not combine.
+bool window_ok(int window, int alibi, int causal, const int32_t* seq_q, const int32_t* seq_k) {
+  if (window < 0 || (alibi != 0 && alibi != 1) || (window > 0 && alibi)) return false;
+  return (window == 0 && alibi == 0) || (causal == 1 && seq_q == nullptr && seq_k == nullptr);
 }
 
 // Work list of a padded-batch launch: one (b, block) pair of int32 per item.
@@ -78,11 +79,11 @@ bool int_ptr_ok(const int32_t* p) { return p != nullptr && reinterpret_cast<uint
 attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const void* k, attn_strides sk,
                      const void* v, attn_strides sv, void* o, attn_strides so, float* lse, const int32_t* seq_q,
                      const int32_t* seq_k, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
-                     int window, void* workspace, size_t workspace_bytes, void* stream) {
+                     int window, int alibi, void* workspace, size_t workspace_bytes, void* stream) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
-  if (!window_ok(window, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
+  if (!window_ok(window, alibi, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
   Extent eq, ek, ev, eo;
   if ((st = check_tensor(q, sq, B, NH, T, d_qk, &eq)) != ATTN_OK) return st;
   if ((st = check_tensor(k, sk, B, NH, T, d_qk, &ek)) != ATTN_OK) return st;
@@ -116,6 +117,7 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   p.B = B; p.NH = NH; p.T = T;
   p.scale_log2 = scale * kLog2e;
   p.win = window > 0 ? window : attn53::kNoWindow;
+  p.alibi = alibi;
   const hipStream_t s = (hipStream_t)stream;
   if (varlen) {
     attn53::PlanParams pp{seq_q, seq_k, static_cast<int*>(workspace), B, T, kFwdBlock, attn53::PLAN_Q, causal};
@@ -139,14 +141,14 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
                      const void* v, attn_strides sv, const void* o, attn_strides so, const float* lse,
                      const void* do_, attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk,
                      void* dv, attn_strides sdv, const int32_t* seq_q, const int32_t* seq_k, int B, int NH, int T,
-                     int d_qk, int d_v, float scale, int causal, int window, int deterministic, void* workspace,
-                     size_t workspace_bytes, void* stream, unsigned stages) {
+                     int d_qk, int d_v, float scale, int causal, int window, int alibi, int deterministic,
+                     void* workspace, size_t workspace_bytes, void* stream, unsigned stages) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1) ||
       (deterministic != 0 && deterministic != 1))
     return ATTN_ERR_ARG;
-  if (!window_ok(window, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
+  if (!window_ok(window, alibi, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
   if (stages == 0 || (stages & ~ATTN_BWD_ALL) != 0) return ATTN_ERR_ARG;
   const bool varlen = seq_q != nullptr || seq_k != nullptr;
   if (varlen) {
@@ -190,6 +192,7 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
   p.win = window > 0 ? window : attn53::kNoWindow;
+  p.alibi = alibi;
   char* ws = static_cast<char*>(workspace);
   p.D = reinterpret_cast<float*>(ws);
   p.lse2 = reinterpret_cast<float*>(ws + ws_D_bytes(B, NH, T));
@@ -257,7 +260,7 @@ int attn_version(void) { return 300; }
 attn_status attn_fwd(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
                      attn_strides sv, void* o, attn_strides so, float* lse, int B, int NH, int T, int d_qk,
                      int d_v, float scale, int causal, void* stream) {
-  return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale, causal, 0, nullptr, 0,
+  return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale, causal, 0, 0, nullptr, 0,
                   stream);
 }
 
@@ -272,7 +275,7 @@ attn_status attn_fwd_varlen(const void* q, attn_strides sq, const void* k, attn_
                             int causal, void* workspace, size_t workspace_bytes, void* stream) {
   if (seq_len_q == nullptr || seq_len_kv == nullptr) return ATTN_ERR_NULL;
   return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, seq_len_q, seq_len_kv, B, NH, T, d_qk, d_v, scale, causal,
-                  0, workspace, workspace_bytes, stream);
+                  0, 0, workspace, workspace_bytes, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic) {
@@ -286,7 +289,7 @@ attn_status attn_bwd_staged(const void* q, attn_strides sq, const void* k, attn_
                             int deterministic, void* workspace, size_t workspace_bytes, void* stream,
                             unsigned stages) {
   return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr, nullptr, B, NH, T,
-                  d_qk, d_v, scale, causal, 0, deterministic, workspace, workspace_bytes, stream, stages);
+                  d_qk, d_v, scale, causal, 0, 0, deterministic, workspace, workspace_bytes, stream, stages);
 }
 
 attn_status attn_bwd(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v, attn_strides sv,
@@ -295,7 +298,7 @@ attn_status attn_bwd(const void* q, attn_strides sq, const void* k, attn_strides
                      int d_qk, int d_v, float scale, int causal, int deterministic, void* workspace,
                      size_t workspace_bytes, void* stream) {
   return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr, nullptr, B, NH, T,
-                  d_qk, d_v, scale, causal, 0, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
+                  d_qk, d_v, scale, causal, 0, 0, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
 }
 
 size_t attn_bwd_varlen_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic) {
@@ -310,30 +313,30 @@ attn_status attn_bwd_varlen(const void* q, attn_strides sq, const void* k, attn_
                             size_t workspace_bytes, void* stream) {
   if (seq_len_q == nullptr || seq_len_kv == nullptr) return ATTN_ERR_NULL;
   return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, seq_len_q, seq_len_kv, B, NH,
-                  T, d_qk, d_v, scale, causal, 0, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
+                  T, d_qk, d_v, scale, causal, 0, 0, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
 }
 
 attn_status attn_fwd_typed(attn_dtype dtype, const void* q, attn_strides sq, const void* k, attn_strides sk,
                            const void* v, attn_strides sv, void* o, attn_strides so, float* lse,
                            const int32_t* seq_len_q, const int32_t* seq_len_kv, int B, int NH, int T, int d_qk,
-                           int d_v, float scale, int causal, int window, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           int d_v, float scale, int causal, int window, int alibi, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_ARG;
   return fwd_impl(elem_type(dtype), q, sq, k, sk, v, sv, o, so, lse, seq_len_q, seq_len_kv, B, NH, T, d_qk, d_v,
-                  scale, causal, window, workspace, workspace_bytes, stream);
+                  scale, causal, window, alibi, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_bwd_typed(attn_dtype dtype, const void* q, attn_strides sq, const void* k, attn_strides sk,
                            const void* v, attn_strides sv, const void* o, attn_strides so, const float* lse,
                            const void* do_, attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk,
                            void* dv, attn_strides sdv, const int32_t* seq_len_q, const int32_t* seq_len_kv, int B,
-                           int NH, int T, int d_qk, int d_v, float scale, int causal, int window,
+                           int NH, int T, int d_qk, int d_v, float scale, int causal, int window, int alibi,
                            int deterministic, void* workspace, size_t workspace_bytes, void* stream,
                            unsigned stages) {
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_ARG;
   return bwd_impl(elem_type(dtype), q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, seq_len_q,
-                  seq_len_kv, B, NH, T, d_qk, d_v, scale, causal, window, deterministic, workspace, workspace_bytes,
-                  stream, stages);
+                  seq_len_kv, B, NH, T, d_qk, d_v, scale, causal, window, alibi, deterministic, workspace,
+                  workspace_bytes, stream, stages);
 }
 
 }  // extern "C"

@@ -26,15 +26,19 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int 
   return et == ELEM_F16 ? pre_t<f16>(p, d_qk, d_v, zero_acc, s) : pre_t<bf16>(p, d_qk, d_v, zero_acc, s);
 }
 
-// mask mode of the launchers: 0 none, 1 causal, 2 causal with a sliding window
-static inline int mask_mode(const BwdParams& p, bool causal) { return !causal ? 0 : p.win < kNoWindow ? 2 : 1; }
+// mask mode of the launchers: 0 none, 1 causal, 2 causal with a sliding window, 3 causal
+// with the ALiBi bias
+static inline int mask_mode(const BwdParams& p, bool causal) {
+  return !causal ? 0 : p.win < kNoWindow ? 2 : p.alibi ? 3 : 1;
+}
 
 template <class E, int DQK, int DV>
 static hipError_t main_m(const BwdParams& p, bool causal, bool det, hipStream_t s) {
   switch (mask_mode(p, causal)) {
     case 0: return bwd_main_t<E, DQK, DV, 0>(p, det, s);
     case 1: return bwd_main_t<E, DQK, DV, 1>(p, det, s);
-    default: return bwd_main_t<E, DQK, DV, 2>(p, det, s);
+    case 2: return bwd_main_t<E, DQK, DV, 2>(p, det, s);
+    default: return bwd_main_t<E, DQK, DV, 3>(p, det, s);
   }
 }
 
@@ -57,7 +61,8 @@ static hipError_t dq_m(const BwdParams& p, bool causal, hipStream_t s) {
   switch (mask_mode(p, causal)) {
     case 0: return bwd_dq_t<E, DQK, DV, 0>(p, s);
     case 1: return bwd_dq_t<E, DQK, DV, 1>(p, s);
-    default: return bwd_dq_t<E, DQK, DV, 2>(p, s);
+    case 2: return bwd_dq_t<E, DQK, DV, 2>(p, s);
+    default: return bwd_dq_t<E, DQK, DV, 3>(p, s);
   }
 }
 

@@ -173,8 +173,9 @@ struct KvPlan {
   static_assert(plan.ok, "no feasible placement of the step's VALU work");
 };
 
-// WIN (with CAUSAL only): sliding window of p.win keys.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ATOMIC_DQ>
+// WIN (with CAUSAL only): sliding window of p.win keys.  ALIBI (with CAUSAL only): the
+// linear bias -m_h (i - j) on the scaled scores.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool ATOMIC_DQ>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 64 ? 2 : 1, DQK == 64 ? 2 : 1))) void bwd_kv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
@@ -224,6 +225,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
   const int kw = 32 * w;
   const int my_key = key0 + kw + lq;
   const float c = p.scale_log2;
+  const float ml = ALIBI ? alibi_slope_log2(h, p.NH) : 0.f;  // ALiBi slope, log2 units
   E* dkg = (E*)p.dk + b * p.sdk.b + h * p.sdk.h;
   E* dvg = (E*)p.dv + b * p.sdv.b + h * p.sdv.h;
 
@@ -327,6 +329,9 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
     const ATTN_LDS char* ot = (const ATTN_LDS char*)(BUF ? obuf1 : obuf0);
     const float* lb = BUF ? lse1 : lse0;
     const float* db = BUF ? dd1 : dd0;
+    // ALiBi: m_h log2(e) (key - query) = ab - ml (32 t + 8 (r / 4) + r % 4) for element r of
+    // tile t (query q0 + 32 t + 8 (r / 4) + 4 g + r % 4, key my_key)
+    const float ab = ALIBI ? ml * (float)(my_key - q0 - 4 * g) : 0.f;
     if (MASKED && CAUSAL && (key0 + kw > q0 + BWD_BM - 1 || (WIN && q0 - (key0 + kw + 31) >= W))) {
       // every key of this wavefront lies above every query of the block, or below every
       // query's window: P = dS = 0
@@ -365,7 +370,8 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * a + e;
             const int q = q0 + qi + e;
-            const float pv = exp2_fast(__builtin_fmaf(s[t][r], c, -Lv[e]));
+            const float bias = ALIBI ? __builtin_fmaf(-ml, (float)(32 * t + 8 * a + e), ab) : 0.f;
+            const float pv = exp2_fast(__builtin_fmaf(s[t][r], c, bias - Lv[e]));
             s[t][r] = (my_key >= Lk || q >= Lq || (CAUSAL && (my_key > q || (WIN && q - my_key >= W)))) ? 0.f : pv;
           }
         }
@@ -421,7 +427,14 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
           if constexpr (Plan::is_pack(o))
             pb[2 * t + h] = pack8<E>(pv[t], h);
           else
-            pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, -lsev[t][r >> 2][r & 3]));
+          {
+            if constexpr (ALIBI) {
+              const float bias = __builtin_fmaf(-ml, (float)(32 * t + 8 * (r >> 2) + (r & 3)), ab);
+              pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, bias - lsev[t][r >> 2][r & 3]));
+            } else {
+              pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, -lsev[t][r >> 2][r & 3]));
+            }
+          }
         } else {
           if constexpr (Plan::is_pack(o))
             sb[2 * t + h] = pack8<E>(dsv[t], h);
@@ -630,8 +643,9 @@ struct DqShape {
   static constexpr int WAVES_PER_EU = DQK == 64 ? 2 : 1;
 };
 
-// WIN (with CAUSAL only): sliding window of p.win keys.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN>
+// WIN (with CAUSAL only): sliding window of p.win keys.  ALIBI (with CAUSAL only): the
+// linear bias -m_h (i - j) on the scaled scores.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
                                                                          DqShape<DQK>::WAVES_PER_EU)))
 void bwd_dq_kernel(BwdParams p) {
@@ -674,6 +688,7 @@ void bwd_dq_kernel(BwdParams p) {
   const LdsLane L = lds_lane(lane);
   const int q0 = qb * BM, qw = q0 + 32 * QT * w;  // first row of this wavefront
   const float c = p.scale_log2;
+  const float ml = ALIBI ? alibi_slope_log2(h, p.NH) : 0.f;  // ALiBi slope, log2 units
   const int W = WIN ? p.win : kNoWindow;
   const int kv_end = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int n_kv = (kv_end + DQ_BN - 1) / DQ_BN;
@@ -760,7 +775,10 @@ void bwd_dq_kernel(BwdParams p) {
       for (int u = 0; u < QT; ++u)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pv = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
+          float bias = 0.f;
+          if constexpr (ALIBI)  // m_h log2(e) (key - query), key key0 + 32 t + 8 (r / 4) + 4 g + r % 4
+            bias = ml * (float)(key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3) - (qw + 32 * u + lq));
+          float pv = exp2_fast(__builtin_fmaf(s[t][u][r], c, bias - lse2[u]));
           if constexpr (MASKED) {
             const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
             const int q = qw + 32 * u + lq;
@@ -819,12 +837,18 @@ void bwd_dq_kernel(BwdParams p) {
 
   // ---- unmasked tiles: an explicit pipeline (DqPlan) ----
   using Plan = DqPlan<DQK, DV, QT>;
-  auto tile_pipe = [&](auto bufc) __attribute__((always_inline)) {
+  auto tile_pipe = [&](int key0, auto bufc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
     const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
     f32x16 s[2][QT], dp[2][QT];
     f32x16 pv[QT];         // P, then dS, of the half being worked on
+    // ALiBi: m_h log2(e) (key - query) - LSE log2(e) = abq[u] + ml (32 t + 8 (r / 4) + r % 4)
+    // for element r of half t (key key0 + 32 t + 8 (r / 4) + 4 g + r % 4, query qw + 32 u + lq)
+    float abq[QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u)
+      abq[u] = ALIBI ? __builtin_fmaf(ml, (float)(key0 + 4 * g - (qw + 32 * u + lq)), -lse2[u]) : 0.f;
     vec8<E> sb[2][QT][2];
     vec8<E> fr[Plan::RING];
     auto read_at = [&](auto bc) __attribute__((always_inline)) -> vec8<E> {
@@ -846,7 +870,10 @@ void bwd_dq_kernel(BwdParams p) {
       constexpr int o = decltype(oc)::value, t = Plan::half(o), k = o % (34 * QT);
       if constexpr (Plan::is_p(o)) {
         constexpr int u = k / 16, r = k % 16;
-        pv[u][r] = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
+        if constexpr (ALIBI)
+          pv[u][r] = exp2_fast(__builtin_fmaf(s[t][u][r], c, __builtin_fmaf(ml, (float)(32 * t + 8 * (r >> 2) + (r & 3)), abq[u])));
+        else
+          pv[u][r] = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
       } else {
         constexpr int kk = k - 16 * QT, u = kk / 18, e = kk % 18;
         if constexpr (e == 8 || e == 17) {
@@ -916,7 +943,7 @@ void bwd_dq_kernel(BwdParams p) {
       else
         tile_body(key0, bufc, std::false_type{});
     } else {
-      tile_pipe(bufc);
+      tile_pipe(key0, bufc);
     }
   };
   // The first tiles (the workgroup's diagonal ones under the causal mask, or the ragged
@@ -986,30 +1013,32 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------------
 // per-configuration launchers (each instantiated by one compilation of attn_bwd_inst.hip)
 // ---------------------------------------------------------------------------------
-// MASK: 0 none, 1 causal, 2 causal with a sliding window of p.win keys.
+// MASK: 0 none, 1 causal, 2 causal with a sliding window of p.win keys, 3 causal with the
+// ALiBi bias.
 template <class E, int DQK, int DV, int MASK>
 hipError_t bwd_main_t(const BwdParams& p, bool deterministic, hipStream_t s) {
-  constexpr bool CAUSAL = MASK >= 1, WIN = MASK == 2;
+  constexpr bool CAUSAL = MASK >= 1, WIN = MASK == 2, ALIBI = MASK == 3;
   const int nkb = (p.T + BWD_BN - 1) / BWD_BN;
   const dim3 grid_kv(nkb * p.B * p.NH);
   if (deterministic)
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, false>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, false>), grid_kv, dim3(BWD_NT), 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, true>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, true>), grid_kv, dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
 template <class E, int DQK, int DV, int MASK>
 hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
-  constexpr bool CAUSAL = MASK >= 1, WIN = MASK == 2;
+  constexpr bool CAUSAL = MASK >= 1, WIN = MASK == 2, ALIBI = MASK == 3;
   const int nqb = (p.T + DqShape<DQK>::BM - 1) / DqShape<DQK>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, CAUSAL, WIN>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s,
+                     p);
   return hipGetLastError();
 }
 
-#define ATTN_BWD_CONFIGS(X) \
-  X(64, 64, 0) X(64, 64, 1) X(64, 64, 2) X(128, 128, 0) X(128, 128, 1) X(128, 128, 2) \
-  X(192, 128, 0) X(192, 128, 1) X(192, 128, 2)
+#define ATTN_BWD_CONFIGS(X)                                                                        \
+  X(64, 64, 0) X(64, 64, 1) X(64, 64, 2) X(64, 64, 3) X(128, 128, 0) X(128, 128, 1) X(128, 128, 2) \
+  X(128, 128, 3) X(192, 128, 0) X(192, 128, 1) X(192, 128, 2) X(192, 128, 3)
 #define ATTN_EXTERN_BWD_E(E, DQK, DV, MASK)                                                       \
   extern template hipError_t bwd_main_t<E, DQK, DV, MASK>(const BwdParams&, bool, hipStream_t); \
   extern template hipError_t bwd_dq_t<E, DQK, DV, MASK>(const BwdParams&, hipStream_t);

@@ -336,6 +336,11 @@ __device__ __forceinline__ ListItem list_item(int bid, int NH, const int* list) 
   return ListItem{list[2 * r], h, list[2 * r + 1]};
 }
 
+// ALiBi slope of head h of NH in log2 units: m_h log2(e), m_h = 2^(-8 (h + 1) / NH).
+__device__ __forceinline__ float alibi_slope_log2(int h, int NH) {
+  return __builtin_amdgcn_exp2f(-8.f * (float)(h + 1) / (float)NH) * kLog2e;
+}
+
 // Valid rows of batch b, clamped to [0, T].
 __device__ __forceinline__ int batch_len(const int* seq, int b, int T) { return min(max(seq[b], 0), T); }
 

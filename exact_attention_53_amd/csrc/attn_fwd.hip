@@ -46,8 +46,9 @@ constexpr int FWD_NT = 256;
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 constexpr float kSumLimit = 256.f;        // 2^kRescaleThreshold
 
-// WIN (with CAUSAL only): sliding window of p.win keys.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN>
+// WIN (with CAUSAL only): sliding window of p.win keys.  ALIBI (with CAUSAL only): the
+// linear bias -m_h (i - j) added to the scaled scores.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI>
 __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr int KS = DQK / 16;
   constexpr int NDT = DV / 32;
@@ -125,6 +126,8 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   };
 
   const float c = p.scale_log2;
+  // ALiBi in score units: c (s + sl (j - i)) = c s + m_h log2(e) (j - i)
+  const float sl = ALIBI ? alibi_slope_log2(h, p.NH) / c : 0.f;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[NDT];
@@ -156,6 +159,14 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
       for (int ks = 0; ks < KS; ++ks) {
         s0 = mfma32(lds_row8<E, FWD_BN>(kt, L, 0, ks), qf[ks], s0);
         s1 = mfma32(lds_row8<E, FWD_BN>(kt, L, 32, ks), qf[ks], s1);
+      }
+      if constexpr (ALIBI) {  // key of element r: key0 + 8 (r / 4) + 4 g + r % 4 (+32 in s1)
+        const float b0 = sl * (float)(key0 + 4 * g - my_q);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[r] += __builtin_fmaf(sl, (float)(8 * (r >> 2) + (r & 3)), b0);
+          s1[r] += __builtin_fmaf(sl, (float)(32 + 8 * (r >> 2) + (r & 3)), b0);
+        }
       }
       if constexpr (MASKED) {
 #pragma unroll
@@ -300,11 +311,13 @@ template <class E, int DQK, int DV>
 static hipError_t fwd_launch(const FwdParams& p, bool causal, hipStream_t s) {
   const dim3 grid((p.T + FWD_BM - 1) / FWD_BM * p.B * p.NH);
   if (!causal)
-    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, false, false>), grid, dim3(FWD_NT), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, false, false, false>), grid, dim3(FWD_NT), 0, s, p);
   else if (p.win < kNoWindow)
-    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, true>), grid, dim3(FWD_NT), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, true, false>), grid, dim3(FWD_NT), 0, s, p);
+  else if (p.alibi)
+    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, false, true>), grid, dim3(FWD_NT), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, false>), grid, dim3(FWD_NT), 0, s, p);
+    hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, false, false>), grid, dim3(FWD_NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ struct FwdParams {
   float scale_log2;        // scale * log2(e)
   int win;                 // causal sliding window: query i sees keys i-win+1 .. i
                            // (1 << 30 when there is no window)
+  int alibi;               // 1: causal ALiBi bias -m_h (i - j), m_h = 2^(-8 (h+1) / NH)
   // Padded batches (all three set, or all nullptr): valid query / key rows per batch
   // (B int32 each; clamped to [0, T]) and the sorted work list of (b, query block).
   const int* seq_q;
@@ -41,6 +42,7 @@ struct BwdParams {
   float scale;
   float scale_log2;
   int win;                 // causal sliding window as in FwdParams
+  int alibi;               // ALiBi bias as in FwdParams
   float* D;                // workspace: (B, NH, Tpad) fp32, rowsum(dO * O)
   float* lse2;             // workspace: (B, NH, Tpad) fp32, LSE * log2(e) (+inf on padding)
   float* dq_acc;           // workspace: (B, NH, Tpad, d_qk) fp32, atomic mode only

@@ -238,12 +238,20 @@ typedef enum {
  * band's edges cross carry a mask.  W >= 1 needs causal = 1 and no padded-batch lengths,
  * W < 0 is invalid: otherwise ATTN_ERR_ARG.  Every row keeps at least its own key, so
  * the LSE and the outputs stay finite; the backward must get the forward's window.
+ *
+ * ALiBi bias (`alibi` argument of the two entry points below; the use_alibi_mask option
+ * of [SA8 1.2]).  0: none.  1: the scaled scores get the linear bias -m_h (i - j) for
+ * query i, key j <= i of head h, with the slopes m_h = 2^(-8 (h + 1) / NH) (the page
+ * names the option, not its slopes; this geometric sequence is the reading taken).  The
+ * bias is a constant of the inputs: it changes P, not the gradient formulas.  alibi = 1
+ * needs causal = 1, no padded-batch lengths and window = 0; other values are invalid:
+ * otherwise ATTN_ERR_ARG.  The backward must get the forward's flag.
  */
 
 /*
  * attn_fwd_typed — attn_fwd (seq_len_q == seq_len_kv == NULL; workspace unused and may
  * be NULL) or attn_fwd_varlen (both lengths given; workspace as for attn_fwd_varlen) on
- * tensors of element type `dtype`, with an optional sliding window.  An unknown dtype
+ * tensors of element type `dtype`, with an optional sliding window or ALiBi bias.  An unknown dtype
  * returns ATTN_ERR_ARG; every other argument, layout rule and error is that of
  * attn_fwd / attn_fwd_varlen.
  */
@@ -255,13 +263,13 @@ attn_status attn_fwd_typed(attn_dtype dtype,
                            float* lse,
                            const int32_t* seq_len_q, const int32_t* seq_len_kv,
                            int B, int NH, int T, int d_qk, int d_v,
-                           float scale, int causal, int window,
+                           float scale, int causal, int window, int alibi,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_bwd_typed — attn_bwd_staged (seq_len_q == seq_len_kv == NULL) or the padded-batch
  * backward (both lengths given) on tensors of element type `dtype`, with the forward's
- * sliding window (0 = none), restricted to the
+ * sliding window (0 = none) and ALiBi flag, restricted to the
  * stages in `stages` (ATTN_BWD_ALL for the whole backward).  The workspace is sized by
  * attn_bwd_workspace_bytes / attn_bwd_varlen_workspace_bytes, which do not depend on the
  * element type.  An unknown dtype returns ATTN_ERR_ARG; every other argument, layout rule
@@ -279,7 +287,7 @@ attn_status attn_bwd_typed(attn_dtype dtype,
                            void* dv, attn_strides sdv,
                            const int32_t* seq_len_q, const int32_t* seq_len_kv,
                            int B, int NH, int T, int d_qk, int d_v,
-                           float scale, int causal, int window, int deterministic,
+                           float scale, int causal, int window, int alibi, int deterministic,
                            void* workspace, size_t workspace_bytes, void* stream,
                            unsigned stages);
 

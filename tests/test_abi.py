@@ -133,14 +133,14 @@ def test_typed_validation(lib):
     known types reach the same validation as the bf16 entry points."""
     st, sv = strides(64, 2, 64), strides(64, 2, 64)
 
-    def tfwd(dtype, q=GOOD, o=GOOD + 0x300000, lq=None, lk=None, causal=1, window=0):
+    def tfwd(dtype, q=GOOD, o=GOOD + 0x300000, lq=None, lk=None, causal=1, window=0, alibi=0):
         return lib.attn_fwd_typed(dtype, q, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, o, sv, None, lq, lk,
-                                  1, 2, 64, 64, 64, 0.125, causal, window, GOOD + 0xb00000, 1 << 20, None)
+                                  1, 2, 64, 64, 64, 0.125, causal, window, alibi, GOOD + 0xb00000, 1 << 20, None)
 
-    def tbwd(dtype, dq=GOOD + 0x600000, stages=7, causal=1, window=0, lq=None, lk=None):
+    def tbwd(dtype, dq=GOOD + 0x600000, stages=7, causal=1, window=0, lq=None, lk=None, alibi=0):
         return lib.attn_bwd_typed(dtype, GOOD, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, GOOD + 0x300000, sv,
                                   GOOD + 0x400000, GOOD + 0x500000, sv, dq, st, GOOD + 0x700000, st,
-                                  GOOD + 0x800000, sv, lq, lk, 1, 2, 64, 64, 64, 0.125, causal, window, 0,
+                                  GOOD + 0x800000, sv, lq, lk, 1, 2, 64, 64, 64, 0.125, causal, window, alibi, 0,
                                   GOOD + 0x900000, 1 << 30, None, stages)
 
     for bad in (2, -1, 99):
@@ -157,3 +157,8 @@ def test_typed_validation(lib):
             assert f(dt, window=-1) == ARG
             assert f(dt, causal=0, window=16) == ARG
             assert f(dt, window=16, lq=GOOD + 0xa00000, lk=GOOD + 0xa00100) == ARG
+            # ALiBi: a 0/1 flag, causal only, dense only, not with a window
+            assert f(dt, alibi=2) == ARG
+            assert f(dt, causal=0, alibi=1) == ARG
+            assert f(dt, alibi=1, window=16) == ARG
+            assert f(dt, alibi=1, lq=GOOD + 0xa00000, lk=GOOD + 0xa00100) == ARG

@@ -41,6 +41,7 @@ class Workload:
     sigma_do: float = 1.0    # std of dO
     packed: bool = False     # Q, K, V are views of one (B, T, 3, NH, HS) tensor
     window: int = 0          # causal sliding window: query i sees keys i-window+1 .. i (0 = none)
+    alibi: bool = False      # causal ALiBi bias -m_h (i - j), m_h = 2^(-8 (h+1) / NH)
 
     @property
     def scale(self) -> float:
@@ -69,6 +70,8 @@ WORKLOADS: Dict[str, Workload] = {
     "headline": Workload("headline", 4, 16, 8192, 128, 128, True, 53006),
     # the headline shape under a 1024-key sliding window (local attention)
     "window": Workload("window", 4, 16, 8192, 128, 128, True, 53007, window=1024),
+    # the headline shape with the ALiBi bias
+    "alibi": Workload("alibi", 4, 16, 8192, 128, 128, True, 53008, alibi=True),
 }
 
 
