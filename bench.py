@@ -103,7 +103,14 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
         t_total += time.perf_counter() - t0
         heads.append(hd)
         done += 1
-    threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max((i.get("num_threads", 1) for i in blas), default=1)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": per_head_flops * done / t_total / 1e12,
         "unit": "TFLOP/s",
@@ -111,6 +118,8 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
         "kind": "oracle",
         "sample": f"{done} of {len(all_heads)} (b,h) heads of the {w.name} workload, full forward+backward "
                   f"per head in numpy float64 ({t_total:.1f} s)",
+        "host": {"cpu": cpu_model, "affinity": len(os.sched_getaffinity(0)), "numpy": np.__version__,
+                 "blas": ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in blas)},
     }
 
 
@@ -138,6 +147,8 @@ def main():
     ap.add_argument("--dq-mode", choices=["deterministic", "atomic"], default="deterministic",
                     help="dQ summed in a fixed order without atomics (default) or by fp32 atomics")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="only time the CPU oracle on a bounded sample of the workload (no GPU use)")
     ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
                     help="16-bit element type of Q, K, V, O and the gradients (the metric is quoted for bf16)")
     ap.add_argument("--cold", action="store_true",
@@ -154,6 +165,11 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.cpu_baseline_only:
+        import workloads
+        w = workloads.WORKLOADS[args.workload]
+        print(json.dumps({"workload": w.name, "cpu_baseline": cpu_baseline(w)}), flush=True)
         return
 
     import torch
