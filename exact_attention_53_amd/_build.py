@@ -32,6 +32,14 @@ FLAGS = [
 ]
 
 
+# Key/value kernel: let the MFMAs of S and dP write VGPRs, which the softmax VALU work
+# reads, instead of accumulation registers that each need a v_accvgpr_read first (64 per
+# step at d = 128); the dK / dV accumulators stay in accumulation registers.  (The
+# compiler's pass for this form fails on the d_qk = 192 key/value kernel and on the dQ
+# kernel, which keep the default.)
+KV_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -64,7 +72,8 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
         defs = [f"-DATTN_INST_DQ={int(kind == 'dq')}", f"-DATTN_INST_ELEM={elem}", f"-DATTN_INST_DQK={dqk}",
                 f"-DATTN_INST_DV={dv}", f"-DATTN_INST_MASK={mask}"]
-        cmds.append([hipcc, *FLAGS, *defs, "-c", os.path.join(CSRC, "attn_bwd_inst.hip"), "-o", obj])
+        extra = KV_FLAGS if kind == "kv" and dqk <= 128 else []
+        cmds.append([hipcc, *FLAGS, *extra, *defs, "-c", os.path.join(CSRC, "attn_bwd_inst.hip"), "-o", obj])
     cmds.sort(key=lambda c: "attn_bwd_inst.hip" not in c[-3])  # longest compilations first
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 8)) as ex:
         for out in ex.map(_run, cmds):
