@@ -124,6 +124,46 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
     }
 
 
+def decode_bench(args, w):
+    """One decode step per sequence: the inference forward (no stats) of one query row
+    against each sequence's w.T-row key/value cache (attn_fwd_decode).  HBM-bound:
+    reported as the K, V, Q and O bytes moved per second against the 8 TB/s peak."""
+    import torch
+
+    import exact_attention_53_amd as attn
+    import workloads
+
+    dev = torch.device("cuda:0")
+    B, T, NH = w.B, w.T, w.NH
+    et = torch.bfloat16 if args.dtype == "bf16" else torch.float16
+    k = workloads._randn((B, T, NH, w.d_qk), w.seed + 1, w.sigma, et).to(dev)
+    v = workloads._randn((B, T, NH, w.d_v), w.seed + 2, w.sigma, et).to(dev)
+    q = workloads._randn((B, 1, NH, w.d_qk), w.seed + 0, w.sigma, et).to(dev)
+    o = torch.empty((B, 1, NH, w.d_v), dtype=et, device=dev)
+    for _ in range(args.warmup):
+        attn.fwd_decode(q, k, v, None, w.scale, out=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        attn.fwd_decode(q, k, v, None, w.scale, out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    moved = B * NH * (T * (w.d_qk + w.d_v) * 2 + (w.d_qk + w.d_v) * 2)  # K, V read; q read, o written
+    gbs = moved / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "decode attention forward HBM GB/s", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": f"decode: B={B} NH={NH} one query row against {T} keys, d={w.d_qk}, non-causal, "
+                               f"no stats", "B": B, "NH": NH, "T_kv": T, "d": w.d_qk},
+        "tflops": round(2.0 * (w.d_qk + w.d_v) * B * NH * T / (ms * 1e-3) / 1e12, 2),
+        "roofline": {"kernel": "attn_fwd (decode)", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }), flush=True)
+
+
 def copy_calibration(mib: int):
     """A streaming kernel of known size: an elementwise negation that reads and writes
     exactly mib MiB per launch (a kernel, unlike a DMA copy, is seen by the counters).
@@ -179,6 +219,9 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
+    if w.name == "decode":
+        decode_bench(args, w)
+        return
     dev = torch.device("cuda:0")
     et = torch.bfloat16 if args.dtype == "bf16" else torch.float16
     cpu = workloads.make_inputs(w, et)

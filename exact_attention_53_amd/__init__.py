@@ -27,7 +27,7 @@ import torch
 
 __all__ = [
     "AttnError", "lib_path", "load", "fwd", "fwd_packed", "bwd", "bwd_packed",
-    "workspace_bytes", "fwd_varlen", "bwd_varlen", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
+    "workspace_bytes", "fwd_varlen", "bwd_varlen", "fwd_decode", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +82,8 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_varlen.argtypes = bwd_args[:17] + [vp, vp] + bwd_args[17:]
     lib.attn_fwd_typed.restype = i
     lib.attn_fwd_typed.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.attn_fwd_decode.restype = i
+    lib.attn_fwd_decode.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, i, i, i, i, i, i, f, vp]
     lib.attn_bwd_typed.restype = i
     lib.attn_bwd_typed.argtypes = [i] + bwd_args[:17] + [vp, vp] + bwd_args[17:24] + [i, i] + bwd_args[24:] + [ctypes.c_uint]
     _lib = lib
@@ -236,6 +238,39 @@ def bwd_packed(qkv, o, lse, do, causal: bool = True, scale: Optional[float] = No
     bwd(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], o, lse, do, causal, scale, deterministic,
         dq=dqkv[:, :, 0], dk=dqkv[:, :, 1], dv=dqkv[:, :, 2], workspace=workspace)
     return dqkv
+
+
+def fwd_decode(q, k, v, seq_len_kv: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+               return_lse: bool = False, layout: str = "bthd", out: Optional[torch.Tensor] = None):
+    """Decode-step forward: the Tq query rows of each sequence attend to all rows of its
+    key/value cache (Tk rows, or seq_len_kv[b] of them), no causal mask.  q is
+    (B, Tq, NH, d_qk), k and v (B, Tk, NH, d).  Returns (o, lse); lse is None unless
+    return_lse (the inference mode skips the stats)."""
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("fwd_decode runs on the GPU only; got a CPU tensor")
+    et = _elem(q)
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, n, dev, et)
+    B, NH, Tq, dqk = _dims(q, layout)
+    Tk, dv = _dims(k, layout)[2], v.shape[3]
+    if seq_len_kv is not None:
+        _lengths(seq_len_kv, "seq_len_kv", B, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        shape = (B, Tq, NH, dv) if layout == "bthd" else (B, NH, Tq, dv)
+        out = torch.empty(shape, dtype=et, device=dev)
+    _need(out, "out", dev, et)
+    lse = torch.empty((B, NH, Tq), dtype=torch.float32, device=dev) if return_lse else None
+    with torch.cuda.device(dev):
+        _check(lib.attn_fwd_decode(_DTYPE_CODE[et], q.data_ptr(), _strides(q, layout), k.data_ptr(),
+                                   _strides(k, layout), v.data_ptr(), _strides(v, layout), out.data_ptr(),
+                                   _strides(out, layout), lse.data_ptr() if return_lse else None,
+                                   seq_len_kv.data_ptr() if seq_len_kv is not None else None,
+                                   B, NH, Tq, Tk, dqk, dv, float(scale), _stream(dev)))
+    return out, lse
 
 
 def _lengths(x: torch.Tensor, name: str, B: int, dev: torch.device) -> torch.Tensor:

@@ -114,7 +114,7 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   p.v = v; p.sv = cvt(sv);
   p.o = o; p.so = cvt(so);
   p.lse = lse;
-  p.B = B; p.NH = NH; p.T = T;
+  p.B = B; p.NH = NH; p.T = T; p.Tk = T;
   p.scale_log2 = scale * kLog2e;
   p.win = window > 0 ? window : attn53::kNoWindow;
   p.alibi = alibi;
@@ -314,6 +314,40 @@ attn_status attn_bwd_varlen(const void* q, attn_strides sq, const void* k, attn_
   if (seq_len_q == nullptr || seq_len_kv == nullptr) return ATTN_ERR_NULL;
   return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, seq_len_q, seq_len_kv, B, NH,
                   T, d_qk, d_v, scale, causal, 0, 0, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
+}
+
+attn_status attn_fwd_decode(attn_dtype dtype, const void* q, attn_strides sq, const void* k, attn_strides sk,
+                            const void* v, attn_strides sv, void* o, attn_strides so, float* lse,
+                            const int32_t* seq_len_kv, int B, int NH, int Tq, int Tk, int d_qk, int d_v,
+                            float scale, void* stream) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_ARG;
+  attn_status st = check_sizes(B, NH, Tq, d_qk, d_v);
+  if (st != ATTN_OK) return st;
+  if ((st = check_sizes(B, NH, Tk, d_qk, d_v)) != ATTN_OK) return st;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_ARG;
+  Extent eq, ek, ev, eo;
+  if ((st = check_tensor(q, sq, B, NH, Tq, d_qk, &eq)) != ATTN_OK) return st;
+  if ((st = check_tensor(k, sk, B, NH, Tk, d_qk, &ek)) != ATTN_OK) return st;
+  if ((st = check_tensor(v, sv, B, NH, Tk, d_v, &ev)) != ATTN_OK) return st;
+  if ((st = check_tensor(o, so, B, NH, Tq, d_v, &eo)) != ATTN_OK) return st;
+  if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_ALIGN;
+  if (seq_len_kv != nullptr && !int_ptr_ok(seq_len_kv)) return ATTN_ERR_ALIGN;
+  if (overlaps(eo, eq) || overlaps(eo, ek) || overlaps(eo, ev)) return ATTN_ERR_ALIAS;
+  if (lse != nullptr) {
+    const Extent el{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + (uintptr_t)B * NH * Tq * 4u};
+    if (overlaps(el, eq) || overlaps(el, ek) || overlaps(el, ev) || overlaps(el, eo)) return ATTN_ERR_ALIAS;
+  }
+  FwdParams p{};
+  p.q = q; p.sq = cvt(sq);
+  p.k = k; p.sk = cvt(sk);
+  p.v = v; p.sv = cvt(sv);
+  p.o = o; p.so = cvt(so);
+  p.lse = lse;
+  p.B = B; p.NH = NH; p.T = Tq; p.Tk = Tk;
+  p.scale_log2 = scale * kLog2e;
+  p.win = attn53::kNoWindow;
+  p.seq_k = seq_len_kv;  // with items == nullptr: per-sequence key lengths only
+  return hip_status(attn53::launch_fwd(p, elem_type(dtype), d_qk, d_v, false, (hipStream_t)stream));
 }
 
 attn_status attn_fwd_typed(attn_dtype dtype, const void* q, attn_strides sq, const void* k, attn_strides sk,

@@ -63,13 +63,14 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in a scalar register
   const int T = p.T;
   const int nqb = (T + FWD_BM - 1) / FWD_BM;
-  // Lq / Lk: valid query / key rows of this batch (T, or the padded-batch lengths)
-  int qb, b, h, Lq = T, Lk = T;
+  // Lq / Lk: valid query / key rows of this batch (T and Tk, or the padded-batch lengths)
+  int qb, b, h, Lq = T, Lk = p.Tk;
   if (p.items == nullptr) {
     const Item item = schedule(blockIdx.x, p.B * p.NH);
     qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
     b = item.bh / p.NH;
     h = item.bh % p.NH;
+    if (p.seq_k != nullptr) Lk = batch_len(p.seq_k, b, p.Tk);  // decode: per-sequence cache length
   } else {
     const ListItem it = list_item(blockIdx.x, p.NH, p.items);
     b = it.b;
@@ -262,24 +263,40 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int n_mask = n_kv - first_masked;
   const int mid_end = WIN ? n_tiles - max(0, j_full - j_lo) : n_kv;
   int it = 0;
-  for (; it < n_mask; ++it) {
-    if (it & 1)
-      step(it, B1, MASK);
-    else
-      step(it, B0, MASK);
-  }
-  if ((it & 1) && it < mid_end) step(it++, B1, NOMASK);
-  for (; it + 1 < mid_end; it += 2) {
-    step(it, B0, NOMASK);
-    step(it + 1, B1, NOMASK);
-  }
-  if (it < mid_end) step(it++, B0, NOMASK);
-  if constexpr (WIN) {
+  if (qw >= Lq) {
+    // Every row of this wavefront is padding (the short last query block of a padded
+    // batch, a decode step's single query row, or rows past T): it keeps its share of the
+    // workgroup's tile loads and barriers and skips the arithmetic.
     for (; it < n_tiles; ++it) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (it + 1 < n_tiles) {
+        if (it & 1)
+          load_kv((n_kv - 2 - it) * FWD_BN, B0);
+        else
+          load_kv((n_kv - 2 - it) * FWD_BN, B1);
+      }
+    }
+  } else {
+    for (; it < n_mask; ++it) {
       if (it & 1)
         step(it, B1, MASK);
       else
         step(it, B0, MASK);
+    }
+    if ((it & 1) && it < mid_end) step(it++, B1, NOMASK);
+    for (; it + 1 < mid_end; it += 2) {
+      step(it, B0, NOMASK);
+      step(it + 1, B1, NOMASK);
+    }
+    if (it < mid_end) step(it++, B0, NOMASK);
+    if constexpr (WIN) {
+      for (; it < n_tiles; ++it) {
+        if (it & 1)
+          step(it, B1, MASK);
+        else
+          step(it, B0, MASK);
+      }
     }
   }
 

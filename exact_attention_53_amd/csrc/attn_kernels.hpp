@@ -16,7 +16,8 @@ struct FwdParams {
   const void* v; Strides sv;
   void* o; Strides so;
   float* lse;              // (B, NH, T) or nullptr
-  int B, NH, T;
+  int B, NH, T;            // T: query rows (and key rows unless Tk says otherwise)
+  int Tk;                  // key / value rows (decode: the cache length; otherwise T)
   float scale_log2;        // scale * log2(e)
   int win;                 // causal sliding window: query i sees keys i-win+1 .. i
                            // (1 << 30 when there is no window)

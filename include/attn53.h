@@ -291,6 +291,32 @@ attn_status attn_bwd_typed(attn_dtype dtype,
                            void* workspace, size_t workspace_bytes, void* stream,
                            unsigned stages);
 
+/*
+ * attn_fwd_decode — the inference-shaped forward of a decode step [SA8 1.2, 1.3]: Tq
+ * query rows per sequence (the newest tokens) attend to all Tk key/value rows of that
+ * sequence's cache, no causal mask among them (every query sees every cached key), in
+ * the pages' inference mode when lse is NULL.  Tq and Tk are separate sizes:
+ *   q     : (B, NH, Tq, d_qk), strides sq             (read)
+ *   k, v  : (B, NH, Tk, d_qk / d_v), strides sk, sv   (read)
+ *   o     : (B, NH, Tq, d_v), strides so              (written)
+ *   lse   : (B, NH, Tq) fp32 contiguous, or NULL      (written)
+ *   seq_len_kv : NULL (every cache holds Tk rows) or B int32 on the device, clamped to
+ *                [0, Tk]: sequence b attends to its first seq_len_kv[b] key rows; with
+ *                0 rows its O is 0 and its LSE -inf.
+ * A workgroup owns 128 query rows of one (b, h) and streams the whole cache once;
+ * wavefronts whose rows are all past Tq skip the arithmetic, so a one-row decode step
+ * costs the cache read.  dtype, layout rules and errors as for attn_fwd_typed.
+ */
+attn_status attn_fwd_decode(attn_dtype dtype,
+                            const void* q, attn_strides sq,
+                            const void* k, attn_strides sk,
+                            const void* v, attn_strides sv,
+                            void* o, attn_strides so,
+                            float* lse,
+                            const int32_t* seq_len_kv,
+                            int B, int NH, int Tq, int Tk, int d_qk, int d_v,
+                            float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,3 +162,20 @@ def test_typed_validation(lib):
             assert f(dt, causal=0, alibi=1) == ARG
             assert f(dt, alibi=1, window=16) == ARG
             assert f(dt, alibi=1, lq=GOOD + 0xa00000, lk=GOOD + 0xa00100) == ARG
+
+
+def test_decode_validation(lib):
+    """attn_fwd_decode: separate query and key row counts, validated on the host."""
+    sq, sk = strides(4, 2, 64), strides(64, 2, 64)
+
+    def dec(dtype=0, q=GOOD, o=GOOD + 0x300000, Tq=4, Tk=64, lens=None, scale=0.125):
+        return lib.attn_fwd_decode(dtype, q, sq, GOOD + 0x100000, sk, GOOD + 0x200000, sk, o, sq, None, lens,
+                                   1, 2, Tq, Tk, 64, 64, scale, None)
+
+    assert dec(dtype=5) == ARG
+    assert dec(q=None) == NULL
+    assert dec(Tq=0) == SHAPE
+    assert dec(Tk=0) == SHAPE
+    assert dec(scale=0.0) == ARG
+    assert dec(o=GOOD + 0x100000) == ALIAS       # output overlaps k
+    assert dec(lens=GOOD + 0xa00002) == ALIGN    # lengths must be 4-byte aligned

@@ -72,6 +72,9 @@ WORKLOADS: Dict[str, Workload] = {
     "window": Workload("window", 4, 16, 8192, 128, 128, True, 53007, window=1024),
     # the headline shape with the ALiBi bias
     "alibi": Workload("alibi", 4, 16, 8192, 128, 128, True, 53008, alibi=True),
+    # one decode step (inference forward, no stats): one query row per sequence against
+    # an 8192-row key/value cache, non-causal
+    "decode": Workload("decode", 16, 16, 8192, 128, 128, False, 53009),
 }
 
 
