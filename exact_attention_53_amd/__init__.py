@@ -83,7 +83,9 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_typed.restype = i
     lib.attn_fwd_typed.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.attn_fwd_decode.restype = i
-    lib.attn_fwd_decode.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_decode.argtypes = [i, vp, S, vp, S, vp, S, vp, S, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.attn_fwd_decode_workspace_bytes.restype = sz
+    lib.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_typed.restype = i
     lib.attn_bwd_typed.argtypes = [i] + bwd_args[:17] + [vp, vp] + bwd_args[17:24] + [i, i] + bwd_args[24:] + [ctypes.c_uint]
     _lib = lib
@@ -241,7 +243,8 @@ def bwd_packed(qkv, o, lse, do, causal: bool = True, scale: Optional[float] = No
 
 
 def fwd_decode(q, k, v, seq_len_kv: Optional[torch.Tensor] = None, scale: Optional[float] = None,
-               return_lse: bool = False, layout: str = "bthd", out: Optional[torch.Tensor] = None):
+               return_lse: bool = False, layout: str = "bthd", out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None):
     """Decode-step forward: the Tq query rows of each sequence attend to all rows of its
     key/value cache (Tk rows, or seq_len_kv[b] of them), no causal mask.  q is
     (B, Tq, NH, d_qk), k and v (B, Tk, NH, d).  Returns (o, lse); lse is None unless
@@ -264,12 +267,18 @@ def fwd_decode(q, k, v, seq_len_kv: Optional[torch.Tensor] = None, scale: Option
         out = torch.empty(shape, dtype=et, device=dev)
     _need(out, "out", dev, et)
     lse = torch.empty((B, NH, Tq), dtype=torch.float32, device=dev) if return_lse else None
+    need = int(lib.attn_fwd_decode_workspace_bytes(B, NH, Tq, Tk, dqk, dv))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         _check(lib.attn_fwd_decode(_DTYPE_CODE[et], q.data_ptr(), _strides(q, layout), k.data_ptr(),
                                    _strides(k, layout), v.data_ptr(), _strides(v, layout), out.data_ptr(),
                                    _strides(out, layout), lse.data_ptr() if return_lse else None,
                                    seq_len_kv.data_ptr() if seq_len_kv is not None else None,
-                                   B, NH, Tq, Tk, dqk, dv, float(scale), _stream(dev)))
+                                   B, NH, Tq, Tk, dqk, dv, float(scale),
+                                   workspace.data_ptr() if workspace is not None else None,
+                                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                   _stream(dev)))
     return out, lse
 
 

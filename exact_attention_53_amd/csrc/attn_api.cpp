@@ -316,10 +316,33 @@ attn_status attn_bwd_varlen(const void* q, attn_strides sq, const void* k, attn_
                   T, d_qk, d_v, scale, causal, 0, 0, deterministic, workspace, workspace_bytes, stream, ATTN_BWD_ALL);
 }
 
+// Key split of a decode step: enough workgroups for two per CU (512), chunks of at least
+// 1024 keys, at most 64 splits.
+void decode_split(int B, int NH, int Tq, int Tk, int* nsplit, int* chunk) {
+  const int64_t nbase = (int64_t)((Tq + kFwdBlock - 1) / kFwdBlock) * B * NH;
+  int64_t n = 1;
+  if (nbase < 512) n = std::min<int64_t>((512 + nbase - 1) / nbase, (Tk + 1023) / 1024);
+  n = std::max<int64_t>(1, std::min<int64_t>(n, 64));
+  const int64_t c = ((Tk + n - 1) / n + 63) / 64 * 64;
+  *chunk = (int)c;
+  *nsplit = (int)((Tk + c - 1) / c);
+}
+
+size_t decode_ws_bytes(int B, int NH, int Tq, int Tk, int d_v) {
+  int n, c;
+  decode_split(B, NH, Tq, Tk, &n, &c);
+  return n > 1 ? align256((size_t)n * B * NH * Tq * (d_v + 1) * 4) : 0;
+}
+
+size_t attn_fwd_decode_workspace_bytes(int B, int NH, int Tq, int Tk, int d_qk, int d_v) {
+  if (check_sizes(B, NH, Tq, d_qk, d_v) != ATTN_OK || check_sizes(B, NH, Tk, d_qk, d_v) != ATTN_OK) return 0;
+  return decode_ws_bytes(B, NH, Tq, Tk, d_v);
+}
+
 attn_status attn_fwd_decode(attn_dtype dtype, const void* q, attn_strides sq, const void* k, attn_strides sk,
                             const void* v, attn_strides sv, void* o, attn_strides so, float* lse,
                             const int32_t* seq_len_kv, int B, int NH, int Tq, int Tk, int d_qk, int d_v,
-                            float scale, void* stream) {
+                            float scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_ARG;
   attn_status st = check_sizes(B, NH, Tq, d_qk, d_v);
   if (st != ATTN_OK) return st;
@@ -347,7 +370,18 @@ attn_status attn_fwd_decode(attn_dtype dtype, const void* q, attn_strides sq, co
   p.scale_log2 = scale * kLog2e;
   p.win = attn53::kNoWindow;
   p.seq_k = seq_len_kv;  // with items == nullptr: per-sequence key lengths only
-  return hip_status(attn53::launch_fwd(p, elem_type(dtype), d_qk, d_v, false, (hipStream_t)stream));
+  int nsplit, chunk;
+  decode_split(B, NH, Tq, Tk, &nsplit, &chunk);
+  if (nsplit == 1) return hip_status(attn53::launch_fwd(p, elem_type(dtype), d_qk, d_v, false, (hipStream_t)stream));
+  const size_t need = decode_ws_bytes(B, NH, Tq, Tk, d_v);
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || workspace_bytes < need)
+    return ATTN_ERR_WORKSPACE;
+  const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+  if (overlaps(ew, eq) || overlaps(ew, ek) || overlaps(ew, ev) || overlaps(ew, eo)) return ATTN_ERR_ALIAS;
+  p.nsplit = nsplit;
+  p.kv_chunk = chunk;
+  p.part = static_cast<float*>(workspace);
+  return hip_status(attn53::launch_fwd_split(p, elem_type(dtype), d_qk, d_v, (hipStream_t)stream));
 }
 
 attn_status attn_fwd_typed(attn_dtype dtype, const void* q, attn_strides sq, const void* k, attn_strides sk,

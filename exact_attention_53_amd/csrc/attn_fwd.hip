@@ -48,7 +48,9 @@ constexpr float kSumLimit = 256.f;        // 2^kRescaleThreshold
 
 // WIN (with CAUSAL only): sliding window of p.win keys.  ALIBI (with CAUSAL only): the
 // linear bias -m_h (i - j) added to the scaled scores.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI>
+// SPLIT (non-causal only): one key chunk of p.kv_chunk keys per workgroup, partial
+// results to p.part.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool SPLIT = false>
 __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr int KS = DQK / 16;
   constexpr int NDT = DV / 32;
@@ -65,8 +67,10 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int nqb = (T + FWD_BM - 1) / FWD_BM;
   // Lq / Lk: valid query / key rows of this batch (T and Tk, or the padded-batch lengths)
   int qb, b, h, Lq = T, Lk = p.Tk;
+  const int nbase = nqb * p.B * p.NH;
+  const int split = SPLIT ? (int)blockIdx.x / nbase : 0;
   if (p.items == nullptr) {
-    const Item item = schedule(blockIdx.x, p.B * p.NH);
+    const Item item = schedule(SPLIT ? (int)blockIdx.x % nbase : (int)blockIdx.x, p.B * p.NH);
     qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
     b = item.bh / p.NH;
     h = item.bh % p.NH;
@@ -92,11 +96,25 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int qw = q0 + 32 * w;
   const int my_q = qw + lq;
   const int W = WIN ? p.win : kNoWindow;
-  const int kv_end = CAUSAL ? min(Lk, q0 + FWD_BM) : Lk;
+  // key split: this workgroup's keys are [c0, kv_end)
+  const int c0 = SPLIT ? split * p.kv_chunk : 0;
+  const int kv_end = CAUSAL ? min(Lk, q0 + FWD_BM) : SPLIT ? min(Lk, c0 + p.kv_chunk) : Lk;
   const int n_kv = (kv_end + FWD_BN - 1) / FWD_BN;
   // sliding window: tiles below j_lo hold no key of any row's window
-  const int j_lo = WIN ? max(0, q0 - W + 1) / FWD_BN : 0;
+  const int j_lo = WIN ? max(0, q0 - W + 1) / FWD_BN : SPLIT ? c0 / FWD_BN : 0;
   const int n_tiles = n_kv - j_lo;
+  float* part_o = SPLIT ? p.part + ((int64_t)split * p.B * p.NH + bh) * T * DV : nullptr;
+  float* part_l = SPLIT ? p.part + (int64_t)p.nsplit * p.B * p.NH * T * DV + ((int64_t)split * p.B * p.NH + bh) * T
+                        : nullptr;
+  if (SPLIT && n_tiles <= 0) {  // an empty key chunk: O = 0, LSE = -inf for the merge
+    if (my_q < T) {
+#pragma unroll
+      for (int y = 0; y < DV / 8; ++y)
+        *reinterpret_cast<f32x4*>(part_o + (int64_t)my_q * DV + 8 * y + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (g == 0) part_l[my_q] = -INFINITY;
+    }
+    return;
+  }
   if (q0 >= Lq || n_kv == 0) {  // padding rows only, or no keys: O = 0, LSE = -inf
     if (my_q < T) {
       E* orow = og + (int64_t)my_q * p.so.t;
@@ -261,7 +279,7 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int first_masked = min(min(first_ragged, CAUSAL ? q0 / FWD_BN : n_kv), n_kv);
   const int j_full = WIN ? min((max(0, q0 + FWD_BM - W) + FWD_BN - 1) / FWD_BN, first_masked) : 0;
   const int n_mask = n_kv - first_masked;
-  const int mid_end = WIN ? n_tiles - max(0, j_full - j_lo) : n_kv;
+  const int mid_end = WIN ? n_tiles - max(0, j_full - j_lo) : n_tiles;
   int it = 0;
   if (qw >= Lq) {
     // Every row of this wavefront is padding (the short last query block of a padded
@@ -302,6 +320,23 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 
   // deferred normalisation and stats
   const float l_tot = sum_halves(l_run);
+  if constexpr (SPLIT) {  // normalised partial O and LSE of this key chunk, fp32
+    if (my_q < T) {
+      const bool live = my_q < Lq;
+      const float inv = live ? 1.f / l_tot : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[dt][4 * a + e] * inv;
+          *reinterpret_cast<f32x4*>(part_o + (int64_t)my_q * DV + 32 * dt + 8 * a + 4 * g) = v;
+        }
+      if (g == 0) part_l[my_q] = live ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (my_q < Lq) {
     const float inv = 1.f / l_tot;
     E* orow = og + (int64_t)my_q * p.so.t;
@@ -344,6 +379,71 @@ static hipError_t fwd_dispatch(const FwdParams& p, int d_qk, int d_v, bool causa
   if (d_qk == 128 && d_v == 128) return fwd_launch<E, 128, 128>(p, causal, s);
   if (d_qk == 192 && d_v == 128) return fwd_launch<E, 192, 128>(p, causal, s);
   return hipErrorInvalidValue;
+}
+
+// Merge of the key-split partials: for each query row, O = sum_c e^(LSE_c - LSE) O_c and
+// LSE = ln sum_c e^(LSE_c), over the splits in one fixed order.  One thread per row and 8
+// columns.
+template <class E, int DV>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
+  constexpr int G = DV / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)p.B * p.NH * p.T;
+  if (gid >= rows * G) return;
+  const int64_t row = gid / G;  // over (b, h, t)
+  const int c = (int)(gid % G);
+  const int t = (int)(row % p.T);
+  const int bh = (int)(row / p.T);
+  const int b = bh / p.NH, h = bh % p.NH;
+  const int64_t plane = (int64_t)p.B * p.NH * p.T;
+  const float* lse_c = p.part + (int64_t)p.nsplit * plane * DV + row;
+  float m = -INFINITY;
+  for (int k = 0; k < p.nsplit; ++k) m = fmaxf(m, lse_c[k * plane]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  if (m != -INFINITY) {
+    for (int k = 0; k < p.nsplit; ++k) {
+      const float wgt = exp2_fast((lse_c[k * plane] - m) * kLog2e);
+      const float* oc = p.part + (k * plane + row) * DV + 8 * c;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(oc), x1 = *reinterpret_cast<const f32x4*>(oc + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += wgt * x0[e];
+        acc[4 + e] += wgt * x1[e];
+      }
+      sum += wgt;
+    }
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  vec8<E> v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (E)(acc[e] * inv);
+  E* dst = (E*)p.o + b * p.so.b + h * p.so.h + (int64_t)t * p.so.t + 8 * c;
+  *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, v);
+  if (p.lse != nullptr && c == 0) p.lse[row] = m == -INFINITY ? -INFINITY : m + log2_fast(sum) * kLn2;
+}
+
+template <class E, int DQK, int DV>
+static hipError_t fwd_split_t(const FwdParams& p, hipStream_t s) {
+  const int nbase = (p.T + FWD_BM - 1) / FWD_BM * p.B * p.NH;
+  hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, false, false, false, true>), dim3(nbase * p.nsplit), dim3(FWD_NT), 0,
+                     s, p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  const int64_t threads = (int64_t)p.B * p.NH * p.T * (DV / 8);
+  hipLaunchKernelGGL((fwd_merge_kernel<E, DV>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class E>
+static hipError_t fwd_split_dispatch(const FwdParams& p, int d_qk, int d_v, hipStream_t s) {
+  if (d_qk == 64 && d_v == 64) return fwd_split_t<E, 64, 64>(p, s);
+  if (d_qk == 128 && d_v == 128) return fwd_split_t<E, 128, 128>(p, s);
+  if (d_qk == 192 && d_v == 128) return fwd_split_t<E, 192, 128>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_split(const FwdParams& p, ElemType et, int d_qk, int d_v, hipStream_t s) {
+  return et == ELEM_F16 ? fwd_split_dispatch<f16>(p, d_qk, d_v, s) : fwd_split_dispatch<bf16>(p, d_qk, d_v, s);
 }
 
 hipError_t launch_fwd(const FwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s) {

@@ -18,6 +18,11 @@ struct FwdParams {
   float* lse;              // (B, NH, T) or nullptr
   int B, NH, T;            // T: query rows (and key rows unless Tk says otherwise)
   int Tk;                  // key / value rows (decode: the cache length; otherwise T)
+  // Key split (decode with few (b, h) pairs): workgroup id / nbase is the split; split c
+  // covers keys [c kv_chunk, (c+1) kv_chunk) and writes its normalised fp32 partial O
+  // (nsplit, B*NH, T, d_v) and LSE (nsplit, B*NH, T) to `part` for a merge kernel.
+  int nsplit, kv_chunk;
+  float* part;
   float scale_log2;        // scale * log2(e)
   int win;                 // causal sliding window: query i sees keys i-win+1 .. i
                            // (1 << 30 when there is no window)
@@ -75,6 +80,8 @@ enum ElemType { ELEM_BF16 = 0, ELEM_F16 = 1 };
 
 // Launchers: return hipSuccess or the launch error.  d_qk/d_v already validated.
 hipError_t launch_fwd(const FwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s);
+// Decode with a key split (p.nsplit > 1, non-causal): partial kernels, then the merge.
+hipError_t launch_fwd_split(const FwdParams& p, ElemType et, int d_qk, int d_v, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int d_v, bool zero_acc, hipStream_t s);
 hipError_t launch_bwd_main(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, bool deterministic,
                            hipStream_t s);

@@ -305,8 +305,17 @@ attn_status attn_bwd_typed(attn_dtype dtype,
  *                0 rows its O is 0 and its LSE -inf.
  * A workgroup owns 128 query rows of one (b, h) and streams the whole cache once;
  * wavefronts whose rows are all past Tq skip the arithmetic, so a one-row decode step
- * costs the cache read.  dtype, layout rules and errors as for attn_fwd_typed.
+ * costs the cache read.  With fewer than 512 such workgroups the cache is split into
+ * chunks of keys (at least 1024 keys each, at most 64 chunks) processed by workgroups
+ * of their own; each writes its normalised fp32 partial O and LSE, and a merge kernel
+ * combines them in one fixed order: O = sum_c e^(LSE_c - LSE) O_c, LSE = ln sum_c e^(LSE_c).
+ *   workspace : device memory of at least attn_fwd_decode_workspace_bytes(...) bytes
+ *               (0 when no split is needed; then it may be NULL), 16-byte aligned,
+ *               owned by the caller, clobbered.  Too small: ATTN_ERR_WORKSPACE.
+ * dtype, layout rules and errors as for attn_fwd_typed.
  */
+size_t attn_fwd_decode_workspace_bytes(int B, int NH, int Tq, int Tk, int d_qk, int d_v);
+
 attn_status attn_fwd_decode(attn_dtype dtype,
                             const void* q, attn_strides sq,
                             const void* k, attn_strides sk,
@@ -315,7 +324,7 @@ attn_status attn_fwd_decode(attn_dtype dtype,
                             float* lse,
                             const int32_t* seq_len_kv,
                             int B, int NH, int Tq, int Tk, int d_qk, int d_v,
-                            float scale, void* stream);
+                            float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

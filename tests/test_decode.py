@@ -72,3 +72,21 @@ def test_decode_fp16_and_bhtd():
     o, lse = attn.fwd_decode(perm(q), perm(k), perm(v), None, 1.0 / np.sqrt(d), return_lse=True, layout="bhtd")
     torch.cuda.synchronize()
     _check(q, k, v, [Tk] * B, o.permute(0, 2, 1, 3), lse, 1.0 / np.sqrt(d), (F16_RTOL, F16_ATOL))
+
+
+@pytest.mark.parametrize("Tq", [1, 3])
+def test_decode_key_split(Tq):
+    """Few (b, h) pairs and a long cache: the keys are split into chunks of >= 1024 (here
+    20 chunks) whose partial results are merged; caches of 20000, 5000, 1 and 1025 rows
+    leave different chunks empty."""
+    B, NH, Tk, d = 4, 2, 20000, 128
+    say(f"case decode key split Tq={Tq}")
+    q, k, v = _case(B, NH, Tq, Tk, d, d, 1201 + Tq)
+    dev = torch.device("cuda:0")
+    lens = [Tk, 5000, 1, 1025]
+    lk = torch.tensor(lens, dtype=torch.int32, device=dev)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = attn.fwd_decode(q.to(dev), k.to(dev), v.to(dev), lk, scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert attn.load().attn_fwd_decode_workspace_bytes(B, NH, Tq, Tk, d, d) > 0
+    _check(q, k, v, lens, o, lse, scale, (2e-2, 2e-3))
