@@ -33,12 +33,12 @@ PEAK_HBM_GBS = 8000.0
 # --copy-calibration 1024`, 1 GiB read and 1 GiB written per launch): FETCH_SIZE read
 # 524294.5 KiB there, WRITE_SIZE 1048576 KiB.  The figures hold only for the kernel
 # sources they were taken on, identified by a hash; any change makes them null.
-TRAFFIC_SOURCES = "83f0e86f8c4b6f21"
+TRAFFIC_SOURCES = "d6a1f96cd86b15b0"
 TRAFFIC_KIB = {  # kernel: (FETCH_SIZE, WRITE_SIZE) per dispatch
-    "attn_fwd": (1208233.25, 133173.5),
-    "bwd_preprocess": (133158.0, 4097.875),
-    "bwd_kv": (1268302.9375, 262144.0),
-    "bwd_dq": (837665.3125, 196323.5),
+    "attn_fwd": (1295011.8125, 133134.53125),
+    "bwd_preprocess": (133157.75, 4100.71875),
+    "bwd_kv": (1262104.5, 262144.0),
+    "bwd_dq": (842687.5, 196337.5),
 }
 FETCH_SCALE = 1048576.0 / 524294.5
 WRITE_SCALE = 1048576.0 / 1048576.0
