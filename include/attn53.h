@@ -1,6 +1,6 @@
 /*
  * attn53.h — C ABI of a fused, tiled, exact scaled-dot-product attention library for
- * AMD Instinct MI355X (gfx950).  Forward and backward, bf16 in/out, fp32 accumulation.
+ * AMD Instinct MI355X (gfx950).  Forward and backward, bf16 or fp16 in/out, fp32 accumulation.
  *
  * Pages cited (by title and section):
  *   [SA8]  "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析"
@@ -9,7 +9,8 @@
  *
  * Tensor conventions shared by every entry point
  * ---------------------------------------------
- *  - Q, K, V, O, dO, dQ, dK, dV are bf16 tensors with logical shape (B, NH, T, d).
+ *  - Q, K, V, O, dO, dQ, dK, dV are 16-bit tensors (bf16; fp16 through the entry points
+ *    that take an attn_dtype) with logical shape (B, NH, T, d).
  *    Each is described by a device pointer plus an attn_strides value holding its
  *    element strides along b, h and t; the stride along d is always 1.  This covers
  *    the (B, T, NH, d) layout of the pages' output O, a (B, NH, T, d) layout, and the
@@ -220,7 +221,7 @@ attn_status attn_bwd_varlen(const void* q, attn_strides sq,
 /*
  * 16-bit element types.  The pages run attention with 16-bit inputs and outputs and
  * fp32 accumulation, naming both fp16 and bf16 [SA8 1.3]; every entry point above takes
- * bf16.  The two entry points below take either type, named by `dtype`, for all of q, k,
+ * bf16.  The entry points below take either type, named by `dtype`, for all of q, k,
  * v, o, do_, dq, dk and dv of one call (LSE, D and the workspace stay fp32).  With fp16,
  * P and dS are rounded to fp16 (nearest even) before their products, as they are to bf16
  * in the bf16 path; the arithmetic is otherwise the same.
