@@ -114,6 +114,10 @@ def _strides(x: torch.Tensor, layout: str) -> Strides:
 
 
 def _dims(x: torch.Tensor, layout: str) -> Tuple[int, int, int, int]:
+    if x.dim() != 4:
+        raise ValueError(f"expected a 4-D tensor, got shape {tuple(x.shape)}")
+    if layout not in ("bthd", "bhtd"):
+        raise ValueError(f"layout must be 'bthd' or 'bhtd', not {layout!r}")
     B, a, c, d = x.shape
     return (B, c, a, d) if layout == "bthd" else (B, a, c, d)  # -> B, NH, T, d
 
@@ -126,6 +130,22 @@ def _need(x: torch.Tensor, name: str, dev: torch.device, dtype: torch.dtype = to
         raise TypeError(f"{name} must be {dtype} (the dtype of q), got {x.dtype}")
     if x.device != dev:
         raise ValueError(f"{name} is on {x.device}, expected {dev}")
+
+
+def _shape(x: torch.Tensor, name: str, layout: str, B: int, NH: int, T: int, d: int):
+    """Checks that x is the 4-D (B, NH, T, d) tensor (in `layout` order) that the call
+    needs: the C ABI sees only pointers and strides, so a smaller tensor would be read or
+    written past its end."""
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be a 4-D tensor, got shape {tuple(x.shape)}")
+    got = _dims(x, layout)
+    if got != (B, NH, T, d):
+        raise ValueError(f"{name} has (B, NH, T, d) = {got}, expected {(B, NH, T, d)}")
+
+
+def _on_gpu(fn: str, dev: torch.device):
+    if dev.type != "cuda":
+        raise ValueError(f"{fn} runs on the GPU only; got a CPU tensor")
 
 
 def _elem(q: torch.Tensor) -> torch.dtype:
@@ -146,15 +166,18 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
     (inference mode: the kernel skips the stats).  window > 0 (causal only): query i sees
     keys i-window+1 .. i.  alibi (causal only): linear bias -m_h (i - j) on the scaled
     scores, m_h = 2^(-8 (h+1) / NH)."""
-    lib = load()
+    B, NH, T, dqk = _dims(q, layout)
+    dv = v.shape[-1]
+    _shape(k, "k", layout, B, NH, T, dqk)
+    _shape(v, "v", layout, B, NH, T, dv)
+    if out is not None:
+        _shape(out, "out", layout, B, NH, T, dv)
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("fwd runs on the GPU only; got a CPU tensor")
+    _on_gpu("fwd", dev)
+    lib = load()
     et = _elem(q)
     for n, x in (("q", q), ("k", k), ("v", v)):
         _need(x, n, dev, et)
-    B, NH, T, dqk = _dims(q, layout)
-    dv = v.shape[3]
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
     if out is None:
@@ -194,15 +217,18 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
         alibi: bool = False):
     """Exact attention backward.  Returns (dq, dk, dv).  window, alibi: the forward's
     sliding window (0 = none) and ALiBi flag."""
-    lib = load()
+    B, NH, T, dqk = _dims(q, layout)
+    dvd = v.shape[-1]
+    for n, x, d in (("k", k, dqk), ("v", v, dvd), ("o", o, dvd), ("do", do, dvd), ("dq", dq, dqk), ("dk", dk, dqk),
+                    ("dv", dv, dvd)):
+        if x is not None:
+            _shape(x, n, layout, B, NH, T, d)
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("bwd runs on the GPU only; got a CPU tensor")
+    _on_gpu("bwd", dev)
+    lib = load()
     et = _elem(q)
     for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _need(x, n, dev, et)
-    B, NH, T, dqk = _dims(q, layout)
-    dvd = v.shape[3]
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
     if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
@@ -249,15 +275,20 @@ def fwd_decode(q, k, v, seq_len_kv: Optional[torch.Tensor] = None, scale: Option
     key/value cache (Tk rows, or seq_len_kv[b] of them), no causal mask.  q is
     (B, Tq, NH, d_qk), k and v (B, Tk, NH, d).  Returns (o, lse); lse is None unless
     return_lse (the inference mode skips the stats)."""
-    lib = load()
+    B, NH, Tq, dqk = _dims(q, layout)
+    if k.dim() != 4:
+        raise ValueError(f"k must be a 4-D tensor, got shape {tuple(k.shape)}")
+    Tk, dv = _dims(k, layout)[2], v.shape[-1]
+    _shape(k, "k", layout, B, NH, Tk, dqk)
+    _shape(v, "v", layout, B, NH, Tk, dv)
+    if out is not None:
+        _shape(out, "out", layout, B, NH, Tq, dv)
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("fwd_decode runs on the GPU only; got a CPU tensor")
+    _on_gpu("fwd_decode", dev)
+    lib = load()
     et = _elem(q)
     for n, x in (("q", q), ("k", k), ("v", v)):
         _need(x, n, dev, et)
-    B, NH, Tq, dqk = _dims(q, layout)
-    Tk, dv = _dims(k, layout)[2], v.shape[3]
     if seq_len_kv is not None:
         _lengths(seq_len_kv, "seq_len_kv", B, dev)
     if scale is None:
@@ -296,15 +327,18 @@ def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causa
     """Forward on padded batches: batch b uses the first seq_len_q[b] query rows and the
     first seq_len_kv[b] key/value rows (int32 device tensors of B lengths); padding rows
     of o are written as 0 and of lse as -inf.  Returns (o, lse)."""
-    lib = load()
+    B, NH, T, dqk = _dims(q, layout)
+    dv = v.shape[-1]
+    _shape(k, "k", layout, B, NH, T, dqk)
+    _shape(v, "v", layout, B, NH, T, dv)
+    if out is not None:
+        _shape(out, "out", layout, B, NH, T, dv)
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("fwd_varlen runs on the GPU only; got a CPU tensor")
+    _on_gpu("fwd_varlen", dev)
+    lib = load()
     et = _elem(q)
     for n, x in (("q", q), ("k", k), ("v", v)):
         _need(x, n, dev, et)
-    B, NH, T, dqk = _dims(q, layout)
-    dv = v.shape[3]
     _lengths(seq_len_q, "seq_len_q", B, dev)
     _lengths(seq_len_kv, "seq_len_kv", B, dev)
     if scale is None:
@@ -335,15 +369,16 @@ def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.T
                workspace: Optional[torch.Tensor] = None):
     """Backward on padded batches (see fwd_varlen).  Returns (dq, dk, dv); padding rows
     are written as 0."""
-    lib = load()
+    B, NH, T, dqk = _dims(q, layout)
+    dvd = v.shape[-1]
+    for n, x, d in (("k", k, dqk), ("v", v, dvd), ("o", o, dvd), ("do", do, dvd)):
+        _shape(x, n, layout, B, NH, T, d)
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("bwd_varlen runs on the GPU only; got a CPU tensor")
+    _on_gpu("bwd_varlen", dev)
+    lib = load()
     et = _elem(q)
     for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _need(x, n, dev, et)
-    B, NH, T, dqk = _dims(q, layout)
-    dvd = v.shape[3]
     _lengths(seq_len_q, "seq_len_q", B, dev)
     _lengths(seq_len_kv, "seq_len_kv", B, dev)
     if scale is None:

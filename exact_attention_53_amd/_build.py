@@ -56,8 +56,36 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every source and links libattn53.so; returns its path."""
+def _includes(src: str, seen=None) -> set:
+    """src and every local header it includes (quoted #include, searched next to the
+    including file, then in include/), recursively."""
+    import re
+    seen = set() if seen is None else seen
+    if src in seen or not os.path.exists(src):
+        return seen
+    seen.add(src)
+    with open(src) as f:
+        for name in re.findall(r'^\s*#\s*include\s+"([^"]+)"', f.read(), flags=re.M):
+            for base in (os.path.dirname(src), INCLUDE, CSRC):
+                cand = os.path.normpath(os.path.join(base, name))
+                if os.path.exists(cand):
+                    _includes(cand, seen)
+                    break
+    return seen
+
+
+def _stale(obj: str, src: str) -> bool:
+    """True unless obj is newer than its source, the headers it includes and this script."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) >= t for d in _includes(src) | {os.path.abspath(__file__)})
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compiles every source and links libattn53.so; returns its path.  incremental:
+    skip objects newer than every source (a developer convenience; the default always
+    compiles everything)."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
@@ -74,8 +102,10 @@ def build(verbose: bool = False) -> str:
                 f"-DATTN_INST_DV={dv}", f"-DATTN_INST_MASK={mask}"]
         extra = KV_FLAGS if kind == "kv" and dqk <= 128 else []
         cmds.append([hipcc, *FLAGS, *extra, *defs, "-c", os.path.join(CSRC, "attn_bwd_inst.hip"), "-o", obj])
+    if incremental:
+        cmds = [c for c in cmds if _stale(c[-1], c[-3])]
     cmds.sort(key=lambda c: "attn_bwd_inst.hip" not in c[-3])  # longest compilations first
-    with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 8)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(len(cmds), os.cpu_count() or 8))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
@@ -97,4 +127,4 @@ def _check_kernel_stubs(path: str) -> None:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

@@ -47,6 +47,29 @@ attn_status check_tensor(const void* ptr, attn_strides s, int B, int NH, int T, 
 
 bool overlaps(const Extent& a, const Extent& b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// An output tensor must give every (b, h, t) row its own d elements: otherwise concurrent
+// workgroups write the same bytes.  Sufficient (and, for the layouts in use, necessary)
+// condition: with the dimensions of size > 1 sorted by stride, each stride is at least the
+// extent of everything inside it (d for the innermost).
+attn_status check_output_rows(attn_strides s, int B, int NH, int T, int d) {
+  struct Dim {
+    int64_t stride, size;
+  } dims[3] = {{s.b, B}, {s.h, NH}, {s.t, T}};
+  for (int i = 1; i < 3; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && dims[j].stride < dims[j - 1].stride; --j) {
+      const Dim t = dims[j];
+      dims[j] = dims[j - 1];
+      dims[j - 1] = t;
+    }
+  int64_t inner = d;
+  for (const Dim& x : dims) {
+    if (x.size <= 1) continue;
+    if (x.stride < inner) return ATTN_ERR_STRIDE;
+    inner = x.stride * x.size;
+  }
+  return ATTN_OK;
+}
+
 Strides cvt(attn_strides s) { return Strides{s.b, s.h, s.t}; }
 
 int64_t tpad(int T) { return ((int64_t)T + kRowPad - 1) / kRowPad * kRowPad; }
@@ -89,6 +112,7 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   if ((st = check_tensor(k, sk, B, NH, T, d_qk, &ek)) != ATTN_OK) return st;
   if ((st = check_tensor(v, sv, B, NH, T, d_v, &ev)) != ATTN_OK) return st;
   if ((st = check_tensor(o, so, B, NH, T, d_v, &eo)) != ATTN_OK) return st;
+  if ((st = check_output_rows(so, B, NH, T, d_v)) != ATTN_OK) return st;
   if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_ALIGN;
   if (overlaps(eo, eq) || overlaps(eo, ek) || overlaps(eo, ev)) return ATTN_ERR_ALIAS;
   Extent el{0, 0};
@@ -130,7 +154,7 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
 }
 
 size_t bwd_ws_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic, bool varlen) {
-  if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK) return 0;
+  if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK || (deterministic != 0 && deterministic != 1)) return 0;
   size_t n = 2 * ws_D_bytes(B, NH, T);  // D and LSE log2(e)
   if (!deterministic) n += ws_acc_bytes(B, NH, T, d_qk);
   if (varlen) n += ws_list_bytes(B, T, kKvBlock) + ws_list_bytes(B, T, attn53::dq_block_rows(d_qk));
@@ -164,6 +188,9 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   if ((st = check_tensor(dq, sdq, B, NH, T, d_qk, &edq)) != ATTN_OK) return st;
   if ((st = check_tensor(dk, sdk, B, NH, T, d_qk, &edk)) != ATTN_OK) return st;
   if ((st = check_tensor(dv, sdv, B, NH, T, d_v, &edv)) != ATTN_OK) return st;
+  if ((st = check_output_rows(sdq, B, NH, T, d_qk)) != ATTN_OK) return st;
+  if ((st = check_output_rows(sdk, B, NH, T, d_qk)) != ATTN_OK) return st;
+  if ((st = check_output_rows(sdv, B, NH, T, d_v)) != ATTN_OK) return st;
   if (lse == nullptr) return ATTN_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_ALIGN;
   const Extent el{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + (uintptr_t)B * NH * T * 4u};
@@ -353,6 +380,7 @@ attn_status attn_fwd_decode(attn_dtype dtype, const void* q, attn_strides sq, co
   if ((st = check_tensor(k, sk, B, NH, Tk, d_qk, &ek)) != ATTN_OK) return st;
   if ((st = check_tensor(v, sv, B, NH, Tk, d_v, &ev)) != ATTN_OK) return st;
   if ((st = check_tensor(o, so, B, NH, Tq, d_v, &eo)) != ATTN_OK) return st;
+  if ((st = check_output_rows(so, B, NH, Tq, d_v)) != ATTN_OK) return st;
   if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_ALIGN;
   if (seq_len_kv != nullptr && !int_ptr_ok(seq_len_kv)) return ATTN_ERR_ALIGN;
   if (overlaps(eo, eq) || overlaps(eo, ek) || overlaps(eo, ev)) return ATTN_ERR_ALIAS;

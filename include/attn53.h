@@ -22,8 +22,11 @@
  *  - T_q == T_k == T >= 1, any value; partial tiles are masked inside the kernels.
  *  - Every tensor pointer must be 16-byte aligned and every stride a non-negative
  *    multiple of 8 elements, so that all global accesses are 128-bit; the t stride is
- *    at most 2^24 elements.  Otherwise the call returns ATTN_ERR_ALIGN /
- *    ATTN_ERR_STRIDE.  There is no slow fallback.
+ *    at most 2^24 elements.  An output tensor (O, dQ, dK, dV) must also give each
+ *    (b, h, t) row d elements of its own: with its dimensions of size > 1 sorted by
+ *    stride, each stride is at least the extent of the dimensions inside it (d for the
+ *    innermost).  Otherwise the call returns ATTN_ERR_ALIGN / ATTN_ERR_STRIDE.  There is
+ *    no slow fallback.
  *  - LSE ("softmax stats" of [SA8 1.2, 1.3]) is fp32, contiguous (B, NH, T), and holds
  *    the natural-log logsumexp of each row of S = scale * Q K^T (mask applied).
  *  - causal = 1 masks key j > query i (top-left aligned, [SA8 2.2] loop bound).
@@ -58,7 +61,8 @@ typedef enum {
   ATTN_ERR_NULL = 1,       /* a required pointer is NULL                         */
   ATTN_ERR_SHAPE = 2,      /* B, NH or T < 1, or the sizes overflow              */
   ATTN_ERR_HEADDIM = 3,    /* (d_qk, d_v) not one of the supported pairs          */
-  ATTN_ERR_STRIDE = 4,     /* a stride negative, not a multiple of 8, t > 2^24    */
+  ATTN_ERR_STRIDE = 4,     /* a stride negative, not a multiple of 8, t > 2^24,   */
+                           /* or an output whose rows would share elements       */
   ATTN_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned                    */
   ATTN_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required             */
   ATTN_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed          */
@@ -99,10 +103,13 @@ attn_status attn_fwd(const void* q, attn_strides sq,
                      float scale, int causal, void* stream);
 
 /*
- * attn_bwd_workspace_bytes — device workspace that attn_bwd needs for these sizes.
- * Holds D_i = sum_k dO_ik O_ik and LSE_i log2(e) (fp32, one per row, rows padded to
- * a multiple of 128) and, in atomic mode, the fp32 dQ accumulator.  Returns 0 for
- * invalid sizes.
+ * attn_bwd_workspace_bytes — device workspace that attn_bwd needs for these sizes.  The
+ * cuDNN SDPA path of [SA8 1.3] asks the library for the size of the work memory a call
+ * needs and hands it that much memory; here the caller queries this size and owns the
+ * buffer (the library keeps no workspace of its own).  Holds D_i = sum_k dO_ik O_ik and
+ * LSE_i log2(e) (fp32, one per row, rows padded to a multiple of 128) and, in atomic
+ * mode, the fp32 dQ accumulator (B * NH * Tpad * d_qk fp32).  Pure function of its
+ * arguments; launches nothing.  Returns 0 for invalid sizes or flags.
  */
 size_t attn_bwd_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic);
 

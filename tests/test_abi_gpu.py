@@ -1,0 +1,58 @@
+"""The two core entry points, attn_fwd and attn_bwd, called through ctypes directly
+(not through the binding's staged or typed paths), against the CPU oracle.
+
+attn_bwd runs every backward stage in one call; it must equal three attn_bwd_staged
+calls bit for bit in the deterministic mode.
+"""
+import ctypes
+
+import pytest
+import torch
+
+import exact_attention_53_amd as attn
+import workloads
+from tests.gpu_cases import compare, oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _st(x):
+    # (B, T, NH, d) tensor -> element strides along b, h, t
+    return attn.Strides(x.stride(0), x.stride(2), x.stride(1))
+
+
+@pytest.mark.parametrize("deterministic", [0, 1], ids=["atomic", "determ"])
+@pytest.mark.parametrize("dims,T,causal", [((64, 64), 200, 1), ((128, 128), 333, 1), ((128, 128), 256, 0),
+                                           ((192, 128), 129, 1)])
+def test_core_entry_points_direct(dims, T, causal, deterministic):
+    dqk, dv = dims
+    w = workloads.Workload(f"abi_T{T}_d{dqk}", 2, 3, T, dqk, dv, bool(causal), 400 + T)
+    say(f"case direct ABI {w.name} causal={causal} det={deterministic}")
+    lib = attn.load()
+    cpu = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (cpu[n].to(dev) for n in ("q", "k", "v", "do"))
+    B, NH = w.B, w.NH
+    o = torch.empty(B, T, NH, dv, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, NH, T, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    st = lib.attn_fwd(q.data_ptr(), _st(q), k.data_ptr(), _st(k), v.data_ptr(), _st(v), o.data_ptr(), _st(o),
+                      lse.data_ptr(), B, NH, T, dqk, dv, ctypes.c_float(w.scale), causal, stream)
+    assert st == 0, lib.attn_status_string(st)
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    nbytes = lib.attn_bwd_workspace_bytes(B, NH, T, dqk, dv, deterministic)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    st = lib.attn_bwd(q.data_ptr(), _st(q), k.data_ptr(), _st(k), v.data_ptr(), _st(v), o.data_ptr(), _st(o),
+                      lse.data_ptr(), do.data_ptr(), _st(do), dq.data_ptr(), _st(dq), dk.data_ptr(), _st(dk),
+                      dvv.data_ptr(), _st(dvv), B, NH, T, dqk, dv, ctypes.c_float(w.scale), causal, deterministic,
+                      ws.data_ptr(), nbytes, stream)
+    assert st == 0, lib.attn_status_string(st)
+    torch.cuda.synchronize()
+    got = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dvv.cpu()}
+    compare(w, got, oracle(w, cpu))
+    if deterministic:
+        dq2, dk2, dv2 = attn.bwd(q, k, v, o, lse, do, bool(causal), w.scale, deterministic=True)
+        torch.cuda.synchronize()
+        for n, a, b in (("dq", dq, dq2), ("dk", dk, dk2), ("dv", dvv, dv2)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"attn_bwd vs staged: {n} differs"

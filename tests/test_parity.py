@@ -126,7 +126,9 @@ FULL = [
     ("mid_full", False, 3),
     ("mid_full", True, 3),
     ("long", False, 1),
+    ("long", True, 1),
     ("asym", False, 2),
+    ("asym", True, 2),
     ("headline", False, 2),
     ("headline", True, 2),
 ]
