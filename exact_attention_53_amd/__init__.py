@@ -27,7 +27,7 @@ import torch
 
 __all__ = [
     "AttnError", "lib_path", "load", "fwd", "fwd_packed", "bwd", "bwd_packed",
-    "workspace_bytes", "fwd_varlen", "bwd_varlen", "fwd_decode", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
+    "workspace_bytes", "fwd_varlen", "bwd_varlen", "fwd_decode", "bwd_noalloc", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +88,10 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_typed.restype = i
     lib.attn_bwd_typed.argtypes = [i] + bwd_args[:17] + [vp, vp] + bwd_args[17:24] + [i, i] + bwd_args[24:] + [ctypes.c_uint]
+    lib.attn_bwd_noalloc.restype = i
+    lib.attn_bwd_noalloc.argtypes = bwd_args[:25] + [vp]
+    lib.attn_bwd_noalloc_max_workspace_bytes.restype = sz
+    lib.attn_bwd_noalloc_max_workspace_bytes.argtypes = []
     _lib = lib
     return lib
 
@@ -255,6 +259,36 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
         else:
             _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *tensors, None, None, *dims, int(window), int(bool(alibi)),
                                       *rest))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, causal: bool = True, scale: Optional[float] = None,
+                deterministic: bool = False, layout: str = "bthd"):
+    """attn_bwd_noalloc: the backward into caller-supplied dq, dk, dv with the library's
+    fixed per-GPU scratch as its workspace (nothing is allocated, by torch or the
+    library).  Calls that overlap in time on one GPU race; raises AttnError when the sizes
+    need more scratch than the library holds."""
+    B, NH, T, dqk = _dims(q, layout)
+    dvd = v.shape[-1]
+    for n, x, d in (("k", k, dqk), ("v", v, dvd), ("o", o, dvd), ("do", do, dvd), ("dq", dq, dqk), ("dk", dk, dqk),
+                    ("dv", dv, dvd)):
+        _shape(x, n, layout, B, NH, T, d)
+    dev = q.device
+    _on_gpu("bwd_noalloc", dev)
+    lib = load()
+    for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(x, n, dev, torch.bfloat16)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    with torch.cuda.device(dev):
+        _check(lib.attn_bwd_noalloc(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                                    v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
+                                    lse.data_ptr(), do.data_ptr(), _strides(do, layout),
+                                    dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
+                                    dv.data_ptr(), _strides(dv, layout), B, NH, T, dqk, dvd, float(scale),
+                                    int(bool(causal)), int(bool(deterministic)), _stream(dev)))
     return dq, dk, dv
 
 

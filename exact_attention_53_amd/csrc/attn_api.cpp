@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/attn53.h"
 #include "attn_kernels.hpp"
@@ -261,9 +262,61 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   return ATTN_OK;
 }
 
+// ---------------------------------------------------------------------------------
+// Library-owned scratch for attn_bwd_noalloc: one static device array per GPU, so that
+// callers that cannot allocate (graph capture, allocation-free serving loops) can still
+// run the backward.  Its address on each device is looked up once, with that device
+// current, and used for every kernel argument; the array's name is never used as an
+// address in host code.
+// ---------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(64) << 20;  // 64 MiB per device
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+attn_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t attn_bwd_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+attn_status attn_bwd_noalloc(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                             attn_strides sv, const void* o, attn_strides so, const float* lse, const void* do_,
+                             attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk, void* dv,
+                             attn_strides sdv, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
+                             int deterministic, void* stream) {
+  const size_t need = bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, false);
+  if (need > kScratchBytes) return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {  // need == 0: invalid sizes or flags, reported by bwd_impl below
+    const attn_status st = scratch_for_current_device(&ws);
+    if (st != ATTN_OK) return st;
+  }
+  return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr,
+                  nullptr, B, NH, T, d_qk, d_v, scale, causal, 0, 0, deterministic, ws, kScratchBytes, stream,
+                  ATTN_BWD_ALL);
+}
 
 const char* attn_status_string(attn_status s) {
   switch (s) {
@@ -273,7 +326,9 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_HEADDIM: return "unsupported head dims: (d_qk, d_v) must be (64,64), (128,128) or (192,128)";
     case ATTN_ERR_STRIDE: return "strides must be non-negative multiples of 8 elements, the t stride at most 2^24";
     case ATTN_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
-    case ATTN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than attn_bwd_workspace_bytes()";
+    case ATTN_ERR_WORKSPACE:
+      return "workspace is NULL, misaligned or smaller than attn_bwd_workspace_bytes() (attn_bwd_noalloc: the "
+             "sizes need more than its fixed scratch)";
     case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case ATTN_ERR_ARG:
       return "invalid argument: scale must be finite and > 0, flags 0 or 1, stage mask non-empty, dtype known";

@@ -334,6 +334,38 @@ attn_status attn_fwd_decode(attn_dtype dtype,
                             int B, int NH, int Tq, int Tk, int d_qk, int d_v,
                             float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_bwd_noalloc — attn_bwd without a caller-supplied workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, allocation-free serving or
+ * training loops, harnesses that forbid hipMalloc.  The workspace (D, LSE log2(e) and, in
+ * atomic mode, the fp32 dQ accumulator) lives in a static device array of the library,
+ * attn_bwd_noalloc_max_workspace_bytes() = 64 MiB on each GPU, held from the library's
+ * first use on that GPU until the process ends.  Every other argument, layout rule,
+ * result and error is that of attn_bwd (the same kernels run).
+ *   - Sizes whose attn_bwd_workspace_bytes(...) exceeds the maximum are rejected with
+ *     ATTN_ERR_WORKSPACE before anything is launched (deterministic mode: 8 bytes per
+ *     row of B * NH * Tpad, i.e. up to 8M padded rows; atomic mode adds 4 * d_qk bytes
+ *     per row).
+ *   - Allocates nothing: no hipMalloc, no hipFree, no allocating library call.  The
+ *     kernels clear every part of the array they read before reading it.
+ *   - All calls on one GPU share its array: calls that overlap in time on one GPU
+ *     (different streams or threads without ordering between them) race and give
+ *     undefined results.  Calls ordered on one stream are safe.
+ */
+size_t attn_bwd_noalloc_max_workspace_bytes(void);
+
+attn_status attn_bwd_noalloc(const void* q, attn_strides sq,
+                             const void* k, attn_strides sk,
+                             const void* v, attn_strides sv,
+                             const void* o, attn_strides so,
+                             const float* lse,
+                             const void* do_, attn_strides sdo,
+                             void* dq, attn_strides sdq,
+                             void* dk, attn_strides sdk,
+                             void* dv, attn_strides sdv,
+                             int B, int NH, int T, int d_qk, int d_v,
+                             float scale, int causal, int deterministic, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -268,3 +268,15 @@ def test_binding_checks_every_shape_against_q():
     # shapes right, tensors on the CPU: the device error
     with pytest.raises(ValueError, match="GPU only"):
         attn.fwd(q, t(), t())
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """attn_bwd_noalloc runs on a fixed 64 MiB scratch per GPU: sizes that need more
+    workspace are refused before anything is launched or touched."""
+    assert lib.attn_bwd_noalloc_max_workspace_bytes() == 64 << 20
+    z = S(0, 0, 0)
+    args = [GOOD, z] * 4 + [GOOD, GOOD, z] + [GOOD, z] * 3
+    # atomic mode at B 4, NH 16, T 8192, d 128 needs 272 MB
+    assert lib.attn_bwd_noalloc(*args, 4, 16, 8192, 128, 128, 0.088, 1, 0, None) == WORKSPACE
+    # deterministic mode, 2^24 padded rows: 128 MiB
+    assert lib.attn_bwd_noalloc(*args, 16, 16, 65536, 128, 128, 0.088, 1, 1, None) == WORKSPACE
