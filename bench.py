@@ -124,6 +124,105 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
     }
 
 
+POWER_SECONDS = 5.0
+
+
+def sustained_clock_power(run_step, ms_step: float, dev, value: float, keep: str = ""):
+    """Runs steps back to back for about POWER_SECONDS while power_sampler.py (a child
+    process of its own, started before the loop) records the GPU's shader clock and
+    power.  Returns the means over the loop (its first second left out), the throughput of
+    that loop, and the fraction of the bf16 MFMA peak at the clock observed (the spec peak
+    scaled by observed clock / 2400 MHz).  None when the driver's metrics are unreadable."""
+    import subprocess
+    import tempfile
+
+    import torch
+
+    try:
+        pr = torch.cuda.get_device_properties(dev)
+        bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+    except Exception as e:  # noqa: BLE001
+        return {"error": f"no PCI address: {e}"}
+    out = tempfile.NamedTemporaryFile(prefix="power_", suffix=".jsonl", delete=False).name
+    sampler = subprocess.Popen([sys.executable, os.path.join(ROOT, "power_sampler.py"), "--bdf", bdf, "--out", out],
+                               stdout=subprocess.DEVNULL, stderr=subprocess.PIPE)
+    try:
+        time.sleep(1.0)  # the sampler's import and first reads
+        if sampler.poll() is not None:
+            return {"error": "sampler exited: " + sampler.stderr.read().decode()[-300:]}
+        n = max(1, int(POWER_SECONDS * 1e3 / max(ms_step, 1e-3)))
+        torch.cuda.synchronize()
+        t0 = time.time()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            run_step()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        ms = e0.elapsed_time(e1) / n
+    finally:
+        sampler.terminate()
+        try:
+            sampler.wait(timeout=10)
+        except subprocess.TimeoutExpired:
+            sampler.kill()
+    rows = []
+    with open(out) as f:
+        for line in f:
+            r = json.loads(line)
+            if "t" in r and t0 + 1.0 <= r["t"] <= t1:
+                rows.append(r)
+    # the firmware refreshes its metrics about once a second: keep the first sighting of
+    # each refresh (its host time is the refresh time to within one sampling period)
+    snaps, seen = [], set()
+    for r in rows:
+        key = r.get("fw_ts")
+        if key is None or key not in seen:
+            seen.add(key)
+            snaps.append(r)
+    if keep:
+        import shutil
+        shutil.move(out, keep)
+    else:
+        os.unlink(out)
+
+    def mean(key):
+        vals = [r[key] for r in rows if r.get(key) is not None]
+        return sum(vals) / len(vals) if vals else None
+
+    def smean(key):
+        vals = [r[key] for r in snaps if r.get(key) is not None]
+        return sum(vals) / len(vals) if vals else None
+
+    def delta(key, a, b):
+        return b[key] - a[key] if a.get(key) is not None and b.get(key) is not None else None
+
+    clk = smean("gfxclk_mhz")
+    ppt = thm = None
+    if len(snaps) >= 2:
+        dacc = delta("acc", snaps[0], snaps[-1])
+        if dacc:
+            dp, dt_ = delta("ppt_acc", snaps[0], snaps[-1]), delta("thm_acc", snaps[0], snaps[-1])
+            ppt = dp / dacc if dp is not None else None
+            thm = dt_ / dacc if dt_ is not None else None
+    sustained = value * ms_step / ms
+    res = {
+        "seconds": round(t1 - t0, 2), "steps": n, "samples": len(rows), "refreshes": len(snaps),
+        "ms_per_step": round(ms, 4), "tflops": round(sustained, 1),
+        "gfxclk_mhz_mean": round(clk, 1) if clk else None,
+        "gfxclk_mhz_min": min((r["gfxclk_mhz"] for r in snaps if r.get("gfxclk_mhz")), default=None),
+        "power_w_mean": round(smean("power_w"), 1) if smean("power_w") else None,
+        "ppt_limit_residency": round(ppt, 3) if ppt is not None else None,
+        "thermal_limit_residency": round(thm, 3) if thm is not None else None,
+        "temp_c_max": max((r["temp_c"] for r in rows if r.get("temp_c") is not None), default=None),
+        "throttle_status": sorted({str(r.get("throttle")) for r in rows}),
+    }
+    if clk:
+        res["frac_of_peak_at_observed_clock"] = round(sustained / (PEAK_BF16_TFLOPS * clk / 2400.0), 4)
+    return res
+
+
 def decode_bench(args, w):
     """One decode step per sequence: the inference forward (no stats) of one query row
     against each sequence's w.T-row key/value cache (attn_fwd_decode).  HBM-bound:
@@ -188,6 +287,11 @@ def main():
     ap.add_argument("--dq-mode", choices=["deterministic", "atomic"], default="deterministic",
                     help="dQ summed in a fixed order without atomics (default) or by fp32 atomics")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other-dQ-mode timing and the sustained clock/power window")
+    ap.add_argument("--power-seconds", type=float, default=5.0,
+                    help="length of the sustained loop timed beside the clock/power sampler")
+    ap.add_argument("--power-log", default="", help="keep the sampler's samples (JSON lines) in this file")
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="only time the CPU oracle on a bounded sample of the workload (no GPU use)")
     ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
@@ -199,6 +303,8 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB five times (the known-size "
                          "kernel that scales the HBM byte counters)")
     args = ap.parse_args()
+    global POWER_SECONDS
+    POWER_SECONDS = args.power_seconds
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} given): attention shards over "
               f"(batch, head) pairs with no communication, so each GPU runs its share as this "
@@ -239,11 +345,18 @@ def main():
     dk = torch.empty_like(dq)
     dv = torch.empty((B, T, NH, w.d_v), dtype=et, device=dev)
     det = args.dq_mode == "deterministic"
-    ws = torch.empty(attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, det), dtype=torch.uint8, device=dev)
+    workspaces = {}
+
+    def workspace(mode_det):
+        if mode_det not in workspaces:
+            workspaces[mode_det] = torch.empty(attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, mode_det),
+                                               dtype=torch.uint8, device=dev)
+        return workspaces[mode_det]
 
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
 
-    def step(ev=None):
+    def step(ev=None, mode_det=det):
+        ws = workspace(mode_det)
         if flush is not None:
             flush.fill_(1.0)
         if ev is not None:
@@ -251,39 +364,40 @@ def main():
         attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse, window=w.window, alibi=w.alibi)
         if ev is not None:
             ev[1].record()
-        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws,
+        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv, workspace=ws,
                  stages=attn.PREPROCESS, window=w.window, alibi=w.alibi)
         if ev is not None:
             ev[2].record()
-        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws, stages=attn.MAIN,
-                 window=w.window, alibi=w.alibi)
+        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv, workspace=ws,
+                 stages=attn.MAIN, window=w.window, alibi=w.alibi)
         if ev is not None:
             ev[3].record()
-        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, det, dq=dq, dk=dk, dv=dv, workspace=ws,
+        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv, workspace=ws,
                  stages=attn.DQ, window=w.window, alibi=w.alibi)
         if ev is not None:
             ev[4].record()
 
+    def timed(n, mode_det):
+        """n steps bracketed by events; returns (ms per step, per-kernel ms, wall s)."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        start.record()
+        for i in range(n):
+            step(evs[i], mode_det)
+        end.record()
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+
+        def avg(a, b):
+            return sum(e[a].elapsed_time(e[b]) for e in evs) / n
+
+        return start.elapsed_time(end) / n, (avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)), t_wall
+
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step(evs[i])
-    end.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-
-    def avg(a, b):
-        return sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
-
-    t_fwd, t_pre, t_main, t_dq = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    ms_step, (t_fwd, t_pre, t_main, t_dq), t_wall = timed(args.steps, det)
     if args.cold:  # the eviction between steps is not part of the step
         ms_step = t_fwd + t_pre + t_main + t_dq
     f_fwd, f_bwd = flops(w)
@@ -346,6 +460,24 @@ def main():
             "traffic_unit": "bytes per launch",
         },
     }
+    if not args.cold and not args.no_extras:
+        # The other dQ mode on the same inputs, a few steps: the atomic mode's extra time
+        # in the key/value kernel (its partial dQ products and fp32 atomics) as a share of
+        # its step, the analogue of the atomic-add share of total time.
+        step(mode_det=not det)
+        n_alt = max(3, min(10, args.steps))
+        ms_alt, k_alt, _ = timed(n_alt, not det)
+        ms_det, ms_atom = (ms_step, ms_alt) if det else (ms_alt, ms_step)
+        kv_det, kv_atom = (t_main, k_alt[2]) if det else (k_alt[2], t_main)
+        line["dq_modes"] = {
+            "other_mode": "atomic" if det else "deterministic",
+            "other_ms_per_step": round(ms_alt, 4),
+            "other_kernels_ms": dict(zip(("attn_fwd", "bwd_preprocess", "bwd_kv",
+                                          "bwd_dq_convert" if det else "bwd_dq"), (round(x, 4) for x in k_alt))),
+            "atomic_over_deterministic_step_time": round(ms_atom / ms_det, 3),
+            "atomic_share_of_atomic_step": round(max(0.0, kv_atom - kv_det) / ms_atom, 3),
+        }
+        line["clock_power"] = sustained_clock_power(lambda: step(), ms_step, dev, value, args.power_log)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
