@@ -25,6 +25,13 @@ What is computed (the plain definition, S and P materialised, float64 throughout
             S[i, j] -= m_h (i - j) with the head slopes m_h = 2^(-8 (h+1) / NH) of the
             linear-bias scheme (the page names the option but not its slopes; this
             geometric sequence is the reading taken)
+            block-sparse mask (the block-sparse pattern of [2CTA 5.1, 5.2], composed
+            with the causal mask as an independent module): a map M over
+            (query block, key block) pairs of `block` x `block` elements;
+            additionally S[i, j] = -inf where M[i // block, j // block] == 0.  The
+            pages give no format; this map, ANDed with the causal mask, is the
+            reading taken.  A row left with no allowed key gets P = 0, O = 0,
+            LSE = -inf and zero gradients (the logsumexp of an empty set)
             O = P V                                  [SA8 2.1, A.1]
             LSE_i = m_i + ln(sum_j exp(S_ij - m_i)),  m_i = max_j S_ij
             (the pages' "softmax stats" [SA8 1.2, 1.3] are never defined; this
@@ -60,6 +67,7 @@ __all__ = [
     "attn_ref_bwd",
     "attn_ref_heads",
     "attn_ref_varlen",
+    "attn_ref_blocksparse",
     "attn_ref_bwd_loop",
     "alibi_slopes",
 ]
@@ -113,11 +121,36 @@ def _softmax_rows(S: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return e / l, (m + np.log(l))[:, 0]
 
 
+def _softmax_rows_or_empty(S: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """_softmax_rows on the rows holding at least one allowed key; a row with none gets
+    P = 0 and LSE = -inf."""
+    empty = np.all(S == -np.inf, axis=1)
+    if not empty.any():
+        return _softmax_rows(S)
+    P = np.zeros_like(S)
+    lse = np.full(S.shape[0], -np.inf)
+    if (~empty).any():
+        P[~empty], lse[~empty] = _softmax_rows(S[~empty])
+    return P, lse
+
+
+def _block_allowed(block_map: Optional[np.ndarray], block: int, r0: int, r1: int, nk: int):
+    """Element mask of query rows r0 .. r1-1 against keys 0 .. nk-1 from a block map:
+    element (i, j) is allowed iff block_map[i // block, j // block] != 0.  None: no map."""
+    if block_map is None:
+        return None
+    qi = np.arange(r0, r1) // block
+    kj = np.arange(nk) // block
+    return np.asarray(block_map)[qi[:, None], kj[None, :]] != 0
+
+
 def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
                  block_rows: Optional[int] = None, window: int = 0,
-                 slope: float = 0.0) -> Tuple[np.ndarray, np.ndarray]:
+                 slope: float = 0.0, block_map: Optional[np.ndarray] = None,
+                 block: int = 128) -> Tuple[np.ndarray, np.ndarray]:
     """One head: q (T, d_qk), k (Tk, d_qk), v (Tk, d_v) float64 -> O (T, d_v), LSE (T,).
-    Tk >= 1 may differ from T (padded batches); the causal mask stays top-left."""
+    Tk >= 1 may differ from T (padded batches); the causal mask stays top-left.
+    block_map: (ceil(T / block), ceil(Tk / block)) block-sparse map or None."""
     _check_window(causal, window, slope)
     T, Tk = q.shape[0], k.shape[0]
     br = T if block_rows is None else block_rows
@@ -127,16 +160,21 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
         r1 = min(T, r0 + br)
         nk = min(r1, Tk) if causal else Tk  # keys past the last query are all masked
         S = _scores(q[r0:r1], k[:nk], scale, causal, r0, window, slope)
-        P, lse[r0:r1] = _softmax_rows(S)
+        allowed = _block_allowed(block_map, block, r0, r1, nk)
+        if allowed is not None:
+            S = np.where(allowed, S, -np.inf)
+        P, lse[r0:r1] = _softmax_rows_or_empty(S)
         O[r0:r1] = P @ v[:nk]
     return O, lse
 
 
 def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
-                  causal: bool, block_rows: Optional[int] = None, window: int = 0, slope: float = 0.0):
+                  causal: bool, block_rows: Optional[int] = None, window: int = 0, slope: float = 0.0,
+                  block_map: Optional[np.ndarray] = None, block: int = 128):
     """One head: returns dQ, dK, dV and also O, LSE and D = (dP * P) 1 (all float64).
     q, do have T rows, k, v have Tk >= 1 rows (Tk may differ from T).  The bias is a
-    constant of the inputs: it changes P but adds no term to the gradients."""
+    constant of the inputs: it changes P but adds no term to the gradients; neither does
+    the block map (a row with no allowed key has P = 0 and gets zero gradients)."""
     _check_window(causal, window, slope)
     T, Tk = q.shape[0], k.shape[0]
     br = T if block_rows is None else block_rows
@@ -150,7 +188,10 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
         r1 = min(T, r0 + br)
         nk = min(r1, Tk) if causal else Tk
         S = _scores(q[r0:r1], k[:nk], scale, causal, r0, window, slope)
-        P, lse[r0:r1] = _softmax_rows(S)
+        allowed = _block_allowed(block_map, block, r0, r1, nk)
+        if allowed is not None:
+            S = np.where(allowed, S, -np.inf)
+        P, lse[r0:r1] = _softmax_rows_or_empty(S)
         O[r0:r1] = P @ v[:nk]
         dV[:nk] += P.T @ do[r0:r1]                      # dV = P^T dO
         dP = do[r0:r1] @ v[:nk].T                       # dP = dO V^T
@@ -231,6 +272,52 @@ def attn_ref_heads(q, k, v, do, causal: bool, scale: Optional[float] = None,
     return res
 
 
+def attn_ref_blocksparse(q, k, v, do, block_map, causal: bool, scale: Optional[float] = None, block: int = 128,
+                         heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """Block-sparse attention over (B, T, NH, d) tensors.  block_map is indexed
+    [b, h, query block, key block] (any of its two leading dimensions may have size 1,
+    which broadcasts) with ceil(T / block) blocks along each of the last two; element
+    (i, j) of head (b, h) is allowed iff block_map[b, h, i // block, j // block] != 0 and,
+    when causal, j <= i.  do may be None (forward only).  Returns the dict of
+    attn_ref_bwd (o, lse, dq, dk, dv, D) for every head, or for the selected `heads`
+    {(b, h): {...}} as attn_ref_heads does."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    do = None if do is None else to_f64(do)
+    B, T, NH, dqk = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    bm = np.asarray(block_map)
+    nb = (T + block - 1) // block
+    if bm.ndim != 4 or bm.shape[0] not in (1, B) or bm.shape[1] not in (1, NH) or bm.shape[2:] != (nb, nb):
+        raise ValueError(f"block_map must be (B or 1, NH or 1, {nb}, {nb}), got {bm.shape}")
+    br = _block_rows(T, dqk)
+
+    def one(b, h):
+        m = bm[b if bm.shape[0] > 1 else 0, h if bm.shape[1] > 1 else 0]
+        if do is None:
+            o, lse = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, br, block_map=m, block=block)
+            return {"o": o, "lse": lse}
+        r = head_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal, br, block_map=m,
+                          block=block)
+        return dict(zip(("dq", "dk", "dv", "o", "lse", "D"), r))
+
+    if heads is not None:
+        return {(int(b), int(h)): one(int(b), int(h)) for b, h in heads}
+    out = {"o": np.empty((B, T, NH, v.shape[3])), "lse": np.empty((B, NH, T))}
+    if do is not None:
+        out.update(dq=np.empty((B, T, NH, dqk)), dk=np.empty((B, T, NH, dqk)), dv=np.empty((B, T, NH, v.shape[3])),
+                   D=np.empty((B, NH, T)))
+    for b in range(B):
+        for h in range(NH):
+            r = one(b, h)
+            for name, x in r.items():
+                if name in ("lse", "D"):
+                    out[name][b, h] = x
+                else:
+                    out[name][b, :, h] = x
+    return out
+
+
 def attn_ref_varlen(q, k, v, do, seq_q, seq_k, causal: bool, scale: Optional[float] = None):
     """Padded batches: the padding mask with per-batch lengths seq_len_q and seq_len_kv
     among the SDPA options of [SA8 1.2].  Batch b uses query rows 0 .. seq_q[b]-1 and
@@ -269,7 +356,7 @@ def attn_ref_varlen(q, k, v, do, seq_q, seq_k, causal: bool, scale: Optional[flo
 
 
 def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, window: int = 0,
-                      alibi: bool = False):
+                      alibi: bool = False, allowed=None):
     """Independent loop formulation for small T (T <= 64), written from the softmax
     Jacobian dy_i/dx_j = y_i (delta_ij - y_j) [SA8 2.1, A.3] and the per-(b, t, h)
     loop nest of the CPU reference in [SA8 2.2]:
@@ -286,6 +373,9 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
 
     The scale sits inside dpreatt, so dq and dk take no second factor.  It does not
     share a line with head_forward/head_backward and serves to pin them.
+    allowed: None, or a predicate allowed(b, h, t, t2) -> bool; keys it refuses are
+    left out of the row like keys outside the window (a row with no key left gets
+    att = 0, o = 0, lse = -inf and no gradient).
     Returns dq, dk, dv, o (B, T, NH, d) and lse (B, NH, T) in float64.
     """
     _check_window(causal, window, 1.0 if alibi else 0.0)
@@ -306,9 +396,13 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
                 first = max(0, t - window + 1) if window > 0 else 0
                 # forward row by loops: preatt, max, exp, sum, normalise (keys before
                 # `first` get -inf scores: exp gives exactly 0, so they add nothing)
-                pre = [scale * float(np.dot(q[b, t, h], k[b, t2, h])) - slopes[h] * (t - t2) if t2 >= first
-                       else -math.inf for t2 in range(last)]
+                pre = [scale * float(np.dot(q[b, t, h], k[b, t2, h])) - slopes[h] * (t - t2)
+                       if t2 >= first and (allowed is None or allowed(b, h, t, t2)) else -math.inf
+                       for t2 in range(last)]
                 mx = max(pre)
+                if mx == -math.inf:  # no key left in this row
+                    lse[b, h, t] = -math.inf
+                    continue
                 ex = [np.exp(p - mx) for p in pre]
                 tot = sum(ex)
                 att = [e / tot for e in ex]

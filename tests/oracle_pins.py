@@ -497,6 +497,123 @@ def pin_alibi_finite_differences(ref, h: float = 1e-6):
         _close(r[name], g, rtol=1e-6, atol=1e-8, what=f"alibi finite differences {name}")
 
 
+# ---------------------------------------------------------------------------------
+# Block-sparse map (the block-sparse mask pattern of [2CTA 5.1, 5.2]): element (i, j)
+# allowed iff map[i // block, j // block] != 0, ANDed with the causal mask.  The pins use
+# small blocks so that short sequences span several of them.
+# ---------------------------------------------------------------------------------
+def _bs_map(B, NH, nb, seed, density=0.5):
+    rng = np.random.default_rng(seed)
+    return (rng.random((B, NH, nb, nb)) < density).astype(np.uint8)
+
+
+def pin_blocksparse_all_ones_is_dense(ref):
+    """A map with every block live masks nothing: dense (and, with the causal mask,
+    causal) attention exactly."""
+    q, k, v, do = _inputs(2, 37, 2, 16, 24, 881)
+    for causal in (False, True):
+        a = ref.attn_ref_bwd(q, k, v, do, causal)
+        b = ref.attn_ref_blocksparse(q, k, v, do, np.ones((1, 1, 5, 5), np.uint8), causal, block=8)
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            _close(b[n], a[n], rtol=1e-15, atol=1e-15, what=f"all-ones map causal={causal} {n}")
+
+
+def pin_blocksparse_lower_triangle_is_causal(ref):
+    """Without the causal flag, a block-lower-triangular map lets the keys of a query's
+    own block through (up to the block's end), so it differs from causal attention; with
+    the flag it equals causal attention.  Blocks above the diagonal hold nothing the causal
+    mask allows, so removing them changes nothing."""
+    q, k, v, do = _inputs(1, 40, 2, 16, 16, 883)
+    tri = np.tril(np.ones((5, 5), np.uint8))[None, None]
+    a = ref.attn_ref_bwd(q, k, v, do, True)
+    b = ref.attn_ref_blocksparse(q, k, v, do, tri, True, block=8)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        _close(b[n], a[n], rtol=1e-15, atol=1e-15, what=f"lower-triangular map + causal {n}")
+    c = ref.attn_ref_blocksparse(q, k, v, do, tri, False, block=8)
+    assert np.max(np.abs(c["o"] - a["o"])) > 1e-3, "lower-triangular map without the causal flag equals causal"
+    # row 7 (last of block 0) sees keys 0..7 either way; row 0 sees keys 0..7 only without it
+    _close(c["o"][:, 7], a["o"][:, 7], rtol=1e-14, what="row 7 of block 0")
+
+
+def pin_blocksparse_band_is_block_window(ref):
+    """A band of w blocks on and below the diagonal, with the causal mask, lets query i see
+    keys from the start of block i // b - w + 1 up to i: the element mask written out
+    directly through the loop form's predicate."""
+    q, k, v, do = _inputs(1, 45, 2, 8, 8, 885)
+    b, nb, w = 6, 8, 3
+    band = np.array([[1 if 0 <= r - c < w else 0 for c in range(nb)] for r in range(nb)], np.uint8)[None, None]
+    dq, dk, dv, o, lse = ref.attn_ref_bwd_loop(
+        q, k, v, do, True, allowed=lambda bb, hh, t, t2: t2 >= b * max(0, t // b - w + 1))
+    r = ref.attn_ref_blocksparse(q, k, v, do, band, True, block=b)
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv), ("o", o), ("lse", lse)):
+        _close(r[n], x, rtol=1e-12, atol=1e-14, what=f"band map loop form {n}")
+
+
+def pin_blocksparse_random_map_loops(ref):
+    """A random per-head map, causal and not, against the scalar loop nest with the map
+    read element by element (map[b, h, t // block, t2 // block]); rows and key columns
+    left with no live block are among the cases (the map has empty rows)."""
+    q, k, v, do = _inputs(2, 27, 3, 8, 16, 887)
+    blk = 4
+    m = _bs_map(2, 3, 7, 888, density=0.45)
+    m[0, 1, 2, :] = 0  # rows 8..11 of head (0, 1): no key at all
+    m[1, 2, :, 3] = 0  # keys 12..15 of head (1, 2): seen by no query
+    for causal in (False, True):
+        dq, dk, dv, o, lse = ref.attn_ref_bwd_loop(
+            q, k, v, do, causal, allowed=lambda bb, hh, t, t2: m[bb, hh, t // blk, t2 // blk] != 0)
+        r = ref.attn_ref_blocksparse(q, k, v, do, m, causal, block=blk)
+        for n, x in (("dq", dq), ("dk", dk), ("dv", dv), ("o", o)):
+            _close(r[n], x, rtol=1e-12, atol=1e-14, what=f"random map causal={causal} loop form {n}")
+        fin = np.isfinite(lse)
+        assert np.array_equal(fin, np.isfinite(r["lse"])), "rows without keys differ"
+        _close(r["lse"][fin], lse[fin], rtol=1e-12, atol=1e-14, what=f"random map causal={causal} lse")
+    r = ref.attn_ref_blocksparse(q, k, v, do, m, False, block=blk)
+    assert np.all(r["o"][0, 8:12, 1] == 0) and np.all(r["lse"][0, 1, 8:12] == -np.inf), "empty rows: O, LSE"
+    assert np.all(r["dq"][0, 8:12, 1] == 0), "empty rows: dQ"
+    assert np.all(r["dk"][1, 12:16, 2] == 0) and np.all(r["dv"][1, 12:16, 2] == 0), "unseen keys: dK, dV"
+
+
+def pin_blocksparse_zero_queries(ref):
+    """Q = 0: P is uniform over the allowed keys: O_i is the mean of the V rows in the live
+    blocks of row i's block (up to i when causal), LSE_i = ln(count)."""
+    _, k, v, _ = _inputs(1, 30, 2, 16, 24, 889)
+    q = np.zeros_like(k)
+    blk = 5
+    m = _bs_map(1, 1, 6, 890, density=0.6)
+    m[0, 0, np.arange(6), np.arange(6)] = 1  # every row keeps its own block
+    for causal in (False, True):
+        r = ref.attn_ref_blocksparse(q, k, v, None, m, causal, block=blk)
+        for i in range(30):
+            keys = [j for j in range(30) if m[0, 0, i // blk, j // blk] and (not causal or j <= i)]
+            _close(r["o"][0, i], v[0, keys].mean(axis=0), rtol=1e-14, what=f"map zero queries O row {i}")
+            _close(r["lse"][0, :, i], np.full(2, math.log(len(keys))), rtol=1e-14, atol=1e-15,
+                   what=f"map zero queries LSE row {i}")
+
+
+def pin_blocksparse_finite_differences(ref, h: float = 1e-6):
+    """dQ, dK, dV under a map (with an empty row block) equal central differences of
+    sum(O * dO)."""
+    q, k, v, do = _inputs(1, 12, 1, 8, 8, 891)
+    m = np.array([[1, 0, 1], [0, 0, 0], [1, 1, 0]], np.uint8)[None, None]
+    r = ref.attn_ref_blocksparse(q, k, v, do, m, False, block=4)
+
+    def f(qq, kk, vv):
+        return float(np.sum(ref.attn_ref_blocksparse(qq, kk, vv, None, m, False, block=4)["o"] * do))
+
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        g = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if n == name else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+            args_m = [xm if n == name else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+            g[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        _close(r[name], g, rtol=1e-6, atol=1e-8, what=f"map finite differences {name}")
+
+
 ALL_PINS = [
     ("finite_differences_causal", lambda r: pin_finite_differences(r, True)),
     ("finite_differences_full", lambda r: pin_finite_differences(r, False)),
@@ -531,6 +648,12 @@ ALL_PINS = [
     ("window_zero_queries", pin_window_zero_queries),
     ("window_loops", pin_window_loops),
     ("finite_differences_window", pin_window_finite_differences),
+    ("blocksparse_all_ones_is_dense", pin_blocksparse_all_ones_is_dense),
+    ("blocksparse_lower_triangle_is_causal", pin_blocksparse_lower_triangle_is_causal),
+    ("blocksparse_band_is_block_window", pin_blocksparse_band_is_block_window),
+    ("blocksparse_random_map_loops", pin_blocksparse_random_map_loops),
+    ("blocksparse_zero_queries", pin_blocksparse_zero_queries),
+    ("finite_differences_blocksparse", pin_blocksparse_finite_differences),
     ("alibi_slopes", pin_alibi_slopes),
     ("alibi_zero_queries", pin_alibi_zero_queries),
     ("alibi_loops", pin_alibi_loops),

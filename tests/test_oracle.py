@@ -67,6 +67,12 @@ MUTANTS = {
     "window_off_by_one": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = np.where(qi - kj > window, -np.inf, S)"),
     "window_ignored": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = S"),
     "alibi_sign": ("S = S - slope * (qi - kj)", "S = S + slope * (qi - kj)"),
+    "blocksparse_map_transposed": ("return np.asarray(block_map)[qi[:, None], kj[None, :]] != 0",
+                                   "return np.asarray(block_map).T[qi[:, None], kj[None, :]] != 0"),
+    "blocksparse_block_index_off": ("qi = np.arange(r0, r1) // block", "qi = np.arange(r0 + 1, r1 + 1) // block"),
+    "blocksparse_empty_row_lse_zero": ("lse = np.full(S.shape[0], -np.inf)", "lse = np.zeros(S.shape[0])"),
+    "blocksparse_map_ignored": ("            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n    return O, lse",
+                                "            pass\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n    return O, lse"),
     "alibi_slope_index": ("2.0 ** (-8.0 * (h + 1) / NH)", "2.0 ** (-8.0 * h / NH)"),
 }
 
