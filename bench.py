@@ -68,8 +68,16 @@ def hbm_traffic(kernel: str, w, dq_mode: str, dtype: str = "bf16"):
     return round((fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024.0)
 
 
+def pairs_of(w):
+    """Attended (query, key) pairs over all heads (block-sparse: counted from the map)."""
+    if w.name == "blocksparse":
+        import workloads
+        return workloads.block_map_pairs(w, workloads.block_map(w))
+    return w.pairs()
+
+
 def flops(w):
-    pairs = w.pairs()
+    pairs = pairs_of(w)
     return 2.0 * (w.d_qk + w.d_v) * pairs, 2.0 * (3 * w.d_qk + 2 * w.d_v) * pairs
 
 
@@ -99,8 +107,12 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
     while done < len(all_heads) and t_total < seconds_budget * 0.5:
         hd = all_heads[done]
         t0 = time.perf_counter()
-        attn_ref.attn_ref_heads(cpu["q"], cpu["k"], cpu["v"], cpu["do"], w.causal, w.scale, heads=[hd],
-                                window=w.window, alibi=w.alibi)
+        if w.name == "blocksparse":
+            attn_ref.attn_ref_blocksparse(cpu["q"], cpu["k"], cpu["v"], cpu["do"], workloads.block_map(w), w.causal,
+                                          w.scale, heads=[hd])
+        else:
+            attn_ref.attn_ref_heads(cpu["q"], cpu["k"], cpu["v"], cpu["do"], w.causal, w.scale, heads=[hd],
+                                    window=w.window, alibi=w.alibi)
         t_total += time.perf_counter() - t0
         heads.append(hd)
         done += 1
@@ -349,11 +361,32 @@ def main():
 
     def workspace(mode_det):
         if mode_det not in workspaces:
-            workspaces[mode_det] = torch.empty(attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, mode_det),
-                                               dtype=torch.uint8, device=dev)
+            nbytes = (attn.load().attn_bwd_blocksparse_workspace_bytes(B, NH, T, w.d_qk, w.d_v, int(mode_det))
+                      if w.name == "blocksparse" else attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, mode_det))
+            workspaces[mode_det] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         return workspaces[mode_det]
 
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
+
+    bsp = w.name == "blocksparse"
+    if bsp:
+        bmap = torch.from_numpy(workloads.block_map(w)).to(dev)
+        fws = torch.empty(attn.load().attn_fwd_blocksparse_workspace_bytes(B, NH, T, w.d_qk, w.d_v), dtype=torch.uint8,
+                          device=dev)
+
+    def fwd_call():
+        if bsp:
+            attn.fwd_blocksparse(q, k, v, bmap, w.causal, w.scale, out=o, lse=lse, workspace=fws)
+        else:
+            attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse, window=w.window, alibi=w.alibi)
+
+    def bwd_call(mode_det, ws, stages):
+        if bsp:
+            attn.bwd_blocksparse(q, k, v, o, lse, do, bmap, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv,
+                                 workspace=ws, stages=stages)
+        else:
+            attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv, workspace=ws,
+                     stages=stages, window=w.window, alibi=w.alibi)
 
     def step(ev=None, mode_det=det):
         ws = workspace(mode_det)
@@ -361,19 +394,16 @@ def main():
             flush.fill_(1.0)
         if ev is not None:
             ev[0].record()
-        attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse, window=w.window, alibi=w.alibi)
+        fwd_call()
         if ev is not None:
             ev[1].record()
-        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv, workspace=ws,
-                 stages=attn.PREPROCESS, window=w.window, alibi=w.alibi)
+        bwd_call(mode_det, ws, attn.PREPROCESS)
         if ev is not None:
             ev[2].record()
-        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv, workspace=ws,
-                 stages=attn.MAIN, window=w.window, alibi=w.alibi)
+        bwd_call(mode_det, ws, attn.MAIN)
         if ev is not None:
             ev[3].record()
-        attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv, workspace=ws,
-                 stages=attn.DQ, window=w.window, alibi=w.alibi)
+        bwd_call(mode_det, ws, attn.DQ)
         if ev is not None:
             ev[4].record()
 
@@ -405,7 +435,7 @@ def main():
     # Algorithmic flops carried by each kernel (recomputation is not counted): the
     # key/value kernel forms S, dP, dV, dK (and, in atomic mode, the dQ products); the
     # deterministic dQ kernel contributes the dQ product only.
-    pairs = w.pairs()
+    pairs = pairs_of(w)
     f_dq = 2.0 * w.d_qk * pairs
     f_main = f_bwd if not det else f_bwd - f_dq
     kernels = {
@@ -434,7 +464,8 @@ def main():
         "config": {
             "workload": f"{w.name}: B={B} NH={NH} T={T} d_qk={w.d_qk} d_v={w.d_v} "
                         f"{'causal' if w.causal else 'non-causal'}"
-                        f"{f' window {w.window}' if w.window else ''}{' ALiBi' if w.alibi else ''}, "
+                        f"{f' window {w.window}' if w.window else ''}{' ALiBi' if w.alibi else ''}"
+                        f"{' block-sparse map (local band of 8 blocks + block 0)' if w.name == 'blocksparse' else ''}, "
                         f"{'packed QKV' if w.packed else 'BTHD'}, "
                         f"dQ mode {args.dq_mode}",
             "B": B, "NH": NH, "T": T, "d_qk": w.d_qk, "d_v": w.d_v, "causal": w.causal, "window": w.window, "alibi": w.alibi,

@@ -27,7 +27,7 @@ import torch
 
 __all__ = [
     "AttnError", "lib_path", "load", "fwd", "fwd_packed", "bwd", "bwd_packed",
-    "workspace_bytes", "fwd_varlen", "bwd_varlen", "fwd_decode", "bwd_noalloc", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
+    "workspace_bytes", "fwd_varlen", "bwd_varlen", "fwd_decode", "bwd_noalloc", "fwd_blocksparse", "bwd_blocksparse", "BS_BLOCK", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +88,15 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_typed.restype = i
     lib.attn_bwd_typed.argtypes = [i] + bwd_args[:17] + [vp, vp] + bwd_args[17:24] + [i, i] + bwd_args[24:] + [ctypes.c_uint]
+    lib.attn_fwd_blocksparse_workspace_bytes.restype = sz
+    lib.attn_fwd_blocksparse_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_bwd_blocksparse_workspace_bytes.restype = sz
+    lib.attn_bwd_blocksparse_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    i64 = ctypes.c_int64
+    lib.attn_fwd_blocksparse.restype = i
+    lib.attn_fwd_blocksparse.argtypes = [vp, S, vp, S, vp, S, vp, S, vp, vp, i64, i64, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_bwd_blocksparse.restype = i
+    lib.attn_bwd_blocksparse.argtypes = bwd_args[:17] + [vp, i64, i64] + bwd_args[17:] + [ctypes.c_uint]
     lib.attn_bwd_noalloc.restype = i
     lib.attn_bwd_noalloc.argtypes = bwd_args[:25] + [vp]
     lib.attn_bwd_noalloc_max_workspace_bytes.restype = sz
@@ -259,6 +268,106 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
         else:
             _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *tensors, None, None, *dims, int(window), int(bool(alibi)),
                                       *rest))
+    return dq, dk, dv
+
+
+BS_BLOCK = 128  # block-sparse maps: elements per block along each side
+
+
+def _block_map(block_map: torch.Tensor, B: int, NH: int, T: int, dev: torch.device):
+    """Checks a (B or 1, NH or 1, nb, nb) uint8 map and returns its (b, h) strides (0 where
+    the map is shared)."""
+    nb = (T + BS_BLOCK - 1) // BS_BLOCK
+    if block_map.dtype != torch.uint8 or block_map.dim() != 4:
+        raise ValueError("block_map must be a 4-D uint8 tensor (B or 1, NH or 1, nb, nb)")
+    Bm, Hm, r, c = block_map.shape
+    if Bm not in (1, B) or Hm not in (1, NH) or (r, c) != (nb, nb):
+        raise ValueError(f"block_map has shape {tuple(block_map.shape)}, expected (B or 1, NH or 1, {nb}, {nb})")
+    if block_map.stride(3) != 1 or block_map.stride(2) != nb:
+        raise ValueError("each (nb, nb) map must be contiguous and row-major")
+    if block_map.device != dev:
+        raise ValueError(f"block_map is on {block_map.device}, expected {dev}")
+    return (block_map.stride(0) if Bm > 1 else 0), (block_map.stride(1) if Hm > 1 else 0)
+
+
+def fwd_blocksparse(q, k, v, block_map: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+                    return_lse: bool = True, layout: str = "bthd", out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Block-sparse forward (bf16): element (i, j) is attended iff block_map[b, h, i // 128,
+    j // 128] != 0 and, when causal, j <= i.  block_map is uint8 (B or 1, NH or 1, nb, nb) on
+    the device, nb = ceil(T / 128).  Rows with no key get O = 0, LSE = -inf.  Returns (o, lse)."""
+    B, NH, T, dqk = _dims(q, layout)
+    dv = v.shape[-1]
+    _shape(k, "k", layout, B, NH, T, dqk)
+    _shape(v, "v", layout, B, NH, T, dv)
+    if out is not None:
+        _shape(out, "out", layout, B, NH, T, dv)
+    dev = q.device
+    _on_gpu("fwd_blocksparse", dev)
+    lib = load()
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, n, dev, torch.bfloat16)
+    msb, msh = _block_map(block_map, B, NH, T, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        shape = (B, T, NH, dv) if layout == "bthd" else (B, NH, T, dv)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", dev, torch.bfloat16)
+    if return_lse and lse is None:
+        lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    need = int(lib.attn_fwd_blocksparse_workspace_bytes(B, NH, T, dqk, dv))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_fwd_blocksparse(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                                        v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
+                                        lse.data_ptr() if return_lse else None, block_map.data_ptr(), msb, msh,
+                                        B, NH, T, dqk, dv, float(scale), int(bool(causal)), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, (lse if return_lse else None)
+
+
+def bwd_blocksparse(q, k, v, o, lse, do, block_map: torch.Tensor, causal: bool = False,
+                    scale: Optional[float] = None, deterministic: bool = False, layout: str = "bthd",
+                    dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None, stages: int = ALL_STAGES):
+    """Block-sparse backward (bf16) with the forward's map and causal flag.  Returns
+    (dq, dk, dv); rows without keys get dQ = 0, keys no query attends dK = dV = 0."""
+    B, NH, T, dqk = _dims(q, layout)
+    dvd = v.shape[-1]
+    for n, x, d in (("k", k, dqk), ("v", v, dvd), ("o", o, dvd), ("do", do, dvd), ("dq", dq, dqk), ("dk", dk, dqk),
+                    ("dv", dv, dvd)):
+        if x is not None:
+            _shape(x, n, layout, B, NH, T, d)
+    dev = q.device
+    _on_gpu("bwd_blocksparse", dev)
+    lib = load()
+    for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _need(x, n, dev, torch.bfloat16)
+    msb, msh = _block_map(block_map, B, NH, T, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(x, n, dev, torch.bfloat16)
+    need = int(lib.attn_bwd_blocksparse_workspace_bytes(B, NH, T, dqk, dvd, int(bool(deterministic))))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_bwd_blocksparse(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                                        v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
+                                        lse.data_ptr(), do.data_ptr(), _strides(do, layout),
+                                        dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
+                                        dv.data_ptr(), _strides(dv, layout), block_map.data_ptr(), msb, msh,
+                                        B, NH, T, dqk, dvd, float(scale), int(bool(causal)), int(bool(deterministic)),
+                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                        _stream(dev), int(stages)))
     return dq, dk, dv
 
 

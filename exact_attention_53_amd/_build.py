@@ -19,9 +19,13 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 # Each backward launcher configuration (kernel, element type, head dims, mask) is one
 # compilation of attn_bwd_inst.hip, so that they compile in parallel.
+# Masks: 0 none, 1 causal, 2 causal + sliding window, 3 causal + ALiBi, 4 block-sparse map,
+# 5 block-sparse map + causal (bf16 only).
 INSTANCES = [(kind, elem, dqk, dv, mask) for kind in ("kv", "dq") for elem in ("bf16", "f16")
-             for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in (0, 1, 2, 3)]
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_plan.hip", "attn_api.cpp"]
+             for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in (0, 1, 2, 3, 4, 5)
+             if mask < 4 or elem == "bf16"]
+MASK_NAMES = ("full", "causal", "window", "alibi", "bsp", "bsp_causal")
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_plan.hip", "attn_blocksparse.hip", "attn_api.cpp"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU instructions.
 FLAGS = [
@@ -96,7 +100,7 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
         lang = [] if src.endswith(".hip") else ["-x", "hip"]
         cmds.append([hipcc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
     for kind, elem, dqk, dv, mask in INSTANCES:
-        obj = os.path.join(BUILD_DIR, f"attn_bwd_{kind}_{elem}_{dqk}_{dv}_{('full', 'causal', 'window', 'alibi')[mask]}.o")
+        obj = os.path.join(BUILD_DIR, f"attn_bwd_{kind}_{elem}_{dqk}_{dv}_{MASK_NAMES[mask]}.o")
         objs.append(obj)
         defs = [f"-DATTN_INST_DQ={int(kind == 'dq')}", f"-DATTN_INST_ELEM={elem}", f"-DATTN_INST_DQK={dqk}",
                 f"-DATTN_INST_DV={dv}", f"-DATTN_INST_MASK={mask}"]

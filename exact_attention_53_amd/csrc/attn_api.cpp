@@ -100,14 +100,62 @@ constexpr int kKvBlock = 128;   // keys per key/value workgroup
 
 bool int_ptr_ok(const int32_t* p) { return p != nullptr && reinterpret_cast<uintptr_t>(p) % 4 == 0; }
 
+// Block-sparse map of a call (map == nullptr: none).
+struct BsArgs {
+  const uint8_t* map;
+  int64_t sb, sh;  // element (byte) strides along b and h; 0 broadcasts
+};
+
+int bs_nb(int T) { return (T + attn53::kBsBlock - 1) / attn53::kBsBlock; }
+
+// One set of block-sparse lists: per item a slot of nb int32 indices, a count, and the
+// sorted work list (two int32 per item).
+size_t bs_lists_bytes(int64_t items, int nb) {
+  return align256((size_t)items * nb * 4) + align256((size_t)items * 4) + align256((size_t)items * 8);
+}
+
+// Lays out one set of lists at ws, builds them on the device (bs_index_kernel, then the
+// cost-sorted work list); returns the bytes used.
+attn_status bs_build(const BsArgs& bs, int B, int NH, int T, int kind, int group, int causal, char* ws,
+                     attn53::BsList* out, size_t* used, hipStream_t s) {
+  const int nb = bs_nb(T);
+  const int nblk = (nb + group - 1) / group;
+  const int64_t items = (int64_t)B * NH * nblk;
+  int* idx = reinterpret_cast<int*>(ws);
+  int* cnt = reinterpret_cast<int*>(ws + align256((size_t)items * nb * 4));
+  int* list = reinterpret_cast<int*>(ws + align256((size_t)items * nb * 4) + align256((size_t)items * 4));
+  attn53::BsIndexParams ip{bs.map, bs.sb, bs.sh, idx, cnt, NH, B * NH, nb, nblk, group, kind, causal};
+  if (attn53::launch_bs_index(ip, s) != hipSuccess) return ATTN_ERR_HIP;
+  attn53::PlanParams pp{nullptr, nullptr, list, B * NH, T, attn53::kBsBlock * group, attn53::PLAN_Q, causal, cnt};
+  if (attn53::launch_plan(pp, s) != hipSuccess) return ATTN_ERR_HIP;
+  *out = attn53::BsList{list, idx, cnt, nb};
+  *used = bs_lists_bytes(items, nb);
+  return ATTN_OK;
+}
+
+// Validates a block-sparse map and returns its byte extent.
+attn_status check_map(const BsArgs& bs, int B, int NH, int T, Extent* ext) {
+  if (bs.map == nullptr) return ATTN_ERR_NULL;
+  if (bs.sb < 0 || bs.sh < 0) return ATTN_ERR_STRIDE;
+  const int64_t nb = bs_nb(T);
+  ext->lo = reinterpret_cast<uintptr_t>(bs.map);
+  ext->hi = ext->lo + (uintptr_t)(bs.sb * (B - 1) + bs.sh * (NH - 1) + nb * nb);
+  return ATTN_OK;
+}
+
+size_t fwd_bs_ws_bytes(int B, int NH, int T) { return bs_lists_bytes((int64_t)B * NH * bs_nb(T), bs_nb(T)); }
+
 attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const void* k, attn_strides sk,
                      const void* v, attn_strides sv, void* o, attn_strides so, float* lse, const int32_t* seq_q,
                      const int32_t* seq_k, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
-                     int window, int alibi, void* workspace, size_t workspace_bytes, void* stream) {
+                     int window, int alibi, void* workspace, size_t workspace_bytes, void* stream,
+                     const BsArgs* bs = nullptr) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
   if (!window_ok(window, alibi, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
+  if (bs != nullptr && (window != 0 || alibi != 0 || seq_q != nullptr || seq_k != nullptr || et != attn53::ELEM_BF16))
+    return ATTN_ERR_ARG;
   Extent eq, ek, ev, eo;
   if ((st = check_tensor(q, sq, B, NH, T, d_qk, &eq)) != ATTN_OK) return st;
   if ((st = check_tensor(k, sk, B, NH, T, d_qk, &ek)) != ATTN_OK) return st;
@@ -122,15 +170,20 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
     if (overlaps(el, eq) || overlaps(el, ek) || overlaps(el, ev) || overlaps(el, eo)) return ATTN_ERR_ALIAS;
   }
   const bool varlen = seq_q != nullptr || seq_k != nullptr;
-  if (varlen) {
-    if (seq_q == nullptr || seq_k == nullptr) return ATTN_ERR_NULL;
-    if (!int_ptr_ok(seq_q) || !int_ptr_ok(seq_k)) return ATTN_ERR_ALIGN;
-    const size_t need = ws_list_bytes(B, T, kFwdBlock);
+  Extent em{0, 0};
+  if (bs != nullptr) {
+    if ((st = check_map(*bs, B, NH, T, &em)) != ATTN_OK) return st;
+    if (overlaps(eo, em) || (lse != nullptr && overlaps(el, em))) return ATTN_ERR_ALIAS;
+  }
+  if (varlen || bs != nullptr) {
+    if (varlen && (seq_q == nullptr || seq_k == nullptr)) return ATTN_ERR_NULL;
+    if (varlen && (!int_ptr_ok(seq_q) || !int_ptr_ok(seq_k))) return ATTN_ERR_ALIGN;
+    const size_t need = varlen ? ws_list_bytes(B, T, kFwdBlock) : fwd_bs_ws_bytes(B, NH, T);
     if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || workspace_bytes < need)
       return ATTN_ERR_WORKSPACE;
     const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
     if (overlaps(ew, eq) || overlaps(ew, ek) || overlaps(ew, ev) || overlaps(ew, eo) ||
-        (lse != nullptr && overlaps(ew, el)))
+        (lse != nullptr && overlaps(ew, el)) || (bs != nullptr && overlaps(ew, em)))
       return ATTN_ERR_ALIAS;
   }
   FwdParams p{};
@@ -151,14 +204,23 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
     p.seq_k = seq_k;
     p.items = static_cast<const int*>(workspace);
   }
+  if (bs != nullptr) {
+    size_t used = 0;
+    if ((st = bs_build(*bs, B, NH, T, 0, 1, causal, static_cast<char*>(workspace), &p.bs, &used, s)) != ATTN_OK)
+      return st;
+  }
   return hip_status(attn53::launch_fwd(p, et, d_qk, d_v, causal != 0, s));
 }
 
-size_t bwd_ws_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic, bool varlen) {
+size_t bwd_ws_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic, bool varlen, bool bsp = false) {
   if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK || (deterministic != 0 && deterministic != 1)) return 0;
   size_t n = 2 * ws_D_bytes(B, NH, T);  // D and LSE log2(e)
   if (!deterministic) n += ws_acc_bytes(B, NH, T, d_qk);
   if (varlen) n += ws_list_bytes(B, T, kKvBlock) + ws_list_bytes(B, T, attn53::dq_block_rows(d_qk));
+  if (bsp) {  // key-block columns, then groups of dQ query-block rows
+    const int nb = bs_nb(T), group = attn53::dq_block_rows(d_qk) / attn53::kBsBlock;
+    n += bs_lists_bytes((int64_t)B * NH * nb, nb) + bs_lists_bytes((int64_t)B * NH * ((nb + group - 1) / group), nb);
+  }
   return n;
 }
 
@@ -167,13 +229,16 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
                      const void* do_, attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk,
                      void* dv, attn_strides sdv, const int32_t* seq_q, const int32_t* seq_k, int B, int NH, int T,
                      int d_qk, int d_v, float scale, int causal, int window, int alibi, int deterministic,
-                     void* workspace, size_t workspace_bytes, void* stream, unsigned stages) {
+                     void* workspace, size_t workspace_bytes, void* stream, unsigned stages,
+                     const BsArgs* bs = nullptr) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1) ||
       (deterministic != 0 && deterministic != 1))
     return ATTN_ERR_ARG;
   if (!window_ok(window, alibi, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
+  if (bs != nullptr && (window != 0 || alibi != 0 || seq_q != nullptr || seq_k != nullptr || et != attn53::ELEM_BF16))
+    return ATTN_ERR_ARG;
   if (stages == 0 || (stages & ~ATTN_BWD_ALL) != 0) return ATTN_ERR_ARG;
   const bool varlen = seq_q != nullptr || seq_k != nullptr;
   if (varlen) {
@@ -195,11 +260,13 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   if (lse == nullptr) return ATTN_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_ALIGN;
   const Extent el{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + (uintptr_t)B * NH * T * 4u};
-  const size_t need = bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, varlen);
+  Extent em{0, 0};
+  if (bs != nullptr && (st = check_map(*bs, B, NH, T, &em)) != ATTN_OK) return st;
+  const size_t need = bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, varlen, bs != nullptr);
   if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || workspace_bytes < need)
     return ATTN_ERR_WORKSPACE;
   const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
-  const Extent ins[] = {eq, ek, ev, eo, edo, el};
+  const Extent ins[] = {eq, ek, ev, eo, edo, el, em};
   const Extent outs[] = {edq, edk, edv, ew};
   for (const Extent& a : outs)
     for (const Extent& b : ins)
@@ -245,6 +312,19 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
       attn53::PlanParams pp{seq_q, seq_k, list_dq, B, T, attn53::dq_block_rows(d_qk), attn53::PLAN_Q, causal};
       if ((st = hip_status(attn53::launch_plan(pp, s))) != ATTN_OK) return st;
     }
+  }
+  if (bs != nullptr) {
+    size_t used = 0;
+    char* lists = ws + off;
+    if (stages & ATTN_BWD_MAIN) {
+      if ((st = bs_build(*bs, B, NH, T, 1, 1, causal, lists, &p.bs_kv, &used, s)) != ATTN_OK) return st;
+    }
+    const int group = attn53::dq_block_rows(d_qk) / attn53::kBsBlock;
+    lists += bs_lists_bytes((int64_t)B * NH * bs_nb(T), bs_nb(T));
+    if ((stages & ATTN_BWD_DQ) && deterministic) {
+      if ((st = bs_build(*bs, B, NH, T, 2, group, causal, lists, &p.bs_dq, &used, s)) != ATTN_OK) return st;
+    }
+    p.bsp = 1;
   }
   if (stages & ATTN_BWD_PREPROCESS) {
     st = hip_status(attn53::launch_bwd_preprocess(p, et, d_qk, d_v, !deterministic, s));
@@ -337,7 +417,39 @@ const char* attn_status_string(attn_status s) {
   return "unknown attn_status";
 }
 
-int attn_version(void) { return 300; }
+int attn_version(void) { return 400; }
+
+size_t attn_fwd_blocksparse_workspace_bytes(int B, int NH, int T, int d_qk, int d_v) {
+  if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK) return 0;
+  return fwd_bs_ws_bytes(B, NH, T);
+}
+
+attn_status attn_fwd_blocksparse(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                                 attn_strides sv, void* o, attn_strides so, float* lse, const uint8_t* block_map,
+                                 int64_t map_stride_b, int64_t map_stride_h, int B, int NH, int T, int d_qk,
+                                 int d_v, float scale, int causal, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  const BsArgs bs{block_map, map_stride_b, map_stride_h};
+  return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale,
+                  causal, 0, 0, workspace, workspace_bytes, stream, &bs);
+}
+
+size_t attn_bwd_blocksparse_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic) {
+  return bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, false, true);
+}
+
+attn_status attn_bwd_blocksparse(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                                 attn_strides sv, const void* o, attn_strides so, const float* lse, const void* do_,
+                                 attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk, void* dv,
+                                 attn_strides sdv, const uint8_t* block_map, int64_t map_stride_b,
+                                 int64_t map_stride_h, int B, int NH, int T, int d_qk, int d_v, float scale,
+                                 int causal, int deterministic, void* workspace, size_t workspace_bytes,
+                                 void* stream, unsigned stages) {
+  const BsArgs bs{block_map, map_stride_b, map_stride_h};
+  return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr,
+                  nullptr, B, NH, T, d_qk, d_v, scale, causal, 0, 0, deterministic, workspace, workspace_bytes,
+                  stream, stages, &bs);
+}
 
 attn_status attn_fwd(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
                      attn_strides sv, void* o, attn_strides so, float* lse, int B, int NH, int T, int d_qk,

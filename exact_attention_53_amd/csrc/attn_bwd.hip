@@ -1,6 +1,8 @@
 // Exact attention backward for gfx950: launchers of the preprocess and finalize
 // kernels and dispatch of the per-configuration key/value and dQ launchers.  The
 // kernels themselves are in attn_bwd_kernels.hpp.
+#include <type_traits>
+
 #include "attn_bwd_kernels.hpp"
 
 namespace attn53 {
@@ -27,8 +29,9 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int 
 }
 
 // mask mode of the launchers: 0 none, 1 causal, 2 causal with a sliding window, 3 causal
-// with the ALiBi bias
+// with the ALiBi bias, 4 block-sparse map, 5 block-sparse map and causal
 static inline int mask_mode(const BwdParams& p, bool causal) {
+  if (p.bsp) return causal ? 5 : 4;
   return !causal ? 0 : p.win < kNoWindow ? 2 : p.alibi ? 3 : 1;
 }
 
@@ -38,7 +41,12 @@ static hipError_t main_m(const BwdParams& p, bool causal, bool det, hipStream_t 
     case 0: return bwd_main_t<E, DQK, DV, 0>(p, det, s);
     case 1: return bwd_main_t<E, DQK, DV, 1>(p, det, s);
     case 2: return bwd_main_t<E, DQK, DV, 2>(p, det, s);
-    default: return bwd_main_t<E, DQK, DV, 3>(p, det, s);
+    case 3: return bwd_main_t<E, DQK, DV, 3>(p, det, s);
+    default:
+      if constexpr (std::is_same<E, bf16>::value)  // block-sparse maps: bf16 only
+        return mask_mode(p, causal) == 5 ? bwd_main_t<E, DQK, DV, 5>(p, det, s) : bwd_main_t<E, DQK, DV, 4>(p, det, s);
+      else
+        return hipErrorInvalidValue;
   }
 }
 
@@ -62,7 +70,12 @@ static hipError_t dq_m(const BwdParams& p, bool causal, hipStream_t s) {
     case 0: return bwd_dq_t<E, DQK, DV, 0>(p, s);
     case 1: return bwd_dq_t<E, DQK, DV, 1>(p, s);
     case 2: return bwd_dq_t<E, DQK, DV, 2>(p, s);
-    default: return bwd_dq_t<E, DQK, DV, 3>(p, s);
+    case 3: return bwd_dq_t<E, DQK, DV, 3>(p, s);
+    default:
+      if constexpr (std::is_same<E, bf16>::value)
+        return mask_mode(p, causal) == 5 ? bwd_dq_t<E, DQK, DV, 5>(p, s) : bwd_dq_t<E, DQK, DV, 4>(p, s);
+      else
+        return hipErrorInvalidValue;
   }
 }
 

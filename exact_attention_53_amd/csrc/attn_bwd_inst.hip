@@ -3,7 +3,7 @@
 //   ATTN_INST_DQ     0: key/value kernel (bwd_main_t), 1: dQ kernel (bwd_dq_t)
 //   ATTN_INST_ELEM   bf16 or f16
 //   ATTN_INST_DQK, ATTN_INST_DV, ATTN_INST_MASK (0 none, 1 causal, 2 causal + sliding window,
-//                    3 causal + ALiBi bias)
+//                    3 causal + ALiBi bias, 4 block-sparse map, 5 block-sparse map + causal)
 #include "attn_bwd_kernels.hpp"
 
 namespace attn53 {

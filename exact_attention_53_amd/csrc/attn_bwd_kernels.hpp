@@ -174,8 +174,9 @@ struct KvPlan {
 };
 
 // WIN (with CAUSAL only): sliding window of p.win keys.  ALIBI (with CAUSAL only): the
-// linear bias -m_h (i - j) on the scaled scores.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool ATOMIC_DQ>
+// linear bias -m_h (i - j) on the scaled scores.  BSP: block-sparse map (p.bs_kv): the
+// workgroup visits only the query steps of its key block's live query blocks, ascending.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool ATOMIC_DQ, bool BSP = false>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 64 ? 2 : 1, DQK == 64 ? 2 : 1))) void bwd_kv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
@@ -196,7 +197,12 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
   const int T = p.T;
   // Lq / Lk: valid query / key rows of this batch (T, or the padded-batch lengths)
   int kb, b, h, Lq = T, Lk = T;
-  if (p.items_kv == nullptr) {
+  if constexpr (BSP) {  // work list of (b * NH + h, key block), longest first
+    const int bhi = p.bs_kv.items[2 * blockIdx.x];
+    kb = p.bs_kv.items[2 * blockIdx.x + 1];
+    b = bhi / p.NH;
+    h = bhi % p.NH;
+  } else if (p.items_kv == nullptr) {
     const Item item = schedule(blockIdx.x, p.B * p.NH);
     kb = item.rank;  // causal: block 0 has the most query blocks -> first
     b = item.bh / p.NH;
@@ -233,7 +239,19 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
   const int i0 = CAUSAL ? key0 / BWD_BM : 0;
   // sliding window: query blocks past i_end hold no query whose window reaches this block
   const int i_end = WIN ? min(nqb, (key0 + BWD_BN - 1 + W - 1) / BWD_BM + 1) : nqb;
-  const int n_q = i_end - i0;
+  // Block-sparse: the live query blocks (ascending) hold two steps of 64 rows each; the
+  // upper step of the last one may lie wholly past Lq and is then left out.
+  const int* bs_idx = BSP ? p.bs_kv.idx + ((int64_t)bh * p.bs_kv.nb + kb) * p.bs_kv.nb : nullptr;
+  const int bs_cnt = BSP ? p.bs_kv.cnt[bh * p.bs_kv.nb + kb] : 0;
+  const int bs_skip = (BSP && bs_cnt > 0 && bs_idx[bs_cnt - 1] * kBsBlock + BWD_BM >= Lq) ? 1 : 0;
+  const int n_q = BSP ? 2 * bs_cnt - bs_skip : i_end - i0;
+  // query step (64 rows) visited at position it
+  auto qstep = [&](int it) {
+    if constexpr (BSP)
+      return 2 * bs_idx[it >> 1] + (it & 1);
+    else
+      return i0 + it;
+  };
   if (key0 >= Lk || n_q <= 0) {  // padding keys only, or no query sees them: dK = dV = 0
     if (my_key < T) {
 #pragma unroll
@@ -316,7 +334,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
     }
   };
 
-  load_step(i0, std::integral_constant<int, 0>{});
+  load_step(qstep(0), std::integral_constant<int, 0>{});
 
   // One query block.  MASKED: the block touches the diagonal or a ragged edge.  The
   // body is one basic block in source order S, dP, P, dV, dS, dK so that the matrix
@@ -489,13 +507,13 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
 
   auto step = [&](int it, auto bufc, auto maskc) {
     constexpr int BUF = decltype(bufc)::value;
-    const int qb = i0 + it;
+    const int qb = qstep(it);
     const int q0 = qb * BWD_BM;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads (and its atomics of the step before) are done
     __syncthreads();                // every wave's tiles are in; the other buffers are free
-    if (it + 1 < n_q) load_step(qb + 1, std::integral_constant<int, 1 - BUF>{});
+    if (it + 1 < n_q) load_step(qstep(it + 1), std::integral_constant<int, 1 - BUF>{});
     if constexpr (ATOMIC_DQ) {
-      if (it > 0) dq_partial((const ATTN_LDS char*)((ST_DOUBLE && !BUF) ? st1 : st0), q0 - BWD_BM);
+      if (it > 0) dq_partial((const ATTN_LDS char*)((ST_DOUBLE && !BUF) ? st1 : st0), qstep(it - 1) * BWD_BM);
     }
     step_body(q0, bufc, maskc);
   };
@@ -507,8 +525,10 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
   constexpr auto B0 = std::integral_constant<int, 0>{};
   constexpr auto B1 = std::integral_constant<int, 1>{};
   const bool ragged_keys = key0 + BWD_BN > Lk;
-  const int n_head = ragged_keys ? n_q : (CAUSAL ? min(BWD_BN / BWD_BM, n_q) : 0);  // even, or n_q
-  const int n_tail = (n_head < n_q && Lq % BWD_BM != 0) ? 1 : 0;
+  // block-sparse: only a live diagonal block (the first in the list) carries the causal mask
+  const bool diag_first = !BSP || (bs_cnt > 0 && bs_idx[0] == kb);
+  const int n_head = ragged_keys ? n_q : ((CAUSAL && diag_first) ? min(BWD_BN / BWD_BM, n_q) : 0);  // even, or n_q
+  const int n_tail = (n_head < n_q && qstep(n_q - 1) * BWD_BM + BWD_BM > Lq) ? 1 : 0;
   // sliding window: steps from win_start on hold a query past the window of key0
   const int x_win = key0 + W - BWD_BM + 1;
   const int win_start = WIN ? max(n_head, (x_win <= 0 ? 0 : (x_win + BWD_BM - 1) / BWD_BM) - i0) : n_q;
@@ -539,7 +559,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
   if constexpr (ATOMIC_DQ) {
     __syncthreads();  // the last dS^T tile is complete
     const bool last_odd = ((n_q - 1) & 1) != 0;
-    dq_partial((const ATTN_LDS char*)((ST_DOUBLE && last_odd) ? st1 : st0), (i0 + n_q - 1) * BWD_BM);
+    dq_partial((const ATTN_LDS char*)((ST_DOUBLE && last_odd) ? st1 : st0), qstep(n_q - 1) * BWD_BM);
   }
 
   // dK = scale dS^T Q, dV; element r of tile t: key key0 + kw + 8 (r / 4) + 4 g + r % 4,
@@ -644,8 +664,10 @@ struct DqShape {
 };
 
 // WIN (with CAUSAL only): sliding window of p.win keys.  ALIBI (with CAUSAL only): the
-// linear bias -m_h (i - j) on the scaled scores.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI>
+// linear bias -m_h (i - j) on the scaled scores.  BSP: block-sparse map (p.bs_dq): the
+// workgroup visits the key tiles of the live key blocks of any of its query-block rows,
+// descending; a wavefront computes only on the tiles live for its own rows.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool BSP = false>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
                                                                          DqShape<DQK>::WAVES_PER_EU)))
 void bwd_dq_kernel(BwdParams p) {
@@ -663,7 +685,12 @@ void bwd_dq_kernel(BwdParams p) {
   const int nqb = (T + BM - 1) / BM;
   // Lq / Lk: valid query / key rows of this batch (T, or the padded-batch lengths)
   int qb, b, h, Lq = T, Lk = T;
-  if (p.items_dq == nullptr) {
+  if constexpr (BSP) {  // work list of (b * NH + h, query block of BM rows), longest first
+    const int bhi = p.bs_dq.items[2 * blockIdx.x];
+    qb = p.bs_dq.items[2 * blockIdx.x + 1];
+    b = bhi / p.NH;
+    h = bhi % p.NH;
+  } else if (p.items_dq == nullptr) {
     const Item item = schedule(blockIdx.x, p.B * p.NH);
     qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
     b = item.bh / p.NH;
@@ -694,8 +721,15 @@ void bwd_dq_kernel(BwdParams p) {
   const int n_kv = (kv_end + DQ_BN - 1) / DQ_BN;
   // sliding window: tiles below j_lo hold no key of any row's window
   const int j_lo = WIN ? max(0, q0 - W + 1) / DQ_BN : 0;
-  const int n_tiles = n_kv - j_lo;
-  if (q0 >= Lq || n_kv == 0) {  // padding rows only, or no keys: dQ = 0
+  // Block-sparse: the live key blocks of the workgroup's query-block rows (descending, with
+  // a bit per row) hold two tiles each; the upper tile of the highest one may lie wholly
+  // past kv_end and is then left out.  Row bit of this wavefront: its 128-row block.
+  const int* bs_idx = BSP ? p.bs_dq.idx + ((int64_t)bh * nqb + qb) * p.bs_dq.nb : nullptr;
+  const int bs_cnt = BSP ? p.bs_dq.cnt[bh * nqb + qb] : 0;
+  const int bs_skip = (BSP && bs_cnt > 0 && (bs_idx[0] & 0xffff) * kBsBlock + DQ_BN >= kv_end) ? 1 : 0;
+  const int bs_row = 16 + (32 * QT * wu) / kBsBlock;
+  const int n_tiles = BSP ? 2 * bs_cnt - bs_skip : n_kv - j_lo;
+  if (q0 >= Lq || n_kv == 0 || (BSP && n_tiles <= 0)) {  // padding rows only, or no keys: dQ = 0
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
       const int q = qw + 32 * u + lq;
@@ -919,14 +953,22 @@ void bwd_dq_kernel(BwdParams p) {
   const int first_ragged = Lk % DQ_BN != 0 ? Lk / DQ_BN : n_kv;
   const int first_masked = min(min(first_ragged, CAUSAL ? q0 / DQ_BN : n_kv), n_kv);
   const int j_mid = WIN ? max(j_lo, min((max(0, q0 + BM - W) + DQ_BN - 1) / DQ_BN, first_masked)) : j_lo;
-  const int n_head = n_kv - first_masked;
-  const int n_msk = n_head + (j_mid - j_lo);
+  int n_head = n_kv - first_masked;
+  int n_msk = n_head + (j_mid - j_lo);
   auto tile_of = [&](int it) {
-    if constexpr (WIN)
+    if constexpr (BSP) {
+      const int u = it + bs_skip;
+      return 2 * (bs_idx[u >> 1] & 0xffff) + 1 - (u & 1);
+    } else if constexpr (WIN)
       return it < n_head ? n_kv - 1 - it : it < n_msk ? j_mid - 1 - (it - n_head) : first_masked - 1 - (it - n_msk);
     else
       return n_kv - 1 - it;
   };
+  if constexpr (BSP) {  // the masked tiles are the highest ones, so they lead the list
+    n_head = 0;
+    while (n_head < n_tiles && tile_of(n_head) >= first_masked) ++n_head;
+    n_msk = n_head;
+  }
   load_kv(tile_of(0) * DQ_BN, std::integral_constant<int, 0>{});
   auto step = [&](int it, auto bufc, auto maskc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
@@ -935,6 +977,7 @@ void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
     if (it + 1 < n_tiles) load_kv(tile_of(it + 1) * DQ_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * DQ_BN;
+    if (BSP && ((bs_idx[(it + bs_skip) >> 1] >> bs_row) & 1) == 0) return;  // no live block for these rows
     if constexpr (decltype(maskc)::value) {
       if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
       if (WIN && key0 + DQ_BN <= qw - W + 1) return;  // tile wholly below its rows' windows
@@ -1014,25 +1057,28 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
 // per-configuration launchers (each instantiated by one compilation of attn_bwd_inst.hip)
 // ---------------------------------------------------------------------------------
 // MASK: 0 none, 1 causal, 2 causal with a sliding window of p.win keys, 3 causal with the
-// ALiBi bias.
+// ALiBi bias, 4 block-sparse map, 5 block-sparse map and causal.
+// MASK 4: block-sparse map; 5: block-sparse map and the causal mask.
 template <class E, int DQK, int DV, int MASK>
 hipError_t bwd_main_t(const BwdParams& p, bool deterministic, hipStream_t s) {
-  constexpr bool CAUSAL = MASK >= 1, WIN = MASK == 2, ALIBI = MASK == 3;
+  constexpr bool CAUSAL = MASK == 1 || MASK == 2 || MASK == 3 || MASK == 5, WIN = MASK == 2, ALIBI = MASK == 3;
+  constexpr bool BSP = MASK >= 4;
   const int nkb = (p.T + BWD_BN - 1) / BWD_BN;
   const dim3 grid_kv(nkb * p.B * p.NH);
   if (deterministic)
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, false>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, false, BSP>), grid_kv, dim3(BWD_NT), 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, true>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, true, BSP>), grid_kv, dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
 template <class E, int DQK, int DV, int MASK>
 hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
-  constexpr bool CAUSAL = MASK >= 1, WIN = MASK == 2, ALIBI = MASK == 3;
+  constexpr bool CAUSAL = MASK == 1 || MASK == 2 || MASK == 3 || MASK == 5, WIN = MASK == 2, ALIBI = MASK == 3;
+  constexpr bool BSP = MASK >= 4;
   const int nqb = (p.T + DqShape<DQK>::BM - 1) / DqShape<DQK>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s,
-                     p);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, BSP>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0,
+                     s, p);
   return hipGetLastError();
 }
 
@@ -1044,5 +1090,9 @@ hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
   extern template hipError_t bwd_dq_t<E, DQK, DV, MASK>(const BwdParams&, hipStream_t);
 #define ATTN_EXTERN_BWD(DQK, DV, MASK) ATTN_EXTERN_BWD_E(bf16, DQK, DV, MASK) ATTN_EXTERN_BWD_E(f16, DQK, DV, MASK)
 ATTN_BWD_CONFIGS(ATTN_EXTERN_BWD)
+// block-sparse maps: bf16 only
+#define ATTN_BWD_BSP_CONFIGS(X) X(64, 64, 4) X(64, 64, 5) X(128, 128, 4) X(128, 128, 5) X(192, 128, 4) X(192, 128, 5)
+#define ATTN_EXTERN_BWD_BF16(DQK, DV, MASK) ATTN_EXTERN_BWD_E(bf16, DQK, DV, MASK)
+ATTN_BWD_BSP_CONFIGS(ATTN_EXTERN_BWD_BF16)
 
 }  // namespace attn53

@@ -49,8 +49,9 @@ constexpr float kSumLimit = 256.f;        // 2^kRescaleThreshold
 // WIN (with CAUSAL only): sliding window of p.win keys.  ALIBI (with CAUSAL only): the
 // linear bias -m_h (i - j) added to the scaled scores.
 // SPLIT (non-causal only): one key chunk of p.kv_chunk keys per workgroup, partial
-// results to p.part.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool SPLIT = false>
+// results to p.part.  BSP: block-sparse map (p.bs): the workgroup visits only the key tiles
+// of its query block's live key blocks, in the descending order of p.bs's list.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool SPLIT = false, bool BSP = false>
 __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr int KS = DQK / 16;
   constexpr int NDT = DV / 32;
@@ -69,7 +70,12 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   int qb, b, h, Lq = T, Lk = p.Tk;
   const int nbase = nqb * p.B * p.NH;
   const int split = SPLIT ? (int)blockIdx.x / nbase : 0;
-  if (p.items == nullptr) {
+  if constexpr (BSP) {  // work list of (b * NH + h, query block), longest first
+    const int bhi = p.bs.items[2 * blockIdx.x];
+    qb = p.bs.items[2 * blockIdx.x + 1];
+    b = bhi / p.NH;
+    h = bhi % p.NH;
+  } else if (p.items == nullptr) {
     const Item item = schedule(SPLIT ? (int)blockIdx.x % nbase : (int)blockIdx.x, p.B * p.NH);
     qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
     b = item.bh / p.NH;
@@ -102,7 +108,21 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int n_kv = (kv_end + FWD_BN - 1) / FWD_BN;
   // sliding window: tiles below j_lo hold no key of any row's window
   const int j_lo = WIN ? max(0, q0 - W + 1) / FWD_BN : SPLIT ? c0 / FWD_BN : 0;
-  const int n_tiles = n_kv - j_lo;
+  // Block-sparse: the live key blocks (descending) hold two tiles each; the upper tile of
+  // the highest one may lie wholly past kv_end and is then left out.
+  const int* bs_idx = BSP ? p.bs.idx + ((int64_t)bh * nqb + qb) * p.bs.nb : nullptr;
+  const int bs_cnt = BSP ? p.bs.cnt[bh * nqb + qb] : 0;
+  const int bs_skip = (BSP && bs_cnt > 0 && bs_idx[0] * kBsBlock + FWD_BN >= kv_end) ? 1 : 0;
+  const int n_tiles = BSP ? 2 * bs_cnt - bs_skip : n_kv - j_lo;
+  // key tile visited at position it (0 .. n_tiles-1): descending
+  auto tile_of = [&](int it) {
+    if constexpr (BSP) {
+      const int u = it + bs_skip;
+      return 2 * bs_idx[u >> 1] + 1 - (u & 1);
+    } else {
+      return n_kv - 1 - it;
+    }
+  };
   float* part_o = SPLIT ? p.part + ((int64_t)split * p.B * p.NH + bh) * T * DV : nullptr;
   float* part_l = SPLIT ? p.part + (int64_t)p.nsplit * p.B * p.NH * T * DV + ((int64_t)split * p.B * p.NH + bh) * T
                         : nullptr;
@@ -115,7 +135,7 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     }
     return;
   }
-  if (q0 >= Lq || n_kv == 0) {  // padding rows only, or no keys: O = 0, LSE = -inf
+  if (q0 >= Lq || n_kv == 0 || (BSP && n_tiles <= 0)) {  // padding rows only, or no keys: O = 0, LSE = -inf
     if (my_q < T) {
       E* orow = og + (int64_t)my_q * p.so.t;
 #pragma unroll
@@ -153,17 +173,17 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = zero16();
 
-  load_kv((n_kv - 1) * FWD_BN, std::integral_constant<int, 0>{});
+  load_kv(tile_of(0) * FWD_BN, std::integral_constant<int, 0>{});
 
   // One key/value tile; BUF is this tile's buffer, the next tile goes to the other one.
   // MASKED: the tile may hold keys past a row's diagonal or past T (the first tiles).
   auto step = [&](int it, auto bufc, auto maskc) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASKED = decltype(maskc)::value;
-    const int j = n_kv - 1 - it;  // diagonal / tail tile first
+    const int j = tile_of(it);  // diagonal / tail tile first
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile j has landed in LDS
     __syncthreads();                // ... and every other wave's; the other buffer is free
-    if (it + 1 < n_tiles) load_kv((j - 1) * FWD_BN, std::integral_constant<int, 1 - BUF>{});
+    if (it + 1 < n_tiles) load_kv(tile_of(it + 1) * FWD_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * FWD_BN;
     if (MASKED && CAUSAL && key0 > qw + 31) return;  // tile wholly above this wavefront's rows
     if (MASKED && WIN && key0 + FWD_BN <= qw - W + 1) return;  // wholly below its windows
@@ -278,7 +298,11 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   const int first_ragged = Lk % FWD_BN != 0 ? Lk / FWD_BN : n_kv;
   const int first_masked = min(min(first_ragged, CAUSAL ? q0 / FWD_BN : n_kv), n_kv);
   const int j_full = WIN ? min((max(0, q0 + FWD_BM - W) + FWD_BN - 1) / FWD_BN, first_masked) : 0;
-  const int n_mask = n_kv - first_masked;
+  int n_mask = n_kv - first_masked;
+  if constexpr (BSP) {  // the masked tiles are the highest ones, so they lead the list
+    n_mask = 0;
+    while (n_mask < n_tiles && tile_of(n_mask) >= first_masked) ++n_mask;
+  }
   const int mid_end = WIN ? n_tiles - max(0, j_full - j_lo) : n_tiles;
   int it = 0;
   if (qw >= Lq) {
@@ -290,9 +314,9 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
       __syncthreads();
       if (it + 1 < n_tiles) {
         if (it & 1)
-          load_kv((n_kv - 2 - it) * FWD_BN, B0);
+          load_kv(tile_of(it + 1) * FWD_BN, B0);
         else
-          load_kv((n_kv - 2 - it) * FWD_BN, B1);
+          load_kv(tile_of(it + 1) * FWD_BN, B1);
       }
     }
   } else {
@@ -362,7 +386,12 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 template <class E, int DQK, int DV>
 static hipError_t fwd_launch(const FwdParams& p, bool causal, hipStream_t s) {
   const dim3 grid((p.T + FWD_BM - 1) / FWD_BM * p.B * p.NH);
-  if (!causal)
+  if (p.bs.items != nullptr) {
+    if (causal)
+      hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, false, false, false, true>), grid, dim3(FWD_NT), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, false, false, false, false, true>), grid, dim3(FWD_NT), 0, s, p);
+  } else if (!causal)
     hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, false, false, false>), grid, dim3(FWD_NT), 0, s, p);
   else if (p.win < kNoWindow)
     hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, true, false>), grid, dim3(FWD_NT), 0, s, p);

@@ -10,6 +10,20 @@ struct Strides {
   int64_t b, h, t;
 };
 
+// Block-sparse map in the form the kernels walk (built on the device by bs_index_kernel
+// from the caller's map, attn_blocksparse.hip).  For every work item (bh, blk) of a
+// kernel, idx[(bh * nblk + blk) * nb ...] lists its live blocks of the other side in the
+// order the kernel visits them and cnt[bh * nblk + blk] counts them; items[] is the work
+// list (bh, blk) sorted by cost, longest first.  Blocks are kBsBlock x kBsBlock
+// elements.  The dQ kernel's lists hold key block | (live query block rows of the
+// item) << 16.  All nullptr: no block-sparse map.
+struct BsList {
+  const int* items;
+  const int* idx;
+  const int* cnt;
+  int nb;                  // blocks along T: ceil(T / kBsBlock)
+};
+
 struct FwdParams {
   const void* q; Strides sq;
   const void* k; Strides sk;
@@ -32,6 +46,7 @@ struct FwdParams {
   const int* seq_q;
   const int* seq_k;
   const int* items;
+  BsList bs;               // block-sparse map: live key blocks per query block
 };
 
 struct BwdParams {
@@ -59,6 +74,9 @@ struct BwdParams {
   const int* seq_k;
   const int* items_kv;
   const int* items_dq;
+  int bsp;                 // 1: block-sparse map (the lists below, built for the stages run)
+  BsList bs_kv;            // block-sparse map: live query blocks per key block (ascending)
+  BsList bs_dq;            // ... live key blocks per dQ query block (descending, row bits)
 };
 
 // Work lists of padded batches (see attn_plan.hip).  KIND_Q: query blocks of `block`
@@ -70,9 +88,12 @@ struct PlanParams {
   const int* seq_k;
   int* items;    // out: 2 int32 per item (b, block), longest first
   int B, T, block, kind, causal;
+  const int* counts;  // block-sparse: live blocks per item (B = B * NH items of T / block
+                      // blocks); the cost is two 64-row tiles per live block
 };
 
 constexpr int kRowPad = 128;
+constexpr int kBsBlock = 128;  // block-sparse map: elements per block along each side
 constexpr int kNoWindow = 1 << 30;  // a window wider than any sequence
 
 // 16-bit element type of Q, K, V, O, dO, dQ, dK, dV (one type per call).
@@ -88,6 +109,18 @@ hipError_t launch_bwd_main(const BwdParams& p, ElemType et, int d_qk, int d_v, b
 hipError_t launch_bwd_dq(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s);
 hipError_t launch_bwd_finalize(const BwdParams& p, ElemType et, int d_qk, hipStream_t s);
 hipError_t launch_plan(const PlanParams& p, hipStream_t s);
+// Block-sparse map -> per-item lists (see BsList).  kind: 0 query-block rows (forward,
+// descending live key blocks, causal: up to the diagonal), 1 key-block columns (key/value
+// kernel, ascending live query blocks, causal: from the diagonal), 2 groups of `group`
+// query-block rows (dQ kernel, descending union of their live key blocks with row bits).
+struct BsIndexParams {
+  const unsigned char* map;
+  int64_t msb, msh;        // element strides of the map along b and h (0: broadcast)
+  int* idx;
+  int* cnt;
+  int NH, nbh, nb, nblk, group, kind, causal;
+};
+hipError_t launch_bs_index(const BsIndexParams& p, hipStream_t s);
 // Query rows per workgroup of the dQ kernel (its work list uses blocks of this size).
 int dq_block_rows(int d_qk);
 

@@ -1,4 +1,4 @@
-// Work lists for padded batches.
+// Work lists for padded batches and block-sparse maps.
 //
 // Pages cited (by title and section):
 //   [2CTA] "深度学习反向传播优化：2-CTA MMA模式与内存访问优化" 3.2 (load balancing: a
@@ -6,7 +6,8 @@
 //   [SA8]  "ops(8)：self-attention 的 CUDA 实现及优化 (下) - 深度分析" 1.2 (padding mask with
 //          per-batch query and key/value lengths)
 //
-// With per-batch lengths the work of a (batch, block) item is known only on the device.
+// With per-batch lengths, or a block-sparse map, the work of an item is known only on the
+// device.
 // One workgroup costs every item (the number of 64-row tiles its loop visits), sorts the
 // items by cost, longest first, with a counting sort in LDS, and writes the list that
 // the attention kernels then walk in launch order.  Items of cost 0 (blocks wholly in
@@ -22,6 +23,10 @@ constexpr int PLAN_NT = 1024;
 constexpr int PLAN_BUCKETS = PLAN_NT;  // costs above PLAN_BUCKETS - 1 share the top bucket
 
 __device__ __forceinline__ int item_cost(const PlanParams& p, int b, int blk) {
+  if (p.counts != nullptr) {  // block-sparse: two tiles per live block
+    const int nblk = (p.T + p.block - 1) / p.block;
+    return 2 * p.counts[b * nblk + blk];
+  }
   const int lq = batch_len(p.seq_q, b, p.T), lk = batch_len(p.seq_k, b, p.T);
   if (p.kind == PLAN_Q) {  // query block: key tiles of 64 up to its diagonal / Lk
     const int q0 = blk * p.block;

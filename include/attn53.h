@@ -335,6 +335,61 @@ attn_status attn_fwd_decode(attn_dtype dtype,
                             float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block-sparse attention — the block-sparse mask pattern of the FA4 framework, a mask
+ * module composed with the causal mask and with unchanged compute and scheduling
+ * [2CTA 5.1, 5.2].  The pages give no format; this is the reading taken:
+ *   block_map : device pointer to uint8 entries, one per (query block, key block) pair of
+ *               128 x 128 elements, nb = ceil(T / 128) blocks along each side.  The map of
+ *               head (b, h) starts at block_map + b * map_stride_b + h * map_stride_h
+ *               (strides in bytes, >= 0; 0 shares one map across batches / heads) and is
+ *               row-major (nb, nb): entry [qb * nb + kb].  Non-zero = live.  Read only.
+ *   Element (i, j) is attended iff map[i / 128][j / 128] != 0 and, when causal = 1,
+ *   j <= i.  Key blocks that are not live are never loaded; a live block that the
+ *   causal mask or the end of the sequence cuts is a "partial" block and carries the
+ *   element mask, every other live block is "full" and runs mask-free.  A query row left
+ *   with no key gets O = 0 and LSE = -inf, and zero gradients; a key no query attends
+ *   gets dK = dV = 0.
+ *   workspace : device memory of at least the matching *_workspace_bytes, 16-byte
+ *               aligned, owned by the caller, clobbered.  It holds the lists of live
+ *               blocks that a preprocessing kernel builds from the map for every work
+ *               item, and the work list ordered by cost, longest first [2CTA 3.2]
+ *               (forward: about 4 * B * NH * nb * (nb + 3) bytes; the backward twice that
+ *               plus what attn_bwd keeps there).  Too small: ATTN_ERR_WORKSPACE.
+ * Element type bf16 (as attn_fwd / attn_bwd); every other argument, layout rule and error
+ * is that of attn_fwd / attn_bwd_staged (map NULL: ATTN_ERR_NULL; a negative map stride:
+ * ATTN_ERR_STRIDE; an output overlapping the map: ATTN_ERR_ALIAS).  The backward must
+ * get the forward's map and causal flag.
+ */
+size_t attn_fwd_blocksparse_workspace_bytes(int B, int NH, int T, int d_qk, int d_v);
+
+attn_status attn_fwd_blocksparse(const void* q, attn_strides sq,
+                                 const void* k, attn_strides sk,
+                                 const void* v, attn_strides sv,
+                                 void* o, attn_strides so,
+                                 float* lse,
+                                 const uint8_t* block_map, int64_t map_stride_b, int64_t map_stride_h,
+                                 int B, int NH, int T, int d_qk, int d_v,
+                                 float scale, int causal,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+size_t attn_bwd_blocksparse_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic);
+
+attn_status attn_bwd_blocksparse(const void* q, attn_strides sq,
+                                 const void* k, attn_strides sk,
+                                 const void* v, attn_strides sv,
+                                 const void* o, attn_strides so,
+                                 const float* lse,
+                                 const void* do_, attn_strides sdo,
+                                 void* dq, attn_strides sdq,
+                                 void* dk, attn_strides sdk,
+                                 void* dv, attn_strides sdv,
+                                 const uint8_t* block_map, int64_t map_stride_b, int64_t map_stride_h,
+                                 int B, int NH, int T, int d_qk, int d_v,
+                                 float scale, int causal, int deterministic,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 unsigned stages);
+
+/*
  * attn_bwd_noalloc — attn_bwd without a caller-supplied workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, allocation-free serving or
  * training loops, harnesses that forbid hipMalloc.  The workspace (D, LSE log2(e) and, in

@@ -280,3 +280,55 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
     assert lib.attn_bwd_noalloc(*args, 4, 16, 8192, 128, 128, 0.088, 1, 0, None) == WORKSPACE
     # deterministic mode, 2^24 padded rows: 128 MiB
     assert lib.attn_bwd_noalloc(*args, 16, 16, 65536, 128, 128, 0.088, 1, 1, None) == WORKSPACE
+
+
+def test_blocksparse_validation(lib):
+    """attn_fwd_blocksparse / attn_bwd_blocksparse: the map is validated on the host like
+    every tensor; the workspace holds the per-item block lists and work lists."""
+    st, sv = strides(64, 2, 64), strides(64, 2, 64)
+    MAP = GOOD + 0xc00000
+
+    def bfwd(m=MAP, msb=0, msh=0, o=GOOD + 0x300000, ws=GOOD + 0xb00000, ws_bytes=1 << 20):
+        return lib.attn_fwd_blocksparse(GOOD, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, o, sv, None, m, msb, msh,
+                                        1, 2, 64, 64, 64, 0.125, 1, ws, ws_bytes, None)
+
+    def bbwd(m=MAP, msb=0, msh=0, dq=GOOD + 0x600000, ws=GOOD + 0x900000, ws_bytes=1 << 20, stages=7):
+        return lib.attn_bwd_blocksparse(GOOD, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, GOOD + 0x300000, sv,
+                                        GOOD + 0x400000, GOOD + 0x500000, sv, dq, st, GOOD + 0x700000, st,
+                                        GOOD + 0x800000, sv, m, msb, msh, 1, 2, 64, 64, 64, 0.125, 1, 1, ws,
+                                        ws_bytes, None, stages)
+
+    for f in (bfwd, bbwd):
+        assert f(m=None) == NULL
+        assert f(msh=-1) == STRIDE
+        assert f(ws=None) == WORKSPACE
+        assert f(ws_bytes=16) == WORKSPACE
+    assert bfwd(o=MAP) == ALIAS            # the output overlaps the map
+    assert bbwd(dq=MAP) == ALIAS
+    assert bbwd(stages=0) == ARG
+    # workspace: per item nb int32 indices, a count and a work-list entry (8 bytes), each
+    # part 256-aligned; forward: one item per query block
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    nb = 64  # T = 8192
+    items = 4 * 16 * nb
+    fw = a256(items * nb * 4) + a256(items * 4) + a256(items * 8)
+    assert lib.attn_fwd_blocksparse_workspace_bytes(4, 16, 8192, 128, 128) == fw
+    # backward (d = 128: the dQ kernel owns 256 rows, so its items are pairs of query blocks)
+    items_dq = 4 * 16 * nb // 2
+    dq_lists = a256(items_dq * nb * 4) + a256(items_dq * 4) + a256(items_dq * 8)
+    assert lib.attn_bwd_blocksparse_workspace_bytes(4, 16, 8192, 128, 128, 1) == \
+        lib.attn_bwd_workspace_bytes(4, 16, 8192, 128, 128, 1) + fw + dq_lists
+    assert lib.attn_fwd_blocksparse_workspace_bytes(0, 16, 8192, 128, 128) == 0
+
+
+def test_binding_blocksparse_map_checks():
+    import torch
+    q = torch.zeros(2, 300, 3, 64, dtype=torch.bfloat16)
+    for m, why in ((torch.zeros(2, 3, 3, 3, dtype=torch.int32), "dtype"),
+                   (torch.zeros(2, 3, 2, 3, dtype=torch.uint8), "shape"),
+                   (torch.zeros(3, 3, 3, 3, dtype=torch.uint8), "shape"),
+                   (torch.zeros(2, 3, 3, 6, dtype=torch.uint8)[..., ::2], "contiguous")):
+        with pytest.raises(ValueError):  # wrong map: its dtype, shape or layout
+            attn._block_map(m, 2, 3, 300, torch.device("cpu"))
+    b, h = attn._block_map(torch.zeros(1, 3, 3, 3, dtype=torch.uint8), 2, 3, 300, torch.device("cpu"))
+    assert (b, h) == (0, 9)

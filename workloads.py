@@ -75,7 +75,43 @@ WORKLOADS: Dict[str, Workload] = {
     # one decode step (inference forward, no stats): one query row per sequence against
     # an 8192-row key/value cache, non-causal
     "decode": Workload("decode", 16, 16, 8192, 128, 128, False, 53009),
+    # the headline shape under a block-sparse map (see block_map): causal, each query
+    # block sees the 8 most recent key blocks (1024 keys) and the first one
+    "blocksparse": Workload("blocksparse", 4, 16, 8192, 128, 128, True, 53010),
 }
+
+BS_BLOCK = 128
+
+
+def block_map(w: Workload):
+    """The block-sparse map of a workload, uint8 (1, 1, nb, nb), one map for every head:
+    query block r sees key blocks r - 7 .. r (a local band) and block 0 (a global block).
+    Combined with the causal mask inside the diagonal block."""
+    import numpy as np
+
+    nb = (w.T + BS_BLOCK - 1) // BS_BLOCK
+    r = np.arange(nb)[:, None]
+    c = np.arange(nb)[None, :]
+    return (((r - c >= 0) & (r - c < 8)) | (c == 0)).astype(np.uint8)[None, None]
+
+
+def block_map_pairs(w: Workload, m) -> int:
+    """Attended (query, key) pairs of a block-sparse workload, counted element by element
+    over one head's map times B * NH (maps are shared across heads here)."""
+    import numpy as np
+
+    T = w.T
+    nb = m.shape[-1]
+    total = 0
+    for qb in range(nb):
+        rows = np.arange(qb * BS_BLOCK, min(T, (qb + 1) * BS_BLOCK))
+        for kb in np.nonzero(m[0, 0, qb])[0]:
+            k0, k1 = kb * BS_BLOCK, min(T, (kb + 1) * BS_BLOCK)
+            if w.causal:
+                total += int(np.clip(rows + 1 - k0, 0, k1 - k0).sum())
+            else:
+                total += len(rows) * (k1 - k0)
+    return total * w.B * w.NH
 
 
 def _randn(shape, seed: int, sigma: float, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
