@@ -7,6 +7,7 @@ from .attn_ref import (  # noqa: F401
     alibi_slopes,
     attn_ref_bwd,
     attn_ref_blocksparse,
+    attn_ref_keybias,
     attn_ref_bwd_loop,
     attn_ref_fwd,
     attn_ref_varlen,

@@ -32,6 +32,10 @@ What is computed (the plain definition, S and P materialised, float64 throughout
             pages give no format; this map, ANDed with the causal mask, is the
             reading taken.  A row left with no allowed key gets P = 0, O = 0,
             LSE = -inf and zero gradients (the logsumexp of an empty set)
+            key bias (the `bias` option among the SDPA options of [SA8 1.2], whose
+            shape the page does not give; a per-key bias broadcast over the queries
+            is the reading taken): additionally S[i, j] += bias[j] (finite values;
+            a large negative value masks a key)
             O = P V                                  [SA8 2.1, A.1]
             LSE_i = m_i + ln(sum_j exp(S_ij - m_i)),  m_i = max_j S_ij
             (the pages' "softmax stats" [SA8 1.2, 1.3] are never defined; this
@@ -41,6 +45,8 @@ What is computed (the plain definition, S and P materialised, float64 throughout
             dS = P * (dP - (dP * P) 1)               [SA8 2.1 step 3, A.2]
             dQ = scale * dS K                        [SA8 2.1 step 4, A.2]
             dK = scale * dS^T Q                      [SA8 2.1 step 5, A.2]
+            dbias[j] = sum_i dS[i, j]  (S is linear in the bias with slope 1; summed
+            further over the heads and batches that share one bias row)
 
 Layout: every tensor argument is (B, T, NH, d) (token-major, heads inside), the layout
 of the pages' output O; LSE is (B, NH, T).  Inputs may be numpy arrays or torch
@@ -68,6 +74,7 @@ __all__ = [
     "attn_ref_heads",
     "attn_ref_varlen",
     "attn_ref_blocksparse",
+    "attn_ref_keybias",
     "attn_ref_bwd_loop",
     "alibi_slopes",
 ]
@@ -147,7 +154,7 @@ def _block_allowed(block_map: Optional[np.ndarray], block: int, r0: int, r1: int
 def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
                  block_rows: Optional[int] = None, window: int = 0,
                  slope: float = 0.0, block_map: Optional[np.ndarray] = None,
-                 block: int = 128) -> Tuple[np.ndarray, np.ndarray]:
+                 block: int = 128, key_bias: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """One head: q (T, d_qk), k (Tk, d_qk), v (Tk, d_v) float64 -> O (T, d_v), LSE (T,).
     Tk >= 1 may differ from T (padded batches); the causal mask stays top-left.
     block_map: (ceil(T / block), ceil(Tk / block)) block-sparse map or None."""
@@ -160,6 +167,8 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
         r1 = min(T, r0 + br)
         nk = min(r1, Tk) if causal else Tk  # keys past the last query are all masked
         S = _scores(q[r0:r1], k[:nk], scale, causal, r0, window, slope)
+        if key_bias is not None:
+            S = S + key_bias[None, :nk]
         allowed = _block_allowed(block_map, block, r0, r1, nk)
         if allowed is not None:
             S = np.where(allowed, S, -np.inf)
@@ -170,11 +179,14 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
 
 def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
                   causal: bool, block_rows: Optional[int] = None, window: int = 0, slope: float = 0.0,
-                  block_map: Optional[np.ndarray] = None, block: int = 128):
+                  block_map: Optional[np.ndarray] = None, block: int = 128,
+                  key_bias: Optional[np.ndarray] = None):
     """One head: returns dQ, dK, dV and also O, LSE and D = (dP * P) 1 (all float64).
     q, do have T rows, k, v have Tk >= 1 rows (Tk may differ from T).  The bias is a
     constant of the inputs: it changes P but adds no term to the gradients; neither does
-    the block map (a row with no allowed key has P = 0 and gets zero gradients)."""
+    the block map (a row with no allowed key has P = 0 and gets zero gradients).  With a
+    key bias (Tk,) the result also holds dbias (Tk,) = sum over queries of dS, as an
+    eighth entry."""
     _check_window(causal, window, slope)
     T, Tk = q.shape[0], k.shape[0]
     br = T if block_rows is None else block_rows
@@ -182,12 +194,15 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
     lse = np.empty(T)
     D = np.empty(T)
     dQ = np.empty_like(q)
+    dbias = np.zeros(Tk)
     dK = np.zeros_like(k)
     dV = np.zeros_like(v)
     for r0 in range(0, T, br):
         r1 = min(T, r0 + br)
         nk = min(r1, Tk) if causal else Tk
         S = _scores(q[r0:r1], k[:nk], scale, causal, r0, window, slope)
+        if key_bias is not None:
+            S = S + key_bias[None, :nk]
         allowed = _block_allowed(block_map, block, r0, r1, nk)
         if allowed is not None:
             S = np.where(allowed, S, -np.inf)
@@ -200,6 +215,10 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
         dQ[r0:r1] = scale * (dS @ k[:nk])               # dQ = dS K / sqrt(d_k)
         dK[:nk] += scale * (dS.T @ q[r0:r1])            # dK = dS^T Q / sqrt(d_k)
         D[r0:r1] = Dr
+        if key_bias is not None:
+            dbias[:nk] += dS.sum(axis=0)                # dbias_j = sum_i dS_ij
+    if key_bias is not None:
+        return dQ, dK, dV, O, lse, D, dbias
     return dQ, dK, dV, O, lse, D
 
 
@@ -318,6 +337,51 @@ def attn_ref_blocksparse(q, k, v, do, block_map, causal: bool, scale: Optional[f
     return out
 
 
+def attn_ref_keybias(q, k, v, do, bias, causal: bool, scale: Optional[float] = None,
+                     heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """Attention with a key bias over (B, T, NH, d) tensors: S = scale Q K^T + bias, the
+    bias indexed [b, h, j] with any of its two leading dimensions of size 1 (shared by
+    the batches / heads).  do may be None (forward only).  Returns the dict of
+    attn_ref_bwd plus "dbias" of the bias's own shape: sum over queries of dS, summed over
+    the batches and heads that share a bias row.  With `heads`, only those heads, as
+    {(b, h): {...}} with each head's own (T,) dbias contribution."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    do = None if do is None else to_f64(do)
+    bias = to_f64(bias)
+    B, T, NH, dqk = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    if bias.ndim != 3 or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, NH) or bias.shape[2] != T:
+        raise ValueError(f"bias must be (B or 1, NH or 1, {T}), got {bias.shape}")
+    br = _block_rows(T, dqk)
+
+    def one(b, h):
+        kb = bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0]
+        if do is None:
+            o, lse = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, br, key_bias=kb)
+            return {"o": o, "lse": lse}
+        r = head_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal, br, key_bias=kb)
+        return dict(zip(("dq", "dk", "dv", "o", "lse", "D", "dbias"), r))
+
+    if heads is not None:
+        return {(int(b), int(h)): one(int(b), int(h)) for b, h in heads}
+    out = {"o": np.empty((B, T, NH, v.shape[3])), "lse": np.empty((B, NH, T))}
+    if do is not None:
+        out.update(dq=np.empty((B, T, NH, dqk)), dk=np.empty((B, T, NH, dqk)), dv=np.empty((B, T, NH, v.shape[3])),
+                   D=np.empty((B, NH, T)), dbias=np.zeros(bias.shape))
+    for b in range(B):
+        for h in range(NH):
+            r = one(b, h)
+            for name, x in r.items():
+                if name in ("lse", "D"):
+                    out[name][b, h] = x
+                elif name == "dbias":
+                    out["dbias"][b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0] += x
+                else:
+                    out[name][b, :, h] = x
+    return out
+
+
 def attn_ref_varlen(q, k, v, do, seq_q, seq_k, causal: bool, scale: Optional[float] = None):
     """Padded batches: the padding mask with per-batch lengths seq_len_q and seq_len_kv
     among the SDPA options of [SA8 1.2].  Batch b uses query rows 0 .. seq_q[b]-1 and
@@ -356,7 +420,7 @@ def attn_ref_varlen(q, k, v, do, seq_q, seq_k, causal: bool, scale: Optional[flo
 
 
 def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, window: int = 0,
-                      alibi: bool = False, allowed=None):
+                      alibi: bool = False, allowed=None, key_bias=None):
     """Independent loop formulation for small T (T <= 64), written from the softmax
     Jacobian dy_i/dx_j = y_i (delta_ij - y_j) [SA8 2.1, A.3] and the per-(b, t, h)
     loop nest of the CPU reference in [SA8 2.2]:
@@ -376,6 +440,9 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
     allowed: None, or a predicate allowed(b, h, t, t2) -> bool; keys it refuses are
     left out of the row like keys outside the window (a row with no key left gets
     att = 0, o = 0, lse = -inf and no gradient).
+    key_bias: None, or a function key_bias(b, h, t2) added to preatt[t2]; the gradient
+    with respect to it is dpreatt / scale (preatt is scale * q.k plus the bias), summed
+    into dbias[b, h, t2], returned as a sixth value.
     Returns dq, dk, dv, o (B, T, NH, d) and lse (B, NH, T) in float64.
     """
     _check_window(causal, window, 1.0 if alibi else 0.0)
@@ -389,6 +456,7 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
     dv = np.zeros_like(v)
     o = np.zeros((B, T, NH, v.shape[3]))
     lse = np.zeros((B, NH, T))
+    dbias = np.zeros((B, NH, T))
     for b in range(B):
         for t in range(T):
             for h in range(NH):
@@ -397,6 +465,7 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
                 # forward row by loops: preatt, max, exp, sum, normalise (keys before
                 # `first` get -inf scores: exp gives exactly 0, so they add nothing)
                 pre = [scale * float(np.dot(q[b, t, h], k[b, t2, h])) - slopes[h] * (t - t2)
+                       + (key_bias(b, h, t2) if key_bias is not None else 0.0)
                        if t2 >= first and (allowed is None or allowed(b, h, t, t2)) else -math.inf
                        for t2 in range(last)]
                 mx = max(pre)
@@ -419,8 +488,11 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
                     for t3 in range(last):
                         ind = 1.0 if t2 == t3 else 0.0
                         dpre[t3] += scale * att[t2] * (ind - att[t3]) * datt[t2]
-                # backward through preatt = scale * q . k
+                # backward through preatt = scale * q . k (+ bias)
                 for t2 in range(last):
                     dq[b, t, h] += dpre[t2] * k[b, t2, h]
                     dk[b, t2, h] += dpre[t2] * q[b, t, h]
+                    dbias[b, h, t2] += dpre[t2] / scale
+    if key_bias is not None:
+        return dq, dk, dv, o, lse, dbias
     return dq, dk, dv, o, lse

@@ -614,6 +614,95 @@ def pin_blocksparse_finite_differences(ref, h: float = 1e-6):
         _close(r[name], g, rtol=1e-6, atol=1e-8, what=f"map finite differences {name}")
 
 
+# ---------------------------------------------------------------------------------
+# Key bias (the `bias` option of [SA8 1.2], read as a per-key bias broadcast over the
+# queries): S_ij += bias_j; dbias_j = sum_i dS_ij.
+# ---------------------------------------------------------------------------------
+def _bias(B, NH, T, seed, sd=1.0):
+    return np.random.default_rng(seed).standard_normal((B, NH, T)) * sd
+
+
+def pin_keybias_zero_is_plain(ref):
+    """A zero bias changes nothing, and dbias = sum over queries of dS sums to zero over
+    the keys of each head (every row of dS sums to zero)."""
+    q, k, v, do = _inputs(2, 29, 2, 16, 24, 901)
+    for causal in (False, True):
+        a = ref.attn_ref_bwd(q, k, v, do, causal)
+        b = ref.attn_ref_keybias(q, k, v, do, np.zeros((2, 2, 29)), causal)
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            _close(b[n], a[n], rtol=1e-15, atol=1e-15, what=f"zero bias causal={causal} {n}")
+        _close(b["dbias"].sum(axis=2), np.zeros((2, 2)), rtol=0, atol=1e-12, what="sum of dbias over keys")
+
+
+def pin_keybias_constant_shift(ref):
+    """A bias equal for every key shifts each row of S by one constant: P, O and the
+    gradients do not change, LSE moves by that constant (non-causal)."""
+    q, k, v, do = _inputs(1, 31, 2, 16, 16, 903)
+    a = ref.attn_ref_bwd(q, k, v, do, False)
+    b = ref.attn_ref_keybias(q, k, v, do, np.full((1, 2, 31), 2.5), False)
+    for n in ("o", "dq", "dk", "dv"):
+        _close(b[n], a[n], rtol=1e-12, atol=1e-14, what=f"constant bias {n}")
+    _close(b["lse"], a["lse"] + 2.5, rtol=1e-14, what="constant bias LSE")
+
+
+def pin_keybias_loops(ref):
+    """Matrix form against the scalar loop nest with the bias in preatt, dbias included,
+    causal and not, per head and shared."""
+    q, k, v, do = _inputs(2, 21, 3, 8, 16, 905)
+    for shape in ((2, 3, 21), (1, 1, 21)):
+        bias = _bias(*shape, 906, sd=2.0)
+        for causal in (False, True):
+            dq, dk, dv, o, lse, dbias = ref.attn_ref_bwd_loop(
+                q, k, v, do, causal, key_bias=lambda b, h, t2: bias[b % shape[0], h % shape[1], t2])
+            r = ref.attn_ref_keybias(q, k, v, do, bias, causal)
+            for n, x in (("dq", dq), ("dk", dk), ("dv", dv), ("o", o), ("lse", lse)):
+                _close(r[n], x, rtol=1e-12, atol=1e-14, what=f"bias {shape} causal={causal} loop form {n}")
+            want = dbias.sum(axis=(0, 1), keepdims=True) if shape[0] == 1 else dbias
+            _close(r["dbias"], want, rtol=1e-12, atol=1e-14, what=f"bias {shape} causal={causal} dbias")
+
+
+def pin_keybias_padding(ref):
+    """A key-padding bias (0 on the first L keys, -1e9 on the rest) equals attention over
+    the first L keys only; the padded keys get exactly zero dK, dV and dbias."""
+    q, k, v, do = _inputs(1, 24, 2, 16, 16, 907)
+    L = 17
+    bias = np.zeros((1, 1, 24))
+    bias[..., L:] = -1e9
+    r = ref.attn_ref_keybias(q, k, v, do, bias, False)
+    for h in range(2):
+        o, lse = ref.head_forward(q[0, :, h], k[0, :L, h], v[0, :L, h], 1 / 4, False)
+        _close(r["o"][0, :, h], o, rtol=1e-14, what="padding bias O")
+        _close(r["lse"][0, h], lse, rtol=1e-14, what="padding bias LSE")
+        g = ref.head_backward(q[0, :, h], k[0, :L, h], v[0, :L, h], do[0, :, h], 1 / 4, False)
+        _close(r["dq"][0, :, h], g[0], rtol=1e-13, atol=1e-15, what="padding bias dQ")
+        _close(r["dk"][0, :L, h], g[1], rtol=1e-13, atol=1e-15, what="padding bias dK")
+    assert np.all(r["dk"][0, L:] == 0) and np.all(r["dv"][0, L:] == 0) and np.all(r["dbias"][..., L:] == 0)
+
+
+def pin_keybias_finite_differences(ref, h: float = 1e-6):
+    """dbias (and dQ, dK, dV) equal central differences of sum(O * dO)."""
+    q, k, v, do = _inputs(1, 10, 2, 8, 8, 909)
+    bias = _bias(1, 2, 10, 910)
+    r = ref.attn_ref_keybias(q, k, v, do, bias, True)
+
+    def f(qq, kk, vv, bb):
+        return float(np.sum(ref.attn_ref_keybias(qq, kk, vv, None, bb, True)["o"] * do))
+
+    ins = (("dq", q), ("dk", k), ("dv", v), ("dbias", bias))
+    for name, x in ins:
+        g = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if n == name else y for n, y in ins]
+            args_m = [xm if n == name else y for n, y in ins]
+            g[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        _close(r[name], g, rtol=1e-6, atol=1e-8, what=f"bias finite differences {name}")
+
+
 ALL_PINS = [
     ("finite_differences_causal", lambda r: pin_finite_differences(r, True)),
     ("finite_differences_full", lambda r: pin_finite_differences(r, False)),
@@ -654,6 +743,11 @@ ALL_PINS = [
     ("blocksparse_random_map_loops", pin_blocksparse_random_map_loops),
     ("blocksparse_zero_queries", pin_blocksparse_zero_queries),
     ("finite_differences_blocksparse", pin_blocksparse_finite_differences),
+    ("keybias_zero_is_plain", pin_keybias_zero_is_plain),
+    ("keybias_constant_shift", pin_keybias_constant_shift),
+    ("keybias_loops", pin_keybias_loops),
+    ("keybias_padding", pin_keybias_padding),
+    ("finite_differences_keybias", pin_keybias_finite_differences),
     ("alibi_slopes", pin_alibi_slopes),
     ("alibi_zero_queries", pin_alibi_zero_queries),
     ("alibi_loops", pin_alibi_loops),

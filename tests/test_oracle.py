@@ -67,6 +67,14 @@ MUTANTS = {
     "window_off_by_one": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = np.where(qi - kj > window, -np.inf, S)"),
     "window_ignored": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = S"),
     "alibi_sign": ("S = S - slope * (qi - kj)", "S = S + slope * (qi - kj)"),
+    "keybias_sign": ("            S = S + key_bias[None, :nk]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n        dV",
+                     "            S = S - key_bias[None, :nk]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n        dV"),
+    "keybias_on_queries": ("            S = S + key_bias[None, :nk]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n        dV",
+                           "            S = S + key_bias[r0:r1, None]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n        dV"),
+    "dbias_from_dP": ("dbias[:nk] += dS.sum(axis=0)", "dbias[:nk] += dP.sum(axis=0)"),
+    "dbias_scaled": ("dbias[:nk] += dS.sum(axis=0)", "dbias[:nk] += scale * dS.sum(axis=0)"),
+    "dbias_shared_not_summed": ('out["dbias"][b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0] += x',
+                                'out["dbias"][b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0] = x'),
     "blocksparse_map_transposed": ("return np.asarray(block_map)[qi[:, None], kj[None, :]] != 0",
                                    "return np.asarray(block_map).T[qi[:, None], kj[None, :]] != 0"),
     "blocksparse_block_index_off": ("qi = np.arange(r0, r1) // block", "qi = np.arange(r0 + 1, r1 + 1) // block"),
