@@ -107,7 +107,10 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
     while done < len(all_heads) and t_total < seconds_budget * 0.5:
         hd = all_heads[done]
         t0 = time.perf_counter()
-        if w.name == "blocksparse":
+        if w.name == "keybias":
+            attn_ref.attn_ref_keybias(cpu["q"], cpu["k"], cpu["v"], cpu["do"], workloads.key_bias(w), w.causal,
+                                      w.scale, heads=[hd])
+        elif w.name == "blocksparse":
             attn_ref.attn_ref_blocksparse(cpu["q"], cpu["k"], cpu["v"], cpu["do"], workloads.block_map(w), w.causal,
                                           w.scale, heads=[hd])
         else:
@@ -361,27 +364,43 @@ def main():
 
     def workspace(mode_det):
         if mode_det not in workspaces:
-            nbytes = (attn.load().attn_bwd_blocksparse_workspace_bytes(B, NH, T, w.d_qk, w.d_v, int(mode_det))
-                      if w.name == "blocksparse" else attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, mode_det))
+            lib = attn.load()
+            if w.name == "blocksparse":
+                nbytes = lib.attn_bwd_blocksparse_workspace_bytes(B, NH, T, w.d_qk, w.d_v, int(mode_det))
+            elif w.name == "keybias":
+                nbytes = lib.attn_bwd_keybias_workspace_bytes(B, NH, T, w.d_qk, w.d_v, int(mode_det))
+            else:
+                nbytes = attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, mode_det)
             workspaces[mode_det] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         return workspaces[mode_det]
 
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
 
     bsp = w.name == "blocksparse"
+    kbw = w.name == "keybias"
+    if kbw:
+        kbias = torch.from_numpy(workloads.key_bias(w)).to(dev)
+        dbias = torch.empty_like(kbias)
+        fws = torch.empty(attn.load().attn_fwd_keybias_workspace_bytes(B, NH, T, w.d_qk, w.d_v), dtype=torch.uint8,
+                          device=dev)
     if bsp:
         bmap = torch.from_numpy(workloads.block_map(w)).to(dev)
         fws = torch.empty(attn.load().attn_fwd_blocksparse_workspace_bytes(B, NH, T, w.d_qk, w.d_v), dtype=torch.uint8,
                           device=dev)
 
     def fwd_call():
-        if bsp:
+        if kbw:
+            attn.fwd_keybias(q, k, v, kbias, w.causal, w.scale, out=o, lse=lse, workspace=fws)
+        elif bsp:
             attn.fwd_blocksparse(q, k, v, bmap, w.causal, w.scale, out=o, lse=lse, workspace=fws)
         else:
             attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse, window=w.window, alibi=w.alibi)
 
     def bwd_call(mode_det, ws, stages):
-        if bsp:
+        if kbw:
+            attn.bwd_keybias(q, k, v, o, lse, do, kbias, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv,
+                             dbias=dbias, workspace=ws, stages=stages)
+        elif bsp:
             attn.bwd_blocksparse(q, k, v, o, lse, do, bmap, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv,
                                  workspace=ws, stages=stages)
         else:
@@ -465,7 +484,8 @@ def main():
             "workload": f"{w.name}: B={B} NH={NH} T={T} d_qk={w.d_qk} d_v={w.d_v} "
                         f"{'causal' if w.causal else 'non-causal'}"
                         f"{f' window {w.window}' if w.window else ''}{' ALiBi' if w.alibi else ''}"
-                        f"{' block-sparse map (local band of 8 blocks + block 0)' if w.name == 'blocksparse' else ''}, "
+                        f"{' block-sparse map (local band of 8 blocks + block 0)' if w.name == 'blocksparse' else ''}"
+                        f"{' per-head key bias with dbias' if w.name == 'keybias' else ''}, "
                         f"{'packed QKV' if w.packed else 'BTHD'}, "
                         f"dQ mode {args.dq_mode}",
             "B": B, "NH": NH, "T": T, "d_qk": w.d_qk, "d_v": w.d_v, "causal": w.causal, "window": w.window, "alibi": w.alibi,

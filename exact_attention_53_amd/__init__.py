@@ -27,7 +27,8 @@ import torch
 
 __all__ = [
     "AttnError", "lib_path", "load", "fwd", "fwd_packed", "bwd", "bwd_packed",
-    "workspace_bytes", "fwd_varlen", "bwd_varlen", "fwd_decode", "bwd_noalloc", "fwd_blocksparse", "bwd_blocksparse", "BS_BLOCK", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
+    "workspace_bytes", "fwd_varlen", "bwd_varlen", "fwd_decode", "bwd_noalloc", "fwd_blocksparse", "bwd_blocksparse", "BS_BLOCK",
+    "fwd_keybias", "bwd_keybias", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +98,14 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_blocksparse.argtypes = [vp, S, vp, S, vp, S, vp, S, vp, vp, i64, i64, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_bwd_blocksparse.restype = i
     lib.attn_bwd_blocksparse.argtypes = bwd_args[:17] + [vp, i64, i64] + bwd_args[17:] + [ctypes.c_uint]
+    lib.attn_fwd_keybias_workspace_bytes.restype = sz
+    lib.attn_fwd_keybias_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_bwd_keybias_workspace_bytes.restype = sz
+    lib.attn_bwd_keybias_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_fwd_keybias.restype = i
+    lib.attn_fwd_keybias.argtypes = [vp, S, vp, S, vp, S, vp, S, vp, vp, i64, i64, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_bwd_keybias.restype = i
+    lib.attn_bwd_keybias.argtypes = bwd_args[:17] + [vp, vp, i64, i64] + bwd_args[17:] + [ctypes.c_uint]
     lib.attn_bwd_noalloc.restype = i
     lib.attn_bwd_noalloc.argtypes = bwd_args[:25] + [vp]
     lib.attn_bwd_noalloc_max_workspace_bytes.restype = sz
@@ -369,6 +378,112 @@ def bwd_blocksparse(q, k, v, o, lse, do, block_map: torch.Tensor, causal: bool =
                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                         _stream(dev), int(stages)))
     return dq, dk, dv
+
+
+def _key_bias(bias: torch.Tensor, B: int, NH: int, T: int, dev: torch.device):
+    """Checks a (B or 1, NH or 1, T) float32 key bias and returns its (b, h) element strides
+    (0 where it is shared)."""
+    if bias.dtype != torch.float32 or bias.dim() != 3:
+        raise ValueError("bias must be a 3-D float32 tensor (B or 1, NH or 1, T)")
+    Bb, Hb, Tb = bias.shape
+    if Bb not in (1, B) or Hb not in (1, NH) or Tb != T:
+        raise ValueError(f"bias has shape {tuple(bias.shape)}, expected (B or 1, NH or 1, {T})")
+    if bias.stride(2) != 1:
+        raise ValueError("bias must be contiguous along the keys")
+    if bias.device != dev:
+        raise ValueError(f"bias is on {bias.device}, expected {dev}")
+    return (bias.stride(0) if Bb > 1 else 0), (bias.stride(1) if Hb > 1 else 0)
+
+
+def fwd_keybias(q, k, v, bias: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+                return_lse: bool = True, layout: str = "bthd", out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Forward with a key bias (bf16): S = scale Q K^T + bias[b, h, key], bias float32
+    (B or 1, NH or 1, T) on the device, finite values (mask a key with a large negative
+    value).  Returns (o, lse)."""
+    B, NH, T, dqk = _dims(q, layout)
+    dv = v.shape[-1]
+    _shape(k, "k", layout, B, NH, T, dqk)
+    _shape(v, "v", layout, B, NH, T, dv)
+    if out is not None:
+        _shape(out, "out", layout, B, NH, T, dv)
+    dev = q.device
+    _on_gpu("fwd_keybias", dev)
+    lib = load()
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, n, dev, torch.bfloat16)
+    sb, sh = _key_bias(bias, B, NH, T, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        shape = (B, T, NH, dv) if layout == "bthd" else (B, NH, T, dv)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", dev, torch.bfloat16)
+    if return_lse and lse is None:
+        lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    need = int(lib.attn_fwd_keybias_workspace_bytes(B, NH, T, dqk, dv))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_fwd_keybias(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                                    v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
+                                    lse.data_ptr() if return_lse else None, bias.data_ptr(), sb, sh,
+                                    B, NH, T, dqk, dv, float(scale), int(bool(causal)), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, (lse if return_lse else None)
+
+
+def bwd_keybias(q, k, v, o, lse, do, bias: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+                deterministic: bool = False, layout: str = "bthd", dq=None, dk=None, dv=None,
+                dbias: Optional[torch.Tensor] = None, need_dbias: bool = True,
+                workspace: Optional[torch.Tensor] = None, stages: int = ALL_STAGES):
+    """Backward with the forward's key bias (bf16).  Returns (dq, dk, dv, dbias); dbias has
+    the bias's shape (summed over the batches / heads that share a row), None when
+    need_dbias is False."""
+    B, NH, T, dqk = _dims(q, layout)
+    dvd = v.shape[-1]
+    for n, x, d in (("k", k, dqk), ("v", v, dvd), ("o", o, dvd), ("do", do, dvd), ("dq", dq, dqk), ("dk", dk, dqk),
+                    ("dv", dv, dvd)):
+        if x is not None:
+            _shape(x, n, layout, B, NH, T, d)
+    dev = q.device
+    _on_gpu("bwd_keybias", dev)
+    lib = load()
+    for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _need(x, n, dev, torch.bfloat16)
+    sb, sh = _key_bias(bias, B, NH, T, dev)
+    if need_dbias:
+        if dbias is None:
+            dbias = torch.empty_strided(bias.shape, bias.stride(), dtype=torch.float32, device=dev)
+        if dbias.shape != bias.shape or dbias.stride() != bias.stride() or dbias.dtype != torch.float32:
+            raise ValueError("dbias must be float32 with the bias's shape and strides")
+    else:
+        dbias = None
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(x, n, dev, torch.bfloat16)
+    need = int(lib.attn_bwd_keybias_workspace_bytes(B, NH, T, dqk, dvd, int(bool(deterministic))))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_bwd_keybias(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                                    v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
+                                    lse.data_ptr(), do.data_ptr(), _strides(do, layout),
+                                    dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
+                                    dv.data_ptr(), _strides(dv, layout), bias.data_ptr(),
+                                    dbias.data_ptr() if dbias is not None else None, sb, sh,
+                                    B, NH, T, dqk, dvd, float(scale), int(bool(causal)), int(bool(deterministic)),
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream(dev), int(stages)))
+    return dq, dk, dv, dbias
 
 
 def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, causal: bool = True, scale: Optional[float] = None,

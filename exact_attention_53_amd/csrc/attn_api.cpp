@@ -133,6 +133,36 @@ attn_status bs_build(const BsArgs& bs, int B, int NH, int T, int kind, int group
   return ATTN_OK;
 }
 
+// Key bias of a call (bias == nullptr: none): fp32, (B or 1, NH or 1, T) through element
+// strides along b and h (0 broadcasts), contiguous along t; dbias (or nullptr) has the
+// same strides.
+struct KbArgs {
+  const float* bias;
+  int64_t sb, sh;
+  float* dbias;
+};
+
+// Byte extent of a (B, NH, T) fp32 tensor with element strides sb, sh, 1.
+Extent f32_extent(const void* ptr, int64_t sb, int64_t sh, int B, int NH, int T) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+  return Extent{lo, lo + (uintptr_t)(sb * (B - 1) + sh * (NH - 1) + T) * 4u};
+}
+
+attn_status check_kbias(const KbArgs& kb, int B, int NH, int T) {
+  if (kb.bias == nullptr) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(kb.bias) % 4 != 0) return ATTN_ERR_ALIGN;
+  if (kb.dbias != nullptr && reinterpret_cast<uintptr_t>(kb.dbias) % 4 != 0) return ATTN_ERR_ALIGN;
+  if (kb.sb < 0 || kb.sh < 0) return ATTN_ERR_STRIDE;
+  if (kb.dbias != nullptr) {  // distinct dbias rows must not share elements
+    const int Bb = (B > 1 && kb.sb == 0) ? 1 : B, Hb = (NH > 1 && kb.sh == 0) ? 1 : NH;
+    // rows (b, h) of T elements: the (b, h) strides as the outer dimensions of T-wide rows
+    if (check_output_rows(attn_strides{0, kb.sb, kb.sh}, 1, Bb, Hb, T) != ATTN_OK) return ATTN_ERR_STRIDE;
+  }
+  return ATTN_OK;
+}
+
+size_t kb_ws_bytes(int B, int NH, int T) { return align256((size_t)B * NH * tpad(T) * 4); }
+
 // Validates a block-sparse map and returns its byte extent.
 attn_status check_map(const BsArgs& bs, int B, int NH, int T, Extent* ext) {
   if (bs.map == nullptr) return ATTN_ERR_NULL;
@@ -149,13 +179,15 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
                      const void* v, attn_strides sv, void* o, attn_strides so, float* lse, const int32_t* seq_q,
                      const int32_t* seq_k, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
                      int window, int alibi, void* workspace, size_t workspace_bytes, void* stream,
-                     const BsArgs* bs = nullptr) {
+                     const BsArgs* bs = nullptr, const KbArgs* kb = nullptr) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
   if (!window_ok(window, alibi, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
-  if (bs != nullptr && (window != 0 || alibi != 0 || seq_q != nullptr || seq_k != nullptr || et != attn53::ELEM_BF16))
+  if ((bs != nullptr || kb != nullptr) &&
+      (window != 0 || alibi != 0 || seq_q != nullptr || seq_k != nullptr || et != attn53::ELEM_BF16))
     return ATTN_ERR_ARG;
+  if (kb != nullptr && (st = check_kbias(*kb, B, NH, T)) != ATTN_OK) return st;
   Extent eq, ek, ev, eo;
   if ((st = check_tensor(q, sq, B, NH, T, d_qk, &eq)) != ATTN_OK) return st;
   if ((st = check_tensor(k, sk, B, NH, T, d_qk, &ek)) != ATTN_OK) return st;
@@ -175,15 +207,21 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
     if ((st = check_map(*bs, B, NH, T, &em)) != ATTN_OK) return st;
     if (overlaps(eo, em) || (lse != nullptr && overlaps(el, em))) return ATTN_ERR_ALIAS;
   }
-  if (varlen || bs != nullptr) {
+  if (kb != nullptr) {
+    const Extent eb = f32_extent(kb->bias, kb->sb, kb->sh, B, NH, T);
+    if (overlaps(eo, eb) || (lse != nullptr && overlaps(el, eb))) return ATTN_ERR_ALIAS;
+    em = eb;  // the workspace must not overlap it either
+  }
+  if (varlen || bs != nullptr || kb != nullptr) {
     if (varlen && (seq_q == nullptr || seq_k == nullptr)) return ATTN_ERR_NULL;
     if (varlen && (!int_ptr_ok(seq_q) || !int_ptr_ok(seq_k))) return ATTN_ERR_ALIGN;
-    const size_t need = varlen ? ws_list_bytes(B, T, kFwdBlock) : fwd_bs_ws_bytes(B, NH, T);
+    const size_t need = varlen ? ws_list_bytes(B, T, kFwdBlock) : kb != nullptr ? kb_ws_bytes(B, NH, T)
+                                                                                : fwd_bs_ws_bytes(B, NH, T);
     if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || workspace_bytes < need)
       return ATTN_ERR_WORKSPACE;
     const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
     if (overlaps(ew, eq) || overlaps(ew, ek) || overlaps(ew, ev) || overlaps(ew, eo) ||
-        (lse != nullptr && overlaps(ew, el)) || (bs != nullptr && overlaps(ew, em)))
+        (lse != nullptr && overlaps(ew, el)) || ((bs != nullptr || kb != nullptr) && overlaps(ew, em)))
       return ATTN_ERR_ALIAS;
   }
   FwdParams p{};
@@ -209,10 +247,19 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
     if ((st = bs_build(*bs, B, NH, T, 0, 1, causal, static_cast<char*>(workspace), &p.bs, &used, s)) != ATTN_OK)
       return st;
   }
+  if (kb != nullptr) {
+    float* kbs = static_cast<float*>(workspace);
+    if ((st = hip_status(attn53::launch_bias_prep(kb->bias, kb->sb, kb->sh, 1.f / scale, kbs, (int)tpad(T), B, NH, T,
+                                                  s))) != ATTN_OK)
+      return st;
+    p.kbias = kbs;
+    p.kbias_ld = (int)tpad(T);
+  }
   return hip_status(attn53::launch_fwd(p, et, d_qk, d_v, causal != 0, s));
 }
 
-size_t bwd_ws_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic, bool varlen, bool bsp = false) {
+size_t bwd_ws_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic, bool varlen, bool bsp = false,
+                    bool kbias = false) {
   if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK || (deterministic != 0 && deterministic != 1)) return 0;
   size_t n = 2 * ws_D_bytes(B, NH, T);  // D and LSE log2(e)
   if (!deterministic) n += ws_acc_bytes(B, NH, T, d_qk);
@@ -221,6 +268,7 @@ size_t bwd_ws_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic, 
     const int nb = bs_nb(T), group = attn53::dq_block_rows(d_qk) / attn53::kBsBlock;
     n += bs_lists_bytes((int64_t)B * NH * nb, nb) + bs_lists_bytes((int64_t)B * NH * ((nb + group - 1) / group), nb);
   }
+  if (kbias) n += 2 * kb_ws_bytes(B, NH, T);  // the bias in score units; the per-head dbias sums
   return n;
 }
 
@@ -230,15 +278,17 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
                      void* dv, attn_strides sdv, const int32_t* seq_q, const int32_t* seq_k, int B, int NH, int T,
                      int d_qk, int d_v, float scale, int causal, int window, int alibi, int deterministic,
                      void* workspace, size_t workspace_bytes, void* stream, unsigned stages,
-                     const BsArgs* bs = nullptr) {
+                     const BsArgs* bs = nullptr, const KbArgs* kb = nullptr) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1) ||
       (deterministic != 0 && deterministic != 1))
     return ATTN_ERR_ARG;
   if (!window_ok(window, alibi, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
-  if (bs != nullptr && (window != 0 || alibi != 0 || seq_q != nullptr || seq_k != nullptr || et != attn53::ELEM_BF16))
+  if ((bs != nullptr || kb != nullptr) &&
+      (window != 0 || alibi != 0 || seq_q != nullptr || seq_k != nullptr || et != attn53::ELEM_BF16))
     return ATTN_ERR_ARG;
+  if (kb != nullptr && (st = check_kbias(*kb, B, NH, T)) != ATTN_OK) return st;
   if (stages == 0 || (stages & ~ATTN_BWD_ALL) != 0) return ATTN_ERR_ARG;
   const bool varlen = seq_q != nullptr || seq_k != nullptr;
   if (varlen) {
@@ -262,7 +312,8 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   const Extent el{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + (uintptr_t)B * NH * T * 4u};
   Extent em{0, 0};
   if (bs != nullptr && (st = check_map(*bs, B, NH, T, &em)) != ATTN_OK) return st;
-  const size_t need = bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, varlen, bs != nullptr);
+  if (kb != nullptr) em = f32_extent(kb->bias, kb->sb, kb->sh, B, NH, T);
+  const size_t need = bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, varlen, bs != nullptr, kb != nullptr);
   if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || workspace_bytes < need)
     return ATTN_ERR_WORKSPACE;
   const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
@@ -272,6 +323,12 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
     for (const Extent& b : ins)
       if (overlaps(a, b)) return ATTN_ERR_ALIAS;
   if (overlaps(ew, edq) || overlaps(ew, edk) || overlaps(ew, edv)) return ATTN_ERR_ALIAS;
+  if (kb != nullptr && kb->dbias != nullptr) {
+    const Extent edb = f32_extent(kb->dbias, kb->sb, kb->sh, B, NH, T);
+    for (const Extent& a : ins)
+      if (overlaps(edb, a)) return ATTN_ERR_ALIAS;
+    if (overlaps(edb, ew) || overlaps(edb, edq) || overlaps(edb, edk) || overlaps(edb, edv)) return ATTN_ERR_ALIAS;
+  }
 
   BwdParams p{};
   p.q = q; p.sq = cvt(sq);
@@ -326,6 +383,15 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
     }
     p.bsp = 1;
   }
+  if (kb != nullptr) {  // the bias in score units (read by both kernels), the per-head dbias sums
+    float* kbs = reinterpret_cast<float*>(ws + off);
+    p.kbias = kbs;
+    p.dbias_part = kb->dbias != nullptr ? reinterpret_cast<float*>(ws + off + kb_ws_bytes(B, NH, T)) : nullptr;
+    if (stages & (ATTN_BWD_MAIN | ATTN_BWD_DQ)) {
+      st = hip_status(attn53::launch_bias_prep(kb->bias, kb->sb, kb->sh, 1.f / scale, kbs, p.Tpad, B, NH, T, s));
+      if (st != ATTN_OK) return st;
+    }
+  }
   if (stages & ATTN_BWD_PREPROCESS) {
     st = hip_status(attn53::launch_bwd_preprocess(p, et, d_qk, d_v, !deterministic, s));
     if (st != ATTN_OK) return st;
@@ -333,6 +399,10 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   if (stages & ATTN_BWD_MAIN) {
     st = hip_status(attn53::launch_bwd_main(p, et, d_qk, d_v, causal != 0, deterministic != 0, s));
     if (st != ATTN_OK) return st;
+    if (p.dbias_part != nullptr) {
+      st = hip_status(attn53::launch_dbias_reduce(p.dbias_part, p.Tpad, kb->dbias, kb->sb, kb->sh, B, NH, T, s));
+      if (st != ATTN_OK) return st;
+    }
   }
   if (stages & ATTN_BWD_DQ) {
     st = hip_status(deterministic ? attn53::launch_bwd_dq(p, et, d_qk, d_v, causal != 0, s)
@@ -432,6 +502,37 @@ attn_status attn_fwd_blocksparse(const void* q, attn_strides sq, const void* k, 
   const BsArgs bs{block_map, map_stride_b, map_stride_h};
   return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale,
                   causal, 0, 0, workspace, workspace_bytes, stream, &bs);
+}
+
+size_t attn_fwd_keybias_workspace_bytes(int B, int NH, int T, int d_qk, int d_v) {
+  if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK) return 0;
+  return kb_ws_bytes(B, NH, T);
+}
+
+attn_status attn_fwd_keybias(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                             attn_strides sv, void* o, attn_strides so, float* lse, const float* bias,
+                             int64_t bias_stride_b, int64_t bias_stride_h, int B, int NH, int T, int d_qk, int d_v,
+                             float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  const KbArgs kb{bias, bias_stride_b, bias_stride_h, nullptr};
+  return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale,
+                  causal, 0, 0, workspace, workspace_bytes, stream, nullptr, &kb);
+}
+
+size_t attn_bwd_keybias_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic) {
+  return bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, false, false, true);
+}
+
+attn_status attn_bwd_keybias(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                             attn_strides sv, const void* o, attn_strides so, const float* lse, const void* do_,
+                             attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk, void* dv,
+                             attn_strides sdv, const float* bias, float* dbias, int64_t bias_stride_b,
+                             int64_t bias_stride_h, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
+                             int deterministic, void* workspace, size_t workspace_bytes, void* stream,
+                             unsigned stages) {
+  const KbArgs kb{bias, bias_stride_b, bias_stride_h, dbias};
+  return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr,
+                  nullptr, B, NH, T, d_qk, d_v, scale, causal, 0, 0, deterministic, workspace, workspace_bytes,
+                  stream, stages, nullptr, &kb);
 }
 
 size_t attn_bwd_blocksparse_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic) {

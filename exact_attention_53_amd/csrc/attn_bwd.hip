@@ -29,9 +29,11 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int 
 }
 
 // mask mode of the launchers: 0 none, 1 causal, 2 causal with a sliding window, 3 causal
-// with the ALiBi bias, 4 block-sparse map, 5 block-sparse map and causal
+// with the ALiBi bias, 4 block-sparse map, 5 block-sparse map and causal, 6 key bias,
+// 7 key bias and causal
 static inline int mask_mode(const BwdParams& p, bool causal) {
   if (p.bsp) return causal ? 5 : 4;
+  if (p.kbias != nullptr) return causal ? 7 : 6;
   return !causal ? 0 : p.win < kNoWindow ? 2 : p.alibi ? 3 : 1;
 }
 
@@ -43,10 +45,16 @@ static hipError_t main_m(const BwdParams& p, bool causal, bool det, hipStream_t 
     case 2: return bwd_main_t<E, DQK, DV, 2>(p, det, s);
     case 3: return bwd_main_t<E, DQK, DV, 3>(p, det, s);
     default:
-      if constexpr (std::is_same<E, bf16>::value)  // block-sparse maps: bf16 only
-        return mask_mode(p, causal) == 5 ? bwd_main_t<E, DQK, DV, 5>(p, det, s) : bwd_main_t<E, DQK, DV, 4>(p, det, s);
-      else
+      if constexpr (std::is_same<E, bf16>::value) {  // block-sparse maps and the key bias: bf16 only
+        switch (mask_mode(p, causal)) {
+          case 4: return bwd_main_t<E, DQK, DV, 4>(p, det, s);
+          case 5: return bwd_main_t<E, DQK, DV, 5>(p, det, s);
+          case 6: return bwd_main_t<E, DQK, DV, 6>(p, det, s);
+          default: return bwd_main_t<E, DQK, DV, 7>(p, det, s);
+        }
+      } else {
         return hipErrorInvalidValue;
+      }
   }
 }
 
@@ -72,10 +80,16 @@ static hipError_t dq_m(const BwdParams& p, bool causal, hipStream_t s) {
     case 2: return bwd_dq_t<E, DQK, DV, 2>(p, s);
     case 3: return bwd_dq_t<E, DQK, DV, 3>(p, s);
     default:
-      if constexpr (std::is_same<E, bf16>::value)
-        return mask_mode(p, causal) == 5 ? bwd_dq_t<E, DQK, DV, 5>(p, s) : bwd_dq_t<E, DQK, DV, 4>(p, s);
-      else
+      if constexpr (std::is_same<E, bf16>::value) {
+        switch (mask_mode(p, causal)) {
+          case 4: return bwd_dq_t<E, DQK, DV, 4>(p, s);
+          case 5: return bwd_dq_t<E, DQK, DV, 5>(p, s);
+          case 6: return bwd_dq_t<E, DQK, DV, 6>(p, s);
+          default: return bwd_dq_t<E, DQK, DV, 7>(p, s);
+        }
+      } else {
         return hipErrorInvalidValue;
+      }
   }
 }
 

@@ -176,7 +176,10 @@ struct KvPlan {
 // WIN (with CAUSAL only): sliding window of p.win keys.  ALIBI (with CAUSAL only): the
 // linear bias -m_h (i - j) on the scaled scores.  BSP: block-sparse map (p.bs_kv): the
 // workgroup visits only the query steps of its key block's live query blocks, ascending.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool ATOMIC_DQ, bool BSP = false>
+// KBIAS: a per-key bias (p.kbias) on the scores; each lane's key is fixed, so the bias is
+// one register, and the lane sums dS over the queries for dbias (p.dbias_part).
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool ATOMIC_DQ, bool BSP = false,
+          bool KBIAS = false>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 64 ? 2 : 1, DQK == 64 ? 2 : 1))) void bwd_kv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
@@ -232,6 +235,9 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
   const int my_key = key0 + kw + lq;
   const float c = p.scale_log2;
   const float ml = ALIBI ? alibi_slope_log2(h, p.NH) : 0.f;  // ALiBi slope, log2 units
+  // key bias of this lane's key in log2 units, and this lane's partial sums of dS
+  const float kb2 = KBIAS ? p.kbias[(int64_t)bh * p.Tpad + min(my_key, p.Tpad - 1)] * c : 0.f;
+  float dbacc[2] = {0.f, 0.f};
   E* dkg = (E*)p.dk + b * p.sdk.b + h * p.sdk.h;
   E* dvg = (E*)p.dv + b * p.sdv.b + h * p.sdv.h;
 
@@ -388,7 +394,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * a + e;
             const int q = q0 + qi + e;
-            const float bias = ALIBI ? __builtin_fmaf(-ml, (float)(32 * t + 8 * a + e), ab) : 0.f;
+            const float bias = (ALIBI ? __builtin_fmaf(-ml, (float)(32 * t + 8 * a + e), ab) : 0.f) + kb2;
             const float pv = exp2_fast(__builtin_fmaf(s[t][r], c, bias - Lv[e]));
             s[t][r] = (my_key >= Lk || q >= Lq || (CAUSAL && (my_key > q || (WIN && q - my_key >= W)))) ? 0.f : pv;
           }
@@ -407,7 +413,10 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
         for (int a = 0; a < 4; ++a) {
           const f32x4 Dd = *reinterpret_cast<const f32x4*>(db + 32 * t + 8 * a + 4 * g);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dp[t][4 * a + e] = s[t][4 * a + e] * (dp[t][4 * a + e] - Dd[e]);
+          for (int e = 0; e < 4; ++e) {
+            dp[t][4 * a + e] = s[t][4 * a + e] * (dp[t][4 * a + e] - Dd[e]);
+            if constexpr (KBIAS) dbacc[t] += dp[t][4 * a + e];
+          }
         }
 #pragma unroll
       for (int m = 0; m < 4; ++m) sb[m] = pack8<E>(dp[m >> 1], m & 1);
@@ -449,6 +458,8 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
             if constexpr (ALIBI) {
               const float bias = __builtin_fmaf(-ml, (float)(32 * t + 8 * (r >> 2) + (r & 3)), ab);
               pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, bias - lsev[t][r >> 2][r & 3]));
+            } else if constexpr (KBIAS) {
+              pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, kb2 - lsev[t][r >> 2][r & 3]));
             } else {
               pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, -lsev[t][r >> 2][r & 3]));
             }
@@ -456,8 +467,10 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
         } else {
           if constexpr (Plan::is_pack(o))
             sb[2 * t + h] = pack8<E>(dsv[t], h);
-          else
+          else {
             dsv[t][r] = pv[t][r] * (dp[t][r] - ddv[t][r >> 2][r & 3]);
+            if constexpr (KBIAS) dbacc[t] += dsv[t][r];
+          }
         }
       };
       static_for<0, LA>([&](auto jc) { fr[decltype(jc)::value % RING] = read_frag(jc); });
@@ -562,6 +575,10 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
     dq_partial((const ATTN_LDS char*)((ST_DOUBLE && last_odd) ? st1 : st0), qstep(n_q - 1) * BWD_BM);
   }
 
+  if constexpr (KBIAS) {  // dbias_j = sum over queries of dS_ij: this lane's two halves
+    const float tot = sum_halves(dbacc[0] + dbacc[1]);
+    if (p.dbias_part != nullptr && g == 0 && my_key < T) p.dbias_part[(int64_t)bh * p.Tpad + my_key] = tot;
+  }
   // dK = scale dS^T Q, dV; element r of tile t: key key0 + kw + 8 (r / 4) + 4 g + r % 4,
   // column 32 t + lq.
 #pragma unroll
@@ -666,8 +683,10 @@ struct DqShape {
 // WIN (with CAUSAL only): sliding window of p.win keys.  ALIBI (with CAUSAL only): the
 // linear bias -m_h (i - j) on the scaled scores.  BSP: block-sparse map (p.bs_dq): the
 // workgroup visits the key tiles of the live key blocks of any of its query-block rows,
-// descending; a wavefront computes only on the tiles live for its own rows.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool BSP = false>
+// descending; a wavefront computes only on the tiles live for its own rows.  KBIAS: a
+// per-key bias (p.kbias) on the scores, 64 values per key tile in LDS; every tile then
+// runs the plain (compiler-scheduled) tile body.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool BSP = false, bool KBIAS = false>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
                                                                          DqShape<DQK>::WAVES_PER_EU)))
 void bwd_dq_kernel(BwdParams p) {
@@ -677,6 +696,7 @@ void bwd_dq_kernel(BwdParams p) {
   constexpr int VT_BYTES = DQ_BN * DV * 2;
   __shared__ __attribute__((aligned(1024))) char kbuf0[KT_BYTES], kbuf1[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[VT_BYTES], vbuf1[VT_BYTES];
+  __shared__ __attribute__((aligned(256))) float kbl0[KBIAS ? DQ_BN : 1], kbl1[KBIAS ? DQ_BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int w = tid >> 6;
@@ -772,6 +792,10 @@ void bwd_dq_kernel(BwdParams p) {
     constexpr int BUF = decltype(bufc)::value;
     kload.issue(kg + key0 * skt, skt, Lk - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), wu);
     vload.issue(vg + key0 * svt, svt, Lk - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), wu);
+    if constexpr (KBIAS) {
+      if (wu == 0) load_f32x64_lds(p.kbias + (int64_t)bh * p.Tpad + key0, Lk - key0,
+                                   (ATTN_LDS float*)(BUF ? kbl1 : kbl0), lane);
+    }
   };
 
   f32x16 dq[QT][NDQ];
@@ -803,6 +827,14 @@ void bwd_dq_kernel(BwdParams p) {
         for (int u = 0; u < QT; ++u) dp[t][u] = mfma32(a, df[u][ks], ks == 0 ? zero16() : dp[t][u]);
       }
     // P^T = 2^(S^T c - LSE log2 e)
+    f32x4 kbv[2][4];  // key bias of element r of half t: kbv[t][r / 4][r % 4] (score units)
+    if constexpr (KBIAS) {
+      const float* kb = BUF ? kbl1 : kbl0;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) kbv[t][a] = *reinterpret_cast<const f32x4*>(kb + 32 * t + 8 * a + 4 * g);
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -810,6 +842,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float bias = 0.f;
+          if constexpr (KBIAS) bias = kbv[t][r >> 2][r & 3] * c;
           if constexpr (ALIBI)  // m_h log2(e) (key - query), key key0 + 32 t + 8 (r / 4) + 4 g + r % 4
             bias = ml * (float)(key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3) - (qw + 32 * u + lq));
           float pv = exp2_fast(__builtin_fmaf(s[t][u][r], c, bias - lse2[u]));
@@ -840,7 +873,7 @@ void bwd_dq_kernel(BwdParams p) {
           for (int u = 0; u < QT; ++u) dq[u][n] = mfma32(a, sb[u][hh], dq[u][n]);
         }
     }
-    if constexpr (!MASKED) {
+    if constexpr (!MASKED && !KBIAS) {
       // MFMA software pipeline: operand reads run ahead; the P computation fills the
       // dP products, the second half's dS the first half's dQ products.
       ATTN_SCHED_GROUP(kSchedDsRead, 2);
@@ -985,6 +1018,8 @@ void bwd_dq_kernel(BwdParams p) {
         tile_body(key0, bufc, std::true_type{});
       else
         tile_body(key0, bufc, std::false_type{});
+    } else if constexpr (KBIAS) {
+      tile_body(key0, bufc, std::false_type{});
     } else {
       tile_pipe(key0, bufc);
     }
@@ -1057,28 +1092,37 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
 // per-configuration launchers (each instantiated by one compilation of attn_bwd_inst.hip)
 // ---------------------------------------------------------------------------------
 // MASK: 0 none, 1 causal, 2 causal with a sliding window of p.win keys, 3 causal with the
-// ALiBi bias, 4 block-sparse map, 5 block-sparse map and causal.
-// MASK 4: block-sparse map; 5: block-sparse map and the causal mask.
+// ALiBi bias, 4 block-sparse map, 5 block-sparse map and causal, 6 key bias, 7 key bias
+// and causal.
+// MASK 4: block-sparse map; 5: block-sparse map and the causal mask; 6: key bias;
+// 7: key bias and the causal mask.
+template <int MASK>
+struct MaskMode {
+  static constexpr bool CAUSAL = MASK == 1 || MASK == 2 || MASK == 3 || MASK == 5 || MASK == 7;
+  static constexpr bool WIN = MASK == 2, ALIBI = MASK == 3, BSP = MASK == 4 || MASK == 5;
+  static constexpr bool KBIAS = MASK == 6 || MASK == 7;
+};
+
 template <class E, int DQK, int DV, int MASK>
 hipError_t bwd_main_t(const BwdParams& p, bool deterministic, hipStream_t s) {
-  constexpr bool CAUSAL = MASK == 1 || MASK == 2 || MASK == 3 || MASK == 5, WIN = MASK == 2, ALIBI = MASK == 3;
-  constexpr bool BSP = MASK >= 4;
+  using M = MaskMode<MASK>;
   const int nkb = (p.T + BWD_BN - 1) / BWD_BN;
   const dim3 grid_kv(nkb * p.B * p.NH);
   if (deterministic)
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, false, BSP>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, M::CAUSAL, M::WIN, M::ALIBI, false, M::BSP, M::KBIAS>), grid_kv,
+                       dim3(BWD_NT), 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, true, BSP>), grid_kv, dim3(BWD_NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, M::CAUSAL, M::WIN, M::ALIBI, true, M::BSP, M::KBIAS>), grid_kv,
+                       dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
 template <class E, int DQK, int DV, int MASK>
 hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
-  constexpr bool CAUSAL = MASK == 1 || MASK == 2 || MASK == 3 || MASK == 5, WIN = MASK == 2, ALIBI = MASK == 3;
-  constexpr bool BSP = MASK >= 4;
+  using M = MaskMode<MASK>;
   const int nqb = (p.T + DqShape<DQK>::BM - 1) / DqShape<DQK>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, CAUSAL, WIN, ALIBI, BSP>), dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0,
-                     s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, M::CAUSAL, M::WIN, M::ALIBI, M::BSP, M::KBIAS>),
+                     dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1090,8 +1134,10 @@ hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
   extern template hipError_t bwd_dq_t<E, DQK, DV, MASK>(const BwdParams&, hipStream_t);
 #define ATTN_EXTERN_BWD(DQK, DV, MASK) ATTN_EXTERN_BWD_E(bf16, DQK, DV, MASK) ATTN_EXTERN_BWD_E(f16, DQK, DV, MASK)
 ATTN_BWD_CONFIGS(ATTN_EXTERN_BWD)
-// block-sparse maps: bf16 only
-#define ATTN_BWD_BSP_CONFIGS(X) X(64, 64, 4) X(64, 64, 5) X(128, 128, 4) X(128, 128, 5) X(192, 128, 4) X(192, 128, 5)
+// block-sparse maps and the key bias: bf16 only
+#define ATTN_BWD_BSP_CONFIGS(X)                                                                       \
+  X(64, 64, 4) X(64, 64, 5) X(128, 128, 4) X(128, 128, 5) X(192, 128, 4) X(192, 128, 5) X(64, 64, 6) \
+  X(64, 64, 7) X(128, 128, 6) X(128, 128, 7) X(192, 128, 6) X(192, 128, 7)
 #define ATTN_EXTERN_BWD_BF16(DQK, DV, MASK) ATTN_EXTERN_BWD_E(bf16, DQK, DV, MASK)
 ATTN_BWD_BSP_CONFIGS(ATTN_EXTERN_BWD_BF16)
 

@@ -50,8 +50,11 @@ constexpr float kSumLimit = 256.f;        // 2^kRescaleThreshold
 // linear bias -m_h (i - j) added to the scaled scores.
 // SPLIT (non-causal only): one key chunk of p.kv_chunk keys per workgroup, partial
 // results to p.part.  BSP: block-sparse map (p.bs): the workgroup visits only the key tiles
-// of its query block's live key blocks, in the descending order of p.bs's list.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool SPLIT = false, bool BSP = false>
+// of its query block's live key blocks, in the descending order of p.bs's list.  KBIAS: a
+// per-key bias (p.kbias, score units) added to the scores; each tile's 64 values travel
+// with its keys into LDS.
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool SPLIT = false, bool BSP = false,
+          bool KBIAS = false>
 __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr int KS = DQK / 16;
   constexpr int NDT = DV / 32;
@@ -61,6 +64,7 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   // from the direct loads in flight into the other and does not wait on them.
   __shared__ __attribute__((aligned(1024))) char kbuf0[KT_BYTES], kbuf1[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[VT_BYTES], vbuf1[VT_BYTES];
+  __shared__ __attribute__((aligned(256))) float kbl0[KBIAS ? FWD_BN : 1], kbl1[KBIAS ? FWD_BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lq = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in a scalar register
@@ -162,6 +166,10 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     constexpr int BUF = decltype(bufc)::value;
     kload.issue(kg + key0 * skt, skt, Lk - key0, (ATTN_LDS char*)(BUF ? kbuf1 : kbuf0), w);
     vload.issue(vg + key0 * svt, svt, Lk - key0, (ATTN_LDS char*)(BUF ? vbuf1 : vbuf0), w);
+    if constexpr (KBIAS) {  // this tile's 64 key biases (zero past Lk)
+      if (w == 0) load_f32x64_lds(p.kbias + (int64_t)bh * p.kbias_ld + key0, Lk - key0,
+                                  (ATTN_LDS float*)(BUF ? kbl1 : kbl0), lane);
+    }
   };
 
   const float c = p.scale_log2;
@@ -198,6 +206,19 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
       for (int ks = 0; ks < KS; ++ks) {
         s0 = mfma32(lds_row8<E, FWD_BN>(kt, L, 0, ks), qf[ks], s0);
         s1 = mfma32(lds_row8<E, FWD_BN>(kt, L, 32, ks), qf[ks], s1);
+      }
+      if constexpr (KBIAS) {  // key of element r: key0 + 8 (r / 4) + 4 g + r % 4 (+32 in s1)
+        const float* kb = BUF ? kbl1 : kbl0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 b0 = *reinterpret_cast<const f32x4*>(kb + 8 * a + 4 * g);
+          const f32x4 b1 = *reinterpret_cast<const f32x4*>(kb + 32 + 8 * a + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s0[4 * a + e] += b0[e];
+            s1[4 * a + e] += b1[e];
+          }
+        }
       }
       if constexpr (ALIBI) {  // key of element r: key0 + 8 (r / 4) + 4 g + r % 4 (+32 in s1)
         const float b0 = sl * (float)(key0 + 4 * g - my_q);
@@ -386,7 +407,14 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 template <class E, int DQK, int DV>
 static hipError_t fwd_launch(const FwdParams& p, bool causal, hipStream_t s) {
   const dim3 grid((p.T + FWD_BM - 1) / FWD_BM * p.B * p.NH);
-  if (p.bs.items != nullptr) {
+  if (p.kbias != nullptr) {
+    if (causal)
+      hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, false, false, false, false, true>), grid, dim3(FWD_NT), 0, s,
+                         p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, false, false, false, false, false, true>), grid, dim3(FWD_NT), 0,
+                         s, p);
+  } else if (p.bs.items != nullptr) {
     if (causal)
       hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, false, false, false, true>), grid, dim3(FWD_NT), 0, s, p);
     else

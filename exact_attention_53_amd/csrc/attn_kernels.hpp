@@ -47,6 +47,10 @@ struct FwdParams {
   const int* seq_k;
   const int* items;
   BsList bs;               // block-sparse map: live key blocks per query block
+  // Key bias (nullptr: none): kbias[(b * NH + h) * kbias_ld + j], the caller's bias of key j
+  // divided by the scale (so that it adds to the unscaled scores), zero past T.
+  const float* kbias;
+  int kbias_ld;
 };
 
 struct BwdParams {
@@ -75,6 +79,9 @@ struct BwdParams {
   const int* items_kv;
   const int* items_dq;
   int bsp;                 // 1: block-sparse map (the lists below, built for the stages run)
+  const float* kbias;      // key bias as in FwdParams, (B * NH, Tpad), or nullptr
+  float* dbias_part;       // workspace: (B * NH, Tpad) fp32, sum over queries of dS per key
+                           // (written by the key/value kernel when not nullptr)
   BsList bs_kv;            // block-sparse map: live query blocks per key block (ascending)
   BsList bs_dq;            // ... live key blocks per dQ query block (descending, row bits)
 };
@@ -121,6 +128,14 @@ struct BsIndexParams {
   int NH, nbh, nb, nblk, group, kind, causal;
 };
 hipError_t launch_bs_index(const BsIndexParams& p, hipStream_t s);
+// Key bias: the caller's bias (element strides sb, sh along b and h, 1 along t) divided by
+// the scale into out (B * NH, ld) fp32, zero for t >= T; and the reduction of the per-head
+// sums over queries of dS into the caller's dbias (same strides as the bias): each dbias
+// element sums the (b, h) pairs that share it, b outer, h inner.
+hipError_t launch_bias_prep(const float* bias, int64_t sb, int64_t sh, float inv_scale, float* out, int ld, int B,
+                            int NH, int T, hipStream_t s);
+hipError_t launch_dbias_reduce(const float* part, int ld, float* dbias, int64_t sb, int64_t sh, int B, int NH, int T,
+                               hipStream_t s);
 // Query rows per workgroup of the dQ kernel (its work list uses blocks of this size).
 int dq_block_rows(int d_qk);
 

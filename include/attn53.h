@@ -390,6 +390,56 @@ attn_status attn_bwd_blocksparse(const void* q, attn_strides sq,
                                  unsigned stages);
 
 /*
+ * Key bias — the attention bias of the SDPA options [SA8 1.2] (`bias`, `set_bias`), whose
+ * shape the page does not give; read as a per-key additive bias broadcast over the
+ * queries (which covers key-padding masks):
+ *   S_ij = scale * <q_i, k_j> + bias[b, h, j],   dbias[b, h, j] = sum_i dS_ij
+ * summed further over the batches / heads that share one bias row.
+ *   bias  : fp32 device pointer, 4-byte aligned (read): bias + b * bias_stride_b +
+ *           h * bias_stride_h + j for key j of head (b, h); strides in elements, >= 0, 0 to
+ *           share one row across batches / heads; contiguous along the keys.  Values must be
+ *           finite: mask a key with a large negative value (e.g. -1e9), not -inf.
+ *   dbias : fp32 device pointer with the bias's strides (written; attn_bwd_keybias only),
+ *           or NULL when no bias gradient is wanted.  Each element is the sum over its
+ *           (b, h) pairs in one fixed order, so it is bit-stable; distinct elements must
+ *           not share memory (ATTN_ERR_STRIDE).
+ *   workspace : at least the matching *_workspace_bytes (the bias divided by the scale,
+ *               B * NH * Tpad fp32; the backward adds the per-head sums of dS and what
+ *               attn_bwd keeps there), 16-byte aligned, owned by the caller, clobbered.
+ * Element type bf16; every other argument, layout rule and error is that of attn_fwd /
+ * attn_bwd_staged (bias NULL: ATTN_ERR_NULL; an output overlapping the bias:
+ * ATTN_ERR_ALIAS).  The backward must get the forward's bias and causal flag.
+ */
+size_t attn_fwd_keybias_workspace_bytes(int B, int NH, int T, int d_qk, int d_v);
+
+attn_status attn_fwd_keybias(const void* q, attn_strides sq,
+                             const void* k, attn_strides sk,
+                             const void* v, attn_strides sv,
+                             void* o, attn_strides so,
+                             float* lse,
+                             const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                             int B, int NH, int T, int d_qk, int d_v,
+                             float scale, int causal,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+size_t attn_bwd_keybias_workspace_bytes(int B, int NH, int T, int d_qk, int d_v, int deterministic);
+
+attn_status attn_bwd_keybias(const void* q, attn_strides sq,
+                             const void* k, attn_strides sk,
+                             const void* v, attn_strides sv,
+                             const void* o, attn_strides so,
+                             const float* lse,
+                             const void* do_, attn_strides sdo,
+                             void* dq, attn_strides sdq,
+                             void* dk, attn_strides sdk,
+                             void* dv, attn_strides sdv,
+                             const float* bias, float* dbias, int64_t bias_stride_b, int64_t bias_stride_h,
+                             int B, int NH, int T, int d_qk, int d_v,
+                             float scale, int causal, int deterministic,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             unsigned stages);
+
+/*
  * attn_bwd_noalloc — attn_bwd without a caller-supplied workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, allocation-free serving or
  * training loops, harnesses that forbid hipMalloc.  The workspace (D, LSE log2(e) and, in

@@ -332,3 +332,35 @@ def test_binding_blocksparse_map_checks():
             attn._block_map(m, 2, 3, 300, torch.device("cpu"))
     b, h = attn._block_map(torch.zeros(1, 3, 3, 3, dtype=torch.uint8), 2, 3, 300, torch.device("cpu"))
     assert (b, h) == (0, 9)
+
+
+def test_keybias_validation(lib):
+    st, sv = strides(64, 2, 64), strides(64, 2, 64)
+    BIAS, DB = GOOD + 0xc00000, GOOD + 0xd00000
+
+    def kfwd(bias=BIAS, sb=128, sh=64, o=GOOD + 0x300000, ws=GOOD + 0xb00000, ws_bytes=1 << 20):
+        return lib.attn_fwd_keybias(GOOD, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, o, sv, None, bias, sb, sh,
+                                    1, 2, 64, 64, 64, 0.125, 1, ws, ws_bytes, None)
+
+    def kbwd(bias=BIAS, dbias=DB, sb=128, sh=64, dq=GOOD + 0x600000, ws=GOOD + 0x900000, ws_bytes=1 << 20):
+        return lib.attn_bwd_keybias(GOOD, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, GOOD + 0x300000, sv,
+                                    GOOD + 0x400000, GOOD + 0x500000, sv, dq, st, GOOD + 0x700000, st,
+                                    GOOD + 0x800000, sv, bias, dbias, sb, sh, 1, 2, 64, 64, 64, 0.125, 1, 1, ws,
+                                    ws_bytes, None, 7)
+
+    for f in (kfwd, kbwd):
+        assert f(bias=None) == NULL
+        assert f(bias=BIAS + 2) == ALIGN
+        assert f(sh=-64) == STRIDE
+        assert f(ws=None) == WORKSPACE
+        assert f(ws_bytes=16) == WORKSPACE
+    assert kfwd(o=BIAS) == ALIAS                 # output overlaps the bias
+    assert kbwd(dbias=BIAS) == ALIAS             # dbias overlaps the bias
+    assert kbwd(dbias=GOOD + 0x100000) == ALIAS  # dbias overlaps k
+    assert kbwd(dbias=DB + 2) == ALIGN
+    assert kbwd(sh=32) == STRIDE                 # two heads' dbias rows (64 keys) would share elements
+    assert kbwd(dq=BIAS) == ALIAS
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert lib.attn_fwd_keybias_workspace_bytes(4, 16, 8192, 128, 128) == a256(4 * 16 * 8192 * 4)
+    assert lib.attn_bwd_keybias_workspace_bytes(4, 16, 8192, 128, 128, 1) == \
+        lib.attn_bwd_workspace_bytes(4, 16, 8192, 128, 128, 1) + 2 * a256(4 * 16 * 8192 * 4)

@@ -78,6 +78,8 @@ WORKLOADS: Dict[str, Workload] = {
     # the headline shape under a block-sparse map (see block_map): causal, each query
     # block sees the 8 most recent key blocks (1024 keys) and the first one
     "blocksparse": Workload("blocksparse", 4, 16, 8192, 128, 128, True, 53010),
+    # the headline shape with a per-head key bias (see key_bias)
+    "keybias": Workload("keybias", 4, 16, 8192, 128, 128, True, 53011),
 }
 
 BS_BLOCK = 128
@@ -137,3 +139,12 @@ def make_inputs(w: Workload, dtype: torch.dtype = torch.bfloat16) -> Dict[str, t
     v = _randn((B, T, NH, w.d_v), w.seed + 2, w.sigma, dtype)
     do = _randn((B, T, NH, w.d_v), w.seed + 3, w.sigma_do, dtype)
     return {"q": q, "k": k, "v": v, "do": do}
+
+
+def key_bias(w: Workload):
+    """The key bias of a workload, float32 (B, NH, T): N(0, 1) per (b, h, key) from seed
+    w.seed + 10, and in the odd batches the last quarter of the keys padded with -1e9."""
+    g = torch.Generator().manual_seed(w.seed + 10)
+    b = torch.randn((w.B, w.NH, w.T), generator=g, dtype=torch.float32)
+    b[1::2, :, w.T - w.T // 4:] = -1e9
+    return b.numpy()
