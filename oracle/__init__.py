@@ -8,6 +8,8 @@ from .attn_ref import (  # noqa: F401
     attn_ref_bwd,
     attn_ref_blocksparse,
     attn_ref_keybias,
+    attn_ref_fwd_fp8,
+    e4m3_to_f64,
     attn_ref_bwd_loop,
     attn_ref_fwd,
     attn_ref_varlen,

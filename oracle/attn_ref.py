@@ -75,6 +75,8 @@ __all__ = [
     "attn_ref_varlen",
     "attn_ref_blocksparse",
     "attn_ref_keybias",
+    "attn_ref_fwd_fp8",
+    "e4m3_to_f64",
     "attn_ref_bwd_loop",
     "alibi_slopes",
 ]
@@ -380,6 +382,32 @@ def attn_ref_keybias(q, k, v, do, bias, causal: bool, scale: Optional[float] = N
                 else:
                     out[name][b, :, h] = x
     return out
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Decodes 8-bit floating-point codes of the e4m3 format (1 sign bit, 4 exponent bits
+    with bias 7, 3 mantissa bits; exponent field 0 is subnormal, m / 8 * 2^-6; the code
+    with every exponent and mantissa bit set is NaN; there is no infinity; largest finite
+    value 448) to float64, exactly."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def attn_ref_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, causal: bool,
+                     scale: Optional[float] = None):
+    """Forward on fp8 (e4m3) inputs with per-tensor descale factors: the real inputs are
+    descale * decode(code), and the result is the plain definition (attn_ref_fwd) on them,
+    in float64.  q8, k8, v8 are (B, T, NH, d) uint8 code arrays.  P is not rounded here:
+    the GPU's rounding of P to e4m3 is an error of the kernel, bounded in its tolerance."""
+    q = e4m3_to_f64(q8) * descale_q
+    k = e4m3_to_f64(k8) * descale_k
+    v = e4m3_to_f64(v8) * descale_v
+    return attn_ref_fwd(q, k, v, causal, scale)
 
 
 def attn_ref_varlen(q, k, v, do, seq_q, seq_k, causal: bool, scale: Optional[float] = None):

@@ -703,6 +703,49 @@ def pin_keybias_finite_differences(ref, h: float = 1e-6):
         _close(r[name], g, rtol=1e-6, atol=1e-8, what=f"bias finite differences {name}")
 
 
+# ---------------------------------------------------------------------------------
+# fp8 (e4m3) inputs: the decoder of the 8-bit format, and the forward on decoded inputs.
+# ---------------------------------------------------------------------------------
+def pin_e4m3_code_points(ref):
+    """Code points fixed by the format: 0 and -0, the smallest subnormal 2^-9, the largest
+    subnormal 7/8 * 2^-6, the smallest normal 2^-6, 1, 1.125 (one mantissa step), 2, the
+    largest finite 448 (and its negative), NaN; positive codes increase monotonically."""
+    d = ref.e4m3_to_f64
+    pts = {0x00: 0.0, 0x80: -0.0, 0x01: 2.0 ** -9, 0x07: 7 / 8 * 2.0 ** -6, 0x08: 2.0 ** -6, 0x38: 1.0,
+           0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xFE: -448.0, 0xB8: -1.0}
+    for c, v in pts.items():
+        assert d([c])[0] == v, f"e4m3 code {c:#x}: {d([c])[0]} != {v}"
+    assert np.isnan(d([0x7F])[0]) and np.isnan(d([0xFF])[0]), "e4m3 NaN codes"
+    pos = d(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0), "positive codes not increasing"
+
+
+def pin_e4m3_library(ref):
+    """Every code against torch's float8_e4m3fn (an independent implementation of the
+    same format)."""
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = ref.e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(lib)), "NaN codes differ"
+    ok = ~np.isnan(lib)
+    assert np.array_equal(got[ok], lib[ok]), "e4m3 decode differs from the library"
+
+
+def pin_fp8_forward_zero_queries(ref):
+    """fp8 codes with descales: Q = 0 gives O_i = descale_v * mean of the decoded V rows up
+    to i (causal) and LSE_i = ln(i + 1), whatever descale_q and descale_k are."""
+    rng = np.random.default_rng(911)
+    k8 = rng.integers(0, 0x7F, size=(1, 21, 2, 16), dtype=np.uint8)
+    v8 = rng.integers(0, 0xFF, size=(1, 21, 2, 16), dtype=np.uint8)
+    v8[(v8 & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    q8 = np.zeros_like(k8)
+    o, lse = ref.attn_ref_fwd_fp8(q8, k8, v8, 3.0, 0.5, 0.25, True)
+    vd = ref.e4m3_to_f64(v8) * 0.25
+    for i in range(21):
+        _close(o[0, i], vd[0, :i + 1].mean(axis=0), rtol=1e-14, atol=1e-300, what=f"fp8 zero queries O row {i}")
+    _close(lse[0], np.log(np.arange(1, 22))[None, :].repeat(2, 0), rtol=1e-14, atol=1e-15, what="fp8 LSE")
+
+
 ALL_PINS = [
     ("finite_differences_causal", lambda r: pin_finite_differences(r, True)),
     ("finite_differences_full", lambda r: pin_finite_differences(r, False)),
@@ -748,6 +791,9 @@ ALL_PINS = [
     ("keybias_loops", pin_keybias_loops),
     ("keybias_padding", pin_keybias_padding),
     ("finite_differences_keybias", pin_keybias_finite_differences),
+    ("e4m3_code_points", pin_e4m3_code_points),
+    ("e4m3_library", pin_e4m3_library),
+    ("fp8_forward_zero_queries", pin_fp8_forward_zero_queries),
     ("alibi_slopes", pin_alibi_slopes),
     ("alibi_zero_queries", pin_alibi_zero_queries),
     ("alibi_loops", pin_alibi_loops),

@@ -75,6 +75,10 @@ MUTANTS = {
     "dbias_scaled": ("dbias[:nk] += dS.sum(axis=0)", "dbias[:nk] += scale * dS.sum(axis=0)"),
     "dbias_shared_not_summed": ('out["dbias"][b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0] += x',
                                 'out["dbias"][b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0] = x'),
+    "e4m3_bias_8": ("(1.0 + m / 8.0) * np.exp2(e - 7.0)", "(1.0 + m / 8.0) * np.exp2(e - 8.0)"),
+    "e4m3_no_subnormals": ("np.where(e == 0, m / 8.0 * 2.0 ** -6,", "np.where(e == 0, 0.0 * m,"),
+    "e4m3_mantissa_quarters": ("(1.0 + m / 8.0) * np.exp2", "(1.0 + m / 4.0) * np.exp2"),
+    "fp8_descale_v_dropped": ("    v = e4m3_to_f64(v8) * descale_v\n", "    v = e4m3_to_f64(v8)\n"),
     "blocksparse_map_transposed": ("return np.asarray(block_map)[qi[:, None], kj[None, :]] != 0",
                                    "return np.asarray(block_map).T[qi[:, None], kj[None, :]] != 0"),
     "blocksparse_block_index_off": ("qi = np.arange(r0, r1) // block", "qi = np.arange(r0 + 1, r1 + 1) // block"),
