@@ -278,6 +278,64 @@ def decode_bench(args, w):
     }), flush=True)
 
 
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA: twice the bf16 rate
+
+
+def fp8_bench(args, w):
+    """The fp8 (e4m3) forward alone (its transpose of V included): forward TFLOP/s against
+    the dense fp8 MFMA peak, with the bf16 forward of the same workload timed beside it."""
+    import torch
+
+    import exact_attention_53_amd as attn
+    import workloads
+
+    dev = torch.device("cuda:0")
+    x = workloads.make_fp8_inputs(w)
+    q8, k8, v8 = (x[n].to(dev) for n in ("q8", "k8", "v8"))
+    B, T, NH = w.B, w.T, w.NH
+    o = torch.empty((B, T, NH, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(attn.load().attn_fwd_fp8_workspace_bytes(B, NH, T, w.d_qk, w.d_v), dtype=torch.uint8,
+                     device=dev)
+
+    def run():
+        attn.fwd_fp8(q8, k8, v8, x["descale_q"], x["descale_k"], x["descale_v"], w.causal, w.scale, out=o, lse=lse,
+                     workspace=ws)
+
+    def timeit(fn, n):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timeit(run, args.steps)
+    cpu = workloads.make_inputs(w)
+    qb, kb, vb = (cpu[n].to(dev) for n in ("q", "k", "v"))
+    del cpu
+    ms_bf16 = timeit(lambda: attn.fwd(qb, kb, vb, w.causal, w.scale, out=o, lse=lse), args.steps)
+    f_fwd = flops(w)[0]
+    tf = f_fwd / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "causal attention fwd TFLOP/s (fp8 e4m3 inputs) and % of MI355X fp8 MFMA peak", "value": round(tf, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+        "config": {"workload": f"{w.name} forward only, fp8 e4m3 Q/K/V with per-tensor descales, bf16 O: B={B} NH={NH} "
+                               f"T={T} d={w.d_qk} {'causal' if w.causal else 'non-causal'}",
+                   "B": B, "NH": NH, "T": T, "d_qk": w.d_qk, "d_v": w.d_v, "causal": w.causal},
+        "pct_of_peak": round(100.0 * tf / PEAK_FP8_TFLOPS, 2),
+        "bf16_fwd_same_workload": {"ms": round(ms_bf16, 4), "tflops": round(f_fwd / (ms_bf16 * 1e-3) / 1e12, 2)},
+        "speedup_over_bf16_fwd": round(ms_bf16 / ms, 3),
+        "roofline": {"kernel": "attn_fwd_fp8", "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
+    }), flush=True)
+
+
 def copy_calibration(mib: int):
     """A streaming kernel of known size: an elementwise negation that reads and writes
     exactly mib MiB per launch (a kernel, unlike a DMA copy, is seen by the counters).
@@ -309,8 +367,9 @@ def main():
     ap.add_argument("--power-log", default="", help="keep the sampler's samples (JSON lines) in this file")
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="only time the CPU oracle on a bounded sample of the workload (no GPU use)")
-    ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
-                    help="16-bit element type of Q, K, V, O and the gradients (the metric is quoted for bf16)")
+    ap.add_argument("--dtype", choices=["bf16", "f16", "fp8"], default="bf16",
+                    help="element type of Q, K, V, O and the gradients (the metric is quoted for bf16); fp8: the "
+                         "e4m3 forward alone")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB buffer before every step (evicts the 256 MB last-level cache); "
                          "the step time is then the sum of the kernel intervals, without the eviction")
@@ -342,6 +401,9 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     if w.name == "decode":
         decode_bench(args, w)
+        return
+    if args.dtype == "fp8":
+        fp8_bench(args, w)
         return
     dev = torch.device("cuda:0")
     et = torch.bfloat16 if args.dtype == "bf16" else torch.float16

@@ -28,7 +28,7 @@ import torch
 __all__ = [
     "AttnError", "lib_path", "load", "fwd", "fwd_packed", "bwd", "bwd_packed",
     "workspace_bytes", "fwd_varlen", "bwd_varlen", "fwd_decode", "bwd_noalloc", "fwd_blocksparse", "bwd_blocksparse", "BS_BLOCK",
-    "fwd_keybias", "bwd_keybias", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
+    "fwd_keybias", "bwd_keybias", "fwd_fp8", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -106,6 +106,10 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_keybias.argtypes = [vp, S, vp, S, vp, S, vp, S, vp, vp, i64, i64, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_bwd_keybias.restype = i
     lib.attn_bwd_keybias.argtypes = bwd_args[:17] + [vp, vp, i64, i64] + bwd_args[17:] + [ctypes.c_uint]
+    lib.attn_fwd_fp8_workspace_bytes.restype = sz
+    lib.attn_fwd_fp8_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_fwd_fp8.restype = i
+    lib.attn_fwd_fp8.argtypes = [vp, S, vp, S, vp, S, vp, S, vp, f, f, f, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_bwd_noalloc.restype = i
     lib.attn_bwd_noalloc.argtypes = bwd_args[:25] + [vp]
     lib.attn_bwd_noalloc_max_workspace_bytes.restype = sz
@@ -484,6 +488,52 @@ def bwd_keybias(q, k, v, o, lse, do, bias: torch.Tensor, causal: bool = False, s
                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                     _stream(dev), int(stages)))
     return dq, dk, dv, dbias
+
+
+_FP8_TYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def fwd_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float, causal: bool = True,
+            scale: Optional[float] = None, return_lse: bool = True, layout: str = "bthd",
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None):
+    """Forward on fp8 e4m3 inputs (torch.float8_e4m3fn, or uint8 holding the codes) with
+    per-tensor descale factors: the real inputs are descale_x * x.  d_qk = d_v in {64, 128}.
+    Returns (o, lse), o in bf16."""
+    B, NH, T, dqk = _dims(q, layout)
+    dv = v.shape[-1]
+    _shape(k, "k", layout, B, NH, T, dqk)
+    _shape(v, "v", layout, B, NH, T, dv)
+    if out is not None:
+        _shape(out, "out", layout, B, NH, T, dv)
+    dev = q.device
+    _on_gpu("fwd_fp8", dev)
+    lib = load()
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        if x.dtype not in _FP8_TYPES:
+            raise TypeError(f"{n} must hold e4m3 codes (float8_e4m3fn or uint8), got {x.dtype}")
+        if x.device != dev:
+            raise ValueError(f"{n} is on {x.device}, expected {dev}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        shape = (B, T, NH, dv) if layout == "bthd" else (B, NH, T, dv)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", dev, torch.bfloat16)
+    if return_lse and lse is None:
+        lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    need = int(lib.attn_fwd_fp8_workspace_bytes(B, NH, T, dqk, dv))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_fwd_fp8(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                                v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
+                                lse.data_ptr() if return_lse else None, float(descale_q), float(descale_k),
+                                float(descale_v), B, NH, T, dqk, dv, float(scale), int(bool(causal)),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, (lse if return_lse else None)
 
 
 def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, causal: bool = True, scale: Optional[float] = None,

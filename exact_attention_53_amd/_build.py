@@ -25,7 +25,8 @@ INSTANCES = [(kind, elem, dqk, dv, mask) for kind in ("kv", "dq") for elem in ("
              for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in range(8)
              if mask < 4 or elem == "bf16"]
 MASK_NAMES = ("full", "causal", "window", "alibi", "bsp", "bsp_causal", "kbias", "kbias_causal")
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_plan.hip", "attn_blocksparse.hip", "attn_bias.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_plan.hip", "attn_blocksparse.hip", "attn_bias.hip",
+           "attn_api.cpp"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU instructions.
 FLAGS = [

@@ -504,6 +504,64 @@ attn_status attn_fwd_blocksparse(const void* q, attn_strides sq, const void* k, 
                   causal, 0, 0, workspace, workspace_bytes, stream, &bs);
 }
 
+size_t fp8_vt_ld(int T) { return ((size_t)T + 63) / 64 * 64; }
+
+size_t attn_fwd_fp8_workspace_bytes(int B, int NH, int T, int d_qk, int d_v) {
+  if (B < 1 || NH < 1 || T < 1 || (int64_t)B * NH * ((int64_t)T + kRowPad) > (int64_t)INT32_MAX) return 0;
+  if (d_qk != d_v || (d_qk != 64 && d_qk != 128)) return 0;
+  return align256((size_t)B * NH * d_v * fp8_vt_ld(T));
+}
+
+attn_status attn_fwd_fp8(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                         attn_strides sv, void* o, attn_strides so, float* lse, float descale_q, float descale_k,
+                         float descale_v, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || NH < 1 || T < 1 || (int64_t)B * NH * ((int64_t)T + kRowPad) > (int64_t)INT32_MAX)
+    return ATTN_ERR_SHAPE;
+  if (d_qk != d_v || (d_qk != 64 && d_qk != 128)) return ATTN_ERR_HEADDIM;
+  for (float x : {scale, descale_q, descale_k, descale_v})
+    if (!std::isfinite(x) || !(x > 0.f)) return ATTN_ERR_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  // fp8 tensors: one byte per element; rows 16-byte aligned for the 128-bit loads
+  Extent e8[3];
+  const void* ptrs[3] = {q, k, v};
+  const attn_strides strd[3] = {sq, sk, sv};
+  for (int i = 0; i < 3; ++i) {
+    const attn_strides x = strd[i];
+    if (ptrs[i] == nullptr) return ATTN_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16 != 0) return ATTN_ERR_ALIGN;
+    if (x.b < 0 || x.h < 0 || x.t < 0 || x.b % 16 || x.h % 16 || x.t % 16 || x.t > (int64_t)1 << 24)
+      return ATTN_ERR_STRIDE;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ptrs[i]);
+    e8[i] = Extent{lo, lo + (uintptr_t)(x.b * (B - 1) + x.h * (NH - 1) + x.t * (int64_t)(T - 1) + d_qk)};
+  }
+  attn_status st;
+  Extent eo;
+  if ((st = check_tensor(o, so, B, NH, T, d_v, &eo)) != ATTN_OK) return st;
+  if ((st = check_output_rows(so, B, NH, T, d_v)) != ATTN_OK) return st;
+  if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_ALIGN;
+  const Extent el{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + (uintptr_t)B * NH * T * 4u};
+  const size_t need = attn_fwd_fp8_workspace_bytes(B, NH, T, d_qk, d_v);
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || workspace_bytes < need)
+    return ATTN_ERR_WORKSPACE;
+  const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+  for (const Extent& a : e8) {
+    if (overlaps(eo, a) || overlaps(ew, a) || (lse != nullptr && overlaps(el, a))) return ATTN_ERR_ALIAS;
+  }
+  if (overlaps(ew, eo) || (lse != nullptr && (overlaps(el, eo) || overlaps(el, ew)))) return ATTN_ERR_ALIAS;
+  attn53::Fp8FwdParams p{};
+  p.q = q; p.sq = cvt(sq);
+  p.k = k; p.sk = cvt(sk);
+  p.v = v; p.sv = cvt(sv);
+  p.vt = workspace; p.vt_ld = (int)fp8_vt_ld(T);
+  p.o = o; p.so = cvt(so);
+  p.lse = lse;
+  p.B = B; p.NH = NH; p.T = T;
+  p.scale_log2 = scale * descale_q * descale_k * kLog2e;
+  p.descale_v = descale_v;
+  return hip_status(attn53::launch_fwd_fp8(p, d_qk, causal != 0, (hipStream_t)stream));
+}
+
 size_t attn_fwd_keybias_workspace_bytes(int B, int NH, int T, int d_qk, int d_v) {
   if (check_sizes(B, NH, T, d_qk, d_v) != ATTN_OK) return 0;
   return kb_ws_bytes(B, NH, T);

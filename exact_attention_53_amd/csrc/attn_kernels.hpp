@@ -53,6 +53,21 @@ struct FwdParams {
   int kbias_ld;
 };
 
+// Forward on fp8 (e4m3) inputs.  q, k, v hold e4m3 codes (strides in bytes); vt is the
+// workspace's transposed copy of v, (B * NH, d, vt_ld) bytes with vt_ld = T rounded up to
+// 64 (zero past T), written by the call's first kernel.
+struct Fp8FwdParams {
+  const void* q; Strides sq;
+  const void* k; Strides sk;
+  const void* v; Strides sv;
+  void* vt; int vt_ld;
+  void* o; Strides so;     // bf16
+  float* lse;              // (B, NH, T) or nullptr
+  int B, NH, T;
+  float scale_log2;        // scale * descale_q * descale_k * log2(e)
+  float descale_v;
+};
+
 struct BwdParams {
   const void* q; Strides sq;
   const void* k; Strides sk;
@@ -116,6 +131,8 @@ hipError_t launch_bwd_main(const BwdParams& p, ElemType et, int d_qk, int d_v, b
 hipError_t launch_bwd_dq(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s);
 hipError_t launch_bwd_finalize(const BwdParams& p, ElemType et, int d_qk, hipStream_t s);
 hipError_t launch_plan(const PlanParams& p, hipStream_t s);
+// fp8 forward (d_qk = d_v = d in {64, 128}): the transpose of v, then the forward kernel.
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int d, bool causal, hipStream_t s);
 // Block-sparse map -> per-item lists (see BsList).  kind: 0 query-block rows (forward,
 // descending live key blocks, causal: up to the diagonal), 1 key-block columns (key/value
 // kernel, ascending live query blocks, causal: from the diagonal), 2 groups of `group`

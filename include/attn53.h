@@ -440,6 +440,39 @@ attn_status attn_bwd_keybias(const void* q, attn_strides sq,
                              unsigned stages);
 
 /*
+ * attn_fwd_fp8 — the forward on fp8 inputs, the FP8 lever of [FAT 5.3.4, 6] (less memory
+ * traffic and twice the bf16 matrix rate); the pages give no recipe, so this is the
+ * reading taken:
+ *   q, k, v : e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+ *             finite 448, no infinity), (B, NH, T, d) through strides in elements (= bytes),
+ *             16-byte aligned, strides multiples of 16 (read).  The real inputs are
+ *             descale_q * q, descale_k * k, descale_v * v (per-tensor fp32 factors, finite,
+ *             > 0; a caller typically picks descale = max|x| / 448).
+ *   o       : bf16 (B, NH, T, d), strides so (written); lse as for attn_fwd (natural-log
+ *             logsumexp of the scaled scores; NULL for inference).
+ *   d_qk = d_v = 64 or 128 (otherwise ATTN_ERR_HEADDIM); causal 0 / 1.
+ * S = scale descale_q descale_k Q K^T is formed exactly in fp32 by the fp8 matrix
+ * instruction; P is rounded to e4m3 for O = P V (P <= 2^8 by the lazy-rescale rule, inside
+ * e4m3's range), while the row sum adds the unrounded fp32 P; O = descale_v P V / l.  The
+ * rounding of P (3 mantissa bits) is the path's one approximation beyond the fp32 sums.
+ *   workspace : at least attn_fwd_fp8_workspace_bytes(...) bytes (a transposed copy of v,
+ *               B * NH * d * ceil(T / 64) * 64 bytes, which the call writes first),
+ *               16-byte aligned, owned by the caller, clobbered.
+ * Forward only: the backward takes 16-bit tensors.  Other rules as for attn_fwd.
+ */
+size_t attn_fwd_fp8_workspace_bytes(int B, int NH, int T, int d_qk, int d_v);
+
+attn_status attn_fwd_fp8(const void* q, attn_strides sq,
+                         const void* k, attn_strides sk,
+                         const void* v, attn_strides sv,
+                         void* o, attn_strides so,
+                         float* lse,
+                         float descale_q, float descale_k, float descale_v,
+                         int B, int NH, int T, int d_qk, int d_v,
+                         float scale, int causal,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_bwd_noalloc — attn_bwd without a caller-supplied workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, allocation-free serving or
  * training loops, harnesses that forbid hipMalloc.  The workspace (D, LSE log2(e) and, in

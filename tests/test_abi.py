@@ -364,3 +364,30 @@ def test_keybias_validation(lib):
     assert lib.attn_fwd_keybias_workspace_bytes(4, 16, 8192, 128, 128) == a256(4 * 16 * 8192 * 4)
     assert lib.attn_bwd_keybias_workspace_bytes(4, 16, 8192, 128, 128, 1) == \
         lib.attn_bwd_workspace_bytes(4, 16, 8192, 128, 128, 1) + 2 * a256(4 * 16 * 8192 * 4)
+
+
+def test_fp8_validation(lib):
+    s8 = S(64 * 2 * 64, 64, 2 * 64)          # (B, T, NH, d) e4m3, strides in bytes
+    so = strides(64, 2, 64)                  # bf16 output
+
+    def f8(q=GOOD, sq=s8, o=GOOD + 0x300000, dqk=64, dv=64, dsq=1.0, ws=GOOD + 0xb00000, ws_bytes=1 << 20,
+           causal=1):
+        return lib.attn_fwd_fp8(q, sq, GOOD + 0x100000, s8, GOOD + 0x200000, s8, o, so, None, dsq, 1.0, 1.0,
+                                1, 2, 64, dqk, dv, 0.125, causal, ws, ws_bytes, None)
+
+    assert f8(q=None) == NULL
+    assert f8(q=GOOD + 8) == ALIGN
+    assert f8(sq=S(64 * 2 * 64, 64, 2 * 64 + 8)) == STRIDE   # fp8 strides: multiples of 16 bytes
+    assert f8(dqk=192, dv=128) == HEADDIM
+    assert f8(dqk=128, dv=64) == HEADDIM
+    assert f8(dsq=0.0) == ARG
+    assert f8(dsq=float("nan")) == ARG
+    assert f8(causal=3) == ARG
+    assert f8(o=GOOD) == ALIAS
+    assert f8(ws=None) == WORKSPACE
+    assert f8(ws_bytes=100) == WORKSPACE
+    assert f8(ws=GOOD + 0x100000) == ALIAS
+    # workspace: the transposed V, d bytes x T rounded up to 64 per head
+    assert lib.attn_fwd_fp8_workspace_bytes(4, 16, 8192, 128, 128) == 4 * 16 * 128 * 8192
+    assert lib.attn_fwd_fp8_workspace_bytes(1, 2, 100, 64, 64) == (2 * 64 * 128 + 255) // 256 * 256
+    assert lib.attn_fwd_fp8_workspace_bytes(1, 2, 100, 192, 128) == 0

@@ -148,3 +148,23 @@ def key_bias(w: Workload):
     b = torch.randn((w.B, w.NH, w.T), generator=g, dtype=torch.float32)
     b[1::2, :, w.T - w.T // 4:] = -1e9
     return b.numpy()
+
+
+E4M3_MAX = 448.0
+
+
+def make_fp8_inputs(w: Workload):
+    """fp8 (e4m3) inputs of a workload: the same float32 normals as make_inputs (Q, K, V from
+    seeds w.seed + 0, 1, 2), each tensor scaled by one descale factor max|x| / 448 so that
+    its largest value maps to the largest e4m3 value, and rounded to e4m3 (nearest even,
+    torch's float8_e4m3fn conversion).  Returns uint8 codes q8, k8, v8 (B, T, NH, d) and the
+    descale factors."""
+    B, T, NH = w.B, w.T, w.NH
+    out = {}
+    for name, k, d in (("q", 0, w.d_qk), ("k", 1, w.d_qk), ("v", 2, w.d_v)):
+        g = torch.Generator().manual_seed(w.seed + k)
+        x = torch.randn((B, T, NH, d), generator=g, dtype=torch.float32) * w.sigma
+        ds = float(x.abs().max()) / E4M3_MAX
+        out[name + "8"] = (x / ds).to(torch.float8_e4m3fn).view(torch.uint8)
+        out["descale_" + name] = ds
+    return out
