@@ -10,6 +10,10 @@ from .attn_ref import (  # noqa: F401
     attn_ref_keybias,
     attn_ref_fwd_fp8,
     e4m3_to_f64,
+    philox4x32_10,
+    philox_keep,
+    dropout_threshold,
+    attn_ref_dropout,
     attn_ref_bwd_loop,
     attn_ref_fwd,
     attn_ref_varlen,

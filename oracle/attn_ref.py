@@ -32,6 +32,10 @@ What is computed (the plain definition, S and P materialised, float64 throughout
             pages give no format; this map, ANDed with the causal mask, is the
             reading taken.  A row left with no allowed key gets P = 0, O = 0,
             LSE = -inf and zero gradients (the logsumexp of an empty set)
+            dropout (the `dropout` option of [SA8 1.2], whose form the page does not
+            give; inverted dropout on the attention weights is the reading taken):
+            O = (P * Z) V / (1 - p) with the keep mask Z of philox_keep, the LSE from the
+            undropped P; backward dV = (P * Z)^T dO / (1 - p), dP = (dO V^T) * Z / (1 - p)
             key bias (the `bias` option among the SDPA options of [SA8 1.2], whose
             shape the page does not give; a per-key bias broadcast over the queries
             is the reading taken): additionally S[i, j] += bias[j] (finite values;
@@ -77,6 +81,10 @@ __all__ = [
     "attn_ref_keybias",
     "attn_ref_fwd_fp8",
     "e4m3_to_f64",
+    "philox4x32_10",
+    "philox_keep",
+    "dropout_threshold",
+    "attn_ref_dropout",
     "attn_ref_bwd_loop",
     "alibi_slopes",
 ]
@@ -182,13 +190,14 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
 def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
                   causal: bool, block_rows: Optional[int] = None, window: int = 0, slope: float = 0.0,
                   block_map: Optional[np.ndarray] = None, block: int = 128,
-                  key_bias: Optional[np.ndarray] = None):
+                  key_bias: Optional[np.ndarray] = None, keep: Optional[np.ndarray] = None, p_drop: float = 0.0):
     """One head: returns dQ, dK, dV and also O, LSE and D = (dP * P) 1 (all float64).
     q, do have T rows, k, v have Tk >= 1 rows (Tk may differ from T).  The bias is a
     constant of the inputs: it changes P but adds no term to the gradients; neither does
     the block map (a row with no allowed key has P = 0 and gets zero gradients).  With a
     key bias (Tk,) the result also holds dbias (Tk,) = sum over queries of dS, as an
-    eighth entry."""
+    eighth entry.  keep (T, Tk) bool: dropout with probability p_drop, the kept weights
+    scaled by 1 / (1 - p_drop) (O and the gradients; LSE and D as without it)."""
     _check_window(causal, window, slope)
     T, Tk = q.shape[0], k.shape[0]
     br = T if block_rows is None else block_rows
@@ -209,9 +218,12 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
         if allowed is not None:
             S = np.where(allowed, S, -np.inf)
         P, lse[r0:r1] = _softmax_rows_or_empty(S)
-        O[r0:r1] = P @ v[:nk]
-        dV[:nk] += P.T @ do[r0:r1]                      # dV = P^T dO
+        Pk = P if keep is None else P * (keep[r0:r1, :nk] / (1.0 - p_drop))  # weights after dropout
+        O[r0:r1] = Pk @ v[:nk]
+        dV[:nk] += Pk.T @ do[r0:r1]                     # dV = P^T dO
         dP = do[r0:r1] @ v[:nk].T                       # dP = dO V^T
+        if keep is not None:
+            dP = dP * (keep[r0:r1, :nk] / (1.0 - p_drop))  # through the dropout
         Dr = (dP * P).sum(axis=1)                       # (dP * P) 1
         dS = P * (dP - Dr[:, None])                     # dS = P * (dP - (dP * P) 1)
         dQ[r0:r1] = scale * (dS @ k[:nk])               # dQ = dS K / sqrt(d_k)
@@ -410,6 +422,81 @@ def attn_ref_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: 
     return attn_ref_fwd(q, k, v, causal, scale)
 
 
+# Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2,
+# 3", SC'11): a 128-bit counter and a 64-bit key; ten rounds of two 32x32 -> 64-bit
+# multiplications, the key bumped by the Weyl constants before every round but the first.
+PHILOX_M0, PHILOX_M1 = 0xD2511F53, 0xCD9E8D57
+PHILOX_W0, PHILOX_W1 = 0x9E3779B9, 0xBB67AE85
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """ctr: (..., 4) integers < 2^32, key: two integers < 2^32 -> (..., 4) uint32."""
+    c = [np.asarray(ctr, dtype=np.uint64)[..., i] for i in range(4)]
+    k0, k1 = np.uint64(key[0]), np.uint64(key[1])
+    mask = np.uint64(0xFFFFFFFF)
+    for r in range(10):
+        if r > 0:
+            k0 = (k0 + np.uint64(PHILOX_W0)) & mask
+            k1 = (k1 + np.uint64(PHILOX_W1)) & mask
+        p0 = np.uint64(PHILOX_M0) * c[0]
+        p1 = np.uint64(PHILOX_M1) * c[2]
+        c = [(p1 >> np.uint64(32)) ^ c[1] ^ k0, p1 & mask, (p0 >> np.uint64(32)) ^ c[3] ^ k1, p0 & mask]
+    return np.stack(c, axis=-1).astype(np.uint32)
+
+
+def dropout_threshold(p_drop: float) -> int:
+    """A weight is kept when its 16-bit random value is >= this (p quantised to 1/65536)."""
+    if not 0.0 <= p_drop < 1.0:
+        raise ValueError("the dropout probability must be in [0, 1)")
+    return min(65536, int(np.floor(p_drop * 65536.0 + 0.5)))
+
+
+def philox_keep(b: int, h: int, NH: int, T: int, p_drop: float, seed: int, offset: int) -> np.ndarray:
+    """Keep mask (T, T) of head (b, h): element (i, j) takes 16-bit value j % 8 of the
+    Philox4x32-10 output at counter (j // 8, i, b * NH + h, offset), key (seed mod 2^32,
+    seed // 2^32): output word (j % 8) // 2, low half for even j, high half for odd j; it is
+    kept iff that value >= dropout_threshold(p_drop)."""
+    i = np.arange(T, dtype=np.uint64)[:, None]
+    g = (np.arange((T + 7) // 8, dtype=np.uint64))[None, :]
+    ctr = np.stack(np.broadcast_arrays(g, i, np.uint64(b * NH + h), np.uint64(offset & 0xFFFFFFFF)), axis=-1)
+    x = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))  # (T, ngroups, 4)
+    u = np.empty((T, x.shape[1], 8), dtype=np.uint32)
+    for e in range(8):
+        u[:, :, e] = (x[:, :, e // 2] >> (16 * (e % 2))) & 0xFFFF
+    return (u.reshape(T, -1)[:, :T] >= dropout_threshold(p_drop))
+
+
+def attn_ref_dropout(q, k, v, do, p_drop: float, seed: int, offset: int, causal: bool,
+                     scale: Optional[float] = None, heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """Attention with dropout on the weights over (B, T, NH, d) tensors, the keep mask of
+    each head from philox_keep.  Returns the dict of attn_ref_bwd (o, lse, dq, dk, dv, D),
+    or for the selected `heads` {(b, h): {...}}."""
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    B, T, NH, dqk = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    br = _block_rows(T, dqk)
+
+    def one(b, h):
+        keep = philox_keep(b, h, NH, T, p_drop, seed, offset)
+        r = head_backward(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal, br, keep=keep,
+                          p_drop=p_drop)
+        return dict(zip(("dq", "dk", "dv", "o", "lse", "D"), r))
+
+    if heads is not None:
+        return {(int(b), int(h)): one(int(b), int(h)) for b, h in heads}
+    out = {"dq": np.empty((B, T, NH, dqk)), "dk": np.empty((B, T, NH, dqk)), "dv": np.empty((B, T, NH, v.shape[3])),
+           "o": np.empty((B, T, NH, v.shape[3])), "lse": np.empty((B, NH, T)), "D": np.empty((B, NH, T))}
+    for b in range(B):
+        for h in range(NH):
+            for name, x in one(b, h).items():
+                if name in ("lse", "D"):
+                    out[name][b, h] = x
+                else:
+                    out[name][b, :, h] = x
+    return out
+
+
 def attn_ref_varlen(q, k, v, do, seq_q, seq_k, causal: bool, scale: Optional[float] = None):
     """Padded batches: the padding mask with per-batch lengths seq_len_q and seq_len_kv
     among the SDPA options of [SA8 1.2].  Batch b uses query rows 0 .. seq_q[b]-1 and
@@ -448,7 +535,7 @@ def attn_ref_varlen(q, k, v, do, seq_q, seq_k, causal: bool, scale: Optional[flo
 
 
 def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, window: int = 0,
-                      alibi: bool = False, allowed=None, key_bias=None):
+                      alibi: bool = False, allowed=None, key_bias=None, keep=None, p_drop: float = 0.0):
     """Independent loop formulation for small T (T <= 64), written from the softmax
     Jacobian dy_i/dx_j = y_i (delta_ij - y_j) [SA8 2.1, A.3] and the per-(b, t, h)
     loop nest of the CPU reference in [SA8 2.2]:
@@ -471,6 +558,9 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
     key_bias: None, or a function key_bias(b, h, t2) added to preatt[t2]; the gradient
     with respect to it is dpreatt / scale (preatt is scale * q.k plus the bias), summed
     into dbias[b, h, t2], returned as a sixth value.
+    keep: None, or a predicate keep(b, h, t, t2) -> bool: dropout, the value path uses
+    att[t2] * z[t2] with z = keep / (1 - p_drop) (o and dv), and the gradient w.r.t. att
+    is datt[t2] * z[t2].
     Returns dq, dk, dv, o (B, T, NH, d) and lse (B, NH, T) in float64.
     """
     _check_window(causal, window, 1.0 if alibi else 0.0)
@@ -504,12 +594,14 @@ def attn_ref_bwd_loop(q, k, v, do, causal: bool, scale: Optional[float] = None, 
                 tot = sum(ex)
                 att = [e / tot for e in ex]
                 lse[b, h, t] = mx + np.log(tot)
+                z = [1.0 if keep is None else (1.0 / (1.0 - p_drop) if keep(b, h, t, t2) else 0.0)
+                     for t2 in range(last)]
                 for t2 in range(last):
-                    o[b, t, h] += att[t2] * v[b, t2, h]
-                # backward through O = att . V
-                datt = [float(np.dot(v[b, t2, h], do[b, t, h])) for t2 in range(last)]
+                    o[b, t, h] += att[t2] * z[t2] * v[b, t2, h]
+                # backward through O = (att z) . V
+                datt = [float(np.dot(v[b, t2, h], do[b, t, h])) * z[t2] for t2 in range(last)]
                 for t2 in range(last):
-                    dv[b, t2, h] += att[t2] * do[b, t, h]
+                    dv[b, t2, h] += att[t2] * z[t2] * do[b, t, h]
                 # backward through the softmax by its Jacobian
                 dpre = [0.0] * last
                 for t2 in range(last):

@@ -746,6 +746,103 @@ def pin_fp8_forward_zero_queries(ref):
     _close(lse[0], np.log(np.arange(1, 22))[None, :].repeat(2, 0), rtol=1e-14, atol=1e-15, what="fp8 LSE")
 
 
+# ---------------------------------------------------------------------------------
+# Dropout (the dropout option of [SA8 1.2]): Philox4x32-10 keep masks and inverted
+# dropout on the attention weights.
+# ---------------------------------------------------------------------------------
+def pin_philox_known_answers(ref):
+    """The published known-answer vectors of Philox4x32-10 (Random123's test vectors)."""
+    kat = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+           ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+           ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+            (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+    for ctr, key, want in kat:
+        got = ref.philox4x32_10(np.array([ctr], dtype=np.uint64), key)[0]
+        assert tuple(int(x) for x in got) == want, f"Philox4x32-10 {ctr}: {[hex(int(x)) for x in got]}"
+
+
+def _philox_scalar(ctr, key):
+    """Philox4x32-10 on Python integers: a second implementation for the keep-mask pin."""
+    c, k = list(ctr), list(key)
+    for r in range(10):
+        if r:
+            k = [(k[0] + 0x9E3779B9) & 0xFFFFFFFF, (k[1] + 0xBB67AE85) & 0xFFFFFFFF]
+        a, b = 0xD2511F53 * c[0], 0xCD9E8D57 * c[2]
+        c = [(b >> 32) ^ c[1] ^ k[0], b & 0xFFFFFFFF, (a >> 32) ^ c[3] ^ k[1], a & 0xFFFFFFFF]
+    return c
+
+
+def pin_keep_mask_element_by_element(ref):
+    """The keep mask against its definition evaluated one element at a time: element (i, j)
+    of head (b, h) is kept iff 16-bit value j % 8 of Philox4x32-10 at counter
+    (j // 8, i, b NH + h, offset), key (seed low, seed high) is >= round(p 65536)."""
+    NH, T, p, seed, offset = 3, 37, 0.3, 0x0123456789ABCDEF, 77
+    thr = int(np.floor(p * 65536 + 0.5))
+    rng = np.random.default_rng(5)
+    for b, h in ((0, 0), (1, 2)):
+        m = ref.philox_keep(b, h, NH, T, p, seed, offset)
+        for _ in range(60):
+            i, j = int(rng.integers(T)), int(rng.integers(T))
+            x = _philox_scalar((j // 8, i, b * NH + h, offset), (seed & 0xFFFFFFFF, seed >> 32))
+            u = (x[(j % 8) // 2] >> (16 * (j % 2))) & 0xFFFF
+            assert bool(m[i, j]) == (u >= thr), f"keep mask ({b},{h},{i},{j})"
+
+
+def pin_keep_fraction(ref):
+    """Kept fraction of a large mask within five standard deviations of 1 - p."""
+    for p in (0.1, 0.5, 0.9):
+        m = np.concatenate([ref.philox_keep(0, h, 4, 256, p, 1234, 5) for h in range(4)])
+        n = m.size
+        assert abs(m.mean() - (1 - p)) < 5 * np.sqrt(p * (1 - p) / n), f"keep fraction at p={p}: {m.mean()}"
+    assert ref.philox_keep(0, 0, 1, 64, 0.0, 1, 0).all(), "p = 0 keeps everything"
+
+
+def pin_dropout_zero_is_plain(ref):
+    """p = 0 keeps every weight: plain attention, exactly."""
+    q, k, v, do = _inputs(2, 23, 2, 16, 24, 921)
+    for causal in (False, True):
+        a = ref.attn_ref_bwd(q, k, v, do, causal)
+        b = ref.attn_ref_dropout(q, k, v, do, 0.0, 99, 0, causal)
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            _close(b[n], a[n], rtol=1e-15, atol=1e-15, what=f"dropout p=0 causal={causal} {n}")
+
+
+def pin_dropout_loops(ref):
+    """Matrix form against the scalar loop nest with the keep mask in the value path."""
+    q, k, v, do = _inputs(2, 19, 2, 8, 16, 923)
+    p, seed, off = 0.35, 0xDEADBEEF12345, 3
+    masks = {(b, h): ref.philox_keep(b, h, 2, 19, p, seed, off) for b in range(2) for h in range(2)}
+    for causal in (False, True):
+        dq, dk, dv, o, lse = ref.attn_ref_bwd_loop(q, k, v, do, causal, keep=lambda b, h, t, t2: masks[(b, h)][t, t2],
+                                                  p_drop=p)
+        r = ref.attn_ref_dropout(q, k, v, do, p, seed, off, causal)
+        for n, x in (("dq", dq), ("dk", dk), ("dv", dv), ("o", o), ("lse", lse)):
+            _close(r[n], x, rtol=1e-12, atol=1e-14, what=f"dropout causal={causal} loop form {n}")
+
+
+def pin_dropout_finite_differences(ref, h: float = 1e-6):
+    """With the mask held fixed, dQ, dK, dV equal central differences of sum(O * dO)."""
+    q, k, v, do = _inputs(1, 12, 1, 8, 8, 925)
+    p, seed, off = 0.4, 42, 9
+    r = ref.attn_ref_dropout(q, k, v, do, p, seed, off, True)
+
+    def f(qq, kk, vv):
+        return float(np.sum(ref.attn_ref_dropout(qq, kk, vv, do, p, seed, off, True)["o"] * do))
+
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        g = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if n == name else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+            args_m = [xm if n == name else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+            g[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        _close(r[name], g, rtol=1e-6, atol=1e-8, what=f"dropout finite differences {name}")
+
+
 ALL_PINS = [
     ("finite_differences_causal", lambda r: pin_finite_differences(r, True)),
     ("finite_differences_full", lambda r: pin_finite_differences(r, False)),
@@ -794,6 +891,12 @@ ALL_PINS = [
     ("e4m3_code_points", pin_e4m3_code_points),
     ("e4m3_library", pin_e4m3_library),
     ("fp8_forward_zero_queries", pin_fp8_forward_zero_queries),
+    ("philox_known_answers", pin_philox_known_answers),
+    ("keep_mask_element_by_element", pin_keep_mask_element_by_element),
+    ("keep_fraction", pin_keep_fraction),
+    ("dropout_zero_is_plain", pin_dropout_zero_is_plain),
+    ("dropout_loops", pin_dropout_loops),
+    ("finite_differences_dropout", pin_dropout_finite_differences),
     ("alibi_slopes", pin_alibi_slopes),
     ("alibi_zero_queries", pin_alibi_zero_queries),
     ("alibi_loops", pin_alibi_loops),

@@ -51,7 +51,7 @@ def test_selected_heads_match_full_run():
 MUTANTS = {
     "drop_D_term": ("dS = P * (dP - Dr[:, None])", "dS = P * dP"),
     "dS_sign": ("dS = P * (dP - Dr[:, None])", "dS = P * (Dr[:, None] - dP)"),
-    "dV_untransposed": ("dV[:nk] += P.T @ do[r0:r1]", "dV[:nk] += P @ do[r0:r1]"),
+    "dV_untransposed": ("dV[:nk] += Pk.T @ do[r0:r1]", "dV[:nk] += Pk @ do[r0:r1]"),
     "dQ_no_scale": ("dQ[r0:r1] = scale * (dS @ k[:nk])", "dQ[r0:r1] = (dS @ k[:nk])"),
     "dK_no_scale": ("dK[:nk] += scale * (dS.T @ q[r0:r1])", "dK[:nk] += (dS.T @ q[r0:r1])"),
     "dK_uses_k": ("dK[:nk] += scale * (dS.T @ q[r0:r1])", "dK[:nk] += scale * (dS.T @ k[r0:r1])"),
@@ -67,10 +67,10 @@ MUTANTS = {
     "window_off_by_one": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = np.where(qi - kj > window, -np.inf, S)"),
     "window_ignored": ("S = np.where(qi - kj >= window, -np.inf, S)", "S = S"),
     "alibi_sign": ("S = S - slope * (qi - kj)", "S = S + slope * (qi - kj)"),
-    "keybias_sign": ("            S = S + key_bias[None, :nk]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n        dV",
-                     "            S = S - key_bias[None, :nk]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n        dV"),
-    "keybias_on_queries": ("            S = S + key_bias[None, :nk]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n        dV",
-                           "            S = S + key_bias[r0:r1, None]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        O[r0:r1] = P @ v[:nk]\n        dV"),
+    "keybias_sign": ("            S = S + key_bias[None, :nk]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        Pk = P if keep is None",
+                     "            S = S - key_bias[None, :nk]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        Pk = P if keep is None"),
+    "keybias_on_queries": ("            S = S + key_bias[None, :nk]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        Pk = P if keep is None",
+                           "            S = S + key_bias[r0:r1, None]\n        allowed = _block_allowed(block_map, block, r0, r1, nk)\n        if allowed is not None:\n            S = np.where(allowed, S, -np.inf)\n        P, lse[r0:r1] = _softmax_rows_or_empty(S)\n        Pk = P if keep is None"),
     "dbias_from_dP": ("dbias[:nk] += dS.sum(axis=0)", "dbias[:nk] += dP.sum(axis=0)"),
     "dbias_scaled": ("dbias[:nk] += dS.sum(axis=0)", "dbias[:nk] += scale * dS.sum(axis=0)"),
     "dbias_shared_not_summed": ('out["dbias"][b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0] += x',
@@ -79,6 +79,16 @@ MUTANTS = {
     "e4m3_no_subnormals": ("np.where(e == 0, m / 8.0 * 2.0 ** -6,", "np.where(e == 0, 0.0 * m,"),
     "e4m3_mantissa_quarters": ("(1.0 + m / 8.0) * np.exp2", "(1.0 + m / 4.0) * np.exp2"),
     "fp8_descale_v_dropped": ("    v = e4m3_to_f64(v8) * descale_v\n", "    v = e4m3_to_f64(v8)\n"),
+    "dropout_no_rescale": ("Pk = P if keep is None else P * (keep[r0:r1, :nk] / (1.0 - p_drop))",
+                           "Pk = P if keep is None else P * keep[r0:r1, :nk]"),
+    "dropout_dP_unmasked": ("            dP = dP * (keep[r0:r1, :nk] / (1.0 - p_drop))  # through the dropout",
+                            "            dP = dP / (1.0 - p_drop)  # through the dropout"),
+    "philox_bump_first_round": ("        if r > 0:\n            k0 = (k0 + np.uint64(PHILOX_W0)) & mask",
+                                "        if r >= 0:\n            k0 = (k0 + np.uint64(PHILOX_W0)) & mask"),
+    "philox_swapped_words": ("c = [(p1 >> np.uint64(32)) ^ c[1] ^ k0, p1 & mask,", "c = [p1 & mask, (p1 >> np.uint64(32)) ^ c[1] ^ k0,"),
+    "keep_counter_fields_swapped": ("np.broadcast_arrays(g, i, np.uint64(b * NH + h)", "np.broadcast_arrays(i, g, np.uint64(b * NH + h)"),
+    "keep_halves_swapped": ("u[:, :, e] = (x[:, :, e // 2] >> (16 * (e % 2))) & 0xFFFF",
+                            "u[:, :, e] = (x[:, :, e // 2] >> (16 * (1 - e % 2))) & 0xFFFF"),
     "blocksparse_map_transposed": ("return np.asarray(block_map)[qi[:, None], kj[None, :]] != 0",
                                    "return np.asarray(block_map).T[qi[:, None], kj[None, :]] != 0"),
     "blocksparse_block_index_off": ("qi = np.arange(r0, r1) // block", "qi = np.arange(r0 + 1, r1 + 1) // block"),
