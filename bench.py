@@ -107,7 +107,10 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
     while done < len(all_heads) and t_total < seconds_budget * 0.5:
         hd = all_heads[done]
         t0 = time.perf_counter()
-        if w.name == "keybias":
+        if w.name == "dropout":
+            attn_ref.attn_ref_dropout(cpu["q"], cpu["k"], cpu["v"], cpu["do"], workloads.DROPOUT_P, w.seed, 0, w.causal,
+                                      w.scale, heads=[hd])
+        elif w.name == "keybias":
             attn_ref.attn_ref_keybias(cpu["q"], cpu["k"], cpu["v"], cpu["do"], workloads.key_bias(w), w.causal,
                                       w.scale, heads=[hd])
         elif w.name == "blocksparse":
@@ -440,6 +443,9 @@ def main():
 
     bsp = w.name == "blocksparse"
     kbw = w.name == "keybias"
+    drw = w.name == "dropout"
+    if drw:  # the keep bits are drawn inside every timed step (before the forward)
+        dmask = attn.dropout_mask(workloads.DROPOUT_P, w.seed, 0, B, NH, T, w.causal, device=dev)
     if kbw:
         kbias = torch.from_numpy(workloads.key_bias(w)).to(dev)
         dbias = torch.empty_like(kbias)
@@ -451,7 +457,10 @@ def main():
                           device=dev)
 
     def fwd_call():
-        if kbw:
+        if drw:
+            attn.dropout_mask(workloads.DROPOUT_P, w.seed, 0, B, NH, T, w.causal, device=dev, out=dmask)
+            attn.fwd_dropout(q, k, v, dmask, workloads.DROPOUT_P, w.causal, w.scale, out=o, lse=lse)
+        elif kbw:
             attn.fwd_keybias(q, k, v, kbias, w.causal, w.scale, out=o, lse=lse, workspace=fws)
         elif bsp:
             attn.fwd_blocksparse(q, k, v, bmap, w.causal, w.scale, out=o, lse=lse, workspace=fws)
@@ -459,7 +468,10 @@ def main():
             attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse, window=w.window, alibi=w.alibi)
 
     def bwd_call(mode_det, ws, stages):
-        if kbw:
+        if drw:
+            attn.bwd_dropout(q, k, v, o, lse, do, dmask, workloads.DROPOUT_P, w.causal, w.scale, mode_det, dq=dq, dk=dk,
+                             dv=dv, workspace=ws, stages=stages)
+        elif kbw:
             attn.bwd_keybias(q, k, v, o, lse, do, kbias, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv,
                              dbias=dbias, workspace=ws, stages=stages)
         elif bsp:
@@ -547,7 +559,8 @@ def main():
                         f"{'causal' if w.causal else 'non-causal'}"
                         f"{f' window {w.window}' if w.window else ''}{' ALiBi' if w.alibi else ''}"
                         f"{' block-sparse map (local band of 8 blocks + block 0)' if w.name == 'blocksparse' else ''}"
-                        f"{' per-head key bias with dbias' if w.name == 'keybias' else ''}, "
+                        f"{' per-head key bias with dbias' if w.name == 'keybias' else ''}"
+                        f"{f' dropout p={workloads.DROPOUT_P} (Philox keep bits drawn each step)' if w.name == 'dropout' else ''}, "
                         f"{'packed QKV' if w.packed else 'BTHD'}, "
                         f"dQ mode {args.dq_mode}",
             "B": B, "NH": NH, "T": T, "d_qk": w.d_qk, "d_v": w.d_v, "causal": w.causal, "window": w.window, "alibi": w.alibi,

@@ -28,7 +28,7 @@ import torch
 __all__ = [
     "AttnError", "lib_path", "load", "fwd", "fwd_packed", "bwd", "bwd_packed",
     "workspace_bytes", "fwd_varlen", "bwd_varlen", "fwd_decode", "bwd_noalloc", "fwd_blocksparse", "bwd_blocksparse", "BS_BLOCK",
-    "fwd_keybias", "bwd_keybias", "fwd_fp8", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
+    "fwd_keybias", "bwd_keybias", "fwd_fp8", "dropout_mask", "fwd_dropout", "bwd_dropout", "PREPROCESS", "MAIN", "DQ", "ALL_STAGES", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -110,6 +110,14 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_fp8_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_fwd_fp8.restype = i
     lib.attn_fwd_fp8.argtypes = [vp, S, vp, S, vp, S, vp, S, vp, f, f, f, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_dropout_mask_bytes.restype = sz
+    lib.attn_dropout_mask_bytes.argtypes = [i, i, i]
+    lib.attn_dropout_mask.restype = i
+    lib.attn_dropout_mask.argtypes = [f, ctypes.c_uint64, ctypes.c_uint32, i, i, i, i, vp, sz, vp]
+    lib.attn_fwd_dropout.restype = i
+    lib.attn_fwd_dropout.argtypes = [vp, S, vp, S, vp, S, vp, S, vp, vp, f, i, i, i, i, i, f, i, vp]
+    lib.attn_bwd_dropout.restype = i
+    lib.attn_bwd_dropout.argtypes = bwd_args[:17] + [vp, f] + bwd_args[17:] + [ctypes.c_uint]
     lib.attn_bwd_noalloc.restype = i
     lib.attn_bwd_noalloc.argtypes = bwd_args[:25] + [vp]
     lib.attn_bwd_noalloc_max_workspace_bytes.restype = sz
@@ -534,6 +542,103 @@ def fwd_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float, causa
                                 float(descale_v), B, NH, T, dqk, dv, float(scale), int(bool(causal)),
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev)))
     return out, (lse if return_lse else None)
+
+
+def dropout_mask(p_drop: float, seed: int, offset: int, B: int, NH: int, T: int, causal: bool = True,
+                 device=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The keep bits of dropout with probability p_drop for one step (Philox4x32-10 at
+    counter (key / 8, query, b * NH + h, offset), key seed): a uint8 buffer of both bit
+    layouts, to be passed to fwd_dropout and bwd_dropout."""
+    lib = load()
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    _on_gpu("dropout_mask", dev)
+    need = int(lib.attn_dropout_mask_bytes(B, NH, T))
+    if need == 0:
+        raise ValueError("invalid sizes for a dropout mask")
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_dropout_mask(float(p_drop), int(seed) & (2 ** 64 - 1), int(offset) & 0xFFFFFFFF, B, NH, T,
+                                     int(bool(causal)), out.data_ptr(), out.numel(), _stream(dev)))
+    return out
+
+
+def fwd_dropout(q, k, v, mask: torch.Tensor, p_drop: float, causal: bool = True, scale: Optional[float] = None,
+                return_lse: bool = True, layout: str = "bthd", out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None):
+    """Forward with dropout on the attention weights (bf16), the keep bits from dropout_mask
+    (same p_drop, causal flag and sizes).  Returns (o, lse); LSE is that of the undropped
+    weights."""
+    B, NH, T, dqk = _dims(q, layout)
+    dv = v.shape[-1]
+    _shape(k, "k", layout, B, NH, T, dqk)
+    _shape(v, "v", layout, B, NH, T, dv)
+    if out is not None:
+        _shape(out, "out", layout, B, NH, T, dv)
+    dev = q.device
+    _on_gpu("fwd_dropout", dev)
+    lib = load()
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, n, dev, torch.bfloat16)
+    if mask.dtype != torch.uint8 or mask.device != dev or mask.numel() < int(lib.attn_dropout_mask_bytes(B, NH, T)):
+        raise ValueError("mask must be the uint8 buffer from dropout_mask for these sizes, on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        shape = (B, T, NH, dv) if layout == "bthd" else (B, NH, T, dv)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", dev, torch.bfloat16)
+    if return_lse and lse is None:
+        lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    with torch.cuda.device(dev):
+        _check(lib.attn_fwd_dropout(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                                    v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
+                                    lse.data_ptr() if return_lse else None, mask.data_ptr(), float(p_drop),
+                                    B, NH, T, dqk, dv, float(scale), int(bool(causal)), _stream(dev)))
+    return out, (lse if return_lse else None)
+
+
+def bwd_dropout(q, k, v, o, lse, do, mask: torch.Tensor, p_drop: float, causal: bool = True,
+                scale: Optional[float] = None, deterministic: bool = False, layout: str = "bthd",
+                dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None, stages: int = ALL_STAGES):
+    """Backward with the forward's dropout mask and p_drop (bf16).  Returns (dq, dk, dv)."""
+    B, NH, T, dqk = _dims(q, layout)
+    dvd = v.shape[-1]
+    for n, x, d in (("k", k, dqk), ("v", v, dvd), ("o", o, dvd), ("do", do, dvd), ("dq", dq, dqk), ("dk", dk, dqk),
+                    ("dv", dv, dvd)):
+        if x is not None:
+            _shape(x, n, layout, B, NH, T, d)
+    dev = q.device
+    _on_gpu("bwd_dropout", dev)
+    lib = load()
+    for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _need(x, n, dev, torch.bfloat16)
+    if mask.dtype != torch.uint8 or mask.device != dev or mask.numel() < int(lib.attn_dropout_mask_bytes(B, NH, T)):
+        raise ValueError("mask must be the uint8 buffer from dropout_mask for these sizes, on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(x, n, dev, torch.bfloat16)
+    need = workspace_bytes(B, NH, T, dqk, dvd, deterministic)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.attn_bwd_dropout(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
+                                    v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
+                                    lse.data_ptr(), do.data_ptr(), _strides(do, layout),
+                                    dq.data_ptr(), _strides(dq, layout), dk.data_ptr(), _strides(dk, layout),
+                                    dv.data_ptr(), _strides(dv, layout), mask.data_ptr(), float(p_drop),
+                                    B, NH, T, dqk, dvd, float(scale), int(bool(causal)), int(bool(deterministic)),
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream(dev), int(stages)))
+    return dq, dk, dv
 
 
 def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, causal: bool = True, scale: Optional[float] = None,

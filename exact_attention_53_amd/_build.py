@@ -20,13 +20,14 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 # Each backward launcher configuration (kernel, element type, head dims, mask) is one
 # compilation of attn_bwd_inst.hip, so that they compile in parallel.
 # Masks: 0 none, 1 causal, 2 causal + sliding window, 3 causal + ALiBi, 4 block-sparse map,
-# 5 block-sparse map + causal, 6 key bias, 7 key bias + causal (4-7 bf16 only).
+# 5 block-sparse map + causal, 6 key bias, 7 key bias + causal, 8 dropout, 9 dropout + causal
+# (4-9 bf16 only).
 INSTANCES = [(kind, elem, dqk, dv, mask) for kind in ("kv", "dq") for elem in ("bf16", "f16")
-             for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in range(8)
+             for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in range(10)
              if mask < 4 or elem == "bf16"]
-MASK_NAMES = ("full", "causal", "window", "alibi", "bsp", "bsp_causal", "kbias", "kbias_causal")
+MASK_NAMES = ("full", "causal", "window", "alibi", "bsp", "bsp_causal", "kbias", "kbias_causal", "drop", "drop_causal")
 SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_plan.hip", "attn_blocksparse.hip", "attn_bias.hip",
-           "attn_api.cpp"]
+           "attn_dropout.hip", "attn_api.cpp"]
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU instructions.
 FLAGS = [

@@ -163,6 +163,28 @@ attn_status check_kbias(const KbArgs& kb, int B, int NH, int T) {
 
 size_t kb_ws_bytes(int B, int NH, int T) { return align256((size_t)B * NH * tpad(T) * 4); }
 
+// Dropout of a call (mask == nullptr: none): the keep bits written by attn_dropout_mask.
+struct DrArgs {
+  const void* mask;
+  float p;
+};
+
+int64_t drop_tp(int T) { return ((int64_t)T + 127) / 128 * 128; }
+
+size_t drop_mask_bytes(int B, int NH, int T) {
+  const int64_t tp = drop_tp(T);
+  return (size_t)2 * B * NH * tp * (tp / 8);
+}
+
+attn_status check_dropout(const DrArgs& d, int B, int NH, int T, Extent* ext) {
+  if (d.mask == nullptr) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(d.mask) % 16 != 0) return ATTN_ERR_ALIGN;
+  if (!std::isfinite(d.p) || d.p < 0.f || d.p >= 1.f) return ATTN_ERR_ARG;
+  ext->lo = reinterpret_cast<uintptr_t>(d.mask);
+  ext->hi = ext->lo + drop_mask_bytes(B, NH, T);
+  return ATTN_OK;
+}
+
 // Validates a block-sparse map and returns its byte extent.
 attn_status check_map(const BsArgs& bs, int B, int NH, int T, Extent* ext) {
   if (bs.map == nullptr) return ATTN_ERR_NULL;
@@ -179,15 +201,17 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
                      const void* v, attn_strides sv, void* o, attn_strides so, float* lse, const int32_t* seq_q,
                      const int32_t* seq_k, int B, int NH, int T, int d_qk, int d_v, float scale, int causal,
                      int window, int alibi, void* workspace, size_t workspace_bytes, void* stream,
-                     const BsArgs* bs = nullptr, const KbArgs* kb = nullptr) {
+                     const BsArgs* bs = nullptr, const KbArgs* kb = nullptr, const DrArgs* dr = nullptr) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
   if (!window_ok(window, alibi, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
-  if ((bs != nullptr || kb != nullptr) &&
+  if ((bs != nullptr || kb != nullptr || dr != nullptr) &&
       (window != 0 || alibi != 0 || seq_q != nullptr || seq_k != nullptr || et != attn53::ELEM_BF16))
     return ATTN_ERR_ARG;
   if (kb != nullptr && (st = check_kbias(*kb, B, NH, T)) != ATTN_OK) return st;
+  Extent edr{0, 0};
+  if (dr != nullptr && (st = check_dropout(*dr, B, NH, T, &edr)) != ATTN_OK) return st;
   Extent eq, ek, ev, eo;
   if ((st = check_tensor(q, sq, B, NH, T, d_qk, &eq)) != ATTN_OK) return st;
   if ((st = check_tensor(k, sk, B, NH, T, d_qk, &ek)) != ATTN_OK) return st;
@@ -202,6 +226,7 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
     if (overlaps(el, eq) || overlaps(el, ek) || overlaps(el, ev) || overlaps(el, eo)) return ATTN_ERR_ALIAS;
   }
   const bool varlen = seq_q != nullptr || seq_k != nullptr;
+  if (dr != nullptr && (overlaps(eo, edr) || (lse != nullptr && overlaps(el, edr)))) return ATTN_ERR_ALIAS;
   Extent em{0, 0};
   if (bs != nullptr) {
     if ((st = check_map(*bs, B, NH, T, &em)) != ATTN_OK) return st;
@@ -255,6 +280,11 @@ attn_status fwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
     p.kbias = kbs;
     p.kbias_ld = (int)tpad(T);
   }
+  if (dr != nullptr) {
+    p.drop_rows = static_cast<const unsigned char*>(dr->mask);
+    p.drop_ld = (int)(drop_tp(T) / 8);
+    p.drop_scale = 1.f / (1.f - dr->p);
+  }
   return hip_status(attn53::launch_fwd(p, et, d_qk, d_v, causal != 0, s));
 }
 
@@ -278,17 +308,19 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
                      void* dv, attn_strides sdv, const int32_t* seq_q, const int32_t* seq_k, int B, int NH, int T,
                      int d_qk, int d_v, float scale, int causal, int window, int alibi, int deterministic,
                      void* workspace, size_t workspace_bytes, void* stream, unsigned stages,
-                     const BsArgs* bs = nullptr, const KbArgs* kb = nullptr) {
+                     const BsArgs* bs = nullptr, const KbArgs* kb = nullptr, const DrArgs* dr = nullptr) {
   attn_status st = check_sizes(B, NH, T, d_qk, d_v);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1) ||
       (deterministic != 0 && deterministic != 1))
     return ATTN_ERR_ARG;
   if (!window_ok(window, alibi, causal, seq_q, seq_k)) return ATTN_ERR_ARG;
-  if ((bs != nullptr || kb != nullptr) &&
+  if ((bs != nullptr || kb != nullptr || dr != nullptr) &&
       (window != 0 || alibi != 0 || seq_q != nullptr || seq_k != nullptr || et != attn53::ELEM_BF16))
     return ATTN_ERR_ARG;
   if (kb != nullptr && (st = check_kbias(*kb, B, NH, T)) != ATTN_OK) return st;
+  Extent edr{0, 0};
+  if (dr != nullptr && (st = check_dropout(*dr, B, NH, T, &edr)) != ATTN_OK) return st;
   if (stages == 0 || (stages & ~ATTN_BWD_ALL) != 0) return ATTN_ERR_ARG;
   const bool varlen = seq_q != nullptr || seq_k != nullptr;
   if (varlen) {
@@ -313,6 +345,7 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
   Extent em{0, 0};
   if (bs != nullptr && (st = check_map(*bs, B, NH, T, &em)) != ATTN_OK) return st;
   if (kb != nullptr) em = f32_extent(kb->bias, kb->sb, kb->sh, B, NH, T);
+  if (dr != nullptr) em = edr;  // the mask is an input like the others
   const size_t need = bwd_ws_bytes(B, NH, T, d_qk, d_v, deterministic, varlen, bs != nullptr, kb != nullptr);
   if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || workspace_bytes < need)
     return ATTN_ERR_WORKSPACE;
@@ -382,6 +415,14 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
       if ((st = bs_build(*bs, B, NH, T, 2, group, causal, lists, &p.bs_dq, &used, s)) != ATTN_OK) return st;
     }
     p.bsp = 1;
+  }
+  if (dr != nullptr) {
+    const int64_t tp = drop_tp(T);
+    p.drop_rows = static_cast<const unsigned char*>(dr->mask);
+    p.drop_cols = p.drop_rows + (int64_t)B * NH * tp * (tp / 8);
+    p.drop_ld = (int)(tp / 8);
+    p.drop_tp = (int)tp;
+    p.drop_scale = 1.f / (1.f - dr->p);
   }
   if (kb != nullptr) {  // the bias in score units (read by both kernels), the per-head dbias sums
     float* kbs = reinterpret_cast<float*>(ws + off);
@@ -502,6 +543,52 @@ attn_status attn_fwd_blocksparse(const void* q, attn_strides sq, const void* k, 
   const BsArgs bs{block_map, map_stride_b, map_stride_h};
   return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale,
                   causal, 0, 0, workspace, workspace_bytes, stream, &bs);
+}
+
+size_t attn_dropout_mask_bytes(int B, int NH, int T) {
+  if (B < 1 || NH < 1 || T < 1 || (int64_t)B * NH * ((int64_t)T + kRowPad) > (int64_t)INT32_MAX) return 0;
+  const int64_t tp = drop_tp(T);
+  if ((int64_t)B * NH * (tp / 64) * (tp / 128) > (int64_t)INT32_MAX) return 0;  // the mask kernel's grid
+  return drop_mask_bytes(B, NH, T);
+}
+
+attn_status attn_dropout_mask(float p_drop, uint64_t seed, uint32_t offset, int B, int NH, int T, int causal,
+                              void* mask, size_t mask_bytes, void* stream) {
+  const size_t need = attn_dropout_mask_bytes(B, NH, T);
+  if (need == 0) return ATTN_ERR_SHAPE;
+  if (!std::isfinite(p_drop) || p_drop < 0.f || p_drop >= 1.f || (causal != 0 && causal != 1)) return ATTN_ERR_ARG;
+  if (mask == nullptr) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(mask) % 16 != 0) return ATTN_ERR_ALIGN;
+  if (mask_bytes < need) return ATTN_ERR_WORKSPACE;
+  attn53::DropoutMaskParams p{};
+  p.mask = static_cast<unsigned char*>(mask);
+  p.B = B; p.NH = NH; p.Tp = (int)drop_tp(T); p.causal = causal;
+  p.offset = offset;
+  p.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  p.key1 = (uint32_t)(seed >> 32);
+  const double thr = std::floor((double)p_drop * 65536.0 + 0.5);
+  p.threshold = (uint32_t)(thr > 65536.0 ? 65536.0 : thr);
+  return hip_status(attn53::launch_dropout_mask(p, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_dropout(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                             attn_strides sv, void* o, attn_strides so, float* lse, const void* mask, float p_drop,
+                             int B, int NH, int T, int d_qk, int d_v, float scale, int causal, void* stream) {
+  const DrArgs dr{mask, p_drop};
+  return fwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, nullptr, nullptr, B, NH, T, d_qk, d_v, scale,
+                  causal, 0, 0, nullptr, 0, stream, nullptr, nullptr, &dr);
+}
+
+attn_status attn_bwd_dropout(const void* q, attn_strides sq, const void* k, attn_strides sk, const void* v,
+                             attn_strides sv, const void* o, attn_strides so, const float* lse, const void* do_,
+                             attn_strides sdo, void* dq, attn_strides sdq, void* dk, attn_strides sdk, void* dv,
+                             attn_strides sdv, const void* mask, float p_drop, int B, int NH, int T, int d_qk,
+                             int d_v, float scale, int causal, int deterministic, void* workspace,
+                             size_t workspace_bytes, void* stream, unsigned stages) {
+  const DrArgs dr{mask, p_drop};
+  return bwd_impl(attn53::ELEM_BF16, q, sq, k, sk, v, sv, o, so, lse, do_, sdo, dq, sdq, dk, sdk, dv, sdv, nullptr,
+                  nullptr, B, NH, T, d_qk, d_v, scale, causal, 0, 0, deterministic, workspace, workspace_bytes,
+                  stream, stages, nullptr, nullptr, &dr);
 }
 
 size_t fp8_vt_ld(int T) { return ((size_t)T + 63) / 64 * 64; }

@@ -30,10 +30,11 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int 
 
 // mask mode of the launchers: 0 none, 1 causal, 2 causal with a sliding window, 3 causal
 // with the ALiBi bias, 4 block-sparse map, 5 block-sparse map and causal, 6 key bias,
-// 7 key bias and causal
+// 7 key bias and causal, 8 dropout, 9 dropout and causal
 static inline int mask_mode(const BwdParams& p, bool causal) {
   if (p.bsp) return causal ? 5 : 4;
   if (p.kbias != nullptr) return causal ? 7 : 6;
+  if (p.drop_rows != nullptr) return causal ? 9 : 8;
   return !causal ? 0 : p.win < kNoWindow ? 2 : p.alibi ? 3 : 1;
 }
 
@@ -50,7 +51,9 @@ static hipError_t main_m(const BwdParams& p, bool causal, bool det, hipStream_t 
           case 4: return bwd_main_t<E, DQK, DV, 4>(p, det, s);
           case 5: return bwd_main_t<E, DQK, DV, 5>(p, det, s);
           case 6: return bwd_main_t<E, DQK, DV, 6>(p, det, s);
-          default: return bwd_main_t<E, DQK, DV, 7>(p, det, s);
+          case 7: return bwd_main_t<E, DQK, DV, 7>(p, det, s);
+          case 8: return bwd_main_t<E, DQK, DV, 8>(p, det, s);
+          default: return bwd_main_t<E, DQK, DV, 9>(p, det, s);
         }
       } else {
         return hipErrorInvalidValue;
@@ -85,7 +88,9 @@ static hipError_t dq_m(const BwdParams& p, bool causal, hipStream_t s) {
           case 4: return bwd_dq_t<E, DQK, DV, 4>(p, s);
           case 5: return bwd_dq_t<E, DQK, DV, 5>(p, s);
           case 6: return bwd_dq_t<E, DQK, DV, 6>(p, s);
-          default: return bwd_dq_t<E, DQK, DV, 7>(p, s);
+          case 7: return bwd_dq_t<E, DQK, DV, 7>(p, s);
+          case 8: return bwd_dq_t<E, DQK, DV, 8>(p, s);
+          default: return bwd_dq_t<E, DQK, DV, 9>(p, s);
         }
       } else {
         return hipErrorInvalidValue;

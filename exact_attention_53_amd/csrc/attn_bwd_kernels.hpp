@@ -179,7 +179,7 @@ struct KvPlan {
 // KBIAS: a per-key bias (p.kbias) on the scores; each lane's key is fixed, so the bias is
 // one register, and the lane sums dS over the queries for dbias (p.dbias_part).
 template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool ATOMIC_DQ, bool BSP = false,
-          bool KBIAS = false>
+          bool KBIAS = false, bool DROP = false>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 64 ? 2 : 1, DQK == 64 ? 2 : 1))) void bwd_kv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
@@ -344,8 +344,9 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
 
   // One query block.  MASKED: the block touches the diagonal or a ragged edge.  The
   // body is one basic block in source order S, dP, P, dV, dS, dK so that the matrix
-  // work of dP and dV can run beside the VALU work of P and dS.
-  auto step_body = [&](int q0, auto bufc, auto maskc) {
+  // work of dP and dV can run beside the VALU work of P and dS.  keepc (dropout): this
+  // lane's key's keep bits for the block's 64 queries (bit k of word k / 32).
+  auto step_body = [&](int q0, auto bufc, auto maskc, const u32x2& keepc) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASKED = decltype(maskc)::value;
     ATTN_LDS char* st_cur = (ATTN_LDS char*)((ST_DOUBLE && BUF) ? st1 : st0);
@@ -400,7 +401,10 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
           }
         }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) pb[m] = pack8<E>(s[m >> 1], m & 1);
+      for (int m = 0; m < 4; ++m) {
+        pb[m] = pack8<E>(s[m >> 1], m & 1);
+        if constexpr (DROP) pb[m] = drop8(pb[m], keep_bits8(keepc[m >> 1], m & 1, g));
+      }
       // dV += P^T dO  (contraction over the 64 queries)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -414,7 +418,9 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
           const f32x4 Dd = *reinterpret_cast<const f32x4*>(db + 32 * t + 8 * a + 4 * g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            dp[t][4 * a + e] = s[t][4 * a + e] * (dp[t][4 * a + e] - Dd[e]);
+            float dpk = dp[t][4 * a + e];
+            if constexpr (DROP) dpk = ((keepc[t] >> (8 * a + 4 * g + e)) & 1u) ? dpk * p.drop_scale : 0.f;
+            dp[t][4 * a + e] = s[t][4 * a + e] * (dpk - Dd[e]);
             if constexpr (KBIAS) dbacc[t] += dp[t][4 * a + e];
           }
         }
@@ -451,9 +457,10 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
         constexpr int grp = o / 18, k = o % 18, t = grp & 1;
         constexpr int h = k < 9 ? 0 : 1, r = k < 8 ? k : k - 1;
         if constexpr (grp < 2) {
-          if constexpr (Plan::is_pack(o))
+          if constexpr (Plan::is_pack(o)) {
             pb[2 * t + h] = pack8<E>(pv[t], h);
-          else
+            if constexpr (DROP) pb[2 * t + h] = drop8(pb[2 * t + h], keep_bits8(keepc[t], h, g));
+          } else
           {
             if constexpr (ALIBI) {
               const float bias = __builtin_fmaf(-ml, (float)(32 * t + 8 * (r >> 2) + (r & 3)), ab);
@@ -468,7 +475,9 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
           if constexpr (Plan::is_pack(o))
             sb[2 * t + h] = pack8<E>(dsv[t], h);
           else {
-            dsv[t][r] = pv[t][r] * (dp[t][r] - ddv[t][r >> 2][r & 3]);
+            float dpk = dp[t][r];
+            if constexpr (DROP) dpk = ((keepc[t] >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u) ? dpk * p.drop_scale : 0.f;
+            dsv[t][r] = pv[t][r] * (dpk - ddv[t][r >> 2][r & 3]);
             if constexpr (KBIAS) dbacc[t] += dsv[t][r];
           }
         }
@@ -524,11 +533,16 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
     const int q0 = qb * BWD_BM;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads (and its atomics of the step before) are done
     __syncthreads();                // every wave's tiles are in; the other buffers are free
+    // dropout keep bits of this lane's key for the block's 64 queries, read before the next
+    // step's loads so that waiting for them leaves those in flight
+    u32x2 keepc = {0u, 0u};
+    if constexpr (DROP)
+      keepc = *reinterpret_cast<const u32x2*>(p.drop_cols + ((int64_t)bh * p.drop_tp + my_key) * p.drop_ld + q0 / 8);
     if (it + 1 < n_q) load_step(qstep(it + 1), std::integral_constant<int, 1 - BUF>{});
     if constexpr (ATOMIC_DQ) {
       if (it > 0) dq_partial((const ATTN_LDS char*)((ST_DOUBLE && !BUF) ? st1 : st0), qstep(it - 1) * BWD_BM);
     }
-    step_body(q0, bufc, maskc);
+    step_body(q0, bufc, maskc, keepc);
   };
   // The steps that touch the diagonal (the first BWD_BN / BWD_BM under the causal mask),
   // a ragged key block (all steps) or the ragged last query block carry the mask; they
@@ -588,7 +602,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
 #pragma unroll
       for (int t = 0; t < NDK; ++t) dkg[(int64_t)key * p.sdk.t + 32 * t + lq] = (E)(dk[t][r] * p.scale);
 #pragma unroll
-      for (int t = 0; t < NDV; ++t) dvg[(int64_t)key * p.sdv.t + 32 * t + lq] = (E)dv[t][r];
+      for (int t = 0; t < NDV; ++t) dvg[(int64_t)key * p.sdv.t + 32 * t + lq] = (E)(DROP ? dv[t][r] * p.drop_scale : dv[t][r]);
     }
   }
 }
@@ -686,7 +700,8 @@ struct DqShape {
 // descending; a wavefront computes only on the tiles live for its own rows.  KBIAS: a
 // per-key bias (p.kbias) on the scores, 64 values per key tile in LDS; every tile then
 // runs the plain (compiler-scheduled) tile body.
-template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool BSP = false, bool KBIAS = false>
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool BSP = false, bool KBIAS = false,
+          bool DROP = false>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
                                                                          DqShape<DQK>::WAVES_PER_EU)))
 void bwd_dq_kernel(BwdParams p) {
@@ -804,7 +819,8 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int t = 0; t < NDQ; ++t) dq[u][t] = zero16();
 
-  auto tile_body = [&](int key0, auto bufc, auto maskc) {
+  // keepr (dropout): keep bits of the rows of query tile u for the tile's 64 keys
+  auto tile_body = [&](int key0, auto bufc, auto maskc, const u32x2 (&keepr)[QT]) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASKED = decltype(maskc)::value;
     const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
@@ -860,7 +876,12 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[t][u][r] = s[t][u][r] * (dp[t][u][r] - Dq[u]);
+        for (int r = 0; r < 16; ++r) {
+          float dpk = dp[t][u][r];
+          if constexpr (DROP)
+            dpk = ((keepr[u][t] >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u) ? dpk * p.drop_scale : 0.f;
+          dp[t][u][r] = s[t][u][r] * (dpk - Dq[u]);
+        }
         sb[u][0] = pack8<E>(dp[t][u], 0);
         sb[u][1] = pack8<E>(dp[t][u], 1);
       }
@@ -873,7 +894,7 @@ void bwd_dq_kernel(BwdParams p) {
           for (int u = 0; u < QT; ++u) dq[u][n] = mfma32(a, sb[u][hh], dq[u][n]);
         }
     }
-    if constexpr (!MASKED && !KBIAS) {
+    if constexpr (!MASKED && !KBIAS && !DROP) {
       // MFMA software pipeline: operand reads run ahead; the P computation fills the
       // dP products, the second half's dS the first half's dQ products.
       ATTN_SCHED_GROUP(kSchedDsRead, 2);
@@ -1008,6 +1029,16 @@ void bwd_dq_kernel(BwdParams p) {
     const int j = tile_of(it);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // dropout keep bits of this lane's rows for keys 64 j .. 64 j + 63, read before the next
+    // tile's loads
+    u32x2 keepr[QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      keepr[u] = u32x2{0u, 0u};
+      if constexpr (DROP)
+        keepr[u] = *reinterpret_cast<const u32x2*>(  // rows past the mask's are padding (P = 0)
+            p.drop_rows + ((int64_t)bh * p.drop_tp + min(qw + 32 * u + lq, p.drop_tp - 1)) * p.drop_ld + j * (DQ_BN / 8));
+    }
     if (it + 1 < n_tiles) load_kv(tile_of(it + 1) * DQ_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * DQ_BN;
     if (BSP && ((bs_idx[(it + bs_skip) >> 1] >> bs_row) & 1) == 0) return;  // no live block for these rows
@@ -1015,11 +1046,11 @@ void bwd_dq_kernel(BwdParams p) {
       if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
       if (WIN && key0 + DQ_BN <= qw - W + 1) return;  // tile wholly below its rows' windows
       if ((CAUSAL && (key0 + DQ_BN - 1 > qw || (WIN && key0 < qw + 32 * QT - W))) || key0 + DQ_BN > Lk)
-        tile_body(key0, bufc, std::true_type{});
+        tile_body(key0, bufc, std::true_type{}, keepr);
       else
-        tile_body(key0, bufc, std::false_type{});
-    } else if constexpr (KBIAS) {
-      tile_body(key0, bufc, std::false_type{});
+        tile_body(key0, bufc, std::false_type{}, keepr);
+    } else if constexpr (KBIAS || DROP) {
+      tile_body(key0, bufc, std::false_type{}, keepr);
     } else {
       tile_pipe(key0, bufc);
     }
@@ -1095,12 +1126,12 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
 // ALiBi bias, 4 block-sparse map, 5 block-sparse map and causal, 6 key bias, 7 key bias
 // and causal.
 // MASK 4: block-sparse map; 5: block-sparse map and the causal mask; 6: key bias;
-// 7: key bias and the causal mask.
+// 7: key bias and the causal mask; 8: dropout; 9: dropout and the causal mask.
 template <int MASK>
 struct MaskMode {
-  static constexpr bool CAUSAL = MASK == 1 || MASK == 2 || MASK == 3 || MASK == 5 || MASK == 7;
+  static constexpr bool CAUSAL = MASK == 1 || MASK == 2 || MASK == 3 || MASK == 5 || MASK == 7 || MASK == 9;
   static constexpr bool WIN = MASK == 2, ALIBI = MASK == 3, BSP = MASK == 4 || MASK == 5;
-  static constexpr bool KBIAS = MASK == 6 || MASK == 7;
+  static constexpr bool KBIAS = MASK == 6 || MASK == 7, DROP = MASK == 8 || MASK == 9;
 };
 
 template <class E, int DQK, int DV, int MASK>
@@ -1109,10 +1140,10 @@ hipError_t bwd_main_t(const BwdParams& p, bool deterministic, hipStream_t s) {
   const int nkb = (p.T + BWD_BN - 1) / BWD_BN;
   const dim3 grid_kv(nkb * p.B * p.NH);
   if (deterministic)
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, M::CAUSAL, M::WIN, M::ALIBI, false, M::BSP, M::KBIAS>), grid_kv,
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, M::CAUSAL, M::WIN, M::ALIBI, false, M::BSP, M::KBIAS, M::DROP>), grid_kv,
                        dim3(BWD_NT), 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, M::CAUSAL, M::WIN, M::ALIBI, true, M::BSP, M::KBIAS>), grid_kv,
+    hipLaunchKernelGGL((bwd_kv_kernel<E, DQK, DV, M::CAUSAL, M::WIN, M::ALIBI, true, M::BSP, M::KBIAS, M::DROP>), grid_kv,
                        dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
@@ -1121,7 +1152,7 @@ template <class E, int DQK, int DV, int MASK>
 hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
   using M = MaskMode<MASK>;
   const int nqb = (p.T + DqShape<DQK>::BM - 1) / DqShape<DQK>::BM;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, M::CAUSAL, M::WIN, M::ALIBI, M::BSP, M::KBIAS>),
+  hipLaunchKernelGGL((bwd_dq_kernel<E, DQK, DV, M::CAUSAL, M::WIN, M::ALIBI, M::BSP, M::KBIAS, M::DROP>),
                      dim3(nqb * p.B * p.NH), dim3(BWD_NT), 0, s, p);
   return hipGetLastError();
 }
@@ -1134,10 +1165,11 @@ hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
   extern template hipError_t bwd_dq_t<E, DQK, DV, MASK>(const BwdParams&, hipStream_t);
 #define ATTN_EXTERN_BWD(DQK, DV, MASK) ATTN_EXTERN_BWD_E(bf16, DQK, DV, MASK) ATTN_EXTERN_BWD_E(f16, DQK, DV, MASK)
 ATTN_BWD_CONFIGS(ATTN_EXTERN_BWD)
-// block-sparse maps and the key bias: bf16 only
+// block-sparse maps, the key bias and dropout: bf16 only
 #define ATTN_BWD_BSP_CONFIGS(X)                                                                       \
   X(64, 64, 4) X(64, 64, 5) X(128, 128, 4) X(128, 128, 5) X(192, 128, 4) X(192, 128, 5) X(64, 64, 6) \
-  X(64, 64, 7) X(128, 128, 6) X(128, 128, 7) X(192, 128, 6) X(192, 128, 7)
+  X(64, 64, 7) X(128, 128, 6) X(128, 128, 7) X(192, 128, 6) X(192, 128, 7) X(64, 64, 8) X(64, 64, 9) X(128, 128, 8) \
+  X(128, 128, 9) X(192, 128, 8) X(192, 128, 9)
 #define ATTN_EXTERN_BWD_BF16(DQK, DV, MASK) ATTN_EXTERN_BWD_E(bf16, DQK, DV, MASK)
 ATTN_BWD_BSP_CONFIGS(ATTN_EXTERN_BWD_BF16)
 

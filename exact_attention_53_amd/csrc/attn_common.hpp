@@ -341,6 +341,27 @@ __device__ __forceinline__ float alibi_slope_log2(int h, int NH) {
   return __builtin_amdgcn_exp2f(-8.f * (float)(h + 1) / (float)NH) * kLog2e;
 }
 
+// Dropout keep bits of an 8-element operand fragment.  A fragment pack8(acc, h) of a
+// 32 x 32 accumulator whose rows (the contraction index) are 8 a + 4 g + e holds, for
+// e8 = 0..7, row 16 h + 8 (e8 / 4) + 4 g + e8 % 4; w holds one keep bit per row (bit k for
+// row k) of that accumulator.  Returns the fragment's 8 bits, bit e8 for element e8.
+__device__ __forceinline__ uint32_t keep_bits8(uint32_t w, int h, int g) {
+  const uint32_t x = w >> (16 * h + 4 * g);
+  return (x & 0xFu) | ((x >> 4) & 0xF0u);
+}
+
+// Elements of a 16-bit fragment whose keep bit is 0 are set to zero.
+template <class E>
+__device__ __forceinline__ vec8<E> drop8(const vec8<E>& x, uint32_t bits) {
+  u32x4 w = __builtin_bit_cast(u32x4, x);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = (bits >> (2 * k)) & 1u, hi = (bits >> (2 * k + 1)) & 1u;
+    w[k] &= (lo ? 0x0000FFFFu : 0u) | (hi ? 0xFFFF0000u : 0u);
+  }
+  return __builtin_bit_cast(vec8<E>, w);
+}
+
 // Valid rows of batch b, clamped to [0, T].
 __device__ __forceinline__ int batch_len(const int* seq, int b, int T) { return min(max(seq[b], 0), T); }
 

@@ -52,9 +52,11 @@ constexpr float kSumLimit = 256.f;        // 2^kRescaleThreshold
 // results to p.part.  BSP: block-sparse map (p.bs): the workgroup visits only the key tiles
 // of its query block's live key blocks, in the descending order of p.bs's list.  KBIAS: a
 // per-key bias (p.kbias, score units) added to the scores; each tile's 64 values travel
-// with its keys into LDS.
+// with its keys into LDS.  DROP: dropout with the query-major keep bits p.drop_rows; the
+// row sum takes the undropped p, the product P V the kept ones, the epilogue the
+// 1 / (1 - p) factor.
 template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool SPLIT = false, bool BSP = false,
-          bool KBIAS = false>
+          bool KBIAS = false, bool DROP = false>
 __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
   constexpr int KS = DQK / 16;
   constexpr int NDT = DV / 32;
@@ -191,6 +193,12 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     const int j = tile_of(it);  // diagonal / tail tile first
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile j has landed in LDS
     __syncthreads();                // ... and every other wave's; the other buffer is free
+    // dropout: this row's keep bits for keys 64 j .. 64 j + 63 (bit k of word k / 32), read
+    // before the next tile's loads so that waiting for them leaves those in flight
+    u32x2 keepw = {0u, 0u};
+    if constexpr (DROP)
+      keepw = *reinterpret_cast<const u32x2*>(p.drop_rows + ((int64_t)bh * p.drop_ld * 8 + my_q) * p.drop_ld +
+                                              j * (FWD_BN / 8));
     if (it + 1 < n_tiles) load_kv(tile_of(it + 1) * FWD_BN, std::integral_constant<int, 1 - BUF>{});
     const int key0 = j * FWD_BN;
     if (MASKED && CAUSAL && key0 > qw + 31) return;  // tile wholly above this wavefront's rows
@@ -298,6 +306,10 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
       }
     }
     l_run += rs;
+    if constexpr (DROP) {  // the product takes the kept weights only
+#pragma unroll
+      for (int m = 0; m < 4; ++m) pb[m] = drop8(pb[m], keep_bits8(m < 2 ? keepw[0] : keepw[1], m & 1, g));
+    }
     const vec8<E> pb0 = pb[0], pb1 = pb[1], pb2 = pb[2], pb3 = pb[3];
     // O^T += V^T P^T
 #pragma unroll
@@ -383,7 +395,7 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
     return;
   }
   if (my_q < Lq) {
-    const float inv = 1.f / l_tot;
+    const float inv = (DROP ? p.drop_scale : 1.f) / l_tot;
     E* orow = og + (int64_t)my_q * p.so.t;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -407,7 +419,14 @@ __global__ __launch_bounds__(FWD_NT, 2) void fwd_kernel(FwdParams p) {
 template <class E, int DQK, int DV>
 static hipError_t fwd_launch(const FwdParams& p, bool causal, hipStream_t s) {
   const dim3 grid((p.T + FWD_BM - 1) / FWD_BM * p.B * p.NH);
-  if (p.kbias != nullptr) {
+  if (p.drop_rows != nullptr) {
+    if (causal)
+      hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, false, false, false, false, false, true>), grid, dim3(FWD_NT),
+                         0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, false, false, false, false, false, false, true>), grid,
+                         dim3(FWD_NT), 0, s, p);
+  } else if (p.kbias != nullptr) {
     if (causal)
       hipLaunchKernelGGL((fwd_kernel<E, DQK, DV, true, false, false, false, false, true>), grid, dim3(FWD_NT), 0, s,
                          p);

@@ -51,6 +51,19 @@ struct FwdParams {
   // divided by the scale (so that it adds to the unscaled scores), zero past T.
   const float* kbias;
   int kbias_ld;
+  // Dropout (nullptr: none): query-major keep bits, drop_ld bytes per row, Tp rows per
+  // head (attn_dropout.hip); kept weights are scaled by drop_scale = 1 / (1 - p).
+  const unsigned char* drop_rows;
+  int drop_ld;
+  float drop_scale;
+};
+
+// Dropout keep masks (attn_dropout.hip): Tp = T rounded up to 128; mask holds the
+// query-major bits (B * NH, Tp, Tp / 8 bytes), then the key-major bits of the same size.
+struct DropoutMaskParams {
+  unsigned char* mask;
+  int B, NH, Tp, causal;
+  uint32_t offset, key0, key1, threshold;
 };
 
 // Forward on fp8 (e4m3) inputs.  q, k, v hold e4m3 codes (strides in bytes); vt is the
@@ -97,6 +110,10 @@ struct BwdParams {
   const float* kbias;      // key bias as in FwdParams, (B * NH, Tpad), or nullptr
   float* dbias_part;       // workspace: (B * NH, Tpad) fp32, sum over queries of dS per key
                            // (written by the key/value kernel when not nullptr)
+  const unsigned char* drop_rows;  // dropout keep bits, query-major (nullptr: no dropout)
+  const unsigned char* drop_cols;  // ... key-major
+  int drop_ld, drop_tp;            // bytes per mask row; rows per head (T rounded up to 128)
+  float drop_scale;                // 1 / (1 - p)
   BsList bs_kv;            // block-sparse map: live query blocks per key block (ascending)
   BsList bs_dq;            // ... live key blocks per dQ query block (descending, row bits)
 };
@@ -149,6 +166,7 @@ hipError_t launch_bs_index(const BsIndexParams& p, hipStream_t s);
 // the scale into out (B * NH, ld) fp32, zero for t >= T; and the reduction of the per-head
 // sums over queries of dS into the caller's dbias (same strides as the bias): each dbias
 // element sums the (b, h) pairs that share it, b outer, h inner.
+hipError_t launch_dropout_mask(const DropoutMaskParams& p, hipStream_t s);
 hipError_t launch_bias_prep(const float* bias, int64_t sb, int64_t sh, float inv_scale, float* out, int ld, int B,
                             int NH, int T, hipStream_t s);
 hipError_t launch_dbias_reduce(const float* part, int ld, float* dbias, int64_t sb, int64_t sh, int B, int NH, int T,

@@ -473,6 +473,57 @@ attn_status attn_fwd_fp8(const void* q, attn_strides sq,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dropout on the attention weights — the `dropout` option of the SDPA interface
+ * [SA8 1.2] (`set_dropout`), whose form the page does not give; read as inverted dropout
+ * on P, with the keep decisions drawn from a counter-based generator:
+ *   O = (P * Z) V / (1 - p),  LSE from the undropped P,
+ *   dV = (P * Z)^T dO / (1 - p),  dP = (dO V^T) * Z / (1 - p),  dS = P * (dP - D),
+ * D = rowsum(dO * O) as without dropout (O being the dropped output).
+ * Generator: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key = seed (low word
+ * first).  Element (i, j) of head (b, h) takes 16-bit value j % 8 of the output at counter
+ * (j / 8, i, b * NH + h, offset) — word (j % 8) / 2, low half for even j — and is kept iff
+ * that value >= round(p * 65536) (p is quantised to 1/65536).
+ *
+ * attn_dropout_mask writes the keep bits once per step into a caller-owned buffer of
+ * attn_dropout_mask_bytes(B, NH, T) bytes (two layouts of one bit per element, query-major
+ * and key-major, each B * NH * Tp * Tp / 8 bytes with Tp = T rounded up to 128; 16-byte
+ * aligned); causal = 1 leaves out blocks wholly above the diagonal.  attn_fwd_dropout and
+ * attn_bwd_dropout read it (inputs; outputs must not overlap it) and must get the same p,
+ * causal flag and sizes.  p in [0, 1) (otherwise ATTN_ERR_ARG); bf16; every other argument,
+ * layout rule and error is that of attn_fwd / attn_bwd_staged.  The results are
+ * bit-stable in the deterministic mode for one seed and offset.
+ */
+size_t attn_dropout_mask_bytes(int B, int NH, int T);
+
+attn_status attn_dropout_mask(float p_drop, uint64_t seed, uint32_t offset,
+                              int B, int NH, int T, int causal,
+                              void* mask, size_t mask_bytes, void* stream);
+
+attn_status attn_fwd_dropout(const void* q, attn_strides sq,
+                             const void* k, attn_strides sk,
+                             const void* v, attn_strides sv,
+                             void* o, attn_strides so,
+                             float* lse,
+                             const void* mask, float p_drop,
+                             int B, int NH, int T, int d_qk, int d_v,
+                             float scale, int causal, void* stream);
+
+attn_status attn_bwd_dropout(const void* q, attn_strides sq,
+                             const void* k, attn_strides sk,
+                             const void* v, attn_strides sv,
+                             const void* o, attn_strides so,
+                             const float* lse,
+                             const void* do_, attn_strides sdo,
+                             void* dq, attn_strides sdq,
+                             void* dk, attn_strides sdk,
+                             void* dv, attn_strides sdv,
+                             const void* mask, float p_drop,
+                             int B, int NH, int T, int d_qk, int d_v,
+                             float scale, int causal, int deterministic,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             unsigned stages);
+
+/*
  * attn_bwd_noalloc — attn_bwd without a caller-supplied workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, allocation-free serving or
  * training loops, harnesses that forbid hipMalloc.  The workspace (D, LSE log2(e) and, in

@@ -391,3 +391,40 @@ def test_fp8_validation(lib):
     assert lib.attn_fwd_fp8_workspace_bytes(4, 16, 8192, 128, 128) == 4 * 16 * 128 * 8192
     assert lib.attn_fwd_fp8_workspace_bytes(1, 2, 100, 64, 64) == (2 * 64 * 128 + 255) // 256 * 256
     assert lib.attn_fwd_fp8_workspace_bytes(1, 2, 100, 192, 128) == 0
+
+
+def test_dropout_validation(lib):
+    st, sv = strides(64, 2, 64), strides(64, 2, 64)
+    MASK = GOOD + 0xc00000
+    assert lib.attn_dropout_mask_bytes(1, 2, 64) == 2 * 2 * 128 * 16
+    assert lib.attn_dropout_mask_bytes(4, 16, 8192) == 2 * 64 * 8192 * 1024
+    assert lib.attn_dropout_mask_bytes(0, 2, 64) == 0
+
+    def gen(p=0.1, mask=MASK, nbytes=1 << 20, causal=1, T=64):
+        return lib.attn_dropout_mask(p, 1, 0, 1, 2, T, causal, mask, nbytes, None)
+
+    assert gen(p=1.0) == ARG
+    assert gen(p=-0.1) == ARG
+    assert gen(p=float("nan")) == ARG
+    assert gen(causal=2) == ARG
+    assert gen(mask=None) == NULL
+    assert gen(mask=MASK + 8) == ALIGN
+    assert gen(nbytes=100) == WORKSPACE
+    assert gen(T=0) == SHAPE
+
+    def dfwd(mask=MASK, p=0.1, o=GOOD + 0x300000):
+        return lib.attn_fwd_dropout(GOOD, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, o, sv, None, mask, p,
+                                    1, 2, 64, 64, 64, 0.125, 1, None)
+
+    def dbwd(mask=MASK, p=0.1, dq=GOOD + 0x600000):
+        return lib.attn_bwd_dropout(GOOD, st, GOOD + 0x100000, st, GOOD + 0x200000, sv, GOOD + 0x300000, sv,
+                                    GOOD + 0x400000, GOOD + 0x500000, sv, dq, st, GOOD + 0x700000, st,
+                                    GOOD + 0x800000, sv, mask, p, 1, 2, 64, 64, 64, 0.125, 1, 1, GOOD + 0x900000,
+                                    1 << 20, None, 7)
+
+    for f in (dfwd, dbwd):
+        assert f(mask=None) == NULL
+        assert f(mask=MASK + 8) == ALIGN
+        assert f(p=1.5) == ARG
+    assert dfwd(o=MASK) == ALIAS
+    assert dbwd(dq=MASK) == ALIAS

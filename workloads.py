@@ -80,7 +80,12 @@ WORKLOADS: Dict[str, Workload] = {
     "blocksparse": Workload("blocksparse", 4, 16, 8192, 128, 128, True, 53010),
     # the headline shape with a per-head key bias (see key_bias)
     "keybias": Workload("keybias", 4, 16, 8192, 128, 128, True, 53011),
+    # the headline shape with dropout on the attention weights, p = DROPOUT_P, the
+    # generator seeded with the workload's seed, counter offset 0
+    "dropout": Workload("dropout", 4, 16, 8192, 128, 128, True, 53012),
 }
+
+DROPOUT_P = 0.1
 
 BS_BLOCK = 128
 
