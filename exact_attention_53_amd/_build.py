@@ -38,12 +38,15 @@ FLAGS = [
 ]
 
 
-# Key/value kernel: let the MFMAs of S and dP write VGPRs, which the softmax VALU work
-# reads, instead of accumulation registers that each need a v_accvgpr_read first (64 per
-# step at d = 128); the dK / dV accumulators stay in accumulation registers.  (The
-# compiler's pass for this form fails on the d_qk = 192 key/value kernel and on the dQ
-# kernel, which keep the default.)
+# Key/value kernel and d_qk = 128 dQ kernel: let the MFMAs of S and dP write VGPRs, which
+# the softmax VALU work reads, instead of accumulation registers that each need a
+# v_accvgpr_read first (64 per 64-key step per query tile at d = 128); long-lived operands
+# (the dK / dV accumulators, the dQ kernel's Q and dO fragments) then sit in the
+# accumulation registers.  (The compiler's pass for this form fails
+# on the d_qk = 192 key/value kernel, which keeps the default; at d = 64 both kernels fit
+# in VGPRs without it.)
 KV_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+DQ_FLAGS = KV_FLAGS
 
 
 def _hipcc() -> str:
@@ -106,7 +109,7 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
         objs.append(obj)
         defs = [f"-DATTN_INST_DQ={int(kind == 'dq')}", f"-DATTN_INST_ELEM={elem}", f"-DATTN_INST_DQK={dqk}",
                 f"-DATTN_INST_DV={dv}", f"-DATTN_INST_MASK={mask}"]
-        extra = KV_FLAGS if kind == "kv" and dqk <= 128 else []
+        extra = KV_FLAGS if kind == "kv" and dqk <= 128 else DQ_FLAGS if kind == "dq" and dqk == 128 else []
         cmds.append([hipcc, *FLAGS, *extra, *defs, "-c", os.path.join(CSRC, "attn_bwd_inst.hip"), "-o", obj])
     if incremental:
         cmds = [c for c in cmds if _stale(c[-1], c[-3])]

@@ -820,70 +820,54 @@ void bwd_dq_kernel(BwdParams p) {
     for (int t = 0; t < NDQ; ++t) dq[u][t] = zero16();
 
   // keepr (dropout): keep bits of the rows of query tile u for the tile's 64 keys
-  auto tile_body = [&](int key0, auto bufc, auto maskc, const u32x2 (&keepr)[QT]) {
+  auto tile_body = [&](int key0, auto bufc, auto maskc, const u32x2 (&keepr)[QT]) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASKED = decltype(maskc)::value;
     const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
     const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
-    f32x16 s[2][QT], dp[2][QT];  // [32-key half][query tile]
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const vec8<E> a = lds_row8<E, DQ_BN>(kt, L, 32 * t, ks);
-#pragma unroll
-        for (int u = 0; u < QT; ++u) s[t][u] = mfma32(a, qf[u][ks], ks == 0 ? zero16() : s[t][u]);
-      }
-#pragma unroll
-    for (int ks = 0; ks < KSV; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const vec8<E> a = lds_row8<E, DQ_BN>(vt, L, 32 * t, ks);
-#pragma unroll
-        for (int u = 0; u < QT; ++u) dp[t][u] = mfma32(a, df[u][ks], ks == 0 ? zero16() : dp[t][u]);
-      }
-    // P^T = 2^(S^T c - LSE log2 e)
-    f32x4 kbv[2][4];  // key bias of element r of half t: kbv[t][r / 4][r % 4] (score units)
-    if constexpr (KBIAS) {
-      const float* kb = BUF ? kbl1 : kbl0;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) kbv[t][a] = *reinterpret_cast<const f32x4*>(kb + 32 * t + 8 * a + 4 * g);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < QT; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float bias = 0.f;
-          if constexpr (KBIAS) bias = kbv[t][r >> 2][r & 3] * c;
-          if constexpr (ALIBI)  // m_h log2(e) (key - query), key key0 + 32 t + 8 (r / 4) + 4 g + r % 4
-            bias = ml * (float)(key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3) - (qw + 32 * u + lq));
-          float pv = exp2_fast(__builtin_fmaf(s[t][u][r], c, bias - lse2[u]));
-          if constexpr (MASKED) {
-            const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            const int q = qw + 32 * u + lq;
-            pv = (key >= Lk || (CAUSAL && (key > q || (WIN && q - key >= W)))) ? 0.f : pv;
-          }
-          s[t][u][r] = pv;
-        }
-    // dS^T = P^T (dP^T - D); dQ^T += K^T dS^T, one 32-key half at a time
+    // One 32-key half at a time: S^T and dP^T of half t, then P^T, dS^T = P^T (dP^T - D)
+    // and dQ^T += K^T dS^T for it, so that only one half's scores are live.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      f32x16 s[QT], dp[QT];
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) {
+        const vec8<E> a = lds_row8<E, DQ_BN>(kt, L, 32 * t, ks);
+#pragma unroll
+        for (int u = 0; u < QT; ++u) s[u] = mfma32(a, qf[u][ks], ks == 0 ? zero16() : s[u]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSV; ++ks) {
+        const vec8<E> a = lds_row8<E, DQ_BN>(vt, L, 32 * t, ks);
+#pragma unroll
+        for (int u = 0; u < QT; ++u) dp[u] = mfma32(a, df[u][ks], ks == 0 ? zero16() : dp[u]);
+      }
+      // P^T = 2^(S^T c - LSE log2 e); key of element r: key0 + 32 t + 8 (r / 4) + 4 g + r % 4
+      f32x4 kbv[4];  // key bias of element r: kbv[r / 4][r % 4] (score units)
+      if constexpr (KBIAS) {
+        const float* kb = BUF ? kbl1 : kbl0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) kbv[a] = *reinterpret_cast<const f32x4*>(kb + 32 * t + 8 * a + 4 * g);
+      }
       vec8<E> sb[QT][2];
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float dpk = dp[t][u][r];
+          const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+          const int q = qw + 32 * u + lq;
+          float bias = 0.f;
+          if constexpr (KBIAS) bias = kbv[r >> 2][r & 3] * c;
+          if constexpr (ALIBI) bias = ml * (float)(key - q);  // m_h log2(e) (key - query)
+          float pv = exp2_fast(__builtin_fmaf(s[u][r], c, bias - lse2[u]));
+          if constexpr (MASKED) pv = (key >= Lk || (CAUSAL && (key > q || (WIN && q - key >= W)))) ? 0.f : pv;
+          float dpk = dp[u][r];
           if constexpr (DROP)
             dpk = ((keepr[u][t] >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u) ? dpk * p.drop_scale : 0.f;
-          dp[t][u][r] = s[t][u][r] * (dpk - Dq[u]);
+          dp[u][r] = pv * (dpk - Dq[u]);
         }
-        sb[u][0] = pack8<E>(dp[t][u], 0);
-        sb[u][1] = pack8<E>(dp[t][u], 1);
+        sb[u][0] = pack8<E>(dp[u], 0);
+        sb[u][1] = pack8<E>(dp[u], 1);
       }
 #pragma unroll
       for (int n = 0; n < NDQ; ++n)
@@ -893,33 +877,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int u = 0; u < QT; ++u) dq[u][n] = mfma32(a, sb[u][hh], dq[u][n]);
         }
-    }
-    if constexpr (!MASKED && !KBIAS && !DROP) {
-      // MFMA software pipeline: operand reads run ahead; the P computation fills the
-      // dP products, the second half's dS the first half's dQ products.
-      ATTN_SCHED_GROUP(kSchedDsRead, 2);
-#pragma unroll
-      for (int i = 0; i < 2 * KSQ; ++i) {  // S
-        ATTN_SCHED_GROUP(kSchedMfma, QT);
-        ATTN_SCHED_GROUP(kSchedDsRead, 1);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * KSV; ++i) {  // dP || P
-        ATTN_SCHED_GROUP(kSchedMfma, QT);
-        ATTN_SCHED_GROUP(kSchedDsRead, 1);
-        ATTN_SCHED_GROUP(kSchedValu, 6 * QT);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * NDQ; ++i) {  // dQ (first half) || dS (second half)
-        ATTN_SCHED_GROUP(kSchedMfma, QT);
-        ATTN_SCHED_GROUP(kSchedDsRead, 2);
-        ATTN_SCHED_GROUP(kSchedValu, 6 * QT);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * NDQ; ++i) {  // dQ (second half)
-        ATTN_SCHED_GROUP(kSchedMfma, QT);
-        ATTN_SCHED_GROUP(kSchedDsRead, 2);
-      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the halves apart: one half's scores live
     }
   };
 
