@@ -38,15 +38,22 @@ FLAGS = [
 ]
 
 
-# Key/value kernel and d_qk = 128 dQ kernel: let the MFMAs of S and dP write VGPRs, which
-# the softmax VALU work reads, instead of accumulation registers that each need a
-# v_accvgpr_read first (64 per 64-key step per query tile at d = 128); long-lived operands
-# (the dK / dV accumulators, the dQ kernel's Q and dO fragments) then sit in the
-# accumulation registers.  (The compiler's pass for this form fails
-# on the d_qk = 192 key/value kernel, which keeps the default; at d = 64 both kernels fit
-# in VGPRs without it.)
+# MFMA results in VGPRs (the key/value kernel at d_qk <= 128, the dQ kernel at
+# d_qk >= 128): the MFMAs of S and dP write VGPRs, which the softmax VALU work reads,
+# instead of accumulation registers that each need a v_accvgpr_read first (64 per 64-key
+# step per 32-row tile at d = 128); long-lived operands (the dK / dV accumulators, the dQ
+# kernel's Q and dO fragments) then sit in the accumulation registers.  Measured per
+# kernel: the d_qk = 192 key/value kernel is 10 % slower in this form (and two of its
+# mask modes do not compile in it), so it keeps the default; at d = 64 both kernels fit
+# in VGPRs without it.
 KV_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 DQ_FLAGS = KV_FLAGS
+
+
+def _extra_flags(kind: str, dqk: int, mask: int) -> list:
+    if kind == "kv":
+        return KV_FLAGS if dqk <= 128 else []
+    return DQ_FLAGS if dqk >= 128 else []
 
 
 def _hipcc() -> str:
@@ -109,7 +116,7 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
         objs.append(obj)
         defs = [f"-DATTN_INST_DQ={int(kind == 'dq')}", f"-DATTN_INST_ELEM={elem}", f"-DATTN_INST_DQK={dqk}",
                 f"-DATTN_INST_DV={dv}", f"-DATTN_INST_MASK={mask}"]
-        extra = KV_FLAGS if kind == "kv" and dqk <= 128 else DQ_FLAGS if kind == "dq" and dqk == 128 else []
+        extra = _extra_flags(kind, dqk, mask)
         cmds.append([hipcc, *FLAGS, *extra, *defs, "-c", os.path.join(CSRC, "attn_bwd_inst.hip"), "-o", obj])
     if incremental:
         cmds = [c for c in cmds if _stale(c[-1], c[-3])]

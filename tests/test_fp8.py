@@ -6,7 +6,7 @@ e4m3 (3 mantissa bits) before O = P V.  For weights in e4m3's normal range the r
 moves each weight by at most 2^-4 of itself, and O is a weighted mean of V rows with
 weights summing to one, so |dO| <= 2^-4 max|V|; weights in the subnormal range (p < 2^-6 of
 a row maximum of at least 1) move by at most 2^-10 each, in random directions, far below
-that bound at these sizes.  The bf16 rounding of O adds 2^-9 max|O|.  Hence
+that bound at these sizes.  The bf16 rounding of O adds 2^-8 max|O|.  Hence
   max|O - O_ref| <= 2^-4 max|V| + 2^-8 max|O_ref|       (V: the real, descaled values)
 LSE comes from the unrounded fp32 sums: the 16-bit path's bound, 1e-3 max(1, max|LSE|).
 """

@@ -61,6 +61,29 @@ def test_large_magnitude_scores():
         compare(w, run_gpu(w, gpu, False), oracle(w, cpu))
 
 
+def _d_rounding_terms(w, cpu, ref, b, h):
+    """Bounds of the gradient error that the bf16 rounding of the stored O carries into D.
+
+    The backward takes D_i = sum_k dO_ik O_ik from the bf16 O, whose elements are rounded
+    with relative error at most 2^-8 (8-bit significand), so |dD_i| <= delta_i =
+    2^-8 sum_k |dO_ik O_ik|.  dS_ij = P_ij (dP_ij - D_i) then moves by P_ij dD_i, and
+      |d dQ_i| <= scale delta_i sum_j P_ij |K_j|_inf <= scale delta_i max|K|,
+      |d dK_j| <= scale max|Q| sum_i P_ij delta_i.
+    P comes from the oracle's LSE: P_ij = exp(scale q_i.k_j - LSE_i) on the allowed keys.
+    Returns the largest of each bound over the head's rows (dQ) and keys (dK)."""
+    q = cpu["q"][b, :, h].double().numpy()
+    k = cpu["k"][b, :, h].double().numpy()
+    do = cpu["do"][b, :, h].double().numpy()
+    delta = 2.0 ** -8 * np.sum(np.abs(do * ref["o"][b, :, h]), axis=-1)
+    logits = w.scale * (q @ k.T) - ref["lse"][b, h][:, None]
+    if w.causal:
+        logits[np.triu_indices(w.T, 1)] = -np.inf
+    pm = np.exp(logits)
+    ddq = w.scale * float(np.max(delta)) * float(np.max(np.abs(k)))
+    ddk = w.scale * float(np.max(np.abs(q))) * float(np.max(pm.T @ delta))
+    return ddq, ddk
+
+
 @pytest.mark.parametrize("causal,T", [(True, 333), (False, 320)], ids=["causal", "full"])
 def test_row_maximum_found_late(causal, T):
     """Key 0 is planted with a score far above all others (about 15 against about 1).
@@ -69,10 +92,10 @@ def test_row_maximum_found_late(causal, T):
     the row has been summed.  In the full case with T a multiple of the key tile no tile
     carries a mask, so the first tile is met with no maximum at all.
 
-    Only the forward outputs are compared: with P_i0 close to 1 in every row, dS_i0 =
-    P_i0 (dP_i0 - D_i) cancels almost exactly, and the bf16 rounding of the stored O that
-    D_i is computed from dominates the tiny dK; large scores in the backward are covered
-    by the N(0, 4^2) case."""
+    The backward is compared too.  With P_i0 close to 1 in every row, dS_i0 =
+    P_i0 (dP_i0 - D_i) cancels almost exactly, so dK_0 is tiny and the rounding of the
+    stored bf16 O, from which D_i is computed, dominates its error; the dQ and dK bounds
+    get the D-rounding terms of _d_rounding_terms (dK_0 sums P_i0 dD_i over all T rows)."""
     for dims in HEADDIMS:
         w = _small(T, dims[0], dims[1], causal, B=1, NH=2, seed=13)
         say(f"case late max {w.name}")
@@ -83,11 +106,19 @@ def test_row_maximum_found_late(causal, T):
         k[:, 0, :, 0] = 30.0 * (w.d_qk / 64) ** 0.5
         cpu["q"], cpu["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
         dev = torch.device("cuda:0")
-        gpu = {n: cpu[n].to(dev) for n in ("q", "k", "v")}
-        o, lse = attn.fwd(gpu["q"], gpu["k"], gpu["v"], w.causal, w.scale)
-        ref_o, ref_lse = attn_ref.attn_ref_fwd(cpu["q"], cpu["k"], cpu["v"], w.causal, w.scale)
-        check_bf16(f"{w.name} o", to_np(o), ref_o)
-        check_lse(f"{w.name} lse", to_np(lse), ref_lse)
+        gpu = {n: cpu[n].to(dev) for n in ("q", "k", "v", "do")}
+        ref = oracle(w, cpu)
+        for det in (True, False):
+            got = run_gpu(w, gpu, det)
+            for b, h in [(0, 0), (0, 1)]:
+                tag = f"{w.name} det={det} head {h}"
+                check_bf16(f"{tag} o", to_np(got["o"][b, :, h]), ref["o"][b, :, h])
+                check_lse(f"{tag} lse", to_np(got["lse"][b, h]), ref["lse"][b, h])
+                check_bf16(f"{tag} dv", to_np(got["dv"][b, :, h]), ref["dv"][b, :, h])
+                ddq, ddk = _d_rounding_terms(w, cpu, ref, b, h)
+                rq = check_bf16(f"{tag} dq", to_np(got["dq"][b, :, h]), ref["dq"][b, :, h], atol=2e-3 + ddq)
+                rk = check_bf16(f"{tag} dk", to_np(got["dk"][b, :, h]), ref["dk"][b, :, h], atol=2e-3 + ddk)
+                say(f"  {tag}: dq {rq:.3f}, dk {rk:.3f} of the bound (D terms {ddq:.2e}, {ddk:.2e})")
 
 
 def test_zero_queries_closed_form():
