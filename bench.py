@@ -28,17 +28,17 @@ PEAK_HBM_GBS = 8000.0
 
 # HBM traffic per launch on the headline workload (B4 NH16 T8192 d128 causal,
 # deterministic dQ), from two rocprofv3 --pmc passes over `bench.py --steps 1 --warmup 0
-# --no-cpu-baseline`: FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch.  They are scaled by
+# --no-cpu-baseline --no-extras`: FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch.  They are scaled by
 # what the same counters read for a streaming kernel of known size (`bench.py
 # --copy-calibration 1024`, 1 GiB read and 1 GiB written per launch): FETCH_SIZE read
 # 524294.5 KiB there, WRITE_SIZE 1048576 KiB.  The figures hold only for the kernel
 # sources they were taken on, identified by a hash; any change makes them null.
-TRAFFIC_SOURCES = "d6a1f96cd86b15b0"
+TRAFFIC_SOURCES = "d6de709cfa719375"
 TRAFFIC_KIB = {  # kernel: (FETCH_SIZE, WRITE_SIZE) per dispatch
-    "attn_fwd": (1295011.8125, 133134.53125),
-    "bwd_preprocess": (133157.75, 4100.71875),
-    "bwd_kv": (1262104.5, 262144.0),
-    "bwd_dq": (842687.5, 196337.5),
+    "attn_fwd": (1176878.3125, 133173.3125),
+    "bwd_preprocess": (133166.4375, 4097.96875),
+    "bwd_kv": (1261936.375, 262144.0),
+    "bwd_dq": (807715.0, 153849.625),
 }
 FETCH_SCALE = 1048576.0 / 524294.5
 WRITE_SCALE = 1048576.0 / 1048576.0
