@@ -15,10 +15,18 @@ static inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads 
 template <class E>
 static hipError_t pre_t(const BwdParams& p, int d_qk, int d_v, bool zero_acc, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.NH * p.Tpad;
-  if (d_v == 64)
-    hipLaunchKernelGGL((bwd_pre_kernel<E, 64>), dim3(blocks_for(rows * 8)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
+  // a workgroup covers NP * 256 / G rows, G = d_v / 8 lanes per row; four rows per lane
+  // group where that still leaves at least 2048 workgroups (8 per CU)
+  const int64_t lanes = rows * (d_v / 8);
+  const bool wide = blocks_for(lanes / 4) >= 2048;
+  if (d_v == 64 && wide)
+    hipLaunchKernelGGL((bwd_pre_kernel<E, 64, 4>), dim3(blocks_for(lanes / 4)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
+  else if (d_v == 64)
+    hipLaunchKernelGGL((bwd_pre_kernel<E, 64, 1>), dim3(blocks_for(lanes)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
+  else if (d_v == 128 && wide)
+    hipLaunchKernelGGL((bwd_pre_kernel<E, 128, 4>), dim3(blocks_for(lanes / 4)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
   else if (d_v == 128)
-    hipLaunchKernelGGL((bwd_pre_kernel<E, 128>), dim3(blocks_for(rows * 16)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
+    hipLaunchKernelGGL((bwd_pre_kernel<E, 128, 1>), dim3(blocks_for(lanes)), dim3(256), 0, s, p, d_qk, (int)zero_acc);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -45,43 +45,61 @@ constexpr int DQ_BN = 64;    // dQ kernel: keys per step
 // ---------------------------------------------------------------------------------
 // preprocess: D = rowsum(dO * O); optional clear of the dQ accumulator
 // ---------------------------------------------------------------------------------
-template <class E, int DV>
+// G = DV / 8 lanes per row, 16 bytes of O and of dO each; a workgroup takes NP groups of
+// 256 / G rows and issues the loads of all of them before the first sum, so that every
+// lane has NP pairs of loads in flight (NP = 4 on large grids, 1 on small ones, which
+// need the workgroups more).
+template <class E, int DV, int NP>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int d_qk, int zero_acc) {
-  constexpr int G = DV / 8;  // lanes per row
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / G;  // over B * NH * Tpad
-  const int c = (int)(gid % G);
+  constexpr int G = DV / 8;
+  constexpr int RPP = 256 / G;  // rows per pass
+  const int c = (int)(threadIdx.x % G);
+  const int64_t row0 = (int64_t)blockIdx.x * (NP * RPP) + threadIdx.x / G;  // over B * NH * Tpad
   const int64_t nrows = (int64_t)p.B * p.NH * p.Tpad;
-  float sum = 0.f;
-  if (row < nrows) {
-    const int t = (int)(row % p.Tpad);
-    const int bh = (int)(row / p.Tpad);
-    const int b = bh / p.NH, h = bh % p.NH;
-    const int Lq = p.seq_q != nullptr ? batch_len(p.seq_q, b, p.T) : p.T;
-    if (t < Lq) {
-      const E* orow = (const E*)p.o + b * p.so.b + h * p.so.h + (int64_t)t * p.so.t;
-      const E* drow = (const E*)p.dO + b * p.sdo.b + h * p.sdo.h + (int64_t)t * p.sdo.t;
-      const vec8<E> ov = __builtin_bit_cast(vec8<E>, *reinterpret_cast<const u32x4*>(orow + 8 * c));
-      const vec8<E> dv = __builtin_bit_cast(vec8<E>, *reinterpret_cast<const u32x4*>(drow + 8 * c));
+  vec8<E> ov[NP], dv[NP];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sum += (float)ov[e] * (float)dv[e];
+  for (int k = 0; k < NP; ++k) {
+    const int64_t row = row0 + (int64_t)k * RPP;
+    u32x4 ra = {0u, 0u, 0u, 0u}, rb = {0u, 0u, 0u, 0u};
+    if (row < nrows) {
+      const int t = (int)(row % p.Tpad);
+      const int bh = (int)(row / p.Tpad);
+      const int b = bh / p.NH, h = bh % p.NH;
+      const int Lq = p.seq_q != nullptr ? batch_len(p.seq_q, b, p.T) : p.T;
+      if (t < Lq) {
+        const E* orow = (const E*)p.o + b * p.so.b + h * p.so.h + (int64_t)t * p.so.t;
+        const E* drow = (const E*)p.dO + b * p.sdo.b + h * p.sdo.h + (int64_t)t * p.sdo.t;
+        ra = *reinterpret_cast<const u32x4*>(orow + 8 * c);
+        rb = *reinterpret_cast<const u32x4*>(drow + 8 * c);
+      }
     }
-    if (zero_acc) {
-      float* acc = p.dq_acc + row * d_qk;
-      for (int x = 4 * c; x < d_qk; x += 4 * G) *reinterpret_cast<f32x4*>(acc + x) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    ov[k] = __builtin_bit_cast(vec8<E>, ra);
+    dv[k] = __builtin_bit_cast(vec8<E>, rb);
   }
 #pragma unroll
-  for (int off = G / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, G);
-  if (row < nrows && c == 0) {
-    const int t = (int)(row % p.Tpad);
-    const int bh = (int)(row / p.Tpad);
-    p.D[row] = sum;
-    // LSE in base-2 units; padding rows (past T, past the batch's query length, or
-    // without keys: LSE = -inf) get +inf, which makes their P exactly 0
-    const int Lq = p.seq_q != nullptr ? batch_len(p.seq_q, bh / p.NH, p.T) : p.T;
-    const float l = t < Lq ? p.lse[(int64_t)bh * p.T + t] : -INFINITY;
-    p.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  for (int k = 0; k < NP; ++k) {
+    const int64_t row = row0 + (int64_t)k * RPP;
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += (float)ov[k][e] * (float)dv[k][e];
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, G);
+    if (row < nrows) {
+      if (zero_acc) {
+        float* acc = p.dq_acc + row * d_qk;
+        for (int x = 4 * c; x < d_qk; x += 4 * G) *reinterpret_cast<f32x4*>(acc + x) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if (c == 0) {
+        const int t = (int)(row % p.Tpad);
+        const int bh = (int)(row / p.Tpad);
+        p.D[row] = sum;
+        // LSE in base-2 units; padding rows (past T, past the batch's query length, or
+        // without keys: LSE = -inf) get +inf, which makes their P exactly 0
+        const int Lq = p.seq_q != nullptr ? batch_len(p.seq_q, bh / p.NH, p.T) : p.T;
+        const float l = t < Lq ? p.lse[(int64_t)bh * p.T + t] : -INFINITY;
+        p.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+      }
+    }
   }
 }
 
