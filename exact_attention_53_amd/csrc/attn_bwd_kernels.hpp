@@ -899,10 +899,16 @@ void bwd_dq_kernel(BwdParams p) {
     }
   };
 
-  // ---- unmasked tiles: an explicit pipeline (DqPlan) ----
+  // ---- an explicit pipeline (DqPlan); MASKED: P = 0 on the keys past Lk, past a row's
+  // diagonal or under its window (the tiles that carry a mask, when neither a key bias
+  // nor dropout needs the plain body) ----
   using Plan = DqPlan<DQK, DV, QT>;
-  auto tile_pipe = [&](int key0, auto bufc) __attribute__((always_inline)) {
+  auto tile_pipe = [&](int key0, auto bufc, auto maskc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
+    constexpr bool MASKED = decltype(maskc)::value;
+    // key - query = kq + 32 (t - u) + 8 (r / 4) + r % 4 and Lk - key = lk - 32 t - 8 (r / 4) - r % 4
+    // for element r of half t and query tile u
+    const int kq = key0 + 4 * g - (qw + lq), lk = Lk - key0 - 4 * g;
     const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
     const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
     f32x16 s[2][QT], dp[2][QT];
@@ -938,6 +944,11 @@ void bwd_dq_kernel(BwdParams p) {
           pv[u][r] = exp2_fast(__builtin_fmaf(s[t][u][r], c, __builtin_fmaf(ml, (float)(32 * t + 8 * (r >> 2) + (r & 3)), abq[u])));
         else
           pv[u][r] = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
+        if constexpr (MASKED) {
+          constexpr int off = 32 * t + 8 * (r >> 2) + (r & 3);
+          const int d = kq + off - 32 * u;  // key - query
+          pv[u][r] = (off >= lk || (CAUSAL && (d > 0 || (WIN && -d >= W)))) ? 0.f : pv[u][r];
+        }
       } else {
         constexpr int kk = k - 16 * QT, u = kk / 18, e = kk % 18;
         if constexpr (e == 8 || e == 17) {
@@ -1021,14 +1032,22 @@ void bwd_dq_kernel(BwdParams p) {
     if constexpr (decltype(maskc)::value) {
       if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
       if (WIN && key0 + DQ_BN <= qw - W + 1) return;  // tile wholly below its rows' windows
-      if ((CAUSAL && (key0 + DQ_BN - 1 > qw || (WIN && key0 < qw + 32 * QT - W))) || key0 + DQ_BN > Lk)
-        tile_body(key0, bufc, std::true_type{}, keepr);
-      else
-        tile_body(key0, bufc, std::false_type{}, keepr);
+      const bool need = (CAUSAL && (key0 + DQ_BN - 1 > qw || (WIN && key0 < qw + 32 * QT - W))) || key0 + DQ_BN > Lk;
+      if constexpr (KBIAS || DROP) {
+        if (need)
+          tile_body(key0, bufc, std::true_type{}, keepr);
+        else
+          tile_body(key0, bufc, std::false_type{}, keepr);
+      } else {
+        if (need)
+          tile_pipe(key0, bufc, std::true_type{});
+        else
+          tile_pipe(key0, bufc, std::false_type{});
+      }
     } else if constexpr (KBIAS || DROP) {
       tile_body(key0, bufc, std::false_type{}, keepr);
     } else {
-      tile_pipe(key0, bufc);
+      tile_pipe(key0, bufc, std::false_type{});
     }
   };
   // The first tiles (the workgroup's diagonal ones under the causal mask, or the ragged
