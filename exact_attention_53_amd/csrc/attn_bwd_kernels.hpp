@@ -648,7 +648,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
 // half 1; placed greedily (P element 6, dS element 3, pack 4 cost units) no earlier
 // than two bundles after the MFMAs producing its inputs, with the smallest per-bundle
 // budget for which every pack lands before the dQ bundles that read it.
-template <int DQK, int DV, int QT>
+template <int DQK, int DV, int QT, bool KBIAS = false, bool DROP = false>
 struct DqPlan {
   static constexpr int KSQ = DQK / 16, KSV = DV / 16, NDQ = DQK / 32;
   static constexpr int S0 = 0, P0 = KSQ, S1 = KSQ + KSV, P1 = 2 * KSQ + KSV, Q0 = 2 * KSQ + 2 * KSV;
@@ -664,7 +664,9 @@ struct DqPlan {
   static constexpr bool is_pack(int o) {
     return !is_p(o) && ((o % (34 * QT) - 16 * QT) % 18 == 8 || (o % (34 * QT) - 16 * QT) % 18 == 17);
   }
-  static constexpr int cost(int o) { return is_p(o) ? 6 : (is_pack(o) ? 4 : 3); }
+  // a key bias adds one FMA to a P element; dropout a bit extract and a mask (the dP
+  // multiplier, 1 / (1 - p) or 0) to a dS element, whose subtraction becomes an FMA
+  static constexpr int cost(int o) { return is_p(o) ? (KBIAS ? 7 : 6) : (is_pack(o) ? 4 : (DROP ? 5 : 3)); }
   static constexpr int earliest(int o) {
     const int t = half(o);
     return is_p(o) ? (t ? P1 : P0) + 1 : (t ? Q0 : S1) + 1;
@@ -672,6 +674,7 @@ struct DqPlan {
   static constexpr int deadline(int o) { return (half(o) ? Q1 : Q0) - 1; }
   struct Table {
     int bundle[NOPS];
+    int kb_bundle[2];  // key bias: the bundle that reads half t's 32 bias values from LDS
     int ok;
   };
   static constexpr Table make(int cap) {
@@ -691,6 +694,11 @@ struct DqPlan {
       used += cost(o);
       if ((is_pack(o) && cur > deadline(o)) || cur >= N) tb.ok = 0;
     }
+    // two bundles before the half's first P element, and after the other half's last
+    const int first0 = tb.bundle[0], first1 = tb.bundle[34 * QT], last0 = tb.bundle[16 * QT - 1];
+    tb.kb_bundle[0] = first0 >= 2 ? first0 - 2 : 0;
+    tb.kb_bundle[1] = first1 - 2 > last0 ? first1 - 2 : last0 + 1;
+    if (tb.kb_bundle[1] > first1) tb.ok = 0;
     return tb;
   }
   static constexpr Table choose() {
@@ -716,8 +724,9 @@ struct DqShape {
 // linear bias -m_h (i - j) on the scaled scores.  BSP: block-sparse map (p.bs_dq): the
 // workgroup visits the key tiles of the live key blocks of any of its query-block rows,
 // descending; a wavefront computes only on the tiles live for its own rows.  KBIAS: a
-// per-key bias (p.kbias) on the scores, 64 values per key tile in LDS; every tile then
-// runs the plain (compiler-scheduled) tile body.
+// per-key bias (p.kbias) on the scores, 64 values per key tile in LDS, read into
+// registers half a tile at a time inside the pipeline.  DROP: dropout keep bits
+// (p.drop_rows), one 64-bit word per row and key tile, applied to dP.
 template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool BSP = false, bool KBIAS = false,
           bool DROP = false>
 __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
@@ -837,75 +846,23 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int t = 0; t < NDQ; ++t) dq[u][t] = zero16();
 
-  // keepr (dropout): keep bits of the rows of query tile u for the tile's 64 keys
-  auto tile_body = [&](int key0, auto bufc, auto maskc, const u32x2 (&keepr)[QT]) __attribute__((always_inline)) {
+  // ---- every tile runs as an explicit pipeline (DqPlan).  MASKED: P = 0 on the keys past
+  // Lk, past a row's diagonal or under its window (the tiles that carry a mask).  keepr
+  // (dropout): keep bits of the rows of query tile u for the tile's 64 keys ----
+  using Plan = DqPlan<DQK, DV, QT, KBIAS, DROP>;
+  auto tile_pipe = [&](int key0, auto bufc, auto maskc, const u32x2 (&keepr)[QT]) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASKED = decltype(maskc)::value;
-    const ATTN_LDS char* kt = (const ATTN_LDS char*)(BUF ? kbuf1 : kbuf0);
-    const ATTN_LDS char* vt = (const ATTN_LDS char*)(BUF ? vbuf1 : vbuf0);
-    // One 32-key half at a time: S^T and dP^T of half t, then P^T, dS^T = P^T (dP^T - D)
-    // and dQ^T += K^T dS^T for it, so that only one half's scores are live.
+    // key bias of element r of half t: kbv[t][r / 4][r % 4] (score units), read from LDS
+    f32x4 kbv[2][4];
+    const float* kbl = BUF ? kbl1 : kbl0;
+    // dropout: this lane's keep bits of query tile u and half t, shifted by 4 g so that
+    // element r sits at bit 8 (r / 4) + r % 4
+    uint32_t keepg[QT][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16 s[QT], dp[QT];
+    for (int u = 0; u < QT; ++u)
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) {
-        const vec8<E> a = lds_row8<E, DQ_BN>(kt, L, 32 * t, ks);
-#pragma unroll
-        for (int u = 0; u < QT; ++u) s[u] = mfma32(a, qf[u][ks], ks == 0 ? zero16() : s[u]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < KSV; ++ks) {
-        const vec8<E> a = lds_row8<E, DQ_BN>(vt, L, 32 * t, ks);
-#pragma unroll
-        for (int u = 0; u < QT; ++u) dp[u] = mfma32(a, df[u][ks], ks == 0 ? zero16() : dp[u]);
-      }
-      // P^T = 2^(S^T c - LSE log2 e); key of element r: key0 + 32 t + 8 (r / 4) + 4 g + r % 4
-      f32x4 kbv[4];  // key bias of element r: kbv[r / 4][r % 4] (score units)
-      if constexpr (KBIAS) {
-        const float* kb = BUF ? kbl1 : kbl0;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) kbv[a] = *reinterpret_cast<const f32x4*>(kb + 32 * t + 8 * a + 4 * g);
-      }
-      vec8<E> sb[QT][2];
-#pragma unroll
-      for (int u = 0; u < QT; ++u) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-          const int q = qw + 32 * u + lq;
-          float bias = 0.f;
-          if constexpr (KBIAS) bias = kbv[r >> 2][r & 3] * c;
-          if constexpr (ALIBI) bias = ml * (float)(key - q);  // m_h log2(e) (key - query)
-          float pv = exp2_fast(__builtin_fmaf(s[u][r], c, bias - lse2[u]));
-          if constexpr (MASKED) pv = (key >= Lk || (CAUSAL && (key > q || (WIN && q - key >= W)))) ? 0.f : pv;
-          float dpk = dp[u][r];
-          if constexpr (DROP)
-            dpk = ((keepr[u][t] >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u) ? dpk * p.drop_scale : 0.f;
-          dp[u][r] = pv * (dpk - Dq[u]);
-        }
-        sb[u][0] = pack8<E>(dp[u], 0);
-        sb[u][1] = pack8<E>(dp[u], 1);
-      }
-#pragma unroll
-      for (int n = 0; n < NDQ; ++n)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const vec8<E> a = lds_col8<E, DQ_BN>(kt, L, 32 * t + 16 * hh, 32 * n);
-#pragma unroll
-          for (int u = 0; u < QT; ++u) dq[u][n] = mfma32(a, sb[u][hh], dq[u][n]);
-        }
-      __builtin_amdgcn_sched_barrier(0);  // keep the halves apart: one half's scores live
-    }
-  };
-
-  // ---- an explicit pipeline (DqPlan); MASKED: P = 0 on the keys past Lk, past a row's
-  // diagonal or under its window (the tiles that carry a mask, when neither a key bias
-  // nor dropout needs the plain body) ----
-  using Plan = DqPlan<DQK, DV, QT>;
-  auto tile_pipe = [&](int key0, auto bufc, auto maskc) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(bufc)::value;
-    constexpr bool MASKED = decltype(maskc)::value;
+      for (int t = 0; t < 2; ++t) keepg[u][t] = DROP ? keepr[u][t] >> (4 * g) : 0u;
     // key - query = kq + 32 (t - u) + 8 (r / 4) + r % 4 and Lk - key = lk - 32 t - 8 (r / 4) - r % 4
     // for element r of half t and query tile u
     const int kq = key0 + 4 * g - (qw + lq), lk = Lk - key0 - 4 * g;
@@ -942,6 +899,8 @@ void bwd_dq_kernel(BwdParams p) {
         constexpr int u = k / 16, r = k % 16;
         if constexpr (ALIBI)
           pv[u][r] = exp2_fast(__builtin_fmaf(s[t][u][r], c, __builtin_fmaf(ml, (float)(32 * t + 8 * (r >> 2) + (r & 3)), abq[u])));
+        else if constexpr (KBIAS)
+          pv[u][r] = exp2_fast(__builtin_fmaf(s[t][u][r], c, __builtin_fmaf(kbv[t][r >> 2][r & 3], c, -lse2[u])));
         else
           pv[u][r] = exp2_fast(__builtin_fmaf(s[t][u][r], c, -lse2[u]));
         if constexpr (MASKED) {
@@ -955,7 +914,16 @@ void bwd_dq_kernel(BwdParams p) {
           sb[t][u][e == 8 ? 0 : 1] = pack8<E>(pv[u], e == 8 ? 0 : 1);
         } else {
           constexpr int r = e < 8 ? e : e - 1;
-          pv[u][r] = pv[u][r] * (dp[t][u][r] - Dq[u]);
+          if constexpr (DROP) {
+            // keep bit of element r (bit 8 (r / 4) + r % 4 of this lane's shifted word)
+            // spread to all 32 bits, then 1 / (1 - p) or 0 as the multiplier of dP
+            constexpr int pos = 8 * (r >> 2) + (r & 3);
+            const uint32_t km = (uint32_t)((int32_t)(keepg[u][t] << (31 - pos)) >> 31);
+            const float ks = __builtin_bit_cast(float, km & __builtin_bit_cast(uint32_t, p.drop_scale));
+            pv[u][r] = pv[u][r] * __builtin_fmaf(dp[t][u][r], ks, -Dq[u]);
+          } else {
+            pv[u][r] = pv[u][r] * (dp[t][u][r] - Dq[u]);
+          }
         }
       }
     };
@@ -980,6 +948,14 @@ void bwd_dq_kernel(BwdParams p) {
         }
       }
       if constexpr (b + Plan::LA < Plan::N) fr[(b + Plan::LA) % Plan::RING] = read_at(std::integral_constant<int, b + Plan::LA>{});
+      if constexpr (KBIAS) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          if (b == Plan::plan.kb_bundle[t]) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) kbv[t][a] = *reinterpret_cast<const f32x4*>(kbl + 32 * t + 8 * a + 4 * g);
+          }
+      }
       static_for<0, Plan::NOPS>([&](auto oc) __attribute__((always_inline)) {
         if constexpr (Plan::plan.bundle[decltype(oc)::value] == b) valu_op(oc);
       });
@@ -1033,21 +1009,12 @@ void bwd_dq_kernel(BwdParams p) {
       if (CAUSAL && key0 > qw + 32 * QT - 1) return;  // tile wholly above this wavefront's rows
       if (WIN && key0 + DQ_BN <= qw - W + 1) return;  // tile wholly below its rows' windows
       const bool need = (CAUSAL && (key0 + DQ_BN - 1 > qw || (WIN && key0 < qw + 32 * QT - W))) || key0 + DQ_BN > Lk;
-      if constexpr (KBIAS || DROP) {
-        if (need)
-          tile_body(key0, bufc, std::true_type{}, keepr);
-        else
-          tile_body(key0, bufc, std::false_type{}, keepr);
-      } else {
-        if (need)
-          tile_pipe(key0, bufc, std::true_type{});
-        else
-          tile_pipe(key0, bufc, std::false_type{});
-      }
-    } else if constexpr (KBIAS || DROP) {
-      tile_body(key0, bufc, std::false_type{}, keepr);
+      if (need)
+        tile_pipe(key0, bufc, std::true_type{}, keepr);
+      else
+        tile_pipe(key0, bufc, std::false_type{}, keepr);
     } else {
-      tile_pipe(key0, bufc, std::false_type{});
+      tile_pipe(key0, bufc, std::false_type{}, keepr);
     }
   };
   // The first tiles (the workgroup's diagonal ones under the causal mask, or the ragged
