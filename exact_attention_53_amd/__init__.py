@@ -177,6 +177,13 @@ def _shape(x: torch.Tensor, name: str, layout: str, B: int, NH: int, T: int, d: 
         raise ValueError(f"{name} has (B, NH, T, d) = {got}, expected {(B, NH, T, d)}")
 
 
+def _check_workspace(ws: Optional[torch.Tensor], dev: torch.device):
+    """A caller's workspace must be device memory of the call's GPU (its size is checked by
+    the library, which returns ATTN_ERR_WORKSPACE when it is too small)."""
+    if ws is not None and (ws.device != dev or not ws.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+
+
 def _on_gpu(fn: str, dev: torch.device):
     if dev.type != "cuda":
         raise ValueError(f"{fn} runs on the GPU only; got a CPU tensor")
@@ -220,8 +227,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
     _need(out, "out", dev, et)
     if return_lse and lse is None:
         lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
-        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor on the device of q")
     tensors = (q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
                v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
                lse.data_ptr() if return_lse else None)
@@ -265,14 +272,15 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: Optional[float] = None,
         _need(x, n, dev, et)
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
-    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
-        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats, on the device of q")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     need = workspace_bytes(B, NH, T, dqk, dvd, deterministic)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
         _need(x, n, dev, et)
     tensors = (q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
@@ -337,11 +345,12 @@ def fwd_blocksparse(q, k, v, block_map: torch.Tensor, causal: bool = False, scal
     _need(out, "out", dev, torch.bfloat16)
     if return_lse and lse is None:
         lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
-        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor on the device of q")
     need = int(lib.attn_fwd_blocksparse_workspace_bytes(B, NH, T, dqk, dv))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib.attn_fwd_blocksparse(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
                                         v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
@@ -370,8 +379,8 @@ def bwd_blocksparse(q, k, v, o, lse, do, block_map: torch.Tensor, causal: bool =
     msb, msh = _block_map(block_map, B, NH, T, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
-    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
-        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats, on the device of q")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -380,6 +389,7 @@ def bwd_blocksparse(q, k, v, o, lse, do, block_map: torch.Tensor, causal: bool =
     need = int(lib.attn_bwd_blocksparse_workspace_bytes(B, NH, T, dqk, dvd, int(bool(deterministic))))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib.attn_bwd_blocksparse(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
                                         v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
@@ -433,11 +443,12 @@ def fwd_keybias(q, k, v, bias: torch.Tensor, causal: bool = False, scale: Option
     _need(out, "out", dev, torch.bfloat16)
     if return_lse and lse is None:
         lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
-        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor on the device of q")
     need = int(lib.attn_fwd_keybias_workspace_bytes(B, NH, T, dqk, dv))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib.attn_fwd_keybias(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
                                     v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
@@ -475,8 +486,8 @@ def bwd_keybias(q, k, v, o, lse, do, bias: torch.Tensor, causal: bool = False, s
         dbias = None
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
-    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
-        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats, on the device of q")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -485,6 +496,7 @@ def bwd_keybias(q, k, v, o, lse, do, bias: torch.Tensor, causal: bool = False, s
     need = int(lib.attn_bwd_keybias_workspace_bytes(B, NH, T, dqk, dvd, int(bool(deterministic))))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib.attn_bwd_keybias(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
                                     v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
@@ -530,11 +542,12 @@ def fwd_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float, causa
     _need(out, "out", dev, torch.bfloat16)
     if return_lse and lse is None:
         lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
-        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor on the device of q")
     need = int(lib.attn_fwd_fp8_workspace_bytes(B, NH, T, dqk, dv))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib.attn_fwd_fp8(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
                                 v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
@@ -590,8 +603,8 @@ def fwd_dropout(q, k, v, mask: torch.Tensor, p_drop: float, causal: bool = True,
     _need(out, "out", dev, torch.bfloat16)
     if return_lse and lse is None:
         lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T):
-        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor on the device of q")
     with torch.cuda.device(dev):
         _check(lib.attn_fwd_dropout(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
                                     v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
@@ -619,8 +632,8 @@ def bwd_dropout(q, k, v, o, lse, do, mask: torch.Tensor, p_drop: float, causal: 
         raise ValueError("mask must be the uint8 buffer from dropout_mask for these sizes, on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
-    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
-        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats, on the device of q")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
@@ -629,6 +642,7 @@ def bwd_dropout(q, k, v, o, lse, do, mask: torch.Tensor, p_drop: float, causal: 
     need = workspace_bytes(B, NH, T, dqk, dvd, deterministic)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib.attn_bwd_dropout(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
                                     v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
@@ -659,8 +673,8 @@ def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, causal: bool = True, scale: Opt
         _need(x, n, dev, torch.bfloat16)
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
-    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
-        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats, on the device of q")
     with torch.cuda.device(dev):
         _check(lib.attn_bwd_noalloc(q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
                                     v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
@@ -714,6 +728,7 @@ def fwd_decode(q, k, v, seq_len_kv: Optional[torch.Tensor] = None, scale: Option
     need = int(lib.attn_fwd_decode_workspace_bytes(B, NH, Tq, Tk, dqk, dv))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib.attn_fwd_decode(_DTYPE_CODE[et], q.data_ptr(), _strides(q, layout), k.data_ptr(),
                                    _strides(k, layout), v.data_ptr(), _strides(v, layout), out.data_ptr(),
@@ -764,6 +779,7 @@ def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causa
     need = int(lib.attn_fwd_varlen_workspace_bytes(B, NH, T, dqk, dv))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     args = (q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
             v.data_ptr(), _strides(v, layout), out.data_ptr(), _strides(out, layout),
             lse.data_ptr() if return_lse else None, seq_len_q.data_ptr(), seq_len_kv.data_ptr(),
@@ -796,14 +812,15 @@ def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.T
     _lengths(seq_len_kv, "seq_len_kv", B, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
-    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T:
-        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats")
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev:
+        raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats, on the device of q")
     dq = torch.empty_like(q, memory_format=torch.contiguous_format)
     dk = torch.empty_like(k, memory_format=torch.contiguous_format)
     dv = torch.empty_like(v, memory_format=torch.contiguous_format)
     need = int(lib.attn_bwd_varlen_workspace_bytes(B, NH, T, dqk, dvd, int(bool(deterministic))))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     args = (q.data_ptr(), _strides(q, layout), k.data_ptr(), _strides(k, layout),
             v.data_ptr(), _strides(v, layout), o.data_ptr(), _strides(o, layout),
             lse.data_ptr(), do.data_ptr(), _strides(do, layout),

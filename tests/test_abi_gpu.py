@@ -56,3 +56,22 @@ def test_core_entry_points_direct(dims, T, causal, deterministic):
         torch.cuda.synchronize()
         for n, a, b in (("dq", dq, dq2), ("dk", dk, dk2), ("dv", dvv, dv2)):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"attn_bwd vs staged: {n} differs"
+
+
+def test_binding_rejects_host_lse_and_workspace():
+    """The library sees only pointers: an lse or workspace left in host memory would be
+    handed to the kernels as a device address.  The binding refuses both before any
+    launch."""
+    w = workloads.Workload("host_bufs", 1, 2, 128, 64, 64, True, 77)
+    cpu = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (cpu[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = attn.fwd(q, k, v, True, w.scale)
+    with pytest.raises(ValueError):
+        attn.bwd(q, k, v, o, lse.cpu(), do, True, w.scale)
+    with pytest.raises(ValueError):
+        attn.fwd(q, k, v, True, w.scale, lse=torch.empty(1, 2, 128, dtype=torch.float32))
+    need = attn.workspace_bytes(1, 2, 128, 64, 64, True)
+    with pytest.raises(ValueError):
+        attn.bwd(q, k, v, o, lse, do, True, w.scale, deterministic=True, workspace=torch.empty(need, dtype=torch.uint8))
+    torch.cuda.synchronize()
