@@ -390,7 +390,16 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
     }
     f32x16 s[2], dp[2];
     vec8<E> pb[4], sb[4];
-    if constexpr (MASKED) {
+    // MASKED: P = 0 for this lane's key past Lk, a query past Lq, the key past the query's
+    // diagonal or under its window; element r of tile t is query q0 + 32 t + 8 (r / 4) +
+    // 4 g + r % 4, so query - key = qk + 32 t + 8 (r / 4) + r % 4 and Lq - query =
+    // lqr - (32 t + 8 (r / 4) + r % 4)
+    const int qk = q0 + 4 * g - my_key, lqr = Lq - q0 - 4 * g;
+    const bool key_ok = my_key < Lk;
+    // d_qk = 128 runs its masked steps in the pipeline too; at d_qk = 64 (two wavefronts
+    // per SIMD, 256 registers) and 192 the pipeline's masked form spills, so their masked
+    // steps keep the plain, compiler-scheduled body
+    if constexpr (MASKED && DQK != 128) {
       // S = Q K^T and dP = dO V^T for 64 queries x this wavefront's 32 keys
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks)
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
 #pragma unroll
         for (int t = 0; t < NDK; ++t) dk[t] = mfma32(sb[m], lds_col8<E, BWD_BM>(qt, L, 16 * m, 32 * t), dk[t]);
     } else {
-      // The same work as an explicit pipeline (KvPlan): bundle i issues MFMA i, the
+      // An explicit pipeline (KvPlan): bundle i issues MFMA i, the
       // operand read of MFMA i + LA and its share of the VALU work; the compiler may
       // reorder only within a bundle.
       using Plan = KvPlan<DQK, DV>;
@@ -487,6 +496,11 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
               pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, kb2 - lsev[t][r >> 2][r & 3]));
             } else {
               pv[t][r] = exp2_fast(__builtin_fmaf(s[t][r], c, -lsev[t][r >> 2][r & 3]));
+            }
+            if constexpr (MASKED) {
+              constexpr int off = 32 * t + 8 * (r >> 2) + (r & 3);
+              const int d = qk + off;  // query - key
+              pv[t][r] = (!key_ok || off >= lqr || (CAUSAL && (d < 0 || (WIN && d >= W)))) ? 0.f : pv[t][r];
             }
           }
         } else {
