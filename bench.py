@@ -32,8 +32,9 @@ PEAK_HBM_GBS = 8000.0
 # what the same counters read for a streaming kernel of known size (`bench.py
 # --copy-calibration 1024`, 1 GiB read and 1 GiB written per launch): FETCH_SIZE read
 # 524294.5 KiB there, WRITE_SIZE 1048576 KiB.  The figures hold only for the kernel
-# sources they were taken on, identified by a hash; any change makes them null.
-TRAFFIC_SOURCES = "b771fa3d3f183725"
+# sources they were taken on, identified by a hash of their code; any change to the code
+# (not to its comments) makes them null.
+TRAFFIC_SOURCES = "7fae938459758ce8"
 TRAFFIC_KIB = {  # kernel: (FETCH_SIZE, WRITE_SIZE) per dispatch
     "attn_fwd": (1187413.9375, 133146.0),
     "bwd_preprocess": (132231.125, 4404.5625),
@@ -44,16 +45,30 @@ FETCH_SCALE = 1048576.0 / 524294.5
 WRITE_SCALE = 1048576.0 / 1048576.0
 
 
+def _code_tokens(text: str, lang: str) -> bytes:
+    """The code of a source file without its comments, as whitespace-separated tokens, so
+    that editing a comment or re-wrapping lines leaves the hash unchanged."""
+    import re
+    if lang == "c":
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+    else:  # Python: whole-line comments only (a '#' inside a string stays)
+        text = re.sub(r"(?m)^\s*#[^\n]*$", " ", text)
+    return " ".join(text.split()).encode()
+
+
 def kernel_sources_hash() -> str:
+    """Hash of the code the kernels are built from: the HIP sources and headers and the
+    build script (whose flags shape the code), comments and layout aside."""
     import glob
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_53_amd", "csrc")
-    build = os.path.join(ROOT, "exact_attention_53_amd", "_build.py")  # compile flags shape the code too
+    build = os.path.join(ROOT, "exact_attention_53_amd", "_build.py")
     for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))) + [build]:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_tokens(fh.read(), "py" if f.endswith(".py") else "c"))
     return h.hexdigest()[:16]
 
 

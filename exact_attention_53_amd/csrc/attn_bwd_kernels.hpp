@@ -578,7 +578,8 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
   };
   // The steps that touch the diagonal (the first BWD_BN / BWD_BM under the causal mask),
   // a ragged key block (all steps) or the ragged last query block carry the mask; they
-  // are peeled off the loop so that its body is one straight-line program.
+  // are peeled off the loop (their pipeline or plain body applies the mask) so that the
+  // loop's body is one straight-line program without mask code.
   constexpr auto MASK = std::true_type{};
   constexpr auto NOMASK = std::false_type{};
   constexpr auto B0 = std::integral_constant<int, 0>{};
@@ -1032,8 +1033,8 @@ void bwd_dq_kernel(BwdParams p) {
     }
   };
   // The first tiles (the workgroup's diagonal ones under the causal mask, or the ragged
-  // last key block) may carry a mask for some wavefront; they run as plain code, the
-  // rest as the pipeline.
+  // last key block) may carry a mask for some wavefront; they run as the pipeline's
+  // masked form, the rest as its unmasked form.
   constexpr auto B0 = std::integral_constant<int, 0>{};
   constexpr auto B1 = std::integral_constant<int, 1>{};
   int it = 0;
