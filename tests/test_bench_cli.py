@@ -38,3 +38,16 @@ def test_algorithmic_bytes():
     rows = 4 * 16 * 8192
     assert fwd == rows * (2 * (2 * 128 + 128) + 2 * 128 + 4)          # Q, K, V read; O, LSE written
     assert bwd == rows * (2 * (2 * 128 + 3 * 128) + 12 + 2 * (2 * 128 + 128))
+
+
+def test_sources_hash_ignores_comments_only():
+    """The traffic figures are keyed to a hash of the kernels' code: comments and line
+    layout do not change it, a change to the code does."""
+    c = "__global__ void k(float* x) {  // one\n  x[0] = 1.f;  /* two\n three */\n}\n"
+    assert bench._code_tokens(c, "c") == bench._code_tokens(
+        "__global__ void k(float* x) {\n  // a longer\n  // comment\n  x[0] = 1.f;\n}\n", "c")
+    assert bench._code_tokens(c, "c") != bench._code_tokens(c.replace("1.f", "2.f"), "c")
+    py = "FLAGS = ['-O3']  # kept\n# a comment line\nX = 1\n"
+    assert bench._code_tokens(py, "py") == bench._code_tokens("FLAGS = ['-O3']  # kept\nX = 1\n", "py")
+    assert bench._code_tokens(py, "py") != bench._code_tokens(py.replace("-O3", "-O2"), "py")
+    assert len(bench.kernel_sources_hash()) == 16
