@@ -388,6 +388,9 @@ def main():
     ap.add_argument("--dtype", choices=["bf16", "f16", "fp8"], default="bf16",
                     help="element type of Q, K, V, O and the gradients (the metric is quoted for bf16); fp8: the "
                          "e4m3 forward alone")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed (no host launch "
+                         "overhead between the kernels); reported as graph_* beside the eager figures")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB buffer before every step (evicts the 256 MB last-level cache); "
                          "the step time is then the sum of the kernel intervals, without the eviction")
@@ -601,6 +604,32 @@ def main():
             "traffic_unit": "bytes per launch",
         },
     }
+    if args.graph and not args.cold:
+        # One step (forward and the three backward stages) captured in a HIP graph on a side
+        # stream, then replayed: the same kernels, launched without the binding's host work
+        # in between, which bounds short steps (the GPT-2 shape) rather than the kernels.
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step()
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_graph = g0.elapsed_time(g1) / args.steps
+        line["graph_ms_per_step"] = round(ms_graph, 4)
+        line["graph_value"] = round((f_fwd + f_bwd) / (ms_graph * 1e-3) / 1e12, 2)
+        del graph
     if not args.cold and not args.no_extras:
         # The other dQ mode on the same inputs, a few steps: the atomic mode's extra time
         # in the key/value kernel (its partial dQ products and fp32 atomics) as a share of
