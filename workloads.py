@@ -83,6 +83,12 @@ WORKLOADS: Dict[str, Workload] = {
     # the headline shape with dropout on the attention weights, p = DROPOUT_P, the
     # generator seeded with the workload's seed, counter offset 0
     "dropout": Workload("dropout", 4, 16, 8192, 128, 128, True, 53012),
+    # tensors past 4 GiB (element offsets past 2^31, byte offsets past 2^32): many causal
+    # sequences (the batch offset grows large) ...
+    "big_batch": Workload("big_batch", 576, 16, 2048, 128, 128, True, 53013),
+    # ... and one long sequence under a sliding window (the row offset grows large; the
+    # last query block is ragged)
+    "big_rows": Workload("big_rows", 1, 16, (1 << 20) + 77, 128, 128, True, 53014, window=256),
 }
 
 DROPOUT_P = 0.1
@@ -124,6 +130,27 @@ def block_map_pairs(w: Workload, m) -> int:
 def _randn(shape, seed: int, sigma: float, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     g = torch.Generator().manual_seed(seed)
     return (torch.randn(shape, generator=g, dtype=torch.float32) * sigma).to(dtype)
+
+
+def make_device_inputs(w: Workload, device, dtype: torch.dtype = torch.bfloat16) -> Dict[str, torch.Tensor]:
+    """q, k, v, do of shape (B, T, NH, d) drawn directly in device memory, for workloads
+    too large to draw on the host: float32 standard normals from a device generator
+    (``torch.Generator(device).manual_seed(seed + k)``, k = 0, 1, 2, 3 for Q, K, V, dO),
+    times sigma, rounded to `dtype`.  A test copies the rows it checks to the host, so
+    both sides still see the very same values."""
+    B, T, NH = w.B, w.T, w.NH
+    out = {}
+    for k, (name, d, sigma) in enumerate((("q", w.d_qk, w.sigma), ("k", w.d_qk, w.sigma), ("v", w.d_v, w.sigma),
+                                          ("do", w.d_v, w.sigma_do))):
+        g = torch.Generator(device=device).manual_seed(w.seed + k)
+        x = torch.empty((B, T, NH, d), dtype=dtype, device=device)
+        flat = x.view(-1)
+        step = 1 << 28  # draw in chunks: the float32 draw is twice the size of the result
+        for i in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - i)
+            flat[i:i + n] = (torch.randn(n, generator=g, dtype=torch.float32, device=device) * sigma).to(dtype)
+        out[name] = x
+    return out
 
 
 def make_inputs(w: Workload, dtype: torch.dtype = torch.bfloat16) -> Dict[str, torch.Tensor]:
