@@ -3,9 +3,10 @@
 Both workloads are drawn in device memory (workloads.make_device_inputs); the rows a
 check needs are copied to the host for the oracle.
 
-* big_batch (B 576, NH 16, T 2048, d 128, causal; 4.5 GiB per tensor): the causal
-  kernels of the headline shape, with batch offsets past 2^32 bytes.  Whole heads of
-  the first and the last sequence are compared, in both dQ modes.
+* big_batch (NH 16, T 2048, causal; d 128 at B 576, as well as d 64 at B 1152 and
+  d (192, 128) at B 384; 4.5 GiB per q tensor): the causal kernels of each head width,
+  with batch offsets past 2^32 bytes.  Whole heads of the first and the last sequence
+  are compared, in both dQ modes.
 * big_rows (B 1, NH 16, T 2^20 + 77, d 128, 256-key sliding window; 4 GiB per tensor):
   row offsets past 2^32 bytes and a ragged last query block.  A windowed row sees only
   the 255 keys before it, so the oracle runs on a slice that starts 255 rows before the
@@ -57,13 +58,18 @@ def _check(tag, got, ref, rows=slice(None), keys=slice(None)):
     check_lse(f"{tag} lse", to_np(got["lse"])[rows], lse[rows])
 
 
+# head widths of the three kernel families; B sized so that q passes 4 GiB
+BIG_DIMS = {(64, 64): 1152, (128, 128): 576, (192, 128): 384}
+
+
 @pytest.mark.parametrize("deterministic", [False, True], ids=["atomic", "determ"])
-def test_big_batch(deterministic):
-    w = workloads.WORKLOADS["big_batch"]
+@pytest.mark.parametrize("dims", list(BIG_DIMS), ids=lambda d: f"d{d[0]}x{d[1]}")
+def test_big_batch(dims, deterministic):
+    w = workloads.WORKLOADS["big_batch"].with_(B=BIG_DIMS[dims], d_qk=dims[0], d_v=dims[1])
     assert w.B * w.T * w.NH * w.d_qk * 2 > 4 * 2**30
     if _free_gib() < _need_gib(w, deterministic):
         pytest.skip(f"needs {_need_gib(w, deterministic):.0f} GiB of free device memory")
-    say(f"case big_batch det={deterministic}: drawing inputs")
+    say(f"case big_batch B={w.B} d={dims} det={deterministic}: drawing inputs")
     gpu = workloads.make_device_inputs(w, DEV)
     say("  fwd + bwd")
     out = _run(w, gpu, deterministic)
