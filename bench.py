@@ -165,7 +165,7 @@ def sustained_clock_power(run_step, ms_step: float, dev, value: float, keep: str
     process of its own, started before the loop) records the GPU's shader clock and
     power.  Returns the means over the loop (its first second left out), the throughput of
     that loop, and the fraction of the bf16 MFMA peak at the clock observed (the spec peak
-    scaled by observed clock / 2400 MHz).  None when the driver's metrics are unreadable."""
+    scaled by observed clock / 2400 MHz).  None when the amdgpu kernel driver's metrics are unreadable."""
     import subprocess
     import tempfile
 
