@@ -570,10 +570,18 @@ def dropout_mask(p_drop: float, seed: int, offset: int, B: int, NH: int, T: int,
         raise ValueError("invalid sizes for a dropout mask")
     if out is None:
         out = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out.dtype != torch.uint8 or out.device != dev or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous uint8 buffer on {dev}")
     with torch.cuda.device(dev):
         _check(lib.attn_dropout_mask(float(p_drop), int(seed) & (2 ** 64 - 1), int(offset) & 0xFFFFFFFF, B, NH, T,
                                      int(bool(causal)), out.data_ptr(), out.numel(), _stream(dev)))
     return out
+
+
+def _dropout_mask_arg(lib, mask: torch.Tensor, B: int, NH: int, T: int, dev: torch.device):
+    if (mask.dtype != torch.uint8 or mask.device != dev or not mask.is_contiguous()
+            or mask.numel() < int(lib.attn_dropout_mask_bytes(B, NH, T))):
+        raise ValueError("mask must be the contiguous uint8 buffer from dropout_mask for these sizes, on q's device")
 
 
 def fwd_dropout(q, k, v, mask: torch.Tensor, p_drop: float, causal: bool = True, scale: Optional[float] = None,
@@ -593,8 +601,7 @@ def fwd_dropout(q, k, v, mask: torch.Tensor, p_drop: float, causal: bool = True,
     lib = load()
     for n, x in (("q", q), ("k", k), ("v", v)):
         _need(x, n, dev, torch.bfloat16)
-    if mask.dtype != torch.uint8 or mask.device != dev or mask.numel() < int(lib.attn_dropout_mask_bytes(B, NH, T)):
-        raise ValueError("mask must be the uint8 buffer from dropout_mask for these sizes, on q's device")
+    _dropout_mask_arg(lib, mask, B, NH, T, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
     if out is None:
@@ -628,8 +635,7 @@ def bwd_dropout(q, k, v, o, lse, do, mask: torch.Tensor, p_drop: float, causal: 
     lib = load()
     for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _need(x, n, dev, torch.bfloat16)
-    if mask.dtype != torch.uint8 or mask.device != dev or mask.numel() < int(lib.attn_dropout_mask_bytes(B, NH, T)):
-        raise ValueError("mask must be the uint8 buffer from dropout_mask for these sizes, on q's device")
+    _dropout_mask_arg(lib, mask, B, NH, T, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
     if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev:

@@ -58,6 +58,31 @@ def test_core_entry_points_direct(dims, T, causal, deterministic):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"attn_bwd vs staged: {n} differs"
 
 
+def test_binding_rejects_bad_dropout_buffers():
+    """The keep-bit buffer is read (and written by dropout_mask) as plain bytes from its
+    first address: a host buffer, another element type or a strided view is refused
+    before any launch."""
+    w = workloads.Workload("drop_bufs", 1, 2, 128, 64, 64, True, 78)
+    cpu = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (cpu[n].to(dev) for n in ("q", "k", "v", "do"))
+    need = int(attn.load().attn_dropout_mask_bytes(1, 2, 128))
+    for bad in (torch.empty(need, dtype=torch.uint8), torch.empty(need, dtype=torch.float32, device=dev),
+                torch.empty(2 * need, dtype=torch.uint8, device=dev)[::2]):
+        with pytest.raises(ValueError):
+            attn.dropout_mask(0.1, 1, 0, 1, 2, 128, True, device=dev, out=bad)
+    mask = attn.dropout_mask(0.1, 1, 0, 1, 2, 128, True, device=dev)
+    strided = torch.empty(2 * mask.numel(), dtype=torch.uint8, device=dev)[::2]
+    strided.copy_(mask)
+    o, lse = attn.fwd_dropout(q, k, v, mask, 0.1, True, w.scale)
+    for bad in (mask.cpu(), strided):
+        with pytest.raises(ValueError):
+            attn.fwd_dropout(q, k, v, bad, 0.1, True, w.scale)
+        with pytest.raises(ValueError):
+            attn.bwd_dropout(q, k, v, o, lse, do, bad, 0.1, True, w.scale)
+    torch.cuda.synchronize()
+
+
 def test_binding_rejects_host_lse_and_workspace():
     """The library sees only pointers: an lse or workspace left in host memory would be
     handed to the kernels as a device address.  The binding refuses both before any
