@@ -268,17 +268,21 @@ def decode_bench(args, w):
     dev = torch.device("cuda:0")
     B, T, NH = w.B, w.T, w.NH
     et = torch.bfloat16 if args.dtype == "bf16" else torch.float16
-    k = workloads._randn((B, T, NH, w.d_qk), w.seed + 1, w.sigma, et).to(dev)
-    v = workloads._randn((B, T, NH, w.d_v), w.seed + 2, w.sigma, et).to(dev)
-    q = workloads._randn((B, 1, NH, w.d_qk), w.seed + 0, w.sigma, et).to(dev)
-    o = torch.empty((B, 1, NH, w.d_v), dtype=et, device=dev)
+    k = workloads._randn((B, T, NH, w.d_qk), w.seed + 1, w.sigma, et)
+    v = workloads._randn((B, T, NH, w.d_v), w.seed + 2, w.sigma, et)
+    q = workloads._randn((B, 1, NH, w.d_qk), w.seed + 0, w.sigma, et)
+    lay = args.layout
+    if lay == "bhtd":  # head-major cache: each head's keys contiguous
+        k, v, q = (x.permute(0, 2, 1, 3).contiguous() for x in (k, v, q))
+    k, v, q = k.to(dev), v.to(dev), q.to(dev)
+    o = torch.empty((B, 1, NH, w.d_v) if lay == "bthd" else (B, NH, 1, w.d_v), dtype=et, device=dev)
     for _ in range(args.warmup):
-        attn.fwd_decode(q, k, v, None, w.scale, out=o)
+        attn.fwd_decode(q, k, v, None, w.scale, out=o, layout=lay)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        attn.fwd_decode(q, k, v, None, w.scale, out=o)
+        attn.fwd_decode(q, k, v, None, w.scale, out=o, layout=lay)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -289,7 +293,8 @@ def decode_bench(args, w):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": f"decode: B={B} NH={NH} one query row against {T} keys, d={w.d_qk}, non-causal, "
-                               f"no stats", "B": B, "NH": NH, "T_kv": T, "d": w.d_qk},
+                               f"no stats, {lay.upper()} cache", "B": B, "NH": NH, "T_kv": T, "d": w.d_qk,
+                   "layout": lay},
         "tflops": round(2.0 * (w.d_qk + w.d_v) * B * NH * T / (ms * 1e-3) / 1e12, 2),
         "roofline": {"kernel": "attn_fwd (decode)", "bound": "hbm", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
@@ -388,6 +393,9 @@ def main():
     ap.add_argument("--dtype", choices=["bf16", "f16", "fp8"], default="bf16",
                     help="element type of Q, K, V, O and the gradients (the metric is quoted for bf16); fp8: the "
                          "e4m3 forward alone")
+    ap.add_argument("--layout", choices=["bthd", "bhtd"], default="bthd",
+                    help="decode workload only: the key/value cache token-major (B, T, NH, d) or head-major "
+                         "(B, NH, T, d)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed (no host launch "
                          "overhead between the kernels); reported as graph_* beside the eager figures")
