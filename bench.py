@@ -507,7 +507,11 @@ def main():
             attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv, workspace=ws,
                      stages=stages, window=w.window, alibi=w.alibi)
 
-    def step(ev=None, mode_det=det):
+    def step(ev=None, mode_det=det, split=False):
+        """One forward and one backward.  The backward is one call, as a user makes it (at
+        d = 64 in deterministic mode the key/value and dQ work then share one launch), or,
+        with split, its three stages as three calls with events between them, for the
+        per-kernel times."""
         ws = workspace(mode_det)
         if flush is not None:
             flush.fill_(1.0)
@@ -516,6 +520,11 @@ def main():
         fwd_call()
         if ev is not None:
             ev[1].record()
+        if not split:
+            bwd_call(mode_det, ws, attn.ALL_STAGES)
+            if ev is not None:
+                ev[4].record()
+            return
         bwd_call(mode_det, ws, attn.PREPROCESS)
         if ev is not None:
             ev[2].record()
@@ -526,15 +535,16 @@ def main():
         if ev is not None:
             ev[4].record()
 
-    def timed(n, mode_det):
-        """n steps bracketed by events; returns (ms per step, per-kernel ms, wall s)."""
+    def timed(n, mode_det, split):
+        """n steps bracketed by events; returns (ms per step, ms of the forward and of the
+        backward call, or with split of the forward and each backward stage, wall s)."""
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n)]
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
         start.record()
         for i in range(n):
-            step(evs[i], mode_det)
+            step(evs[i], mode_det, split)
         end.record()
         torch.cuda.synchronize()
         t_wall = time.perf_counter() - t_wall
@@ -542,13 +552,22 @@ def main():
         def avg(a, b):
             return sum(e[a].elapsed_time(e[b]) for e in evs) / n
 
-        return start.elapsed_time(end) / n, (avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)), t_wall
+        parts = (avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)) if split else (avg(0, 1), avg(1, 4))
+        return start.elapsed_time(end) / n, parts, t_wall
+
+    def measure(n, mode_det):
+        """The timed steps (one backward call each) and, in a second loop of as many steps,
+        the per-kernel split."""
+        ms, (t_f, t_b), wall = timed(n, mode_det, False)
+        step(mode_det=mode_det, split=True)
+        _, per_kernel, _ = timed(n, mode_det, True)
+        if args.cold:  # the eviction between steps is not part of the step
+            ms = t_f + t_b
+        return ms, t_f, t_b, per_kernel, wall
 
     for _ in range(args.warmup):
         step()
-    ms_step, (t_fwd, t_pre, t_main, t_dq), t_wall = timed(args.steps, det)
-    if args.cold:  # the eviction between steps is not part of the step
-        ms_step = t_fwd + t_pre + t_main + t_dq
+    ms_step, t_fwd_call, t_bwd_call, (t_fwd, t_pre, t_main, t_dq), t_wall = measure(args.steps, det)
     f_fwd, f_bwd = flops(w)
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     # Algorithmic flops carried by each kernel (recomputation is not counted): the
@@ -593,12 +612,14 @@ def main():
             "dq_mode": args.dq_mode,
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(f_bwd / ((t_pre + t_main + t_dq) * 1e-3) / 1e12, 2),
+        "fwd_tflops": round(f_fwd / (t_fwd_call * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / (t_bwd_call * 1e-3) / 1e12, 2),
+        "fwd_ms": round(t_fwd_call, 4),
+        "bwd_ms": round(t_bwd_call, 4),
         "kernels_ms": {n: round(v["ms"], 4) for n, v in kernels.items()},
         "kernels_tflops": {n: round(v["tflops"], 1) for n, v in kernels.items() if v["flops"] > 0},
-        "alg_gbs": {"fwd": round(alg_bytes(w)[0] / (t_fwd * 1e-3) / 1e9, 1),
-                    "bwd": round(alg_bytes(w)[1] / ((t_pre + t_main + t_dq) * 1e-3) / 1e9, 1)},
+        "alg_gbs": {"fwd": round(alg_bytes(w)[0] / (t_fwd_call * 1e-3) / 1e9, 1),
+                    "bwd": round(alg_bytes(w)[1] / (t_bwd_call * 1e-3) / 1e9, 1)},
         "cache": "cold (1 GiB written before each step)" if args.cold else "warm",
         "wall_s_timed": round(t_wall, 3),
         "roofline": {
@@ -613,7 +634,7 @@ def main():
         },
     }
     if args.graph and not args.cold:
-        # One step (forward and the three backward stages) captured in a HIP graph on a side
+        # One step (the forward and the backward call) captured in a HIP graph on a side
         # stream, then replayed: the same kernels, launched without the binding's host work
         # in between, which bounds short steps (the GPT-2 shape) rather than the kernels.
         cap = torch.cuda.Stream()
@@ -644,7 +665,7 @@ def main():
         # its step, the analogue of the atomic-add share of total time.
         step(mode_det=not det)
         n_alt = max(3, min(10, args.steps))
-        ms_alt, k_alt, _ = timed(n_alt, not det)
+        ms_alt, _, _, k_alt, _ = measure(n_alt, not det)
         ms_det, ms_atom = (ms_step, ms_alt) if det else (ms_alt, ms_step)
         kv_det, kv_atom = (t_main, k_alt[2]) if det else (k_alt[2], t_main)
         line["dq_modes"] = {

@@ -25,6 +25,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 INSTANCES = [(kind, elem, dqk, dv, mask) for kind in ("kv", "dq") for elem in ("bf16", "f16")
              for dqk, dv in ((64, 64), (128, 128), (192, 128)) for mask in range(10)
              if mask < 4 or elem == "bf16"]
+# the key/value and dQ work of d = 64 in one launch (plain and causal masks)
+INSTANCES += [("kvdq", elem, 64, 64, mask) for elem in ("bf16", "f16") for mask in (0, 1)]
+INST_KIND = {"kv": 0, "dq": 1, "kvdq": 2}
 MASK_NAMES = ("full", "causal", "window", "alibi", "bsp", "bsp_causal", "kbias", "kbias_causal", "drop", "drop_causal")
 SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_plan.hip", "attn_blocksparse.hip", "attn_bias.hip",
            "attn_dropout.hip", "attn_api.cpp"]
@@ -114,7 +117,7 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
     for kind, elem, dqk, dv, mask in INSTANCES:
         obj = os.path.join(BUILD_DIR, f"attn_bwd_{kind}_{elem}_{dqk}_{dv}_{MASK_NAMES[mask]}.o")
         objs.append(obj)
-        defs = [f"-DATTN_INST_DQ={int(kind == 'dq')}", f"-DATTN_INST_ELEM={elem}", f"-DATTN_INST_DQK={dqk}",
+        defs = [f"-DATTN_INST_DQ={INST_KIND[kind]}", f"-DATTN_INST_ELEM={elem}", f"-DATTN_INST_DQK={dqk}",
                 f"-DATTN_INST_DV={dv}", f"-DATTN_INST_MASK={mask}"]
         extra = _extra_flags(kind, dqk, mask)
         cmds.append([hipcc, *FLAGS, *extra, *defs, "-c", os.path.join(CSRC, "attn_bwd_inst.hip"), "-o", obj])

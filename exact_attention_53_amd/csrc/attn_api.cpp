@@ -437,6 +437,10 @@ attn_status bwd_impl(attn53::ElemType et, const void* q, attn_strides sq, const 
     st = hip_status(attn53::launch_bwd_preprocess(p, et, d_qk, d_v, !deterministic, s));
     if (st != ATTN_OK) return st;
   }
+  if ((stages & ATTN_BWD_MAIN) && (stages & ATTN_BWD_DQ) && deterministic &&
+      attn53::kvdq_merge_ok(p, d_qk, d_v, causal != 0)) {
+    return hip_status(attn53::launch_bwd_kvdq(p, et, causal != 0, s));  // both stages in one launch
+  }
   if (stages & ATTN_BWD_MAIN) {
     st = hip_status(attn53::launch_bwd_main(p, et, d_qk, d_v, causal != 0, deterministic != 0, s));
     if (st != ATTN_OK) return st;

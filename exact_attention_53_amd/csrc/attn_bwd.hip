@@ -118,6 +118,16 @@ hipError_t launch_bwd_dq(const BwdParams& p, ElemType et, int d_qk, int d_v, boo
   return et == ELEM_F16 ? dq_t<f16>(p, d_qk, d_v, causal, s) : dq_t<bf16>(p, d_qk, d_v, causal, s);
 }
 
+bool kvdq_merge_ok(const BwdParams& p, int d_qk, int d_v, bool causal) {
+  return d_qk == 64 && d_v == 64 && mask_mode(p, causal) <= 1 && p.items_kv == nullptr && p.items_dq == nullptr &&
+         kvdq64_nkv(p) % 8 == 0;
+}
+
+hipError_t launch_bwd_kvdq(const BwdParams& p, ElemType et, bool causal, hipStream_t s) {
+  if (et == ELEM_F16) return causal ? bwd_kvdq64_t<f16, 1>(p, s) : bwd_kvdq64_t<f16, 0>(p, s);
+  return causal ? bwd_kvdq64_t<bf16, 1>(p, s) : bwd_kvdq64_t<bf16, 0>(p, s);
+}
+
 int dq_block_rows(int d_qk) {
   return d_qk == 64 ? DqShape<64>::BM : d_qk == 128 ? DqShape<128>::BM : DqShape<192>::BM;
 }

@@ -196,9 +196,11 @@ struct KvPlan {
 // workgroup visits only the query steps of its key block's live query blocks, ascending.
 // KBIAS: a per-key bias (p.kbias) on the scores; each lane's key is fixed, so the bias is
 // one register, and the lane sums dS over the queries for dbias (p.dbias_part).
+// The body takes its work item's index `bid`: the kernel below passes its workgroup index,
+// the merged d = 64 kernel further down a share of its own.
 template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool ATOMIC_DQ, bool BSP = false,
           bool KBIAS = false, bool DROP = false>
-__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 64 ? 2 : 1, DQK == 64 ? 2 : 1))) void bwd_kv_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_kv_body(const BwdParams& p, const int bid) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16;
   constexpr int NDK = DQK / 32, NDV = DV / 32;
   constexpr int NDQ = DQK / 32 / 2;  // dQ tiles per wavefront
@@ -219,17 +221,17 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
   // Lq / Lk: valid query / key rows of this batch (T, or the padded-batch lengths)
   int kb, b, h, Lq = T, Lk = T;
   if constexpr (BSP) {  // work list of (b * NH + h, key block), longest first
-    const int bhi = p.bs_kv.items[2 * blockIdx.x];
-    kb = p.bs_kv.items[2 * blockIdx.x + 1];
+    const int bhi = p.bs_kv.items[2 * bid];
+    kb = p.bs_kv.items[2 * bid + 1];
     b = bhi / p.NH;
     h = bhi % p.NH;
   } else if (p.items_kv == nullptr) {
-    const Item item = schedule(blockIdx.x, p.B * p.NH);
+    const Item item = schedule(bid, p.B * p.NH);
     kb = item.rank;  // causal: block 0 has the most query blocks -> first
     b = item.bh / p.NH;
     h = item.bh % p.NH;
   } else {
-    const ListItem it = list_item(blockIdx.x, p.NH, p.items_kv);
+    const ListItem it = list_item(bid, p.NH, p.items_kv);
     b = it.b;
     h = it.h;
     kb = it.blk;
@@ -640,6 +642,12 @@ __global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 6
   }
 }
 
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool ATOMIC_DQ, bool BSP = false,
+          bool KBIAS = false, bool DROP = false>
+__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DQK == 64 ? 2 : 1, DQK == 64 ? 2 : 1))) void bwd_kv_kernel(BwdParams p) {
+  bwd_kv_body<E, DQK, DV, CAUSAL, WIN, ALIBI, ATOMIC_DQ, BSP, KBIAS, DROP>(p, (int)blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------------
 // dQ without atomics: query-stationary, fixed key-block order
 // ---------------------------------------------------------------------------------
@@ -744,9 +752,7 @@ struct DqShape {
 // (p.drop_rows), one 64-bit word per row and key tile, applied to dP.
 template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool BSP = false, bool KBIAS = false,
           bool DROP = false>
-__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
-                                                                         DqShape<DQK>::WAVES_PER_EU)))
-void bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dq_body(const BwdParams& p, const int bid) {
   constexpr int KSQ = DQK / 16, KSV = DV / 16, NDQ = DQK / 32;
   constexpr int QT = DqShape<DQK>::QT, BM = DqShape<DQK>::BM;
   constexpr int KT_BYTES = DQ_BN * DQK * 2;
@@ -763,17 +769,17 @@ void bwd_dq_kernel(BwdParams p) {
   // Lq / Lk: valid query / key rows of this batch (T, or the padded-batch lengths)
   int qb, b, h, Lq = T, Lk = T;
   if constexpr (BSP) {  // work list of (b * NH + h, query block of BM rows), longest first
-    const int bhi = p.bs_dq.items[2 * blockIdx.x];
-    qb = p.bs_dq.items[2 * blockIdx.x + 1];
+    const int bhi = p.bs_dq.items[2 * bid];
+    qb = p.bs_dq.items[2 * bid + 1];
     b = bhi / p.NH;
     h = bhi % p.NH;
   } else if (p.items_dq == nullptr) {
-    const Item item = schedule(blockIdx.x, p.B * p.NH);
+    const Item item = schedule(bid, p.B * p.NH);
     qb = CAUSAL ? nqb - 1 - item.rank : item.rank;
     b = item.bh / p.NH;
     h = item.bh % p.NH;
   } else {
-    const ListItem it = list_item(blockIdx.x, p.NH, p.items_dq);
+    const ListItem it = list_item(bid, p.NH, p.items_dq);
     b = it.b;
     h = it.h;
     qb = it.blk;
@@ -1069,6 +1075,14 @@ void bwd_dq_kernel(BwdParams p) {
   }
 }
 
+template <class E, int DQK, int DV, bool CAUSAL, bool WIN, bool ALIBI, bool BSP = false, bool KBIAS = false,
+          bool DROP = false>
+__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(DqShape<DQK>::WAVES_PER_EU,
+                                                                         DqShape<DQK>::WAVES_PER_EU)))
+void bwd_dq_kernel(BwdParams p) {
+  bwd_dq_body<E, DQK, DV, CAUSAL, WIN, ALIBI, BSP, KBIAS, DROP>(p, (int)blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------------
 // finalize: dQ = scale * accumulator -> bf16
 // ---------------------------------------------------------------------------------
@@ -1134,6 +1148,38 @@ hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// d = 64, deterministic mode: the key/value and dQ work items in one launch
+// ---------------------------------------------------------------------------------
+// The two kernels read only the inputs and the preprocess output, so their work items
+// may run side by side.  At short sequences neither grid fills the GPU by itself (384 +
+// 384 workgroups at the GPT-2 shape against 512 resident slots) and each launch ends in a
+// tail; one launch lets the dQ items fill the slots the key/value items leave.  The first
+// nkv workgroups run the key/value items and the rest the dQ items, each set in its own
+// longest-first order; nkv is a multiple of 8, so both orders keep their XCD grouping.
+// At d = 64 both bodies run at two wavefronts per SIMD, and their LDS tiles together
+// still fit two workgroups per CU.
+template <class E, bool CAUSAL>
+__global__ __launch_bounds__(BWD_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kvdq64_kernel(BwdParams p,
+                                                                                                        int nkv) {
+  if ((int)blockIdx.x < nkv)
+    bwd_kv_body<E, 64, 64, CAUSAL, false, false, false>(p, (int)blockIdx.x);
+  else
+    bwd_dq_body<E, 64, 64, CAUSAL, false, false>(p, (int)blockIdx.x - nkv);
+}
+
+// Workgroups of the key/value and dQ launches at d = 64; the merged launch needs nkv % 8 == 0.
+inline int kvdq64_nkv(const BwdParams& p) { return (p.T + BWD_BN - 1) / BWD_BN * p.B * p.NH; }
+inline int kvdq64_ndq(const BwdParams& p) { return (p.T + DqShape<64>::BM - 1) / DqShape<64>::BM * p.B * p.NH; }
+
+template <class E, int MASK>
+hipError_t bwd_kvdq64_t(const BwdParams& p, hipStream_t s) {
+  static_assert(MASK == 0 || MASK == 1, "the merged launch serves the plain and causal masks only");
+  const int nkv = kvdq64_nkv(p);
+  hipLaunchKernelGGL((bwd_kvdq64_kernel<E, MASK == 1>), dim3(nkv + kvdq64_ndq(p)), dim3(BWD_NT), 0, s, p, nkv);
+  return hipGetLastError();
+}
+
 #define ATTN_BWD_CONFIGS(X)                                                                        \
   X(64, 64, 0) X(64, 64, 1) X(64, 64, 2) X(64, 64, 3) X(128, 128, 0) X(128, 128, 1) X(128, 128, 2) \
   X(128, 128, 3) X(192, 128, 0) X(192, 128, 1) X(192, 128, 2) X(192, 128, 3)
@@ -1149,5 +1195,9 @@ ATTN_BWD_CONFIGS(ATTN_EXTERN_BWD)
   X(128, 128, 9) X(192, 128, 8) X(192, 128, 9)
 #define ATTN_EXTERN_BWD_BF16(DQK, DV, MASK) ATTN_EXTERN_BWD_E(bf16, DQK, DV, MASK)
 ATTN_BWD_BSP_CONFIGS(ATTN_EXTERN_BWD_BF16)
+extern template hipError_t bwd_kvdq64_t<bf16, 0>(const BwdParams&, hipStream_t);
+extern template hipError_t bwd_kvdq64_t<bf16, 1>(const BwdParams&, hipStream_t);
+extern template hipError_t bwd_kvdq64_t<f16, 0>(const BwdParams&, hipStream_t);
+extern template hipError_t bwd_kvdq64_t<f16, 1>(const BwdParams&, hipStream_t);
 
 }  // namespace attn53

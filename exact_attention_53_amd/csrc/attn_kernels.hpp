@@ -146,6 +146,10 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int 
 hipError_t launch_bwd_main(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, bool deterministic,
                            hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s);
+// Deterministic mode, d = 64, plain or causal mask, dense batches: the key/value and dQ
+// kernels' work in one launch (kvdq_merge_ok says whether this configuration qualifies).
+bool kvdq_merge_ok(const BwdParams& p, int d_qk, int d_v, bool causal);
+hipError_t launch_bwd_kvdq(const BwdParams& p, ElemType et, bool causal, hipStream_t s);
 hipError_t launch_bwd_finalize(const BwdParams& p, ElemType et, int d_qk, hipStream_t s);
 hipError_t launch_plan(const PlanParams& p, hipStream_t s);
 // fp8 forward (d_qk = d_v = d in {64, 128}): the transpose of v, then the forward kernel.
