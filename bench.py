@@ -84,10 +84,13 @@ def hbm_traffic(kernel: str, w, dq_mode: str, dtype: str = "bf16"):
 
 
 def pairs_of(w):
-    """Attended (query, key) pairs over all heads (block-sparse: counted from the map)."""
+    """Attended (query, key) pairs over all heads (block-sparse: counted from the map;
+    padded batches: from each sequence's own length)."""
+    import workloads
     if w.name == "blocksparse":
-        import workloads
         return workloads.block_map_pairs(w, workloads.block_map(w))
+    if w.name == "varlen":
+        return w.NH * sum(int(n) * (int(n) + 1) // 2 if w.causal else int(n) ** 2 for n in workloads.varlen_lengths(w))
     return w.pairs()
 
 
@@ -100,7 +103,8 @@ def alg_bytes(w):
     """HBM bytes the method must move (each tensor read or written once): the forward
     reads Q, K, V and writes O and LSE; the backward reads Q, K, V, O, dO and LSE and writes
     dQ, dK, dV (D is its own intermediate: written and read once, 8 bytes per row)."""
-    rows = w.B * w.NH * w.T
+    import workloads
+    rows = w.NH * int(workloads.varlen_lengths(w).sum()) if w.name == "varlen" else w.B * w.NH * w.T
     fwd = rows * (2 * (2 * w.d_qk + w.d_v) + 2 * w.d_v + 4)
     bwd = rows * (2 * (2 * w.d_qk + 3 * w.d_v) + 4 + 8 + 2 * (2 * w.d_qk + w.d_v))
     return float(fwd), float(bwd)
@@ -116,7 +120,15 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
     from oracle import attn_ref
 
     cpu = workloads.make_inputs(w)
-    per_head_flops = sum(flops(w.with_(B=1, NH=1)))
+    lengths = workloads.varlen_lengths(w) if w.name == "varlen" else None
+
+    def head_flops(b):
+        if lengths is None:
+            return sum(flops(w.with_(B=1, NH=1)))
+        n = int(lengths[b])
+        return 2.0 * (4 * w.d_qk + 3 * w.d_v) * (n * (n + 1) // 2 if w.causal else n * n)
+
+    flops_done = 0.0
     done, t_total, heads = 0, 0.0, []
     all_heads = [(b, h) for b in range(w.B) for h in range(w.NH)]
     while done < len(all_heads) and t_total < seconds_budget * 0.5:
@@ -131,10 +143,16 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
         elif w.name == "blocksparse":
             attn_ref.attn_ref_blocksparse(cpu["q"], cpu["k"], cpu["v"], cpu["do"], workloads.block_map(w), w.causal,
                                           w.scale, heads=[hd])
+        elif lengths is not None:  # one sequence, one head, at its own length
+            b_, h_ = hd
+            sl = (slice(b_, b_ + 1), slice(None), slice(h_, h_ + 1))
+            n = lengths[b_:b_ + 1]
+            attn_ref.attn_ref_varlen(cpu["q"][sl], cpu["k"][sl], cpu["v"][sl], cpu["do"][sl], n, n, w.causal, w.scale)
         else:
             attn_ref.attn_ref_heads(cpu["q"], cpu["k"], cpu["v"], cpu["do"], w.causal, w.scale, heads=[hd],
                                     window=w.window, alibi=w.alibi)
         t_total += time.perf_counter() - t0
+        flops_done += head_flops(hd[0])
         heads.append(hd)
         done += 1
     blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
@@ -146,7 +164,7 @@ def cpu_baseline(w, seconds_budget: float = 20.0):
     except OSError:
         pass
     return {
-        "value": per_head_flops * done / t_total / 1e12,
+        "value": flops_done / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
@@ -460,6 +478,8 @@ def main():
                 nbytes = lib.attn_bwd_blocksparse_workspace_bytes(B, NH, T, w.d_qk, w.d_v, int(mode_det))
             elif w.name == "keybias":
                 nbytes = lib.attn_bwd_keybias_workspace_bytes(B, NH, T, w.d_qk, w.d_v, int(mode_det))
+            elif w.name == "varlen":
+                nbytes = lib.attn_bwd_varlen_workspace_bytes(B, NH, T, w.d_qk, w.d_v, int(mode_det))
             else:
                 nbytes = attn.workspace_bytes(B, NH, T, w.d_qk, w.d_v, mode_det)
             workspaces[mode_det] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -470,6 +490,11 @@ def main():
     bsp = w.name == "blocksparse"
     kbw = w.name == "keybias"
     drw = w.name == "dropout"
+    vl = w.name == "varlen"
+    if vl:  # per-sequence lengths on the device; the forward's work list in its own workspace
+        seqs = torch.from_numpy(workloads.varlen_lengths(w)).to(dev)
+        fws = torch.empty(max(1, attn.load().attn_fwd_varlen_workspace_bytes(B, NH, T, w.d_qk, w.d_v)),
+                          dtype=torch.uint8, device=dev)
     if drw:  # the keep bits are drawn inside every timed step (before the forward)
         dmask = attn.dropout_mask(workloads.DROPOUT_P, w.seed, 0, B, NH, T, w.causal, device=dev)
     if kbw:
@@ -490,6 +515,8 @@ def main():
             attn.fwd_keybias(q, k, v, kbias, w.causal, w.scale, out=o, lse=lse, workspace=fws)
         elif bsp:
             attn.fwd_blocksparse(q, k, v, bmap, w.causal, w.scale, out=o, lse=lse, workspace=fws)
+        elif vl:
+            attn.fwd_varlen(q, k, v, seqs, seqs, w.causal, w.scale, out=o, lse=lse, workspace=fws)
         else:
             attn.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse, window=w.window, alibi=w.alibi)
 
@@ -503,6 +530,9 @@ def main():
         elif bsp:
             attn.bwd_blocksparse(q, k, v, o, lse, do, bmap, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv,
                                  workspace=ws, stages=stages)
+        elif vl:
+            attn.bwd_varlen(q, k, v, o, lse, do, seqs, seqs, w.causal, w.scale, mode_det, workspace=ws, dq=dq, dk=dk,
+                            dv=dv, stages=stages)
         else:
             attn.bwd(q, k, v, o, lse, do, w.causal, w.scale, mode_det, dq=dq, dk=dk, dv=dv, workspace=ws,
                      stages=stages, window=w.window, alibi=w.alibi)
@@ -605,7 +635,8 @@ def main():
                         f"{f' window {w.window}' if w.window else ''}{' ALiBi' if w.alibi else ''}"
                         f"{' block-sparse map (local band of 8 blocks + block 0)' if w.name == 'blocksparse' else ''}"
                         f"{' per-head key bias with dbias' if w.name == 'keybias' else ''}"
-                        f"{f' dropout p={workloads.DROPOUT_P} (Philox keep bits drawn each step)' if w.name == 'dropout' else ''}, "
+                        f"{f' dropout p={workloads.DROPOUT_P} (Philox keep bits drawn each step)' if w.name == 'dropout' else ''}"
+                        f"{f' padded batch, sequence lengths {list(map(int, workloads.varlen_lengths(w)))}' if vl else ''}, "
                         f"{'packed QKV' if w.packed else 'BTHD'}, "
                         f"dQ mode {args.dq_mode}",
             "B": B, "NH": NH, "T": T, "d_qk": w.d_qk, "d_v": w.d_v, "causal": w.causal, "window": w.window, "alibi": w.alibi,

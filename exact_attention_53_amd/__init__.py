@@ -757,7 +757,8 @@ def _lengths(x: torch.Tensor, name: str, B: int, dev: torch.device) -> torch.Ten
 
 def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causal: bool = True,
                scale: Optional[float] = None, return_lse: bool = True, layout: str = "bthd",
-               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None):
     """Forward on padded batches: batch b uses the first seq_len_q[b] query rows and the
     first seq_len_kv[b] key/value rows (int32 device tensors of B lengths); padding rows
     of o are written as 0 and of lse as -inf.  Returns (o, lse)."""
@@ -781,7 +782,10 @@ def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causa
         shape = (B, T, NH, dv) if layout == "bthd" else (B, NH, T, dv)
         out = torch.empty(shape, dtype=et, device=dev)
     _need(out, "out", dev, et)
-    lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev) if return_lse else None
+    if return_lse and lse is None:
+        lse = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev):
+        raise ValueError("lse must be a contiguous float32 (B, NH, T) tensor on the device of q")
     need = int(lib.attn_fwd_varlen_workspace_bytes(B, NH, T, dqk, dv))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -796,18 +800,20 @@ def fwd_varlen(q, k, v, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causa
             _check(lib.attn_fwd_varlen(*args))
         else:
             _check(lib.attn_fwd_typed(_DTYPE_CODE[et], *args[:18], 0, 0, *args[18:]))
-    return out, lse
+    return out, (lse if return_lse else None)
 
 
 def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.Tensor, causal: bool = True,
                scale: Optional[float] = None, deterministic: bool = False, layout: str = "bthd",
-               workspace: Optional[torch.Tensor] = None):
+               workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None, stages: int = ALL_STAGES):
     """Backward on padded batches (see fwd_varlen).  Returns (dq, dk, dv); padding rows
-    are written as 0."""
+    are written as 0.  stages: as in bwd."""
     B, NH, T, dqk = _dims(q, layout)
     dvd = v.shape[-1]
-    for n, x, d in (("k", k, dqk), ("v", v, dvd), ("o", o, dvd), ("do", do, dvd)):
-        _shape(x, n, layout, B, NH, T, d)
+    for n, x, d in (("k", k, dqk), ("v", v, dvd), ("o", o, dvd), ("do", do, dvd), ("dq", dq, dqk), ("dk", dk, dqk),
+                    ("dv", dv, dvd)):
+        if x is not None:
+            _shape(x, n, layout, B, NH, T, d)
     dev = q.device
     _on_gpu("bwd_varlen", dev)
     lib = load()
@@ -820,9 +826,11 @@ def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.T
         scale = 1.0 / math.sqrt(dqk)
     if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * NH * T or lse.device != dev:
         raise ValueError("lse must be the forward's contiguous float32 (B, NH, T) stats, on the device of q")
-    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(x, n, dev, et)
     need = int(lib.attn_bwd_varlen_workspace_bytes(B, NH, T, dqk, dvd, int(bool(deterministic))))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -835,8 +843,8 @@ def bwd_varlen(q, k, v, o, lse, do, seq_len_q: torch.Tensor, seq_len_kv: torch.T
             B, NH, T, dqk, dvd, float(scale), int(bool(causal)), int(bool(deterministic)),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev))
     with torch.cuda.device(dev):
-        if et == torch.bfloat16:
+        if et == torch.bfloat16 and stages == ALL_STAGES:
             _check(lib.attn_bwd_varlen(*args))
         else:
-            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *args[:26], 0, 0, *args[26:], ALL_STAGES))
+            _check(lib.attn_bwd_typed(_DTYPE_CODE[et], *args[:26], 0, 0, *args[26:], int(stages)))
     return dq, dk, dv

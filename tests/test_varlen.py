@@ -172,3 +172,29 @@ def test_varlen_decode_shape(dims):
             if rows:
                 check_bf16(f"decode b={b} h={h} o", g[:rows, h], ref["o"][b, :rows, h])
         assert np.all(g[rows:] == 0), f"decode b={b}: padding rows not zero"
+
+
+@pytest.mark.parametrize("deterministic", [False, True], ids=["atomic", "determ"])
+def test_varlen_workload_full_size(deterministic):
+    """The padded-batch workload the bench times (eight sequences padded to T = 8192,
+    lengths from workloads.varlen_lengths), in the same calls, on sampled (b, h) heads:
+    the full-length sequence, the shortest and one more, each against the oracle at its
+    own length; padding rows must be zero (LSE -inf)."""
+    w = workloads.WORKLOADS["varlen"]
+    n = [int(x) for x in workloads.varlen_lengths(w)]
+    heads = sorted({(0, 0), (int(np.argmin(n)), w.NH - 1), (w.B - 1, 5)})
+    say(f"case varlen workload det={deterministic} lengths={n} heads={heads}")
+    cpu = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    gpu = {k: cpu[k].to(dev) for k in ("q", "k", "v", "do")}
+    lens = torch.tensor(n, dtype=torch.int32, device=dev)
+    got = _run(gpu, (lens, lens), w.causal, w.scale, deterministic)
+    del gpu
+    refs = {}
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        r = attn_ref.attn_ref_varlen(cpu["q"][sl], cpu["k"][sl], cpu["v"][sl], cpu["do"][sl], n[b:b + 1], n[b:b + 1],
+                                     w.causal, w.scale)
+        refs[(b, h)] = {"o": r["o"][0, :, 0], "dq": r["dq"][0, :, 0], "dk": r["dk"][0, :, 0], "dv": r["dv"][0, :, 0],
+                        "lse": r["lse"][0, 0]}
+    _compare("varlen workload", got, lambda b, h: refs[(b, h)], n, n, heads=heads)

@@ -83,6 +83,9 @@ WORKLOADS: Dict[str, Workload] = {
     # the headline shape with dropout on the attention weights, p = DROPOUT_P, the
     # generator seeded with the workload's seed, counter offset 0
     "dropout": Workload("dropout", 4, 16, 8192, 128, 128, True, 53012),
+    # padded batches: eight sequences padded to T = 8192 (the headline's width and length),
+    # each of its own length (see varlen_lengths), causal
+    "varlen": Workload("varlen", 8, 16, 8192, 128, 128, True, 53015),
     # tensors past 4 GiB (element offsets past 2^31, byte offsets past 2^32): many causal
     # sequences (the batch offset grows large) ...
     "big_batch": Workload("big_batch", 576, 16, 2048, 128, 128, True, 53013),
@@ -125,6 +128,17 @@ def block_map_pairs(w: Workload, m) -> int:
             else:
                 total += len(rows) * (k1 - k0)
     return total * w.B * w.NH
+
+
+def varlen_lengths(w: Workload):
+    """Per-sequence lengths of a padded-batch workload, int32 (B,): the first sequence is
+    full (T rows), the others uniform in [T / 8, T] from numpy's default_rng(seed)."""
+    import numpy as np
+
+    rng = np.random.default_rng(w.seed)
+    n = rng.integers(w.T // 8, w.T + 1, size=w.B).astype(np.int32)
+    n[0] = w.T
+    return n
 
 
 def _randn(shape, seed: int, sigma: float, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
