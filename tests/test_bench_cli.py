@@ -40,6 +40,23 @@ def test_algorithmic_bytes():
     assert bwd == rows * (2 * (2 * 128 + 3 * 128) + 12 + 2 * (2 * 128 + 128))
 
 
+def test_padded_batch_counts():
+    """Padded batches: seeded lengths (the first full, the others in [T/8, T], the same on
+    every call), and flops and bytes counted over each sequence's own rows only."""
+    w = workloads.WORKLOADS["varlen"]
+    n = workloads.varlen_lengths(w)
+    assert list(n) == list(workloads.varlen_lengths(w)) and len(n) == w.B
+    assert n[0] == w.T and all(w.T // 8 <= x <= w.T for x in n)
+    pairs = 0
+    for x in n:  # causal: a sequence of x rows has x (x + 1) / 2 pairs per head
+        pairs += sum(range(1, int(x) + 1))
+    assert bench.pairs_of(w) == w.NH * pairs
+    f, b = bench.flops(w)
+    assert f == 2 * 256 * w.NH * pairs and b == 2 * 640 * w.NH * pairs
+    fwd, bwd = bench.alg_bytes(w)
+    assert fwd == w.NH * int(sum(n)) * (2 * 384 + 256 + 4)
+
+
 def test_sources_hash_ignores_comments_only():
     """The traffic figures are keyed to a hash of the kernels' code: comments and line
     layout do not change it, a change to the code does."""
