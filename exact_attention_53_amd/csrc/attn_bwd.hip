@@ -118,9 +118,10 @@ hipError_t launch_bwd_dq(const BwdParams& p, ElemType et, int d_qk, int d_v, boo
   return et == ELEM_F16 ? dq_t<f16>(p, d_qk, d_v, causal, s) : dq_t<bf16>(p, d_qk, d_v, causal, s);
 }
 
+// Dense or padded batches (the two bodies walk the planner's work lists, whose sizes are
+// those of the separate launches).
 bool kvdq_merge_ok(const BwdParams& p, int d_qk, int d_v, bool causal) {
-  return d_qk == 64 && d_v == 64 && mask_mode(p, causal) <= 1 && p.items_kv == nullptr && p.items_dq == nullptr &&
-         kvdq64_nkv(p) % 8 == 0;
+  return d_qk == 64 && d_v == 64 && mask_mode(p, causal) <= 1 && kvdq64_nkv(p) % 8 == 0;
 }
 
 hipError_t launch_bwd_kvdq(const BwdParams& p, ElemType et, bool causal, hipStream_t s) {

@@ -1156,7 +1156,8 @@ hipError_t bwd_dq_t(const BwdParams& p, hipStream_t s) {
 // 384 workgroups at the GPT-2 shape against 512 resident slots) and each launch ends in a
 // tail; one launch lets the dQ items fill the slots the key/value items leave.  The first
 // nkv workgroups run the key/value items and the rest the dQ items, each set in its own
-// longest-first order; nkv is a multiple of 8, so both orders keep their XCD grouping.
+// longest-first order (padded batches: the planner's work lists); nkv is a multiple of 8,
+// so both orders keep their XCD grouping.
 // At d = 64 both bodies run at two wavefronts per SIMD, and their LDS tiles together
 // still fit two workgroups per CU.
 template <class E, bool CAUSAL>

@@ -146,8 +146,8 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, ElemType et, int d_qk, int 
 hipError_t launch_bwd_main(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, bool deterministic,
                            hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, ElemType et, int d_qk, int d_v, bool causal, hipStream_t s);
-// Deterministic mode, d = 64, plain or causal mask, dense batches: the key/value and dQ
-// kernels' work in one launch (kvdq_merge_ok says whether this configuration qualifies).
+// Deterministic mode, d = 64, plain or causal mask, dense or padded batches: the key/value
+// and dQ kernels' work in one launch (kvdq_merge_ok says whether this configuration qualifies).
 bool kvdq_merge_ok(const BwdParams& p, int d_qk, int d_v, bool causal);
 hipError_t launch_bwd_kvdq(const BwdParams& p, ElemType et, bool causal, hipStream_t s);
 hipError_t launch_bwd_finalize(const BwdParams& p, ElemType et, int d_qk, hipStream_t s);

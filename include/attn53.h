@@ -146,9 +146,9 @@ attn_status attn_bwd(const void* q, attn_strides sq,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stage bits for attn_bwd_staged; each stage is one kernel launch, except that with the
- * deterministic dQ at d_qk = d_v = 64 (plain or causal mask, dense batches, B * NH *
- * ceil(T / 128) a multiple of 8) ATTN_BWD_MAIN and ATTN_BWD_DQ requested together run as
- * one launch, with results identical to the two launches. */
+ * deterministic dQ at d_qk = d_v = 64 (plain or causal mask, dense or padded batches,
+ * B * NH * ceil(T / 128) a multiple of 8) ATTN_BWD_MAIN and ATTN_BWD_DQ requested together
+ * run as one launch, with results identical to the two launches. */
 #define ATTN_BWD_PREPROCESS 1u /* D = rowsum(dO * O); atomic mode: clear the accumulator */
 #define ATTN_BWD_MAIN 2u       /* key/value-stationary kernel: P recompute, dP, dS, dV,  */
                                /* dK; atomic mode also adds partial dQ sums atomically  */

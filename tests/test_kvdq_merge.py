@@ -1,13 +1,15 @@
 """d = 64, deterministic mode: one backward call runs the key/value and dQ work in one
 launch (when the key/value workgroups number a multiple of 8, plain or causal mask, dense
-batches).  It must equal, bit for bit, the backward run as three separate stage calls
+or padded batches).  It must equal, bit for bit, the backward run as three separate stage calls
 (preprocess, key/value kernel, dQ kernel), and match the oracle."""
 import pytest
 import torch
 
 import exact_attention_53_amd as attn
 import workloads
-from tests.gpu_cases import F16_ATOL, F16_RTOL, BF16_ATOL, BF16_RTOL, compare, gpu_inputs, oracle, say
+from oracle import attn_ref
+from tests.gpu_cases import (F16_ATOL, F16_RTOL, BF16_ATOL, BF16_RTOL, check_bf16, compare, gpu_inputs, oracle, say,
+                             to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,3 +40,34 @@ def test_one_call_equals_stage_calls(shape, causal, f16):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{n}: one call differs from the stage calls"
     got = {"o": o.cpu(), "lse": lse.cpu(), "dq": one[0].cpu(), "dk": one[1].cpu(), "dv": one[2].cpu()}
     compare(w, got, oracle(w, cpu), tol=(F16_RTOL, F16_ATOL) if f16 else (BF16_RTOL, BF16_ATOL))
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_one_call_equals_stage_calls_padded(causal):
+    """Padded batches at d = 64: the one-call backward (one launch over both work lists)
+    equals the three stage calls bit for bit, and valid rows match the oracle."""
+    B, NH, T = 4, 4, 700  # ceil(700 / 128) * 4 * 4 = 96 key/value workgroups
+    n = [700, 1, 333, 0]
+    w = workloads.Workload("kvdq_padded", B, NH, T, 64, 64, causal, 860)
+    say(f"case merged kv+dq padded lengths={n} causal={causal}")
+    cpu, gpu = gpu_inputs(w)
+    q, k, v, do = gpu["q"], gpu["k"], gpu["v"], gpu["do"]
+    lens = torch.tensor(n, dtype=torch.int32, device=q.device)
+    o, lse = attn.fwd_varlen(q, k, v, lens, lens, causal, w.scale)
+    one = attn.bwd_varlen(q, k, v, o, lse, do, lens, lens, causal, w.scale, deterministic=True)
+    ws = torch.empty(int(attn.load().attn_bwd_varlen_workspace_bytes(B, NH, T, 64, 64, 1)), dtype=torch.uint8,
+                     device=q.device)
+    dq, dk, dv = (torch.empty_like(x) for x in (q, k, v))
+    for stage in (attn.PREPROCESS, attn.MAIN, attn.DQ):
+        attn.bwd_varlen(q, k, v, o, lse, do, lens, lens, causal, w.scale, deterministic=True, workspace=ws, dq=dq,
+                        dk=dk, dv=dv, stages=stage)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), one, (dq, dk, dv)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name}: one call differs from the stage calls"
+    ref = attn_ref.attn_ref_varlen(cpu["q"], cpu["k"], cpu["v"], cpu["do"], n, n, causal, w.scale)
+    for b_ in range(B):
+        r = n[b_]
+        if r == 0:
+            continue
+        for name, x in (("o", o), ("dq", one[0]), ("dk", one[1]), ("dv", one[2])):
+            check_bf16(f"padded b={b_} {name}", to_np(x[b_, :r]), ref[name][b_, :r])
